@@ -1,0 +1,369 @@
+"""fp64 CPU oracle for the FLUX.2-style MMDiT denoiser forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run this module.  The product path
+(the HIP library and its Python binding) never imports it and shares no code with it.
+
+It is the plain definition of the forward pass, written out in float64 with numpy; the
+only library primitive used as a step is the matrix product.  There is no blocking,
+fusion or reordering beyond what the definitions state.  Inputs are the same values the
+GPU reads (bf16-rounded for bf16 workloads), converted exactly to float64.
+
+Sources ("pages") cited below:
+  [TRACE]   "FLUX.2 Klein 9B Base 宏观架构" (flux-vis shape trace of FLUX2-KLEIN-9B-BASE-FULL)
+  [DIFF]    "Diffusers 中 Flux2Transformer2DModel 全面解析：架构、配置与源码级原理" (trdm.cn)
+  [KLEIN]   "FLUX.2 [klein]" research note (zhao9797.github.io), section 模型架构
+  [SDPA]    "Transformer架构解析FLUX.2-klein-base-9b-nvfp4…" (kwkr.cn), section 2 (核心引擎：
+            自注意力机制如何工作), the scaled dot-product attention formula
+
+Readings of points the pages leave open (each also listed in the design doc):
+  * sinusoid: 128 frequencies f_k = 10000^(-k/128), layout [cos | sin], argument 1000*t
+  * MLPEmbedder: Linear(256->D), SiLU, Linear(D->D); modulation: Linear(SiLU(temb))
+  * chunk order: (shift, scale, gate) for attention then MLP; final layer (shift, scale)
+  * LayerNorm: no affine, biased variance, eps inside the square root; modulate as
+    (1 + scale) * x_hat + shift
+  * RoPE: adjacent pairs (2p, 2p+1); axis a owns dims [32a, 32a+32); pair j of an axis
+    rotates by pos * theta^(-2j/32)
+  * single block: linear1 output order [q | k | v | gate | up]; linear2 input [attn | mlp]
+  * joint sequence order: text tokens first, then image tokens
+  * no biases anywhere
+
+Parity pins for every function live in tests/test_oracle_pins.py (closed forms,
+invariants and brute force); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+from typing import Mapping, Sequence
+
+import numpy as np
+
+# Hyper-parameters fixed by the pages.
+HEAD_DIM = 128                  # [DIFF] config table: attention_head_dim 128
+EPS = 1e-6                      # [DIFF] config table: eps 1e-6 for LayerNorm / RMSNorm
+ROPE_THETA = 2000.0             # [DIFF] config table rope_theta; [KLEIN] RoPE theta=2000
+AXES_DIM = (32, 32, 32, 32)     # [DIFF] axes_dims_rope; [KLEIN] axes_dim [32,32,32,32]
+TIME_FACTOR = 1000.0            # [DIFF] 时间步缩放: forward multiplies timestep by 1000
+TEMB_CHANNELS = 256             # [DIFF] timestep_guidance_channels 256; [KLEIN] 256-dim sinusoid
+MAX_PERIOD = 10000.0            # reading: the usual sinusoid period (pages give none)
+
+
+def f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------------
+# Elementwise pieces
+# ----------------------------------------------------------------------------------
+def silu(x: np.ndarray) -> np.ndarray:
+    """x * sigmoid(x).  [DIFF] 激活函数与 FFN (SwiGLU); [KLEIN] MLPEmbedder."""
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y = x W^T with W stored [out, in] (bias-free linear layer)."""
+    return np.matmul(x, w.T)
+
+
+# ----------------------------------------------------------------------------------
+# Conditioning: timestep embedding and modulation
+# ----------------------------------------------------------------------------------
+def timestep_embedding(t) -> np.ndarray:
+    """256-channel sinusoid of 1000*t.  [DIFF] 时间步缩放; [KLEIN] 条件注入.
+
+    t: [B] floats in [0, 1] (the pipeline passes t/1000 and the model multiplies by
+    1000, so the model sees tau = 1000 t).  Returns [B, 256] = [cos(tau f) | sin(tau f)]
+    with f_k = MAX_PERIOD^(-k/128), k = 0..127.
+    """
+    tau = TIME_FACTOR * f64(t).reshape(-1)
+    half = TEMB_CHANNELS // 2
+    k = np.arange(half, dtype=np.float64)
+    freqs = MAX_PERIOD ** (-k / half)
+    arg = tau[:, None] * freqs[None, :]
+    return np.concatenate([np.cos(arg), np.sin(arg)], axis=1)
+
+
+def mlp_embedder(e: np.ndarray, w1: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """temb = W2 silu(W1 e).  [KLEIN] 条件注入 (sinusoid -> MLPEmbedder)."""
+    return linear(silu(linear(e, w1)), w2)
+
+
+def modulation(temb: np.ndarray, w_mod: np.ndarray, n_chunks: int) -> list:
+    """Modulation vectors m = W_mod silu(temb), split into n_chunks [B, D] pieces.
+
+    [DIFF] 双流块: each stream has shift/scale/gate for attention and for the MLP
+    (Flux2Modulation.split(temb_mod, 2)); 单流块: one set (mod_param_sets = 1).
+    """
+    m = linear(silu(temb), w_mod)
+    return np.split(m, n_chunks, axis=-1)
+
+
+def conditioning(t, w: Mapping) -> np.ndarray:
+    return mlp_embedder(timestep_embedding(t), f64(w["temb.w1"]), f64(w["temb.w2"]))
+
+
+# ----------------------------------------------------------------------------------
+# Normalisations
+# ----------------------------------------------------------------------------------
+def layernorm_modulate(x: np.ndarray, shift: np.ndarray, scale: np.ndarray,
+                       eps: float = EPS) -> np.ndarray:
+    """(1 + scale) * (x - mean) / sqrt(var + eps) + shift over the last axis.
+
+    [DIFF] 双流块 / 单流块 (AdaLN modulation of the pre-norm), config eps 1e-6.
+    x: [B, N, D]; shift, scale: [B, D].  Biased variance, no affine parameters.
+    """
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    xhat = (x - mu) / np.sqrt(var + eps)
+    return (1.0 + scale[:, None, :]) * xhat + shift[:, None, :]
+
+
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float = EPS) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * gamma over the last axis (one head's 128 dims).
+
+    [DIFF] 双流块 (norm_q / norm_k after projection); 并行化支持 (QK-Norm acts on the
+    full head_dim).
+    """
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * gamma
+
+
+# ----------------------------------------------------------------------------------
+# Rotary position embedding over 4 id axes
+# ----------------------------------------------------------------------------------
+def _ids2d(ids) -> np.ndarray:
+    """[DIFF] 位置 id 的维度: 2-D ids are used as is, 3-D ids take [0]."""
+    a = np.asarray(ids)
+    if a.ndim == 3:
+        a = a[0]
+    if a.ndim != 2 or a.shape[1] != len(AXES_DIM):
+        raise ValueError(f"ids must be [N, {len(AXES_DIM)}], got {a.shape}")
+    return a
+
+
+def rope_positions(txt_ids, img_ids) -> np.ndarray:
+    """Integer position of every rotation pair: [L, 64] int64.
+
+    The joint ids are cat(txt_ids, img_ids) (text first); pair p belongs to the axis
+    whose dims contain 2p, and takes that axis' id.  [DIFF] 位置 id 的维度 (per-axis
+    1-D RoPE, concatenated); [KLEIN] axes_dim [32,32,32,32].
+    """
+    ids = np.concatenate([_ids2d(txt_ids), _ids2d(img_ids)], axis=0).astype(np.int64)
+    cols = []
+    for a, d in enumerate(AXES_DIM):
+        cols.extend([a] * (d // 2))
+    return ids[:, np.array(cols, dtype=np.int64)]
+
+
+def rope_frequencies() -> np.ndarray:
+    """omega for each of the 64 pairs: axis-local pair j of an axis with d dims has
+    omega = theta^(-2j/d).  [DIFF] rope_theta 2000; [KLEIN] RoPE theta=2000."""
+    out = []
+    for d in AXES_DIM:
+        j = np.arange(d // 2, dtype=np.float64)
+        out.append(ROPE_THETA ** (-2.0 * j / d))
+    return np.concatenate(out)
+
+
+def apply_rope(x: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """Rotate adjacent pairs (2p, 2p+1) of each head by phi = pos[:, p] * omega_p.
+
+    x: [B, L, h, 128]; pos: [L, 64] integer.  (x_{2p}, x_{2p+1}) ->
+    (x_{2p} cos phi - x_{2p+1} sin phi, x_{2p} sin phi + x_{2p+1} cos phi).
+    """
+    phi = pos.astype(np.float64) * rope_frequencies()[None, :]     # [L, 64]
+    c = np.cos(phi)[None, :, None, :]
+    s = np.sin(phi)[None, :, None, :]
+    xe = x[..., 0::2]
+    xo = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# Attention
+# ----------------------------------------------------------------------------------
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Exact max-subtracted softmax along the last axis."""
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def attention_weights(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """softmax(q k^T / sqrt(d_k)) for one head: q [Lq, d], k [Lk, d] -> [Lq, Lk].
+
+    [SDPA] the scaled dot-product attention formula (scores scaled by 1/sqrt(d_k),
+    softmax over the key axis)."""
+    return softmax_rows(np.matmul(q, k.T) / np.sqrt(q.shape[-1]))
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Multi-head attention over the full joint sequence, no mask.
+
+    q, k, v: [B, L, h, d] -> [B, L, h*d] (heads concatenated in head order).
+    [TRACE] Joint multi-head attention (separate QKV, shared attention); [SDPA].
+    """
+    B, L, h, d = q.shape
+    out = np.empty((B, L, h, d), dtype=np.float64)
+    for b in range(B):
+        for head in range(h):
+            p = attention_weights(q[b, :, head, :], k[b, :, head, :])
+            out[b, :, head, :] = np.matmul(p, v[b, :, head, :])
+    return out.reshape(B, L, h * d)
+
+
+def swiglu(u: np.ndarray) -> np.ndarray:
+    """silu(gate) * up with u = [gate | up] along the last axis.
+
+    [DIFF] 激活函数与 FFN: the gate linear is fused into the preceding linear
+    (linear_in -> 2x width), SwiGLU halves it, then linear_out."""
+    H = u.shape[-1] // 2
+    return silu(u[..., :H]) * u[..., H:]
+
+
+def _heads(x: np.ndarray) -> np.ndarray:
+    B, N, D = x.shape
+    return x.reshape(B, N, D // HEAD_DIM, HEAD_DIM)
+
+
+# ----------------------------------------------------------------------------------
+# Blocks
+# ----------------------------------------------------------------------------------
+def double_block_mods(t, w: Mapping) -> dict:
+    temb = conditioning(t, w)
+    return {"img": modulation(temb, f64(w["mod_img"]), 6),
+            "txt": modulation(temb, f64(w["mod_txt"]), 6)}
+
+
+def double_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: dict | None = None):
+    """Double-stream block.  Returns (img_out, txt_out), float64.
+
+    [TRACE] section 4 (Double-stream block: modulate image + text streams, joint
+    multi-head attention with separate QKV, per-stream MLP, residual update);
+    [DIFF] 双流块 Flux2TransformerBlock.
+    img: [B, N_img, D]; txt: [B, N_txt, D]; w keys "img.qkv", "img.out", "img.mlp_in",
+    "img.mlp_out", "img.q_norm", "img.k_norm" and the same for "txt."; mods: per stream
+    the six [B, D] chunks (shift1, scale1, gate1, shift2, scale2, gate2), computed from
+    t with "temb.*", "mod_img", "mod_txt" when not given.
+    """
+    streams = {"txt": f64(txt), "img": f64(img)}
+    if mods is None:
+        mods = double_block_mods(t, w)
+    qs, ks, vs = {}, {}, {}
+    for s in ("txt", "img"):
+        shift1, scale1 = mods[s][0], mods[s][1]
+        a = layernorm_modulate(streams[s], shift1, scale1)
+        q, k, v = np.split(linear(a, f64(w[f"{s}.qkv"])), 3, axis=-1)
+        qs[s] = rms_norm(_heads(q), f64(w[f"{s}.q_norm"]))
+        ks[s] = rms_norm(_heads(k), f64(w[f"{s}.k_norm"]))
+        vs[s] = _heads(v)
+    pos = rope_positions(txt_ids, img_ids)
+    q = apply_rope(np.concatenate([qs["txt"], qs["img"]], axis=1), pos)
+    k = apply_rope(np.concatenate([ks["txt"], ks["img"]], axis=1), pos)
+    v = np.concatenate([vs["txt"], vs["img"]], axis=1)
+    o = attention(q, k, v)
+    n_txt = streams["txt"].shape[1]
+    o_s = {"txt": o[:, :n_txt], "img": o[:, n_txt:]}
+    out = {}
+    for s in ("txt", "img"):
+        _, _, gate1, shift2, scale2, gate2 = mods[s]
+        x = streams[s] + gate1[:, None, :] * linear(o_s[s], f64(w[f"{s}.out"]))
+        u = linear(layernorm_modulate(x, shift2, scale2), f64(w[f"{s}.mlp_in"]))
+        x = x + gate2[:, None, :] * linear(swiglu(u), f64(w[f"{s}.mlp_out"]))
+        out[s] = x
+    return out["img"], out["txt"]
+
+
+def single_block_mods(t, w: Mapping) -> list:
+    return modulation(conditioning(t, w), f64(w["mod"]), 3)
+
+
+def single_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: Sequence | None = None):
+    """Single-stream (parallel) block.  Returns (img_out, txt_out), float64.
+
+    [TRACE] section 4 (merge image + text sequence, attention + gated MLP);
+    [DIFF] 单流块 Flux2SingleTransformerBlock: cat the streams, one modulation set,
+    fused to_qkv_mlp_proj (D -> 3D + 2H), attention and SwiGLU in parallel, fused
+    to_out ((D + H) -> D), gated residual.
+    w keys "linear1" [3D+2H, D], "linear2" [D, D+H], "q_norm", "k_norm" (and "temb.*",
+    "mod" when mods is not given); mods = (shift, scale, gate), each [B, D].
+    """
+    txt = f64(txt)
+    img = f64(img)
+    n_txt = txt.shape[1]
+    x = np.concatenate([txt, img], axis=1)
+    D = x.shape[-1]
+    if mods is None:
+        mods = single_block_mods(t, w)
+    shift, scale, gate = mods
+    y = linear(layernorm_modulate(x, shift, scale), f64(w["linear1"]))
+    q, k, v, u = y[..., :D], y[..., D:2 * D], y[..., 2 * D:3 * D], y[..., 3 * D:]
+    pos = rope_positions(txt_ids, img_ids)
+    q = apply_rope(rms_norm(_heads(q), f64(w["q_norm"])), pos)
+    k = apply_rope(rms_norm(_heads(k), f64(w["k_norm"])), pos)
+    o = attention(q, k, _heads(v))
+    x = x + gate[:, None, :] * linear(np.concatenate([o, swiglu(u)], axis=-1),
+                                      f64(w["linear2"]))
+    return x[:, n_txt:], x[:, :n_txt]
+
+
+# ----------------------------------------------------------------------------------
+# Denoiser step
+# ----------------------------------------------------------------------------------
+class _Prefixed(Mapping):
+    """Read-only view of the keys of `w` that start with `prefix` (prefix removed)."""
+
+    def __init__(self, w: Mapping, prefix: str):
+        self._w, self._p = w, prefix
+
+    def __getitem__(self, k):
+        return self._w[self._p + k]
+
+    def __iter__(self):
+        return (k[len(self._p):] for k in self._w if k.startswith(self._p))
+
+    def __len__(self):
+        return sum(1 for _ in self)
+
+
+def step_mods(t, w: Mapping) -> dict:
+    """Model-level modulation shared by all blocks of a kind.
+
+    [DIFF] 双流块 (temb_mod_img / temb_mod_txt are passed into every double block);
+    单流块 (mod_param_sets = 1, declared at model level)."""
+    temb = conditioning(t, w)
+    return {
+        "double": {"img": modulation(temb, f64(w["mod_dimg"]), 6),
+                   "txt": modulation(temb, f64(w["mod_dtxt"]), 6)},
+        "single": modulation(temb, f64(w["mod_single"]), 3),
+        "final": modulation(temb, f64(w["mod_final"]), 2),
+    }
+
+
+def denoiser_step(x, ctx, t, w: Mapping, img_ids, txt_ids, n_double: int, n_single: int,
+                  on_block=None):
+    """One denoiser forward: [B, N_img, in_ch] -> [B, N_img, in_ch], float64.
+
+    [TRACE] section 3 (packed image tokens width 128 -> hidden; text condition joint dim;
+    Double-stream block x8; Single-stream block x24; Project / Unpack keeping the noisy
+    image tokens -> [1, 4096, 128]); [DIFF] 前向传播输入输出约定.
+    Block weights are read as "double.{i}.<key>" and "single.{i}.<key>" so `w` may be a
+    lazy mapping that materialises one block at a time.  `on_block(kind, i)` is called
+    after each block (progress reporting).
+    """
+    mods = step_mods(t, w)
+    img = linear(f64(x), f64(w["img_in"]))
+    txt = linear(f64(ctx), f64(w["txt_in"]))
+    for i in range(n_double):
+        img, txt = double_block(img, txt, None, _Prefixed(w, f"double.{i}."),
+                                img_ids, txt_ids, mods=mods["double"])
+        if on_block:
+            on_block("double", i)
+    for i in range(n_single):
+        img, txt = single_block(img, txt, None, _Prefixed(w, f"single.{i}."),
+                                img_ids, txt_ids, mods=mods["single"])
+        if on_block:
+            on_block("single", i)
+    shift_f, scale_f = mods["final"]
+    return linear(layernorm_modulate(img, shift_f, scale_f), f64(w["proj_out"]))

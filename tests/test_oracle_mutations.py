@@ -1,0 +1,156 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+Every mutation replaces one oracle function with a subtly wrong variant for the duration
+of one check; the pins of tests/test_oracle_pins.py are then run and at least one of
+them must fail.  This shows the pins are strong enough that the oracle cannot be wrong
+in these ways and still pass.
+"""
+import inspect
+
+import numpy as np
+import pytest
+
+import tests.test_oracle_pins as pins
+from oracle import flux_oracle as O
+
+PIN_FUNCS = [f for n, f in inspect.getmembers(pins, inspect.isfunction)
+             if n.startswith("test_") and "manifest" not in n]
+
+
+def _mut_rope_sign(x, pos):
+    phi = pos.astype(np.float64) * O.rope_frequencies()[None, :]
+    c, s = np.cos(phi)[None, :, None, :], np.sin(phi)[None, :, None, :]
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c + x[..., 1::2] * s
+    out[..., 1::2] = -x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
+
+def _mut_rope_halves(x, pos):
+    # rotate (i, i + 64) pairs instead of adjacent pairs
+    phi = pos.astype(np.float64) * O.rope_frequencies()[None, :]
+    c, s = np.cos(phi)[None, :, None, :], np.sin(phi)[None, :, None, :]
+    a, b = x[..., :64], x[..., 64:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def _mut_freq():
+    return np.concatenate([O.ROPE_THETA ** (-np.arange(d // 2) / d) for d in O.AXES_DIM])
+
+
+def _mut_positions(txt_ids, img_ids):
+    return _orig["rope_positions"](img_ids, txt_ids) if len(txt_ids) == len(img_ids) else \
+        np.concatenate([O._ids2d(img_ids), O._ids2d(txt_ids)])[:, np.repeat(np.arange(4), 16)]
+
+
+def _mut_ln_unbiased(x, shift, scale, eps=O.EPS):
+    mu = x.mean(-1, keepdims=True)
+    var = ((x - mu) ** 2).sum(-1, keepdims=True) / max(x.shape[-1] - 1, 1)
+    return (1 + scale[:, None, :]) * (x - mu) / np.sqrt(var + eps) + shift[:, None, :]
+
+
+def _mut_ln_eps_out(x, shift, scale, eps=O.EPS):
+    mu = x.mean(-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(-1, keepdims=True)
+    return (1 + scale[:, None, :]) * (x - mu) / (np.sqrt(var) + eps) + shift[:, None, :]
+
+
+def _mut_ln_no_one(x, shift, scale, eps=O.EPS):
+    mu = x.mean(-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(-1, keepdims=True)
+    return scale[:, None, :] * (x - mu) / np.sqrt(var + eps) + shift[:, None, :]
+
+
+def _mut_rms_sum(x, gamma, eps=O.EPS):
+    return x / np.sqrt((x * x).sum(-1, keepdims=True) + eps) * gamma
+
+
+def _mut_attn_scale(q, k):
+    return O.softmax_rows(q @ k.T / q.shape[-1])
+
+
+def _mut_attn_transposed(q, k):
+    s = q @ k.T / np.sqrt(q.shape[-1])
+    e = np.exp(s - s.max(0, keepdims=True))
+    return e / e.sum(0, keepdims=True)
+
+
+def _mut_swiglu(u):
+    H = u.shape[-1] // 2
+    return O.silu(u[..., H:]) * u[..., :H]
+
+
+def _mut_temb_sin_cos(t):
+    e = _orig["timestep_embedding"](t)
+    return np.concatenate([e[:, 128:], e[:, :128]], axis=1)
+
+
+def _mut_temb_no_scale(t):
+    return _orig["timestep_embedding"](np.asarray(t, dtype=np.float64) / 1000.0)
+
+
+def _mut_silu(x):
+    return x / (1.0 + np.exp(x))
+
+
+def _mut_mod_reversed(temb, w_mod, n):
+    return _orig["modulation"](temb, w_mod, n)[::-1]
+
+
+def _mut_single_qk_swap(img, txt, t, w, img_ids, txt_ids, mods=None):
+    D = np.asarray(txt).shape[-1]
+    w2 = dict(w)
+    l1 = np.asarray(w["linear1"], dtype=np.float64).copy()
+    l1[:D], l1[D:2 * D] = l1[D:2 * D].copy(), l1[:D].copy()
+    w2["linear1"] = l1
+    return _orig["single_block"](img, txt, t, w2, img_ids, txt_ids, mods)
+
+
+def _mut_single_concat(img, txt, t, w, img_ids, txt_ids, mods=None):
+    D = np.asarray(txt).shape[-1]
+    w2 = dict(w)
+    l2 = np.asarray(w["linear2"], dtype=np.float64)
+    w2["linear2"] = np.concatenate([l2[:, -D:], l2[:, :-D]], axis=1)
+    return _orig["single_block"](img, txt, t, w2, img_ids, txt_ids, mods)
+
+
+_orig = {}
+
+MUTATIONS = {
+    "rope_rotation_sign": ("apply_rope", _mut_rope_sign),
+    "rope_half_split_pairs": ("apply_rope", _mut_rope_halves),
+    "rope_frequency_exponent": ("rope_frequencies", _mut_freq),
+    "rope_image_ids_first": ("rope_positions", _mut_positions),
+    "layernorm_unbiased_variance": ("layernorm_modulate", _mut_ln_unbiased),
+    "layernorm_eps_outside_root": ("layernorm_modulate", _mut_ln_eps_out),
+    "modulate_without_one_plus": ("layernorm_modulate", _mut_ln_no_one),
+    "rmsnorm_sum_not_mean": ("rms_norm", _mut_rms_sum),
+    "attention_scale_1_over_d": ("attention_weights", _mut_attn_scale),
+    "softmax_over_query_axis": ("attention_weights", _mut_attn_transposed),
+    "swiglu_halves_swapped": ("swiglu", _mut_swiglu),
+    "sinusoid_sin_first": ("timestep_embedding", _mut_temb_sin_cos),
+    "sinusoid_missing_x1000": ("timestep_embedding", _mut_temb_no_scale),
+    "silu_sign": ("silu", _mut_silu),
+    "modulation_chunks_reversed": ("modulation", _mut_mod_reversed),
+    "single_q_k_split_swapped": ("single_block", _mut_single_qk_swap),
+    "single_concat_mlp_first": ("single_block", _mut_single_concat),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    _orig.clear()
+    _orig.update({k: getattr(O, k) for k in ("rope_positions", "timestep_embedding",
+                                             "modulation", "single_block")})
+    monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for f in PIN_FUNCS:
+        try:
+            with np.errstate(all="ignore"):
+                f()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(f.__name__)
+        if failed:
+            break
+    assert failed, f"no pin caught mutation {name}"

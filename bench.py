@@ -1,0 +1,267 @@
+"""Benchmark: one Klein-9B-shaped 1024^2 denoiser step (8 double + 24 single blocks) on one
+MI355X through the C ABI.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Prints ONE JSON line: step throughput (algorithmic TFLOP/s, whole step), ms per step, the
+roofline of the dominant kernel (timed live with HIP events on the stream it runs on), and
+the fp64 oracle's throughput on a bounded sample of the same workload on the host cores.
+Inputs are synthetic (seeded N(0, 0.02) weights, N(0, 1) activations) and already resident
+in HBM when the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+METRIC = "Klein-9B 1024² denoiser step ms + TFLOP/s (% of bf16 MFMA peak)"
+
+
+# ------------------------------------------------------------------------------------
+# algorithmic FLOPs (2 M N K per linear, 4 L^2 D per attention)
+# ------------------------------------------------------------------------------------
+def block_flops(kind: str, D: int, H: int, n_img: int, n_txt: int, B: int = 1) -> float:
+    L = n_img + n_txt
+    attn = 4.0 * L * L * D * B
+    if kind == "double":
+        per_tok = 2.0 * (3 * D * D + D * D + 2 * H * D + H * D)
+        return per_tok * L * B + attn
+    per_tok = 2.0 * ((3 * D + 2 * H) * D + (D + H) * D)
+    return per_tok * L * B + attn
+
+
+def step_flops(wl) -> float:
+    D, H, B = wl.dim, wl.mlp_hidden, wl.batch
+    f = wl.n_double * block_flops("double", D, H, wl.n_img, wl.n_txt, B)
+    f += wl.n_single * block_flops("single", D, H, wl.n_img, wl.n_txt, B)
+    f += 2.0 * B * (wl.n_img * wl.in_channels * D + wl.n_txt * wl.context_dim * D)   # stems
+    f += 2.0 * B * wl.n_img * D * wl.in_channels                                      # proj_out
+    f += 2.0 * B * (256 * D + D * D + 17 * D * D)                                     # temb + mods
+    return f
+
+
+# ------------------------------------------------------------------------------------
+# device-resident synthetic weights (seeded, generated on the GPU for speed)
+# ------------------------------------------------------------------------------------
+def device_weights(specs: dict, seed: int, dtype):
+    import torch
+    g = torch.Generator(device="cuda")
+    out = {}
+    for i, (name, (shape, kind)) in enumerate(sorted(specs.items())):
+        g.manual_seed(seed * 100003 + i)
+        if kind == "g":
+            out[name] = 1.0 + 0.02 * torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+        else:
+            out[name] = (0.02 * torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)).to(dtype)
+    return out
+
+
+class Events:
+    """HIP events on a given stream."""
+
+    def __init__(self, stream):
+        import torch
+        self.stream = stream
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record(self.stream)
+
+    def stop_ms(self):
+        import torch
+        self.b.record(self.stream)
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+# ------------------------------------------------------------------------------------
+# dominant kernel: the bf16 MFMA GEMM with the fused SwiGLU epilogue, at the single-block
+# MLP-in shape (the largest launch of the step), launched exactly as the step launches it
+# ------------------------------------------------------------------------------------
+def dominant_kernel(F, wl, reps: int = 20):
+    import torch
+    D, H, L = wl.dim, wl.mlp_hidden, wl.seq
+    m, n, k = wl.batch * L, 2 * H, D
+    x = (torch.randn((m, k), device="cuda")).to(torch.bfloat16)
+    w = (0.02 * torch.randn((n, k), device="cuda")).to(torch.bfloat16)
+    y = torch.empty((m, D + H), device="cuda", dtype=torch.bfloat16)
+    cfg = F.make_cfg(D, wl.heads, H)
+    s = torch.cuda.current_stream()
+    call = lambda: F.flux_linear(cfg, F.FLUX_EPI_SWIGLU, m, n, k, x, k, w, k, y[:, D:], D + H, 0,
+                                 stream=s)
+    for _ in range(3):
+        call()
+    ev = Events(s)
+    ev.start()
+    for _ in range(reps):
+        call()
+    ms = ev.stop_ms() / reps
+    flops = 2.0 * m * n * k
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {
+        "kernel": "gemm_bf16_kernel<EpiSwiGLU> (single-block linear1 MLP part)",
+        "shape": [m, n, k],
+        "bound": "mfma",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": None,
+        "avg_launch_us": round(ms * 1e3, 1),
+        "algorithmic_flops_per_launch": flops,
+    }
+
+
+# ------------------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on one double block and one single block of the workload
+# ------------------------------------------------------------------------------------
+def cpu_baseline(wl, flops_step: float):
+    import numpy as np
+    import flux_synth as fs
+    from oracle import flux_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("internal_api") == "openblas"] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    D, H = wl.dim, wl.mlp_hidden
+    times = {}
+    for kind in ("double", "single"):
+        inp = fs.block_inputs(fs.workload(wl.name, kind=kind), kind=kind)
+        fn = O.double_block if kind == "double" else O.single_block
+        t0 = time.perf_counter()
+        fn(inp["img"], inp["txt"], inp["t"], inp["weights"], inp["img_ids"], inp["txt_ids"])
+        times[kind] = time.perf_counter() - t0
+        del inp
+    est = wl.n_double * times["double"] + wl.n_single * times["single"]
+    sample_flops = block_flops("double", D, H, wl.n_img, wl.n_txt) + \
+        block_flops("single", D, H, wl.n_img, wl.n_txt)
+    return {
+        "value": round(flops_step / est / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"one double block ({times['double']:.1f} s) + one single block "
+                   f"({times['single']:.1f} s) of the same workload in fp64 numpy; step time "
+                   f"estimated as {wl.n_double} x double + {wl.n_single} x single = {est:.1f} s "
+                   f"(sample {sample_flops / 1e12:.2f} TFLOP)"),
+        "est_step_s": round(est, 2),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="klein9b_step_1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "path is not built", file=sys.stderr)
+        return 2
+
+    import torch
+    import flux_synth as fs
+    from diffusion_transformer_mmdit_amd import flux as F
+
+    F.lib()
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        return 1
+    wl = fs.workload(args.workload)
+    assert wl.kind == "step"
+    dtype = torch.bfloat16
+    print(f"[bench] {wl.name}: generating {fs.param_count(fs.step_weight_specs(wl)) / 1e9:.3f} B "
+          "params on device", file=sys.stderr, flush=True)
+    w = device_weights(fs.step_weight_specs(wl), wl.seed, dtype)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed)
+    x = torch.randn((wl.batch, wl.n_img, wl.in_channels), generator=g, device="cuda").to(dtype)
+    ctx = torch.randn((wl.batch, wl.n_txt, wl.context_dim), generator=g, device="cuda").to(dtype)
+    t = torch.rand((wl.batch,), generator=g, device="cuda")
+    img_ids = torch.from_numpy(fs.image_ids(wl.n_img)).cuda()
+    txt_ids = torch.from_numpy(fs.text_ids(wl.n_txt)).cuda()
+    cfg = F.make_cfg(wl.dim, wl.heads, wl.mlp_hidden, in_channels=wl.in_channels,
+                     context_dim=wl.context_dim, n_double=wl.n_double, n_single=wl.n_single)
+    mw = F.ModelWeights(w, wl.n_double, wl.n_single)
+    out = torch.empty((wl.batch, wl.n_img, wl.in_channels), device="cuda", dtype=torch.float32)
+    nbytes = F.flux_denoiser_step_workspace_size(cfg, wl.batch, wl.n_img, wl.n_txt)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream()
+
+    def step():
+        F.flux_denoiser_step(cfg, mw, t, None, wl.batch, wl.n_img, wl.n_txt, x, ctx, img_ids,
+                             txt_ids, out, ws, nbytes, s)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    ev = Events(s)
+    torch.cuda.synchronize()
+    ev.start()
+    for _ in range(args.steps):
+        step()
+    total_ms = ev.stop_ms()
+    torch.cuda.synchronize()
+    ms = total_ms / args.steps
+    flops = step_flops(wl)
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] {ms:.2f} ms/step, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if not torch.isfinite(out).all():
+        print("[bench] non-finite output", file=sys.stderr)
+        return 1
+
+    roof = dominant_kernel(F, wl)
+    print(f"[bench] dominant kernel {roof['achieved']} TFLOP/s", file=sys.stderr, flush=True)
+    del w, mw, ws
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on one double + one single block", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(wl, flops)
+
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations, resident in HBM)",
+        "config": {"workload": wl.name, "dim": wl.dim, "heads": wl.heads,
+                   "mlp_hidden": wl.mlp_hidden, "n_img": wl.n_img, "n_txt": wl.n_txt,
+                   "in_channels": wl.in_channels, "context_dim": wl.context_dim,
+                   "n_double": wl.n_double, "n_single": wl.n_single, "global_batch": wl.batch,
+                   "seq_len": wl.seq, "algorithmic_tflop_per_step": round(flops / 1e12, 3),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

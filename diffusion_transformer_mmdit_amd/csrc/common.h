@@ -1,0 +1,66 @@
+// Shared device helpers for the gfx950 kernels of libflux.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define FLUX_DEV __device__ __forceinline__
+
+// ---- scalar conversions -------------------------------------------------------------
+FLUX_DEV float to_f32(float x) { return x; }
+FLUX_DEV float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <class T>
+FLUX_DEV T from_f32(float x);
+template <>
+FLUX_DEV float from_f32<float>(float x) { return x; }
+template <>
+FLUX_DEV bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }  // RNE
+
+// ---- 16-byte vector loads / stores of 8 bf16 or 4 fp32 ------------------------------
+FLUX_DEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+FLUX_DEV void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// 8 bf16 packed in a uint4 -> 8 floats
+FLUX_DEV void unpack8(uint4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+FLUX_DEV uint32_t pack2(float a, float b) {
+  bf16 x = static_cast<bf16>(a), y = static_cast<bf16>(b);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, y)) << 16);
+}
+
+FLUX_DEV uint4 pack8(const float* f) {
+  return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+}
+
+// ---- wave64 reductions ---------------------------------------------------------------
+FLUX_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+FLUX_DEV float group_sum16(float v) {  // sum over aligned groups of 16 lanes
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+FLUX_DEV float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+// ---- dtype tags shared with the host -------------------------------------------------
+enum { DT_BF16 = 0, DT_F32 = 1 };

@@ -1,0 +1,768 @@
+// C ABI of libflux: argument validation, workspace carving and the launch sequences of the
+// double-stream block, the single-stream block and the denoiser step.
+//
+// Block structure follows the Diffusers walk-through of Flux2Transformer2DModel (sections
+// 双流块 Flux2TransformerBlock, 单流块 Flux2SingleTransformerBlock, 激活函数与 FFN,
+// 前向传播输入输出约定) and the FLUX.2 Klein 9B shape trace (sections 3 and 4).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "flux.h"
+#include "kernels.h"
+
+using namespace flux;
+
+// ------------------------------------------------------------------------------------
+// errors
+// ------------------------------------------------------------------------------------
+static thread_local std::string g_err;
+
+static int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(FLUX_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));            \
+  } while (0)
+
+extern "C" const char* flux_last_error(void) { return g_err.c_str(); }
+extern "C" const char* flux_version(void) { return "libflux 0.1 (gfx950)"; }
+
+// ------------------------------------------------------------------------------------
+// validation helpers
+// ------------------------------------------------------------------------------------
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static int esize(int dtype) { return dtype == FLUX_BF16 ? 2 : 4; }
+
+static int check_cfg(const flux_cfg* c) {
+  if (!c) return fail(FLUX_EINVAL, "cfg is NULL");
+  if (c->dtype != FLUX_BF16 && c->dtype != FLUX_F32)
+    return fail(FLUX_EDTYPE, "unknown dtype %d", c->dtype);
+  if (c->head_dim != 128) return fail(FLUX_ESHAPE, "head_dim must be 128 (got %d)", c->head_dim);
+  if (c->heads <= 0 || c->dim != c->heads * c->head_dim)
+    return fail(FLUX_ESHAPE, "dim (%d) must equal heads (%d) * head_dim", c->dim, c->heads);
+  if (c->mlp_hidden <= 0 || c->mlp_hidden % 8)
+    return fail(FLUX_ESHAPE, "mlp_hidden must be a positive multiple of 8 (got %d)", c->mlp_hidden);
+  int sum = 0;
+  for (int a = 0; a < 4; ++a) {
+    if (c->axes_dim[a] < 0 || c->axes_dim[a] % 2)
+      return fail(FLUX_ESHAPE, "axes_dim[%d] = %d must be even and >= 0", a, c->axes_dim[a]);
+    sum += c->axes_dim[a];
+  }
+  if (sum != c->head_dim) return fail(FLUX_ESHAPE, "axes_dim must sum to head_dim (got %d)", sum);
+  if (!(c->rope_theta > 0.f)) return fail(FLUX_EINVAL, "rope_theta must be > 0");
+  if (!(c->eps > 0.f)) return fail(FLUX_EINVAL, "eps must be > 0");
+  if (c->dim > 8192) return fail(FLUX_ESHAPE, "dim > 8192 is not supported");
+  return FLUX_OK;
+}
+
+static int check_sizes(int batch, int n_img, int n_txt) {
+  if (batch <= 0) return fail(FLUX_EINVAL, "batch must be > 0 (got %d)", batch);
+  if (n_img <= 0) return fail(FLUX_EINVAL, "n_img must be > 0 (got %d)", n_img);
+  if (n_txt < 0) return fail(FLUX_EINVAL, "n_txt must be >= 0 (got %d)", n_txt);
+  return FLUX_OK;
+}
+
+#define CHECK(x)              \
+  do {                        \
+    int st_ = (x);            \
+    if (st_ != FLUX_OK) return st_; \
+  } while (0)
+
+static int need(const void* p, const char* name) {
+  if (!p) return fail(FLUX_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(FLUX_EALIGN, "%s is not 16-byte aligned", name);
+  return FLUX_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// workspace carving (a dry run with base == nullptr gives the size)
+// ------------------------------------------------------------------------------------
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t n) {
+    off = (off + 255) & ~size_t(255);
+    T* p = reinterpret_cast<T*>(base + off);
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+static int check_ws(void* ws, size_t have, size_t want) {
+  if (want == 0) return FLUX_OK;
+  if (!ws) return fail(FLUX_EWORKSPACE, "workspace is NULL (need %zu bytes)", want);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u)
+    return fail(FLUX_EWORKSPACE, "workspace is not 256-byte aligned");
+  if (have < want) return fail(FLUX_EWORKSPACE, "workspace has %zu bytes, need %zu", have, want);
+  return FLUX_OK;
+}
+
+// conditioning scratch: sinusoid, hidden, silu(temb)
+struct CondBufs {
+  float* e;
+  float* h1;
+  float* stemb;
+};
+static CondBufs carve_cond(Carver& cv, int B, int D) {
+  CondBufs c;
+  c.e = cv.take<float>((size_t)B * 256);
+  c.h1 = cv.take<float>((size_t)B * D);
+  c.stemb = cv.take<float>((size_t)B * D);
+  return c;
+}
+
+// silu(temb) for every batch row: temb = W2 silu(W1 sinusoid(1000 t))
+static int run_cond(const flux_cfg* c, const flux_temb_weights* tw, const float* t, int B,
+                    const CondBufs& cb, hipStream_t s) {
+  HIP_TRY(timestep_sinusoid(t, B, 128, cb.e, s));
+  HIP_TRY(gemv(c->dtype, tw->w1, c->dim, 256, cb.e, B, false, true, cb.h1, s));
+  HIP_TRY(gemv(c->dtype, tw->w2, c->dim, c->dim, cb.h1, B, false, true, cb.stemb, s));
+  return FLUX_OK;
+}
+
+static int check_temb(const flux_temb_weights* tw) {
+  CHECK(need(tw->w1, "temb.w1"));
+  CHECK(need(tw->w2, "temb.w2"));
+  return FLUX_OK;
+}
+
+// rope tables for the joint sequence
+struct RopeBufs {
+  int32_t* pos;
+  float2* cs;
+};
+static RopeBufs carve_rope(Carver& cv, int L) {
+  RopeBufs r;
+  r.pos = cv.take<int32_t>((size_t)L * 64);
+  r.cs = cv.take<float2>((size_t)L * 64);
+  return r;
+}
+
+// ------------------------------------------------------------------------------------
+// linear helper
+// ------------------------------------------------------------------------------------
+static int lin(const flux_cfg* c, int epi, int m, int n, int k, const void* x, int64_t ldx,
+               const void* w, int64_t ldw, void* y, int64_t ldy, int y_dtype,
+               const void* resid = nullptr, int64_t ldr = 0, int r_dtype = FLUX_F32,
+               const float* gate = nullptr, int64_t gate_bs = 0, int rpb = 1, hipStream_t s = 0) {
+  LinearArgs a;
+  a.epilogue = epi;
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  a.x = x;
+  a.ldx = ldx;
+  a.w = w;
+  a.ldw = ldw;
+  a.y = y;
+  a.ldy = ldy;
+  a.y_dtype = y_dtype;
+  a.resid = resid;
+  a.ldr = ldr;
+  a.r_dtype = r_dtype;
+  a.gate = gate;
+  a.gate_bs = gate_bs;
+  a.rows_per_batch = rpb;
+  HIP_TRY(linear(c->dtype, a, s));
+  return FLUX_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// double-stream block
+// ------------------------------------------------------------------------------------
+struct DoubleScratch {
+  void* ln[2];    // [B*N_s, D] compute dtype       (0 = txt, 1 = img)
+  void* qkv[2];   // [B*N_s, 3D]
+  void* o[2];     // [B*N_s, D]
+  float* mid[2];  // [B*N_s, D] residual after the attention branch
+  void* mlp[2];   // [B*N_s, H]
+};
+
+static DoubleScratch carve_double(Carver& cv, const flux_cfg* c, int B, int Ni, int Nt) {
+  DoubleScratch d;
+  const int es = esize(c->dtype);
+  const int D = c->dim, H = c->mlp_hidden;
+  const int n[2] = {Nt, Ni};
+  for (int i = 0; i < 2; ++i) {
+    const size_t rows = (size_t)B * n[i];
+    d.ln[i] = cv.take<char>(rows * D * es);
+    d.qkv[i] = cv.take<char>(rows * 3 * D * es);
+    d.o[i] = cv.take<char>(rows * D * es);
+    d.mid[i] = cv.take<float>(rows * D);
+    d.mlp[i] = cv.take<char>(rows * H * es);
+  }
+  return d;
+}
+
+static int check_stream(const flux_stream_weights* w, const char* nm) {
+  char buf[64];
+  snprintf(buf, sizeof buf, "%s.qkv", nm);
+  CHECK(need(w->qkv, buf));
+  snprintf(buf, sizeof buf, "%s.out", nm);
+  CHECK(need(w->out, buf));
+  snprintf(buf, sizeof buf, "%s.mlp_in", nm);
+  CHECK(need(w->mlp_in, buf));
+  snprintf(buf, sizeof buf, "%s.mlp_out", nm);
+  CHECK(need(w->mlp_out, buf));
+  snprintf(buf, sizeof buf, "%s.q_norm", nm);
+  CHECK(need(w->q_norm, buf));
+  snprintf(buf, sizeof buf, "%s.k_norm", nm);
+  CHECK(need(w->k_norm, buf));
+  return FLUX_OK;
+}
+
+// in[s] / out[s]: stream residuals [B*N_s, D] of in_dt / out_dt; mods[s]: [B, 6D] f32
+static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B, int Ni, int Nt,
+                      const void* in[2], int in_dt, void* out[2], int out_dt,
+                      const float* mods[2], const float2* cs, const DoubleScratch& d,
+                      hipStream_t s) {
+  const int D = c->dim, H = c->mlp_hidden, T = c->dtype;
+  const int n[2] = {Nt, Ni};
+  const int64_t mbs = 6 * (int64_t)D;
+  for (int i = 0; i < 2; ++i) {
+    if (n[i] == 0) continue;
+    const int rows = B * n[i];
+    HIP_TRY(layernorm_modulate(in_dt, T, in[i], D, d.ln[i], D, rows, D, n[i], mods[i],
+                               mods[i] + D, mbs, c->eps, s));
+    CHECK(lin(c, EPI_STORE, rows, 3 * D, D, d.ln[i], D, sw[i]->qkv, D, d.qkv[i], 3 * D, T,
+              nullptr, 0, 0, nullptr, 0, 1, s));
+  }
+  // joint views: segment 0 = text rows, segment 1 = image rows
+  const int L = Nt + Ni;
+  const int es = esize(T);
+  auto view = [&](int col, void* const* bufs, int64_t ld) {
+    SeqView v;
+    v.base0 = static_cast<char*>(bufs[0]) + (size_t)col * es;
+    v.base1 = static_cast<char*>(bufs[1]) + (size_t)col * es;
+    v.bs0 = (int64_t)Nt * ld;
+    v.bs1 = (int64_t)Ni * ld;
+    v.ld = ld;
+    v.n0 = Nt;
+    return v;
+  };
+  SeqView qv = view(0, d.qkv, 3 * D), kv = view(D, d.qkv, 3 * D), vv = view(2 * D, d.qkv, 3 * D);
+  SeqView ov = view(0, d.o, D);
+  HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, sw[0]->q_norm, sw[0]->k_norm, sw[1]->q_norm,
+                       sw[1]->k_norm, cs, c->eps, s));
+  HIP_TRY(attention(T, qv, kv, vv, ov, B, L, c->heads, s));
+  for (int i = 0; i < 2; ++i) {
+    if (n[i] == 0) continue;
+    const int rows = B * n[i];
+    // x + gate1 * (O W_o^T)  -> mid (f32)
+    CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D, d.o[i], D, sw[i]->out, D, d.mid[i], D, FLUX_F32,
+              in[i], D, in_dt, mods[i] + 2 * D, mbs, n[i], s));
+    HIP_TRY(layernorm_modulate(FLUX_F32, T, d.mid[i], D, d.ln[i], D, rows, D, n[i],
+                               mods[i] + 3 * D, mods[i] + 4 * D, mbs, c->eps, s));
+    CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln[i], D, sw[i]->mlp_in, D, d.mlp[i], H, T,
+              nullptr, 0, 0, nullptr, 0, 1, s));
+    // mid + gate2 * (M W_out^T) -> out
+    CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, H, d.mlp[i], H, sw[i]->mlp_out, H, out[i], D,
+              out_dt, d.mid[i], D, FLUX_F32, mods[i] + 5 * D, mbs, n[i], s));
+  }
+  return FLUX_OK;
+}
+
+extern "C" size_t flux_double_block_workspace_size(const flux_cfg* c, int B, int Ni, int Nt) {
+  if (check_cfg(c) != FLUX_OK || check_sizes(B, Ni, Nt) != FLUX_OK) return 0;
+  Carver cv(nullptr);
+  carve_cond(cv, B, c->dim);
+  cv.take<float>((size_t)B * 12 * c->dim);
+  carve_rope(cv, Ni + Nt);
+  carve_double(cv, c, B, Ni, Nt);
+  return cv.off;
+}
+
+extern "C" int flux_double_block_fwd(const flux_cfg* c, const flux_double_weights* w,
+                                     const float* t, int B, int Ni, int Nt, const void* img,
+                                     const void* txt, const int32_t* img_ids,
+                                     const int32_t* txt_ids, void* img_out, void* txt_out,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(c));
+  CHECK(check_sizes(B, Ni, Nt));
+  if (!w) return fail(FLUX_EINVAL, "weights is NULL");
+  if (!t) return fail(FLUX_EINVAL, "t is NULL");
+  CHECK(check_temb(&w->temb));
+  CHECK(need(w->mod_img, "mod_img"));
+  CHECK(need(w->mod_txt, "mod_txt"));
+  CHECK(check_stream(&w->img, "img"));
+  CHECK(check_stream(&w->txt, "txt"));
+  CHECK(need(img, "img"));
+  CHECK(need(img_out, "img_out"));
+  if (!img_ids) return fail(FLUX_EINVAL, "img_ids is NULL");
+  if (Nt > 0) {
+    CHECK(need(txt, "txt"));
+    CHECK(need(txt_out, "txt_out"));
+    if (!txt_ids) return fail(FLUX_EINVAL, "txt_ids is NULL");
+  }
+  const size_t want = flux_double_block_workspace_size(c, B, Ni, Nt);
+  CHECK(check_ws(ws, ws_bytes, want));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = c->dim;
+
+  Carver cv(ws);
+  CondBufs cb = carve_cond(cv, B, D);
+  float* mods = cv.take<float>((size_t)B * 12 * D);
+  RopeBufs rb = carve_rope(cv, Ni + Nt);
+  DoubleScratch d = carve_double(cv, c, B, Ni, Nt);
+
+  CHECK(run_cond(c, &w->temb, t, B, cb, s));
+  float* mod_txt = mods;
+  float* mod_img = mods + (size_t)B * 6 * D;
+  HIP_TRY(gemv(c->dtype, w->mod_txt, 6 * D, D, cb.stemb, B, false, false, mod_txt, s));
+  HIP_TRY(gemv(c->dtype, w->mod_img, 6 * D, D, cb.stemb, B, false, false, mod_img, s));
+  HIP_TRY(rope_table(txt_ids, img_ids, Nt, Ni, c->axes_dim, c->rope_theta, rb.pos, rb.cs, s));
+
+  const flux_stream_weights* sw[2] = {&w->txt, &w->img};
+  const void* in[2] = {txt, img};
+  void* out[2] = {txt_out, img_out};
+  const float* md[2] = {mod_txt, mod_img};
+  return run_double(c, sw, B, Ni, Nt, in, c->dtype, out, c->dtype, md, rb.cs, d, s);
+}
+
+// ------------------------------------------------------------------------------------
+// single-stream block (on the merged [txt ; img] sequence)
+// ------------------------------------------------------------------------------------
+struct SingleScratch {
+  void* ln;   // [B*L, D]
+  void* qkv;  // [B*L, 3D]
+  void* cat;  // [B*L, D + H]  = [attention output | SwiGLU output]
+};
+
+static SingleScratch carve_single(Carver& cv, const flux_cfg* c, int B, int L) {
+  SingleScratch d;
+  const int es = esize(c->dtype);
+  const size_t rows = (size_t)B * L;
+  d.ln = cv.take<char>(rows * c->dim * es);
+  d.qkv = cv.take<char>(rows * 3 * c->dim * es);
+  d.cat = cv.take<char>(rows * (c->dim + c->mlp_hidden) * es);
+  return d;
+}
+
+static int check_single_w(const flux_single_weights* w, bool with_mod) {
+  if (with_mod) {
+    CHECK(check_temb(&w->temb));
+    CHECK(need(w->mod, "mod"));
+  }
+  CHECK(need(w->linear1, "linear1"));
+  CHECK(need(w->linear2, "linear2"));
+  CHECK(need(w->q_norm, "q_norm"));
+  CHECK(need(w->k_norm, "k_norm"));
+  return FLUX_OK;
+}
+
+// x: merged [B*L, D] of in_dt; out: [B*L, D] of out_dt (may alias x); mod [B, 3D]
+static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, int L, const void* x,
+                      int in_dt, void* out, int out_dt, const float* mod, const float2* cs,
+                      const SingleScratch& d, hipStream_t s) {
+  const int D = c->dim, H = c->mlp_hidden, T = c->dtype, es = esize(T);
+  const int rows = B * L;
+  const int64_t mbs = 3 * (int64_t)D, ldc = D + H;
+  HIP_TRY(layernorm_modulate(in_dt, T, x, D, d.ln, D, rows, D, L, mod, mod + D, mbs, c->eps, s));
+  CHECK(lin(c, EPI_STORE, rows, 3 * D, D, d.ln, D, w->linear1, D, d.qkv, 3 * D, T, nullptr, 0, 0,
+            nullptr, 0, 1, s));
+  const char* w_mlp = static_cast<const char*>(w->linear1) + (size_t)3 * D * D * es;
+  CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln, D, w_mlp, D,
+            static_cast<char*>(d.cat) + (size_t)D * es, ldc, T, nullptr, 0, 0, nullptr, 0, 1, s));
+  auto view = [&](void* base, int col, int64_t ld) {
+    SeqView v;
+    v.base0 = v.base1 = static_cast<char*>(base) + (size_t)col * es;
+    v.bs0 = v.bs1 = (int64_t)L * ld;
+    v.ld = ld;
+    v.n0 = L;
+    return v;
+  };
+  SeqView qv = view(d.qkv, 0, 3 * D), kv = view(d.qkv, D, 3 * D), vv = view(d.qkv, 2 * D, 3 * D);
+  SeqView ov = view(d.cat, 0, ldc);
+  HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, w->q_norm, w->k_norm, w->q_norm, w->k_norm, cs,
+                       c->eps, s));
+  HIP_TRY(attention(T, qv, kv, vv, ov, B, L, c->heads, s));
+  CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D + H, d.cat, ldc, w->linear2, D + H, out, D, out_dt,
+            x, D, in_dt, mod + 2 * D, mbs, L, s));
+  return FLUX_OK;
+}
+
+static SeqView stream_view(const void* txt, const void* img, int Nt, int Ni, int D) {
+  SeqView v;
+  v.base0 = const_cast<void*>(txt);
+  v.base1 = const_cast<void*>(img);
+  v.bs0 = (int64_t)Nt * D;
+  v.bs1 = (int64_t)Ni * D;
+  v.ld = D;
+  v.n0 = Nt;
+  return v;
+}
+
+static SeqView merged_view(void* base, int L, int D) {
+  SeqView v;
+  v.base0 = v.base1 = base;
+  v.bs0 = v.bs1 = (int64_t)L * D;
+  v.ld = D;
+  v.n0 = L;
+  return v;
+}
+
+extern "C" size_t flux_single_block_workspace_size(const flux_cfg* c, int B, int Ni, int Nt) {
+  if (check_cfg(c) != FLUX_OK || check_sizes(B, Ni, Nt) != FLUX_OK) return 0;
+  const int L = Ni + Nt;
+  Carver cv(nullptr);
+  carve_cond(cv, B, c->dim);
+  cv.take<float>((size_t)B * 3 * c->dim);
+  carve_rope(cv, L);
+  cv.take<char>((size_t)B * L * c->dim * esize(c->dtype));
+  carve_single(cv, c, B, L);
+  return cv.off;
+}
+
+extern "C" int flux_single_block_fwd(const flux_cfg* c, const flux_single_weights* w,
+                                     const float* t, int B, int Ni, int Nt, const void* img,
+                                     const void* txt, const int32_t* img_ids,
+                                     const int32_t* txt_ids, void* img_out, void* txt_out,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(c));
+  CHECK(check_sizes(B, Ni, Nt));
+  if (!w) return fail(FLUX_EINVAL, "weights is NULL");
+  if (!t) return fail(FLUX_EINVAL, "t is NULL");
+  CHECK(check_single_w(w, true));
+  CHECK(need(img, "img"));
+  CHECK(need(img_out, "img_out"));
+  if (!img_ids) return fail(FLUX_EINVAL, "img_ids is NULL");
+  if (Nt > 0) {
+    CHECK(need(txt, "txt"));
+    CHECK(need(txt_out, "txt_out"));
+    if (!txt_ids) return fail(FLUX_EINVAL, "txt_ids is NULL");
+  }
+  const size_t want = flux_single_block_workspace_size(c, B, Ni, Nt);
+  CHECK(check_ws(ws, ws_bytes, want));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = c->dim, L = Ni + Nt, T = c->dtype;
+
+  Carver cv(ws);
+  CondBufs cb = carve_cond(cv, B, D);
+  float* mod = cv.take<float>((size_t)B * 3 * D);
+  RopeBufs rb = carve_rope(cv, L);
+  void* xm = cv.take<char>((size_t)B * L * D * esize(T));
+  SingleScratch d = carve_single(cv, c, B, L);
+
+  CHECK(run_cond(c, &w->temb, t, B, cb, s));
+  HIP_TRY(gemv(T, w->mod, 3 * D, D, cb.stemb, B, false, false, mod, s));
+  HIP_TRY(rope_table(txt_ids, img_ids, Nt, Ni, c->axes_dim, c->rope_theta, rb.pos, rb.cs, s));
+  // merge [txt ; img] -> xm, run in place, split back
+  HIP_TRY(copy_rows(T, stream_view(txt, img, Nt, Ni, D), T, merged_view(xm, L, D), B, L, D, s));
+  CHECK(run_single(c, w, B, L, xm, T, xm, T, mod, rb.cs, d, s));
+  HIP_TRY(copy_rows(T, merged_view(xm, L, D), T, stream_view(txt_out, img_out, Nt, Ni, D), B, L, D,
+                    s));
+  return FLUX_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// denoiser step
+// ------------------------------------------------------------------------------------
+struct StepBufs {
+  CondBufs cb;
+  float* mod_dimg;
+  float* mod_dtxt;
+  float* mod_single;
+  float* mod_final;
+  RopeBufs rb;
+  float* res;      // merged residual [B, L, D] f32
+  float* res_txt;  // double-phase stream residuals (alias into res when B == 1)
+  float* res_img;
+  void* ln_head;   // [B*Ni, D] compute dtype
+  DoubleScratch d;
+  SingleScratch sg;
+};
+
+static StepBufs carve_step(Carver& cv, const flux_cfg* c, int B, int Ni, int Nt) {
+  StepBufs sb;
+  const int D = c->dim, L = Ni + Nt;
+  sb.cb = carve_cond(cv, B, D);
+  sb.mod_dimg = cv.take<float>((size_t)B * 6 * D);
+  sb.mod_dtxt = cv.take<float>((size_t)B * 6 * D);
+  sb.mod_single = cv.take<float>((size_t)B * 3 * D);
+  sb.mod_final = cv.take<float>((size_t)B * 2 * D);
+  sb.rb = carve_rope(cv, L);
+  sb.res = cv.take<float>((size_t)B * L * D);
+  if (B == 1) {
+    sb.res_txt = sb.res;
+    sb.res_img = sb.res + (size_t)Nt * D;
+  } else {
+    sb.res_txt = cv.take<float>((size_t)B * Nt * D);
+    sb.res_img = cv.take<float>((size_t)B * Ni * D);
+  }
+  sb.ln_head = cv.take<char>((size_t)B * Ni * D * esize(c->dtype));
+  // block scratch: the double and single phases never overlap, so they share memory
+  Carver dc(cv.base ? cv.base + ((cv.off + 255) & ~size_t(255)) : nullptr);
+  sb.d = carve_double(dc, c, B, Ni, Nt);
+  Carver sc(cv.base ? cv.base + ((cv.off + 255) & ~size_t(255)) : nullptr);
+  sb.sg = carve_single(sc, c, B, L);
+  cv.off = ((cv.off + 255) & ~size_t(255)) + (dc.off > sc.off ? dc.off : sc.off);
+  return sb;
+}
+
+extern "C" size_t flux_denoiser_step_workspace_size(const flux_cfg* c, int B, int Ni, int Nt) {
+  if (check_cfg(c) != FLUX_OK || check_sizes(B, Ni, Nt) != FLUX_OK) return 0;
+  Carver cv(nullptr);
+  carve_step(cv, c, B, Ni, Nt);
+  return cv.off;
+}
+
+extern "C" int flux_denoiser_step(const flux_cfg* c, const flux_model_weights* w, const float* t,
+                                  const float* guidance, int B, int Ni, int Nt, const void* x,
+                                  const void* ctx, const int32_t* img_ids,
+                                  const int32_t* txt_ids, float* out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  CHECK(check_cfg(c));
+  CHECK(check_sizes(B, Ni, Nt));
+  if (guidance) return fail(FLUX_EINVAL, "guidance must be NULL (no guidance embedder)");
+  if (!w) return fail(FLUX_EINVAL, "weights is NULL");
+  if (!t) return fail(FLUX_EINVAL, "t is NULL");
+  if (c->in_channels <= 0 || c->in_channels % 8)
+    return fail(FLUX_ESHAPE, "in_channels must be a positive multiple of 8");
+  if (Nt > 0 && (c->context_dim <= 0 || c->context_dim % 8))
+    return fail(FLUX_ESHAPE, "context_dim must be a positive multiple of 8");
+  if (c->n_double < 0 || c->n_single < 0) return fail(FLUX_EINVAL, "negative block count");
+  CHECK(need(w->img_in, "img_in"));
+  CHECK(check_temb(&w->temb));
+  CHECK(need(w->mod_double_img, "mod_double_img"));
+  CHECK(need(w->mod_double_txt, "mod_double_txt"));
+  CHECK(need(w->mod_single, "mod_single"));
+  CHECK(need(w->mod_final, "mod_final"));
+  CHECK(need(w->proj_out, "proj_out"));
+  if (c->n_double > 0 && !w->double_blocks) return fail(FLUX_EINVAL, "double_blocks is NULL");
+  if (c->n_single > 0 && !w->single_blocks) return fail(FLUX_EINVAL, "single_blocks is NULL");
+  for (int i = 0; i < c->n_double; ++i) {
+    CHECK(check_stream(&w->double_blocks[i].img, "double.img"));
+    CHECK(check_stream(&w->double_blocks[i].txt, "double.txt"));
+  }
+  for (int i = 0; i < c->n_single; ++i) CHECK(check_single_w(&w->single_blocks[i], false));
+  CHECK(need(x, "x"));
+  CHECK(need(out, "out"));
+  if (!img_ids) return fail(FLUX_EINVAL, "img_ids is NULL");
+  if (Nt > 0) {
+    CHECK(need(w->txt_in, "txt_in"));
+    CHECK(need(ctx, "ctx"));
+    if (!txt_ids) return fail(FLUX_EINVAL, "txt_ids is NULL");
+  }
+  const size_t want = flux_denoiser_step_workspace_size(c, B, Ni, Nt);
+  CHECK(check_ws(ws, ws_bytes, want));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = c->dim, L = Ni + Nt, T = c->dtype;
+
+  Carver cv(ws);
+  StepBufs sb = carve_step(cv, c, B, Ni, Nt);
+
+  // conditioning, shared modulation, rope tables
+  CHECK(run_cond(c, &w->temb, t, B, sb.cb, s));
+  HIP_TRY(gemv(T, w->mod_double_img, 6 * D, D, sb.cb.stemb, B, false, false, sb.mod_dimg, s));
+  HIP_TRY(gemv(T, w->mod_double_txt, 6 * D, D, sb.cb.stemb, B, false, false, sb.mod_dtxt, s));
+  HIP_TRY(gemv(T, w->mod_single, 3 * D, D, sb.cb.stemb, B, false, false, sb.mod_single, s));
+  HIP_TRY(gemv(T, w->mod_final, 2 * D, D, sb.cb.stemb, B, false, false, sb.mod_final, s));
+  HIP_TRY(rope_table(txt_ids, img_ids, Nt, Ni, c->axes_dim, c->rope_theta, sb.rb.pos, sb.rb.cs, s));
+
+  // stems (fp32 residual stream)
+  CHECK(lin(c, EPI_STORE, B * Ni, D, c->in_channels, x, c->in_channels, w->img_in, c->in_channels,
+            sb.res_img, D, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s));
+  if (Nt > 0)
+    CHECK(lin(c, EPI_STORE, B * Nt, D, c->context_dim, ctx, c->context_dim, w->txt_in,
+              c->context_dim, sb.res_txt, D, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s));
+
+  // double-stream blocks
+  const void* in[2] = {sb.res_txt, sb.res_img};
+  void* io[2] = {sb.res_txt, sb.res_img};
+  const float* md[2] = {sb.mod_dtxt, sb.mod_dimg};
+  for (int i = 0; i < c->n_double; ++i) {
+    const flux_stream_weights* sw[2] = {&w->double_blocks[i].txt, &w->double_blocks[i].img};
+    CHECK(run_double(c, sw, B, Ni, Nt, in, FLUX_F32, io, FLUX_F32, md, sb.rb.cs, sb.d, s));
+  }
+  // merge [txt ; img] (already merged when B == 1)
+  if (B > 1)
+    HIP_TRY(copy_rows(FLUX_F32, stream_view(sb.res_txt, sb.res_img, Nt, Ni, D), FLUX_F32,
+                      merged_view(sb.res, L, D), B, L, D, s));
+  // single-stream blocks
+  for (int i = 0; i < c->n_single; ++i)
+    CHECK(run_single(c, &w->single_blocks[i], B, L, sb.res, FLUX_F32, sb.res, FLUX_F32,
+                     sb.mod_single, sb.rb.cs, sb.sg, s));
+  // head: keep image tokens, final LayerNorm + modulate, proj_out
+  for (int b = 0; b < B; ++b) {
+    const float* rows = sb.res + ((size_t)b * L + Nt) * D;
+    void* lnb = static_cast<char*>(sb.ln_head) + (size_t)b * Ni * D * esize(T);
+    HIP_TRY(layernorm_modulate(FLUX_F32, T, rows, D, lnb, D, Ni, D, Ni,
+                               sb.mod_final + (size_t)b * 2 * D, sb.mod_final + (size_t)b * 2 * D + D,
+                               2 * D, c->eps, s));
+  }
+  CHECK(lin(c, EPI_STORE, B * Ni, c->in_channels, D, sb.ln_head, D, w->proj_out, D, out,
+            c->in_channels, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s));
+  return FLUX_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// single operations
+// ------------------------------------------------------------------------------------
+extern "C" int flux_rope_positions(const flux_cfg* c, const int32_t* txt_ids,
+                                   const int32_t* img_ids, int n_txt, int n_img, int32_t* pos,
+                                   void* stream) {
+  CHECK(check_cfg(c));
+  if (n_txt < 0 || n_img < 0 || n_txt + n_img <= 0)
+    return fail(FLUX_EINVAL, "need n_txt >= 0, n_img >= 0 and at least one token");
+  if ((n_txt && !txt_ids) || (n_img && !img_ids) || !pos)
+    return fail(FLUX_EINVAL, "NULL pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIP_TRY(rope_table(txt_ids, img_ids, n_txt, n_img, c->axes_dim, c->rope_theta, pos, nullptr, s));
+  return FLUX_OK;
+}
+
+extern "C" size_t flux_modulation_workspace_size(const flux_cfg* c, int B) {
+  if (check_cfg(c) != FLUX_OK || B <= 0) return 0;
+  Carver cv(nullptr);
+  carve_cond(cv, B, c->dim);
+  return cv.off;
+}
+
+extern "C" int flux_modulation(const flux_cfg* c, const flux_temb_weights* tw, const void* w_mod,
+                               int n_out, const float* t, int B, float* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(c));
+  if (B <= 0 || n_out <= 0) return fail(FLUX_EINVAL, "batch and n_out must be > 0");
+  if (!tw || !t || !out) return fail(FLUX_EINVAL, "NULL pointer");
+  CHECK(check_temb(tw));
+  CHECK(need(w_mod, "w_mod"));
+  CHECK(check_ws(ws, ws_bytes, flux_modulation_workspace_size(c, B)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  CondBufs cb = carve_cond(cv, B, c->dim);
+  CHECK(run_cond(c, tw, t, B, cb, s));
+  HIP_TRY(gemv(c->dtype, w_mod, n_out, c->dim, cb.stemb, B, false, false, out, s));
+  return FLUX_OK;
+}
+
+extern "C" int flux_layernorm_modulate(const flux_cfg* c, int rows, int rpb, const void* x,
+                                       int x_dtype, const float* shift, const float* scale,
+                                       void* y, void* stream) {
+  CHECK(check_cfg(c));
+  if (rows <= 0 || rpb <= 0) return fail(FLUX_EINVAL, "rows and rows_per_batch must be > 0");
+  if (x_dtype != FLUX_BF16 && x_dtype != FLUX_F32) return fail(FLUX_EDTYPE, "bad x_dtype");
+  CHECK(need(x, "x"));
+  CHECK(need(y, "y"));
+  CHECK(need(shift, "shift"));
+  CHECK(need(scale, "scale"));
+  HIP_TRY(layernorm_modulate(x_dtype, c->dtype, x, c->dim, y, c->dim, rows, c->dim, rpb, shift,
+                             scale, c->dim, c->eps, static_cast<hipStream_t>(stream)));
+  return FLUX_OK;
+}
+
+extern "C" size_t flux_qk_norm_rope_workspace_size(const flux_cfg* c, int n_txt, int n_img) {
+  if (check_cfg(c) != FLUX_OK || n_txt < 0 || n_img < 0) return 0;
+  Carver cv(nullptr);
+  carve_rope(cv, n_txt + n_img);
+  return cv.off;
+}
+
+extern "C" int flux_qk_norm_rope(const flux_cfg* c, int B, int n_txt, int n_img, void* q, void* k,
+                                 int64_t ld, const float* qg_txt, const float* kg_txt,
+                                 const float* qg_img, const float* kg_img,
+                                 const int32_t* txt_ids, const int32_t* img_ids, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(c));
+  const int L = n_txt + n_img;
+  if (B <= 0 || n_txt < 0 || n_img < 0 || L <= 0) return fail(FLUX_EINVAL, "bad sizes");
+  if (ld < c->dim || (ld * esize(c->dtype)) % 16) return fail(FLUX_EALIGN, "bad ld %lld", (long long)ld);
+  CHECK(need(q, "q"));
+  CHECK(need(k, "k"));
+  CHECK(need(qg_img, "q_norm_img"));
+  CHECK(need(kg_img, "k_norm_img"));
+  CHECK(need(qg_txt, "q_norm_txt"));
+  CHECK(need(kg_txt, "k_norm_txt"));
+  if ((n_txt && !txt_ids) || (n_img && !img_ids)) return fail(FLUX_EINVAL, "ids NULL");
+  CHECK(check_ws(ws, ws_bytes, flux_qk_norm_rope_workspace_size(c, n_txt, n_img)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  RopeBufs rb = carve_rope(cv, L);
+  HIP_TRY(rope_table(txt_ids, img_ids, n_txt, n_img, c->axes_dim, c->rope_theta, rb.pos, rb.cs, s));
+  auto mk = [&](void* base) {
+    SeqView v;
+    v.base0 = base;
+    v.base1 = static_cast<char*>(base) + (size_t)n_txt * ld * esize(c->dtype);
+    v.bs0 = v.bs1 = (int64_t)L * ld;
+    v.ld = ld;
+    v.n0 = n_txt;
+    return v;
+  };
+  HIP_TRY(qk_norm_rope(c->dtype, mk(q), mk(k), B, L, c->heads, qg_txt, kg_txt, qg_img, kg_img,
+                       rb.cs, c->eps, s));
+  return FLUX_OK;
+}
+
+extern "C" int flux_attention(const flux_cfg* c, int B, int seq, const void* q, const void* k,
+                              const void* v, int64_t ld_in, void* o, int64_t ld_out,
+                              void* stream) {
+  CHECK(check_cfg(c));
+  if (B <= 0 || seq <= 0) return fail(FLUX_EINVAL, "batch and seq must be > 0");
+  const int es = esize(c->dtype);
+  if (ld_in < c->dim || ld_out < c->dim || (ld_in * es) % 16 || (ld_out * es) % 16)
+    return fail(FLUX_EALIGN, "leading dimensions must be >= dim and 16-byte multiples");
+  CHECK(need(q, "q"));
+  CHECK(need(k, "k"));
+  CHECK(need(v, "v"));
+  CHECK(need(o, "o"));
+  auto mk = [&](const void* base, int64_t ld) {
+    SeqView sv;
+    sv.base0 = sv.base1 = const_cast<void*>(base);
+    sv.bs0 = sv.bs1 = (int64_t)seq * ld;
+    sv.ld = ld;
+    sv.n0 = seq;
+    return sv;
+  };
+  HIP_TRY(attention(c->dtype, mk(q, ld_in), mk(k, ld_in), mk(v, ld_in), mk(o, ld_out), B, seq,
+                    c->heads, static_cast<hipStream_t>(stream)));
+  return FLUX_OK;
+}
+
+extern "C" int flux_linear(const flux_cfg* c, int epi, int m, int n, int k, const void* x,
+                           int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
+                           int y_dtype, const void* resid, int64_t ldr, const float* gate,
+                           int rpb, void* stream) {
+  CHECK(check_cfg(c));
+  if (m <= 0 || n <= 0 || k <= 0) return fail(FLUX_EINVAL, "m, n, k must be > 0");
+  if (k % 8) return fail(FLUX_ESHAPE, "k must be a multiple of 8");
+  const int es = esize(c->dtype);
+  if (ldx < k || ldw < k || (ldx * es) % 16 || (ldw * es) % 16)
+    return fail(FLUX_EALIGN, "ldx/ldw must be >= k and 16-byte multiples");
+  CHECK(need(x, "x"));
+  CHECK(need(w, "w"));
+  if (!y) return fail(FLUX_EINVAL, "y is NULL");
+  if (epi == FLUX_EPI_SWIGLU) {
+    if (n % 2) return fail(FLUX_ESHAPE, "SwiGLU needs an even n");
+    if (ldy < n / 2) return fail(FLUX_ESHAPE, "ldy < n/2");
+    return lin(c, EPI_SWIGLU, m, n, k, x, ldx, w, ldw, y, ldy, c->dtype, nullptr, 0, 0, nullptr,
+               0, 1, static_cast<hipStream_t>(stream));
+  }
+  if (y_dtype != FLUX_BF16 && y_dtype != FLUX_F32) return fail(FLUX_EDTYPE, "bad y_dtype");
+  if (ldy < n) return fail(FLUX_ESHAPE, "ldy < n");
+  if (epi == FLUX_EPI_STORE)
+    return lin(c, EPI_STORE, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, nullptr, 0, 0, nullptr, 0,
+               1, static_cast<hipStream_t>(stream));
+  if (epi == FLUX_EPI_GATED_RESIDUAL) {
+    if (!resid || !gate) return fail(FLUX_EINVAL, "resid and gate are required");
+    if (rpb <= 0 || m % rpb) return fail(FLUX_ESHAPE, "m must be a multiple of rows_per_batch");
+    if (ldr < n) return fail(FLUX_ESHAPE, "ldr < n");
+    return lin(c, EPI_GATED_RESIDUAL, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid, ldr,
+               y_dtype, gate, n, rpb, static_cast<hipStream_t>(stream));
+  }
+  return fail(FLUX_EINVAL, "unknown epilogue %d", epi);
+}

@@ -1,0 +1,280 @@
+// Bandwidth-bound fused kernels: LayerNorm + modulate, per-head RMSNorm + RoPE, and the
+// RoPE position / angle table.
+//
+// LayerNorm + modulate ("双流块" AdaLN pre-norm of the Diffusers walk-through, eps 1e-6):
+//   y = (1 + scale) * (x - mean) / sqrt(var + eps) + shift   (biased variance, no affine)
+// One wave per row: the row is held in registers (16-byte loads, 8 elements per lane per
+// chunk), mean and variance are two exact passes over the registers with wave64 shuffle
+// reductions, and the output is written with 16-byte stores.
+//
+// QK RMSNorm + RoPE ("双流块" norm_q / norm_k; "位置 id 的维度" per-axis rotary embedding,
+// theta 2000, axes 32/32/32/32): 16 lanes own one (token, head) vector of 128 values;
+// x / sqrt(mean(x^2) + eps) * gamma, then adjacent pairs (2p, 2p+1) rotate by the angle
+// read from the (cos, sin) table built once per call from the integer ids.
+#include "common.h"
+#include "kernels.h"
+
+namespace flux {
+
+// ---- 8-element chunk I/O for bf16 / fp32 --------------------------------------------
+template <class T>
+FLUX_DEV void load8(const T* p, float* f);
+template <>
+FLUX_DEV void load8<bf16>(const bf16* p, float* f) {
+  unpack8(ld16(p), f);
+}
+template <>
+FLUX_DEV void load8<float>(const float* p, float* f) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+template <class T>
+FLUX_DEV void store8(T* p, const float* f);
+template <>
+FLUX_DEV void store8<bf16>(bf16* p, const float* f) {
+  st16(p, pack8(f));
+}
+template <>
+FLUX_DEV void store8<float>(float* p, const float* f) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+// ------------------------------------------------------------------------------------
+// LayerNorm + modulate
+// ------------------------------------------------------------------------------------
+template <class TX, class TY, int MAXI>
+__global__ __launch_bounds__(256) void ln_modulate_kernel(const TX* __restrict__ x, int64_t ldx,
+                                                          TY* __restrict__ y, int64_t ldy,
+                                                          int rows, int dim, int rpb,
+                                                          const float* __restrict__ shift,
+                                                          const float* __restrict__ scale,
+                                                          int64_t mod_bs, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int nch = dim >> 3;
+  const TX* xr = x + (int64_t)row * ldx;
+  float v[MAXI][8];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      load8(xr + c * 8, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[i][e];
+    }
+  }
+  const float mean = wave_sum(s) / dim;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[i][e] -= mean;
+        q += v[i][e] * v[i][e];
+      }
+    }
+  }
+  const float rstd = rsqrtf(wave_sum(q) / dim + eps);
+  const int b = row / rpb;
+  const float* sh = shift + b * mod_bs;
+  const float* sc = scale + b * mod_bs;
+  TY* yr = y + (int64_t)row * ldy;
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float a[8], m[8], o[8];
+      load8(sh + c * 8, a);
+      load8(sc + c * 8, m);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (1.f + m[e]) * (v[i][e] * rstd) + a[e];
+      store8(yr + c * 8, o);
+    }
+  }
+}
+
+template <class TX, class TY>
+static hipError_t ln_dispatch(const void* x, int64_t ldx, void* y, int64_t ldy, int rows, int dim,
+                              int rpb, const float* shift, const float* scale, int64_t mod_bs,
+                              float eps, hipStream_t s) {
+  const int per_lane = (dim / 8 + 63) / 64;
+  dim3 grid((rows + 3) / 4), block(256);
+  auto* xp = static_cast<const TX*>(x);
+  auto* yp = static_cast<TY*>(y);
+#define FLUX_LN(N)                                                                          \
+  hipLaunchKernelGGL((ln_modulate_kernel<TX, TY, N>), grid, block, 0, s, xp, ldx, yp, ldy, \
+                     rows, dim, rpb, shift, scale, mod_bs, eps)
+  if (per_lane <= 1) FLUX_LN(1);
+  else if (per_lane <= 2) FLUX_LN(2);
+  else if (per_lane <= 4) FLUX_LN(4);
+  else if (per_lane <= 6) FLUX_LN(6);
+  else if (per_lane <= 8) FLUX_LN(8);
+  else if (per_lane <= 12) FLUX_LN(12);
+  else if (per_lane <= 16) FLUX_LN(16);
+  else return hipErrorInvalidValue;
+#undef FLUX_LN
+  return hipGetLastError();
+}
+
+hipError_t layernorm_modulate(int x_dtype, int y_dtype, const void* x, int64_t ldx, void* y,
+                              int64_t ldy, int rows, int dim, int rpb, const float* shift,
+                              const float* scale, int64_t mod_bs, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (x_dtype == DT_BF16)
+    return y_dtype == DT_BF16
+               ? ln_dispatch<bf16, bf16>(x, ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps, s)
+               : ln_dispatch<bf16, float>(x, ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps, s);
+  return y_dtype == DT_BF16
+             ? ln_dispatch<float, bf16>(x, ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps, s)
+             : ln_dispatch<float, float>(x, ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps, s);
+}
+
+// ------------------------------------------------------------------------------------
+// RoPE table: integer positions and (cos, sin) of the angles, joint order [txt ; img]
+// ------------------------------------------------------------------------------------
+__global__ void rope_table_kernel(const int32_t* __restrict__ txt_ids,
+                                  const int32_t* __restrict__ img_ids, int n_txt, int n_img,
+                                  int4 axes, float theta, int32_t* __restrict__ pos,
+                                  float2* __restrict__ cs) {
+  constexpr int P = 64;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int L = n_txt + n_img;
+  if (idx >= L * P) return;
+  const int j = idx / P, p = idx % P;
+  // axis a owns pairs [c_a, c_a + d_a / 2)
+  const int d[4] = {axes.x, axes.y, axes.z, axes.w};
+  int a = 0, first = 0;
+  while (a < 3 && p >= first + d[a] / 2) {
+    first += d[a] / 2;
+    ++a;
+  }
+  const int jl = p - first;
+  const int32_t* row = (j < n_txt) ? (txt_ids + (int64_t)j * 4) : (img_ids + (int64_t)(j - n_txt) * 4);
+  const int32_t ps = row[a];
+  pos[idx] = ps;
+  if (!cs) return;  // positions only
+  const double omega = pow((double)theta, -2.0 * jl / (double)d[a]);
+  const double phi = (double)ps * omega;
+  cs[idx] = make_float2((float)cos(phi), (float)sin(phi));
+}
+
+hipError_t rope_table(const int32_t* txt_ids, const int32_t* img_ids, int n_txt, int n_img,
+                      const int32_t* axes_dim, float theta, int32_t* pos, float2* cs,
+                      hipStream_t s) {
+  const int total = (n_txt + n_img) * 64;
+  if (total <= 0) return hipSuccess;
+  int4 axes = make_int4(axes_dim[0], axes_dim[1], axes_dim[2], axes_dim[3]);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((total + 255) / 256), dim3(256), 0, s, txt_ids,
+                     img_ids, n_txt, n_img, axes, theta, pos, cs);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
+// QK RMSNorm + RoPE, in place
+// ------------------------------------------------------------------------------------
+template <class T>
+FLUX_DEV T* seq_ptr(const SeqView& v, int b, int j) {
+  return (j < v.n0) ? static_cast<T*>(v.base0) + b * v.bs0 + (int64_t)j * v.ld
+                    : static_cast<T*>(v.base1) + b * v.bs1 + (int64_t)(j - v.n0) * v.ld;
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(SeqView q, SeqView k, int batch,
+                                                           int seq, int heads,
+                                                           const float* __restrict__ qg0,
+                                                           const float* __restrict__ kg0,
+                                                           const float* __restrict__ qg1,
+                                                           const float* __restrict__ kg1,
+                                                           const float2* __restrict__ cs,
+                                                           float eps) {
+  const int l16 = threadIdx.x & 15;
+  const int64_t unit = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t total = (int64_t)batch * seq * heads * 2;
+  if (unit >= total) return;
+  const int which = unit & 1;                 // 0 = q, 1 = k
+  const int64_t th = unit >> 1;
+  const int head = th % heads;
+  const int64_t bj = th / heads;
+  const int j = bj % seq;
+  const int b = bj / seq;
+  const SeqView& v = which ? k : q;
+  const bool seg1 = j >= v.n0;
+  const float* g = which ? (seg1 ? kg1 : kg0) : (seg1 ? qg1 : qg0);
+  T* p = seq_ptr<T>(v, b, j) + head * 128 + l16 * 8;
+  float x[8], gm[8];
+  load8(p, x);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+  const float r = rsqrtf(group_sum16(ss) * (1.f / 128.f) + eps);
+  load8(g + l16 * 8, gm);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = x[e] * r * gm[e];
+  const float4* c4 = reinterpret_cast<const float4*>(cs + (int64_t)j * 64 + l16 * 4);
+  const float4 c01 = c4[0], c23 = c4[1];
+  const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
+  const float sn[4] = {c01.y, c01.w, c23.y, c23.w};
+  float o[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    o[2 * t] = x[2 * t] * cc[t] - x[2 * t + 1] * sn[t];
+    o[2 * t + 1] = x[2 * t] * sn[t] + x[2 * t + 1] * cc[t];
+  }
+  store8(p, o);
+}
+
+hipError_t qk_norm_rope(int dtype, SeqView q, SeqView k, int batch, int seq, int heads,
+                        const float* qg0, const float* kg0, const float* qg1, const float* kg1,
+                        const float2* cs, float eps, hipStream_t s) {
+  const int64_t units = (int64_t)batch * seq * heads * 2;
+  if (units <= 0) return hipSuccess;
+  dim3 grid((units + 15) / 16), block(256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(qk_norm_rope_kernel<bf16>, grid, block, 0, s, q, k, batch, seq, heads, qg0,
+                       kg0, qg1, kg1, cs, eps);
+  else
+    hipLaunchKernelGGL(qk_norm_rope_kernel<float>, grid, block, 0, s, q, k, batch, seq, heads, qg0,
+                       kg0, qg1, kg1, cs, eps);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
+// Row copies between joint-sequence views (merge / split of the streams)
+// ------------------------------------------------------------------------------------
+template <class TS, class TD>
+__global__ void copy_rows_kernel(SeqView src, SeqView dst, int batch, int seq, int dim) {
+  const int nch = dim >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)batch * seq * nch) return;
+  const int c = idx % nch;
+  const int64_t bj = idx / nch;
+  const int j = bj % seq, b = bj / seq;
+  float f[8];
+  load8(seq_ptr<TS>(src, b, j) + c * 8, f);
+  store8(seq_ptr<TD>(dst, b, j) + c * 8, f);
+}
+
+hipError_t copy_rows(int src_dtype, SeqView src, int dst_dtype, SeqView dst, int batch, int seq,
+                     int dim, hipStream_t s) {
+  const int64_t total = (int64_t)batch * seq * (dim / 8);
+  if (total <= 0) return hipSuccess;
+  dim3 grid((total + 255) / 256), block(256);
+  if (src_dtype == DT_BF16 && dst_dtype == DT_BF16)
+    hipLaunchKernelGGL((copy_rows_kernel<bf16, bf16>), grid, block, 0, s, src, dst, batch, seq, dim);
+  else if (src_dtype == DT_BF16)
+    hipLaunchKernelGGL((copy_rows_kernel<bf16, float>), grid, block, 0, s, src, dst, batch, seq, dim);
+  else if (dst_dtype == DT_BF16)
+    hipLaunchKernelGGL((copy_rows_kernel<float, bf16>), grid, block, 0, s, src, dst, batch, seq, dim);
+  else
+    hipLaunchKernelGGL((copy_rows_kernel<float, float>), grid, block, 0, s, src, dst, batch, seq, dim);
+  return hipGetLastError();
+}
+
+}  // namespace flux

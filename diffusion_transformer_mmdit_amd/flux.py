@@ -1,0 +1,307 @@
+"""Thin ctypes binding of libflux (include/flux.h): same entry-point names, argument
+marshalling only.  Every computation runs in the HIP library; if the library is not built
+the calls raise FluxError (there is no fallback path).
+
+Tensors are passed as device pointers: anything with ``data_ptr()`` (a torch tensor on the
+GPU) or a plain integer address.  ``stream`` is a hipStream_t handle as an integer
+(``torch.cuda.current_stream().cuda_stream``) or None for the default stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Mapping
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflux.so")
+
+FLUX_OK, FLUX_EINVAL, FLUX_ESHAPE, FLUX_EDTYPE, FLUX_EALIGN, FLUX_EWORKSPACE, FLUX_EHIP = range(7)
+FLUX_BF16, FLUX_F32 = 0, 1
+FLUX_EPI_STORE, FLUX_EPI_SWIGLU, FLUX_EPI_GATED_RESIDUAL = 0, 1, 2
+
+STATUS_NAMES = {0: "FLUX_OK", 1: "FLUX_EINVAL", 2: "FLUX_ESHAPE", 3: "FLUX_EDTYPE",
+                4: "FLUX_EALIGN", 5: "FLUX_EWORKSPACE", 6: "FLUX_EHIP"}
+
+
+class FluxError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+# ------------------------------------------------------------------------------------
+# C structures
+# ------------------------------------------------------------------------------------
+vp = ctypes.c_void_p
+
+
+class flux_cfg(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("mlp_hidden", ctypes.c_int32), ("axes_dim", ctypes.c_int32 * 4),
+                ("rope_theta", ctypes.c_float), ("eps", ctypes.c_float),
+                ("in_channels", ctypes.c_int32), ("context_dim", ctypes.c_int32),
+                ("n_double", ctypes.c_int32), ("n_single", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class flux_temb_weights(ctypes.Structure):
+    _fields_ = [("w1", vp), ("w2", vp)]
+
+
+class flux_stream_weights(ctypes.Structure):
+    _fields_ = [("qkv", vp), ("out", vp), ("mlp_in", vp), ("mlp_out", vp), ("q_norm", vp),
+                ("k_norm", vp)]
+
+
+class flux_double_weights(ctypes.Structure):
+    _fields_ = [("temb", flux_temb_weights), ("mod_img", vp), ("mod_txt", vp),
+                ("img", flux_stream_weights), ("txt", flux_stream_weights)]
+
+
+class flux_single_weights(ctypes.Structure):
+    _fields_ = [("temb", flux_temb_weights), ("mod", vp), ("linear1", vp), ("linear2", vp),
+                ("q_norm", vp), ("k_norm", vp)]
+
+
+class flux_model_weights(ctypes.Structure):
+    _fields_ = [("img_in", vp), ("txt_in", vp), ("temb", flux_temb_weights),
+                ("mod_double_img", vp), ("mod_double_txt", vp), ("mod_single", vp),
+                ("mod_final", vp), ("proj_out", vp),
+                ("double_blocks", ctypes.POINTER(flux_double_weights)),
+                ("single_blocks", ctypes.POINTER(flux_single_weights))]
+
+
+# ------------------------------------------------------------------------------------
+# Library loading and prototypes
+# ------------------------------------------------------------------------------------
+_lib = None
+c_size = ctypes.c_size_t
+c_int = ctypes.c_int
+c_i64 = ctypes.c_int64
+P = ctypes.POINTER
+
+_PROTOS = {
+    "flux_last_error": (ctypes.c_char_p, []),
+    "flux_version": (ctypes.c_char_p, []),
+    "flux_double_block_workspace_size": (c_size, [P(flux_cfg), c_int, c_int, c_int]),
+    "flux_double_block_fwd": (c_int, [P(flux_cfg), P(flux_double_weights), vp, c_int, c_int, c_int,
+                                      vp, vp, vp, vp, vp, vp, vp, c_size, vp]),
+    "flux_single_block_workspace_size": (c_size, [P(flux_cfg), c_int, c_int, c_int]),
+    "flux_single_block_fwd": (c_int, [P(flux_cfg), P(flux_single_weights), vp, c_int, c_int, c_int,
+                                      vp, vp, vp, vp, vp, vp, vp, c_size, vp]),
+    "flux_denoiser_step_workspace_size": (c_size, [P(flux_cfg), c_int, c_int, c_int]),
+    "flux_denoiser_step": (c_int, [P(flux_cfg), P(flux_model_weights), vp, vp, c_int, c_int, c_int,
+                                   vp, vp, vp, vp, vp, vp, c_size, vp]),
+    "flux_rope_positions": (c_int, [P(flux_cfg), vp, vp, c_int, c_int, vp, vp]),
+    "flux_modulation_workspace_size": (c_size, [P(flux_cfg), c_int]),
+    "flux_modulation": (c_int, [P(flux_cfg), P(flux_temb_weights), vp, c_int, vp, c_int, vp, vp,
+                                c_size, vp]),
+    "flux_layernorm_modulate": (c_int, [P(flux_cfg), c_int, c_int, vp, c_int, vp, vp, vp, vp]),
+    "flux_qk_norm_rope_workspace_size": (c_size, [P(flux_cfg), c_int, c_int]),
+    "flux_qk_norm_rope": (c_int, [P(flux_cfg), c_int, c_int, c_int, vp, vp, c_i64, vp, vp, vp, vp,
+                                  vp, vp, vp, c_size, vp]),
+    "flux_attention": (c_int, [P(flux_cfg), c_int, c_int, vp, vp, vp, c_i64, vp, c_i64, vp]),
+    "flux_linear": (c_int, [P(flux_cfg), c_int, c_int, c_int, c_int, vp, c_i64, vp, c_i64, vp,
+                            c_i64, c_int, vp, c_i64, vp, c_int, vp]),
+}
+
+EXPORTED = tuple(_PROTOS)
+
+
+def lib(path: str | None = None):
+    """Load libflux.so (once).  Raises FluxError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise FluxError(FLUX_EINVAL, f"{path} not found: build it with "
+                        "`python -m diffusion_transformer_mmdit_amd.build`")
+    L = ctypes.CDLL(path)
+    for name, (res, args) in _PROTOS.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(status: int):
+    if status != FLUX_OK:
+        raise FluxError(status, lib().flux_last_error().decode())
+
+
+def flux_last_error() -> str:
+    return lib().flux_last_error().decode()
+
+
+def flux_version() -> str:
+    return lib().flux_version().decode()
+
+
+# ------------------------------------------------------------------------------------
+# Structure builders (marshalling dicts of device tensors into the C structures)
+# ------------------------------------------------------------------------------------
+def make_cfg(dim: int, heads: int, mlp_hidden: int, dtype: int = FLUX_BF16, head_dim: int = 128,
+             axes_dim=(32, 32, 32, 32), rope_theta: float = 2000.0, eps: float = 1e-6,
+             in_channels: int = 128, context_dim: int = 0, n_double: int = 0,
+             n_single: int = 0) -> flux_cfg:
+    c = flux_cfg()
+    c.dim, c.heads, c.head_dim, c.mlp_hidden = dim, heads, head_dim, mlp_hidden
+    c.axes_dim = (ctypes.c_int32 * 4)(*axes_dim)
+    c.rope_theta, c.eps = rope_theta, eps
+    c.in_channels, c.context_dim = in_channels, context_dim
+    c.n_double, c.n_single, c.dtype = n_double, n_single, dtype
+    return c
+
+
+def temb_weights(w: Mapping, prefix: str = "temb.") -> flux_temb_weights:
+    return flux_temb_weights(_ptr(w[prefix + "w1"]), _ptr(w[prefix + "w2"]))
+
+
+def stream_weights(w: Mapping, prefix: str) -> flux_stream_weights:
+    return flux_stream_weights(*[_ptr(w[prefix + k]) for k in
+                                 ("qkv", "out", "mlp_in", "mlp_out", "q_norm", "k_norm")])
+
+
+def double_weights(w: Mapping, prefix: str = "", with_mod: bool = True) -> flux_double_weights:
+    d = flux_double_weights()
+    if with_mod:
+        d.temb = temb_weights(w)
+        d.mod_img, d.mod_txt = _ptr(w["mod_img"]), _ptr(w["mod_txt"])
+    d.img = stream_weights(w, prefix + "img.")
+    d.txt = stream_weights(w, prefix + "txt.")
+    return d
+
+
+def single_weights(w: Mapping, prefix: str = "", with_mod: bool = True) -> flux_single_weights:
+    s = flux_single_weights()
+    if with_mod:
+        s.temb = temb_weights(w)
+        s.mod = _ptr(w["mod"])
+    s.linear1, s.linear2 = _ptr(w[prefix + "linear1"]), _ptr(w[prefix + "linear2"])
+    s.q_norm, s.k_norm = _ptr(w[prefix + "q_norm"]), _ptr(w[prefix + "k_norm"])
+    return s
+
+
+class ModelWeights:
+    """flux_model_weights plus the host arrays of per-block structures it points to."""
+
+    def __init__(self, w: Mapping, n_double: int, n_single: int):
+        self.doubles = (flux_double_weights * max(n_double, 1))()
+        for i in range(n_double):
+            self.doubles[i] = double_weights(w, prefix=f"double.{i}.", with_mod=False)
+        self.singles = (flux_single_weights * max(n_single, 1))()
+        for i in range(n_single):
+            self.singles[i] = single_weights(w, prefix=f"single.{i}.", with_mod=False)
+        m = flux_model_weights()
+        m.img_in, m.txt_in = _ptr(w["img_in"]), _ptr(w.get("txt_in"))
+        m.temb = temb_weights(w)
+        m.mod_double_img, m.mod_double_txt = _ptr(w["mod_dimg"]), _ptr(w["mod_dtxt"])
+        m.mod_single, m.mod_final = _ptr(w["mod_single"]), _ptr(w["mod_final"])
+        m.proj_out = _ptr(w["proj_out"])
+        m.double_blocks = ctypes.cast(self.doubles, P(flux_double_weights))
+        m.single_blocks = ctypes.cast(self.singles, P(flux_single_weights))
+        self.struct = m
+
+
+# ------------------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ------------------------------------------------------------------------------------
+def flux_double_block_workspace_size(cfg, batch, n_img, n_txt) -> int:
+    return lib().flux_double_block_workspace_size(ctypes.byref(cfg), batch, n_img, n_txt)
+
+
+def flux_double_block_fwd(cfg, w, t, batch, n_img, n_txt, img, txt, img_ids, txt_ids, img_out,
+                          txt_out, workspace, workspace_bytes, stream=None):
+    _check(lib().flux_double_block_fwd(ctypes.byref(cfg), ctypes.byref(w), _ptr(t), batch, n_img,
+                                       n_txt, _ptr(img), _ptr(txt), _ptr(img_ids), _ptr(txt_ids),
+                                       _ptr(img_out), _ptr(txt_out), _ptr(workspace),
+                                       workspace_bytes, _stream(stream)))
+
+
+def flux_single_block_workspace_size(cfg, batch, n_img, n_txt) -> int:
+    return lib().flux_single_block_workspace_size(ctypes.byref(cfg), batch, n_img, n_txt)
+
+
+def flux_single_block_fwd(cfg, w, t, batch, n_img, n_txt, img, txt, img_ids, txt_ids, img_out,
+                          txt_out, workspace, workspace_bytes, stream=None):
+    _check(lib().flux_single_block_fwd(ctypes.byref(cfg), ctypes.byref(w), _ptr(t), batch, n_img,
+                                       n_txt, _ptr(img), _ptr(txt), _ptr(img_ids), _ptr(txt_ids),
+                                       _ptr(img_out), _ptr(txt_out), _ptr(workspace),
+                                       workspace_bytes, _stream(stream)))
+
+
+def flux_denoiser_step_workspace_size(cfg, batch, n_img, n_txt) -> int:
+    return lib().flux_denoiser_step_workspace_size(ctypes.byref(cfg), batch, n_img, n_txt)
+
+
+def flux_denoiser_step(cfg, w, t, guidance, batch, n_img, n_txt, x, ctx, img_ids, txt_ids, out,
+                       workspace, workspace_bytes, stream=None):
+    ws = w.struct if isinstance(w, ModelWeights) else w
+    _check(lib().flux_denoiser_step(ctypes.byref(cfg), ctypes.byref(ws), _ptr(t), _ptr(guidance),
+                                    batch, n_img, n_txt, _ptr(x), _ptr(ctx), _ptr(img_ids),
+                                    _ptr(txt_ids), _ptr(out), _ptr(workspace), workspace_bytes,
+                                    _stream(stream)))
+
+
+def flux_rope_positions(cfg, txt_ids, img_ids, n_txt, n_img, pos_out, stream=None):
+    _check(lib().flux_rope_positions(ctypes.byref(cfg), _ptr(txt_ids), _ptr(img_ids), n_txt,
+                                     n_img, _ptr(pos_out), _stream(stream)))
+
+
+def flux_modulation_workspace_size(cfg, batch) -> int:
+    return lib().flux_modulation_workspace_size(ctypes.byref(cfg), batch)
+
+
+def flux_modulation(cfg, temb, w_mod, n_out, t, batch, out, workspace, workspace_bytes,
+                    stream=None):
+    _check(lib().flux_modulation(ctypes.byref(cfg), ctypes.byref(temb), _ptr(w_mod), n_out,
+                                 _ptr(t), batch, _ptr(out), _ptr(workspace), workspace_bytes,
+                                 _stream(stream)))
+
+
+def flux_layernorm_modulate(cfg, rows, rows_per_batch, x, x_dtype, shift, scale, y, stream=None):
+    _check(lib().flux_layernorm_modulate(ctypes.byref(cfg), rows, rows_per_batch, _ptr(x),
+                                         x_dtype, _ptr(shift), _ptr(scale), _ptr(y),
+                                         _stream(stream)))
+
+
+def flux_qk_norm_rope_workspace_size(cfg, n_txt, n_img) -> int:
+    return lib().flux_qk_norm_rope_workspace_size(ctypes.byref(cfg), n_txt, n_img)
+
+
+def flux_qk_norm_rope(cfg, batch, n_txt, n_img, q, k, ld, q_norm_txt, k_norm_txt, q_norm_img,
+                      k_norm_img, txt_ids, img_ids, workspace, workspace_bytes, stream=None):
+    _check(lib().flux_qk_norm_rope(ctypes.byref(cfg), batch, n_txt, n_img, _ptr(q), _ptr(k), ld,
+                                   _ptr(q_norm_txt), _ptr(k_norm_txt), _ptr(q_norm_img),
+                                   _ptr(k_norm_img), _ptr(txt_ids), _ptr(img_ids),
+                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def flux_attention(cfg, batch, seq, q, k, v, ld_in, o, ld_out, stream=None):
+    _check(lib().flux_attention(ctypes.byref(cfg), batch, seq, _ptr(q), _ptr(k), _ptr(v), ld_in,
+                                _ptr(o), ld_out, _stream(stream)))
+
+
+def flux_linear(cfg, epilogue, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid=None, ldr=0,
+                gate=None, rows_per_batch=1, stream=None):
+    _check(lib().flux_linear(ctypes.byref(cfg), epilogue, m, n, k, _ptr(x), ldx, _ptr(w), ldw,
+                             _ptr(y), ldy, y_dtype, _ptr(resid), ldr, _ptr(gate), rows_per_batch,
+                             _stream(stream)))

@@ -1,0 +1,243 @@
+/*
+ * flux.h - C ABI of libflux, an MI355X (gfx950) forward pass of the FLUX.2-style MMDiT
+ * denoiser: double-stream block, single-stream block and the full denoiser step.
+ *
+ * Sources of the operations (the "pages"):
+ *   [TRACE] "FLUX.2 Klein 9B Base 宏观架构" shape trace (flux-vis), sections 1-4
+ *   [DIFF]  "Diffusers 中 Flux2Transformer2DModel 全面解析" (trdm.cn), sections
+ *           模型配置参数全解, 前向传播输入输出约定, 双流块, 单流块, 激活函数与 FFN
+ *   [KLEIN] "FLUX.2 [klein]" research note (zhao9797.github.io), section 模型架构
+ *   [SDPA]  "Transformer架构解析FLUX.2-klein-base-9b-nvfp4" (kwkr.cn), section 2
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or retains them; scratch memory is the caller's `workspace`
+ *     (size from the matching *_workspace_size query, 256-byte aligned).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Nothing is synchronised.  Overlapping calls on different streams must
+ *     use different workspaces.
+ *   - Arguments are validated before anything is enqueued: a non-OK status means no
+ *     work was enqueued, and flux_last_error() returns a message (thread-local).
+ *   - A HIP launch/runtime error reported while enqueuing returns FLUX_EHIP.  Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Linear weights are stored [out, in] row-major (y = x W^T), no biases.  Every
+ *     activation / weight pointer and leading dimension must be 16-byte aligned.
+ *   - Storage type: `dtype` FLUX_BF16 = bfloat16 (compute: bf16 MFMA, fp32 accumulate);
+ *     FLUX_F32 = float32 everywhere (fp32 compute).  QK-norm scales, timesteps and
+ *     modulation vectors are always float32.
+ */
+#ifndef FLUX_H
+#define FLUX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLUX_OK = 0,
+  FLUX_EINVAL = 1,     /* NULL pointer, non-positive size, unsupported value        */
+  FLUX_ESHAPE = 2,     /* inconsistent dimensions (dim != heads*head_dim, ...)      */
+  FLUX_EDTYPE = 3,     /* unknown dtype                                             */
+  FLUX_EALIGN = 4,     /* pointer or leading dimension not 16-byte aligned          */
+  FLUX_EWORKSPACE = 5, /* workspace NULL / too small / not 256-byte aligned         */
+  FLUX_EHIP = 6        /* HIP runtime error while enqueuing                         */
+} flux_status;
+
+typedef enum { FLUX_BF16 = 0, FLUX_F32 = 1 } flux_dtype;
+
+/* Model hyper-parameters ([DIFF] 模型配置参数全解; [KLEIN] config table).
+ * head_dim must be 128; dim = heads * head_dim; axes_dim are the per-axis RoPE widths
+ * (even, summing to head_dim; the pages use 32,32,32,32); rope_theta 2000; eps 1e-6.
+ * in_channels / context_dim / n_double / n_single are used by the step only. */
+typedef struct {
+  int32_t dim;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t mlp_hidden;
+  int32_t axes_dim[4];
+  float rope_theta;
+  float eps;
+  int32_t in_channels;
+  int32_t context_dim;
+  int32_t n_double;
+  int32_t n_single;
+  int32_t dtype; /* flux_dtype */
+} flux_cfg;
+
+/* Timestep MLPEmbedder: temb = w2 silu(w1 sinusoid(1000 t)); w1 [D,256], w2 [D,D]. */
+typedef struct {
+  const void* w1;
+  const void* w2;
+} flux_temb_weights;
+
+/* One stream of a double block ([DIFF] 双流块):
+ *   qkv [3D, D] rows q | k | v (head-major inside each of q, k, v);  out [D, D];
+ *   mlp_in [2H, D] rows gate | up;  mlp_out [D, H];  q_norm, k_norm [head_dim] fp32. */
+typedef struct {
+  const void* qkv;
+  const void* out;
+  const void* mlp_in;
+  const void* mlp_out;
+  const float* q_norm;
+  const float* k_norm;
+} flux_stream_weights;
+
+/* Double-stream block: mod_img / mod_txt [6D, D] give per stream the chunks
+ * (shift1, scale1, gate1, shift2, scale2, gate2) from silu(temb). */
+typedef struct {
+  flux_temb_weights temb;
+  const void* mod_img;
+  const void* mod_txt;
+  flux_stream_weights img;
+  flux_stream_weights txt;
+} flux_double_weights;
+
+/* Single-stream block ([DIFF] 单流块): mod [3D, D] -> (shift, scale, gate);
+ * linear1 [3D+2H, D] rows q | k | v | gate | up;  linear2 [D, D+H] columns attn | mlp. */
+typedef struct {
+  flux_temb_weights temb;
+  const void* mod;
+  const void* linear1;
+  const void* linear2;
+  const float* q_norm;
+  const float* k_norm;
+} flux_single_weights;
+
+/* Whole denoiser ([TRACE] section 3).  img_in [D, in_channels]; txt_in [D, context_dim];
+ * model-level modulation shared by all blocks of a kind: mod_double_img/_txt [6D, D],
+ * mod_single [3D, D], mod_final [2D, D] -> (shift, scale); proj_out [in_channels, D].
+ * double_blocks[n_double] / single_blocks[n_single] are HOST arrays of per-block
+ * weights whose temb / mod fields are ignored (the step shares its own). */
+typedef struct {
+  const void* img_in;
+  const void* txt_in;
+  flux_temb_weights temb;
+  const void* mod_double_img;
+  const void* mod_double_txt;
+  const void* mod_single;
+  const void* mod_final;
+  const void* proj_out;
+  const flux_double_weights* double_blocks;
+  const flux_single_weights* single_blocks;
+} flux_model_weights;
+
+/* Last error message of the calling thread ("" if none). */
+const char* flux_last_error(void);
+
+/* Library version string. */
+const char* flux_version(void);
+
+/* ---------------------------------------------------------------------------------
+ * Blocks and step
+ * ------------------------------------------------------------------------------- */
+
+/* Double-stream block ([TRACE] section 4; [DIFF] 双流块 Flux2TransformerBlock).
+ *   t        device float[batch], timestep in [0,1] (multiplied by 1000 inside)
+ *   img      device [batch, n_img, dim] (dtype);  txt device [batch, n_txt, dim]
+ *   img_ids  device int32 [n_img, 4];  txt_ids device int32 [n_txt, 4]  (shared by batch)
+ *   img_out, txt_out  device outputs, same shapes; may alias img / txt.
+ * The joint sequence is [txt ; img] (text first).  n_txt may be 0. */
+size_t flux_double_block_workspace_size(const flux_cfg* cfg, int batch, int n_img, int n_txt);
+int flux_double_block_fwd(const flux_cfg* cfg, const flux_double_weights* w, const float* t,
+                          int batch, int n_img, int n_txt, const void* img, const void* txt,
+                          const int32_t* img_ids, const int32_t* txt_ids, void* img_out,
+                          void* txt_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Single-stream block ([TRACE] section 4; [DIFF] 单流块 Flux2SingleTransformerBlock):
+ * merges [txt ; img], LayerNorm+modulate, linear1 -> q,k,v and SwiGLU(gate,up), joint
+ * attention, linear2 on [attn | mlp], gated residual; splits back.  Arguments as for the
+ * double block. */
+size_t flux_single_block_workspace_size(const flux_cfg* cfg, int batch, int n_img, int n_txt);
+int flux_single_block_fwd(const flux_cfg* cfg, const flux_single_weights* w, const float* t,
+                          int batch, int n_img, int n_txt, const void* img, const void* txt,
+                          const int32_t* img_ids, const int32_t* txt_ids, void* img_out,
+                          void* txt_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Full denoiser step ([TRACE] section 3; [DIFF] 前向传播输入输出约定):
+ *   x    device [batch, n_img, in_channels] (dtype), packed noisy latent tokens
+ *   ctx  device [batch, n_txt, context_dim] (dtype), text condition
+ *   t    device float[batch] in [0,1];  guidance must be NULL (no guidance embedder)
+ *   out  device float32 [batch, n_img, in_channels]
+ * Runs timestep embedding and all modulations once, the stems, n_double double blocks,
+ * n_single single blocks, the final LayerNorm+modulate and proj_out.  The residual
+ * stream is kept in float32 between blocks. */
+size_t flux_denoiser_step_workspace_size(const flux_cfg* cfg, int batch, int n_img, int n_txt);
+int flux_denoiser_step(const flux_cfg* cfg, const flux_model_weights* w, const float* t,
+                       const float* guidance, int batch, int n_img, int n_txt, const void* x,
+                       const void* ctx, const int32_t* img_ids, const int32_t* txt_ids,
+                       float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Single operations of the hot path (each is one kernel, or a short fixed sequence,
+ * of the blocks above; exported so each can be checked and timed on its own).
+ * ------------------------------------------------------------------------------- */
+
+/* RoPE position table ([DIFF] 位置 id 的维度): pos_out device int32 [n_txt+n_img, P]
+ * where P = head_dim/2 pairs; row j is joint token j of [txt ; img]; pair p takes the id
+ * of the axis whose dims contain 2p.  Integer work, bit-exact. */
+int flux_rope_positions(const flux_cfg* cfg, const int32_t* txt_ids, const int32_t* img_ids,
+                        int n_txt, int n_img, int32_t* pos_out, void* stream);
+
+/* Modulation vectors ([DIFF] 双流块 / 单流块 AdaLN; [KLEIN] 条件注入):
+ * out[b, :] = w_mod silu(w2 silu(w1 sinusoid(1000 t[b])))  -> device float [batch, n_out].
+ * w_mod [n_out, dim] (dtype).  Workspace from flux_modulation_workspace_size. */
+size_t flux_modulation_workspace_size(const flux_cfg* cfg, int batch);
+int flux_modulation(const flux_cfg* cfg, const flux_temb_weights* temb, const void* w_mod,
+                    int n_out, const float* t, int batch, float* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* LayerNorm (no affine, eps = cfg->eps) + modulate (1 + scale) x_hat + shift, per row
+ * ([DIFF] 双流块 AdaLN pre-norm).  x: device [rows, dim] of x_dtype (FLUX_BF16/FLUX_F32);
+ * shift, scale: device float [batch, dim] where row r uses batch r / rows_per_batch;
+ * y: device [rows, dim] of cfg->dtype. */
+int flux_layernorm_modulate(const flux_cfg* cfg, int rows, int rows_per_batch, const void* x,
+                            int x_dtype, const float* shift, const float* scale, void* y,
+                            void* stream);
+
+/* Per-head RMSNorm (eps = cfg->eps, scales gamma) then 4-axis RoPE, in place
+ * ([DIFF] 双流块 norm_q/norm_k; 位置 id 的维度; [KLEIN] theta 2000).
+ * q, k: device [batch, n_txt+n_img, ld] (cfg->dtype) holding head h of token j at
+ * column h*head_dim of row j; the joint order is [txt ; img].  Rows j < n_txt use
+ * (q_norm_txt, k_norm_txt), the others (q_norm_img, k_norm_img) (device float [128]).
+ * ids as for the blocks.  Workspace from flux_qk_norm_rope_workspace_size. */
+size_t flux_qk_norm_rope_workspace_size(const flux_cfg* cfg, int n_txt, int n_img);
+int flux_qk_norm_rope(const flux_cfg* cfg, int batch, int n_txt, int n_img, void* q, void* k,
+                      int64_t ld, const float* q_norm_txt, const float* k_norm_txt,
+                      const float* q_norm_img, const float* k_norm_img,
+                      const int32_t* txt_ids, const int32_t* img_ids, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Joint attention O = softmax(Q K^T / sqrt(head_dim)) V per head over the whole
+ * sequence, no mask ([SDPA]; [TRACE] Joint multi-head attention).
+ * q, k, v: device [batch, seq, ld_in] (cfg->dtype), head h at columns
+ * [h*head_dim, (h+1)*head_dim); o: device [batch, seq, ld_out]. */
+int flux_attention(const flux_cfg* cfg, int batch, int seq, const void* q, const void* k,
+                   const void* v, int64_t ld_in, void* o, int64_t ld_out, void* stream);
+
+/* Linear layer y = x W^T with an optional fused epilogue ([DIFF] 双流块 / 单流块 / 激活函数
+ * 与 FFN):
+ *   FLUX_EPI_STORE   y[m, n] = acc                                  (y: dtype y_dtype)
+ *   FLUX_EPI_SWIGLU  W has 2*n_half rows [gate | up]; y[m, j] = silu(acc_gate) * acc_up
+ *                    for j < n_half (pass n = 2*n_half)             (y: cfg->dtype)
+ *   FLUX_EPI_GATED_RESIDUAL
+ *                    y[m, n] = resid[m, n] + gate[m / rows_per_batch, n] * acc
+ *                    (resid, y: dtype y_dtype; gate device float [batch, n])
+ * x: device [m, ldx] (cfg->dtype); w: device [n, ldw] (cfg->dtype); k = reduction size. */
+typedef enum {
+  FLUX_EPI_STORE = 0,
+  FLUX_EPI_SWIGLU = 1,
+  FLUX_EPI_GATED_RESIDUAL = 2
+} flux_epilogue;
+int flux_linear(const flux_cfg* cfg, int epilogue, int m, int n, int k, const void* x,
+                int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy, int y_dtype,
+                const void* resid, int64_t ldr, const float* gate, int rows_per_batch,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLUX_H */

@@ -1,0 +1,122 @@
+"""Block-level parity with the fp64 oracle through the C ABI (double-stream block,
+single-stream block), identities that must hold bitwise, and determinism."""
+import numpy as np
+import pytest
+
+import flux_synth as fs
+from oracle import flux_oracle as O
+from tests import flux_gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from diffusion_transformer_mmdit_amd import flux as F
+    F.lib()
+
+
+def oracle_block(kind, inp):
+    fn = O.double_block if kind == "double" else O.single_block
+    return fn(inp["img"], inp["txt"], inp["t"], inp["weights"], inp["img_ids"], inp["txt_ids"])
+
+
+def run(kind, wl, inp):
+    return (G.run_double_block if kind == "double" else G.run_single_block)(wl, inp)
+
+
+def check_block(kind, wl, inp, what):
+    img, txt = run(kind, wl, inp)
+    ref_img, ref_txt = oracle_block(kind, inp)
+    G.assert_close(G.host(img), ref_img, wl.dtype, f"{what} img")
+    if wl.n_txt:
+        G.assert_close(G.host(txt), ref_txt, wl.dtype, f"{what} txt")
+    # the block's own contribution (output - input) must match too, not just the residual
+    d_got = G.host(img) - inp["img"].astype(np.float64)
+    d_ref = ref_img - inp["img"].astype(np.float64)
+    ma, nl = G.errors(d_got, d_ref)
+    rel_bar = 2e-2 if wl.dtype == "bf16" else 1e-4
+    # the output is stored in the workload dtype, so the update inherits the output's
+    # rounding (half an ulp: 2^-9 of |x| for bf16, 2^-24 for fp32) relative to its own norm
+    unit = 2.0 ** -9 if wl.dtype == "bf16" else 2.0 ** -24
+    floor = np.linalg.norm(inp["img"].astype(np.float64)) * unit / max(np.linalg.norm(d_ref), 1e-30)
+    print(f"[parity] {what} img update: nL2={nl:.3e} (bar {rel_bar:.0e} + 2 x rounding floor "
+          f"{floor:.1e})", flush=True)
+    assert nl <= rel_bar + 2 * floor, (nl, floor)
+
+
+# ------------------------------------------------------------------------------------
+# tiny configurations (fp32: the tiny single-stream workload; bf16 variants)
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("kind", ["single", "double"])
+def test_tiny_fp32_block(kind):
+    wl = fs.workload("tiny_single_f32")
+    inp = fs.block_inputs(wl, kind=kind)
+    check_block(kind, wl, inp, f"tiny fp32 {kind}")
+
+
+@pytest.mark.parametrize("kind", ["single", "double"])
+@pytest.mark.parametrize("n_txt,n_img,batch", [(16, 64, 1), (5, 36, 2), (0, 49, 1), (130, 196, 1)])
+def test_small_bf16_block(kind, n_txt, n_img, batch):
+    wl = fs.workload("tiny_single_f32", dtype="bf16", n_txt=n_txt, n_img=n_img, batch=batch,
+                     t_fixed=None, seed=2000 + n_img)
+    inp = fs.block_inputs(wl, kind=kind)
+    check_block(kind, wl, inp, f"bf16 {kind} Nt={n_txt} Ni={n_img} B={batch}")
+
+
+def test_tiny_fp32_single_batch_and_text_free():
+    wl = fs.workload("tiny_single_f32", n_txt=0, batch=2, t_fixed=None)
+    inp = fs.block_inputs(wl, kind="single")
+    check_block("single", wl, inp, "tiny fp32 single B=2 Nt=0")
+
+
+# ------------------------------------------------------------------------------------
+# workload shapes
+# ------------------------------------------------------------------------------------
+def test_klein4b_single_block_512():
+    wl = fs.workload("klein4b_single_512")
+    inp = fs.block_inputs(wl)
+    check_block("single", wl, inp, "Klein-4B single 512^2")
+
+
+def test_klein9b_double_block_1024():
+    wl = fs.workload("klein9b_double_1024")
+    inp = fs.block_inputs(wl)
+    check_block("double", wl, inp, "Klein-9B double 1024^2")
+
+
+# ------------------------------------------------------------------------------------
+# identities and determinism
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("kind,dtype", [("single", "bf16"), ("double", "bf16"), ("double", "f32")])
+def test_zero_gate_block_is_bitwise_identity(kind, dtype):
+    wl = fs.workload("tiny_single_f32", dtype=dtype, n_txt=16, n_img=64)
+    inp = fs.block_inputs(wl, kind=kind)
+    w = dict(inp["weights"])
+    D = wl.dim
+    names = ["mod"] if kind == "single" else ["mod_img", "mod_txt"]
+    chunks = [2] if kind == "single" else [2, 5]
+    for nm in names:
+        m = w[nm].copy()
+        for c in chunks:
+            m[c * D:(c + 1) * D] = 0
+        w[nm] = m
+    inp = dict(inp, weights=w)
+    img, txt = run(kind, wl, inp)
+    assert np.array_equal(G.host(img), inp["img"].astype(np.float64))
+    assert np.array_equal(G.host(txt), inp["txt"].astype(np.float64))
+
+
+@pytest.mark.parametrize("kind", ["single", "double"])
+def test_block_is_deterministic(kind):
+    wl = fs.workload("tiny_single_f32", dtype="bf16", n_txt=64, n_img=256, t_fixed=None,
+                     dim=512, heads=4, mlp_hidden=1536)
+    inp = fs.block_inputs(wl, kind=kind)
+    wd = G.upload_weights(inp["weights"], "bf16")
+    fn = G.run_double_block if kind == "double" else G.run_single_block
+    a = fn(wl, inp, wd)
+    b = fn(wl, inp, wd)
+    assert G.torch().equal(a[0], b[0]) and G.torch().equal(a[1], b[1])

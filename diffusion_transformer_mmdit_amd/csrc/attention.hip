@@ -4,17 +4,20 @@
 // shape trace, section 4).
 //
 // bf16 path (gfx950 MFMA 32x32x16, fp32 softmax and accumulation), flash style:
-//   * a workgroup of 4 waves owns 128 queries of one (batch, head); each wave 32 queries
-//     whose Q fragments stay in registers for the whole key loop;
-//   * K and V tiles of 64 keys are staged in LDS (double buffered, next tile's global
-//     loads issued before the current tile's MFMAs).  K is stored row-major with an XOR
-//     swizzle; V is transposed on its way into LDS (V^T[d][key]) so the PV product reads
-//     contiguous keys;
+//   * a workgroup of NW waves owns 32*NW queries of one (batch, head); each wave keeps
+//     the Q fragments of its 32 queries in registers for the whole key loop;
+//   * K tiles [64 keys][128] and V^T tiles [128][64 keys] are staged in LDS by direct
+//     global->LDS loads, double buffered.  V arrives already transposed (V^T, written by
+//     the QKV projection's epilogue), so no transposition happens here;
 //   * scores are computed transposed, S^T = K Q^T, so each lane owns one query and 32 of
-//     the tile's 64 keys: the row max and row sum need one cross-lane exchange (lane ^ 32);
-//     O^T = V^T P^T is accumulated the same way, so the online-softmax rescale is a
-//     per-lane scalar;
-//   * softmax uses exp2 with log2(e)/sqrt(d) folded into one FMA per score.
+//     the tile's 64 keys; the K rows are fed to the MFMA in a permuted order chosen so
+//     that every lane's 8 probabilities of a 16-key chunk are 8 CONSECUTIVE keys, which
+//     makes the V^T fragment of O^T = V^T P^T a single 16-byte LDS read;
+//   * softmax in the exp2 domain (log2(e)/sqrt(d) folded into one FMA per score) with a
+//     lazy running maximum: O and the row sum are rescaled only when a row's maximum
+//     grows by more than 2^8, which keeps p <= 256 and skips almost all rescales;
+//   * two workgroups per CU (<= 256 registers per wave) so one workgroup's softmax
+//     overlaps the other's MFMAs.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,69 +34,67 @@ FLUX_DEV T* seq_mptr(const SeqView& v, int b, int j) {
                     : static_cast<T*>(v.base1) + b * v.bs1 + (int64_t)(j - v.n0) * v.ld;
 }
 
-constexpr int kHD = 128;       // head dim
-constexpr int kBQ = 128;       // queries per workgroup
-constexpr int kBKV = 64;       // keys per tile
-constexpr int kVTLD = kBKV + 4;  // V^T row pitch (elements): 34 words -> conflict-free reads
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-FLUX_DEV int kswz(int row, int c) { return row * kHD + ((c ^ (row & 15)) << 3); }
+constexpr int kHD = 128;   // head dim
+constexpr int kBKV = 64;   // keys per tile
 
-__global__ __launch_bounds__(256) void flash_attn_bf16_kernel(SeqView qv, SeqView kv, SeqView vv,
-                                                              SeqView ov, int seq, int heads,
-                                                              float scale_log2) {
+// K tile: 64 rows of 256 B (16 chunks); chunk c of row r sits at slot c ^ (r & 15)
+FLUX_DEV int k_off(int row, int c) { return row * kHD + ((c ^ (row & 15)) << 3); }
+// V^T tile: 128 rows (d) of 128 B (8 chunks of 8 keys); slot = c ^ ((d >> 1) & 7)
+FLUX_DEV int v_off(int d, int c) { return d * kBKV + ((c ^ ((d >> 1) & 7)) << 3); }
+// MFMA row m of a 32-key S^T block reads key sigma(m) of the block: with
+// m = 8q + 4g + t the lane group g of register block q gets keys 16(q>>1) + 8g + 4(q&1) + t
+FLUX_DEV int key_perm(int m) {
+  const int q = m >> 3, g = (m >> 2) & 1, t = m & 3;
+  return 16 * (q >> 1) + 8 * g + 4 * (q & 1) + t;
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
+    SeqView qv, SeqView kv, const bf16* __restrict__ vt, int64_t ld_vt, int dim, SeqView ov,
+    int seq, float scale_log2) {
+  constexpr int NT = 64 * NW;
   __shared__ __align__(16) bf16 Ks[2][kBKV * kHD];
-  __shared__ __align__(16) bf16 VTs[2][kHD * kVTLD];
+  __shared__ __align__(16) bf16 Vs[2][kHD * kBKV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int head = blockIdx.y, b = blockIdx.z;
-  const int q0 = blockIdx.x * kBQ + wave * 32;
+  const int q0 = blockIdx.x * (32 * NW) + wave * 32;
   const int hoff = head * kHD;
 
   // ---- Q fragments (B operand of S^T = K Q^T): query l32, dims 16 kk + 8 g .. + 8
   bf16x8 qf[8];
   {
-    const int qi = q0 + l32;
-    if (qi < seq) {
-      const bf16* qp = seq_cptr<bf16>(qv, b, qi) + hoff + 8 * g;
+    const int qi = min(q0 + l32, seq - 1);
+    const bf16* qp = seq_cptr<bf16>(qv, b, qi) + hoff + 8 * g;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[kk][e] = static_cast<bf16>(0.f);
-    }
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
   }
 
-  // ---- tile loaders: K rows (t>>4)+16i, chunk t&15; V keys 4(t&15)+i, dims 8(t>>4)..+8
-  const int kc = tid & 15, kr = tid >> 4;
-  const int vkg = tid & 15, vdc = tid >> 4;
-  uint4 kreg[4], vreg[4];
-  auto load_tile = [&](int kv0) {
+  // ---- direct-load plan.  K: one wave instruction = 4 rows x 256 B; lane -> row
+  // (lane >> 4), slot (lane & 15).  V^T: one instruction = 8 rows x 128 B; lane -> row
+  // (lane >> 3), slot (lane & 7).  Each lane fetches the logical chunk of its slot.
+  constexpr int KI = 16 / NW;  // K instructions per wave per tile (64 rows / 4)
+  constexpr int VI = 16 / NW;  // V instructions per wave per tile (128 rows / 8)
+  const bf16* vt_head = vt + ((int64_t)b * dim + hoff) * ld_vt;
+  auto issue = [&](int buf, int kv0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kv0 + kr + 16 * i;
-      kreg[i] = key < seq ? ld16(seq_cptr<bf16>(kv, b, key) + hoff + kc * 8) : make_uint4(0, 0, 0, 0);
-      const int vkey = kv0 + 4 * vkg + i;
-      vreg[i] = vkey < seq ? ld16(seq_cptr<bf16>(vv, b, vkey) + hoff + vdc * 8) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < KI; ++j) {
+      const int row = (wave * KI + j) * 4 + (lane >> 4);
+      const int key = min(kv0 + row, seq - 1);  // past the end: a valid row, masked later
+      const int c = (lane & 15) ^ (row & 15);
+      const bf16* src = seq_cptr<bf16>(kv, b, key) + hoff + c * 8;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&Ks[buf][(wave * KI + j) * 4 * kHD], 16, 0, 0);
     }
-  };
-  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st16(&Ks[buf][kswz(kr + 16 * i, kc)], kreg[i]);
-    const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
-                              {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
-                              {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
-                              {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16;
-      const uint32_t a0 = (w[0][e >> 1] >> sh) & 0xffffu, a1 = (w[1][e >> 1] >> sh) & 0xffffu;
-      const uint32_t a2 = (w[2][e >> 1] >> sh) & 0xffffu, a3 = (w[3][e >> 1] >> sh) & 0xffffu;
-      uint2 pk = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-      *reinterpret_cast<uint2*>(&VTs[buf][(vdc * 8 + e) * kVTLD + 4 * vkg]) = pk;
+    for (int j = 0; j < VI; ++j) {
+      const int d = (wave * VI + j) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((d >> 1) & 7);
+      const bf16* src = vt_head + (int64_t)d * ld_vt + kv0 + c * 8;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&Vs[buf][(wave * VI + j) * 8 * kBKV], 16, 0, 0);
     }
   };
 
@@ -103,18 +104,19 @@ __global__ __launch_bounds__(256) void flash_attn_bf16_kernel(SeqView qv, SeqVie
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const int krow0 = key_perm(l32), krow1 = 32 + key_perm(l32);
 
   const int ntiles = (seq + kBKV - 1) / kBKV;
-  load_tile(0);
-  store_tile(0);
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
     const int kv0 = it * kBKV;
-    if (it + 1 < ntiles) load_tile(kv0 + kBKV);
+    if (it + 1 < ntiles) issue(cur ^ 1, kv0 + kBKV);
 
-    // S^T = K Q^T for keys [kv0, kv0 + 64): s[0] keys 0..31, s[1] keys 32..63
+    // S^T = K Q^T: s[h] covers MFMA rows of key block h (keys 32 h + key_perm(row))
     f32x16 s[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -122,71 +124,66 @@ __global__ __launch_bounds__(256) void flash_attn_bf16_kernel(SeqView qv, SeqVie
       for (int r = 0; r < 16; ++r) s[h][r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[cur][kswz(l32, 2 * kk + g)]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[cur][kswz(32 + l32, 2 * kk + g)]);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[cur][k_off(krow0, 2 * kk + g)]);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[cur][k_off(krow1, 2 * kk + g)]);
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[kk], s[1], 0, 0, 0);
     }
-
-    // mask keys past the end (only the last tile can have them)
+    // register r of block h holds key 32 h + 16 (r >> 3) + 8 g + (r & 7)
     if (kv0 + kBKV > seq) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= seq) s[h][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kv0 + 32 * h + 16 * (r >> 3) + 8 * g + (r & 7) >= seq) s[h][r] = -INFINITY;
     }
 
-    // online softmax (raw-score units; exp2 argument scaled by log2(e)/sqrt(d))
+    // online softmax with a lazily updated maximum (log2 domain)
     float mx = s[0][0];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f((m_run - m_new) * scale_log2);
-    const float mb = m_new * scale_log2;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    const bool grow = mx > m_run + 8.f;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(s[h][r], scale_log2, -mb));
+        // raw v_exp_f32: arguments are <= 8, results below 2^-126 may flush to zero
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[h][r], scale_log2, -m_run));
         s[h][r] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    l_run += psum;
 
-    // O^T += V^T P^T over 4 chunks of 16 keys
+    // O^T += V^T P^T over 4 chunks of 16 keys; lane group g owns keys 16 c + 8 g .. + 8
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      bf16x8 pf;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pf[i] = static_cast<bf16>(s[c >> 1][8 * (c & 1) + i]);
+      const int h = c >> 1, r0 = 8 * (c & 1);
+      const uint4 pw = make_uint4(pack2(s[h][r0], s[h][r0 + 1]), pack2(s[h][r0 + 2], s[h][r0 + 3]),
+                                  pack2(s[h][r0 + 4], s[h][r0 + 5]), pack2(s[h][r0 + 6], s[h][r0 + 7]));
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const bf16* vrow = &VTs[cur][(32 * dt + l32) * kVTLD + 16 * c + 4 * g];
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 8);
-        bf16x8 vf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vf[i] = lo[i];
-          vf[4 + i] = hi[i];
-        }
+        const bf16x8 vf =
+            *reinterpret_cast<const bf16x8*>(&Vs[cur][v_off(32 * dt + l32, 2 * c + g)]);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[dt], 0, 0, 0);
       }
     }
 
-    if (it + 1 < ntiles) store_tile(cur ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
@@ -209,23 +206,25 @@ __global__ __launch_bounds__(256) void flash_attn_bf16_kernel(SeqView qv, SeqVie
 }
 
 // fp32 path (tiny fp32 workloads): one wave per (query, head); each lane owns 2 dims.
-__global__ __launch_bounds__(64) void attn_f32_kernel(SeqView qv, SeqView kv, SeqView vv,
-                                                      SeqView ov, int seq, int heads, float scale) {
+__global__ __launch_bounds__(64) void attn_f32_kernel(SeqView qv, SeqView kv,
+                                                      const float* __restrict__ vt, int64_t ld_vt,
+                                                      int dim, SeqView ov, int seq, float scale) {
   const int lane = threadIdx.x;
   const int qi = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const int d = head * kHD + 2 * lane;
   const float* qp = seq_cptr<float>(qv, b, qi) + d;
   const float q0 = qp[0], q1 = qp[1];
+  const float* v0 = vt + ((int64_t)b * dim + d) * ld_vt;
+  const float* v1 = v0 + ld_vt;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   for (int j = 0; j < seq; ++j) {
     const float* kp = seq_cptr<float>(kv, b, j) + d;
     const float s = wave_sum(q0 * kp[0] + q1 * kp[1]) * scale;
     const float m_new = fmaxf(m, s);
     const float a = expf(m - m_new), p = expf(s - m_new);
-    const float* vp = seq_cptr<float>(vv, b, j) + d;
     l = l * a + p;
-    o0 = o0 * a + p * vp[0];
-    o1 = o1 * a + p * vp[1];
+    o0 = o0 * a + p * v0[j];
+    o1 = o1 * a + p * v1[j];
     m = m_new;
   }
   float* op = seq_mptr<float>(ov, b, qi) + d;
@@ -233,19 +232,98 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(SeqView qv, SeqView kv, Se
   op[1] = o1 / l;
 }
 
-hipError_t attention(int dtype, SeqView q, SeqView k, SeqView v, SeqView o, int batch, int seq,
-                     int heads, hipStream_t s) {
+static int attn_waves(int seq, int heads, int batch) {
+  // 2 resident workgroups per CU; pick the workgroup size (2 or 4 waves of 32 queries)
+  // that wastes the least of the last round of workgroups
+  const int cus = 256;
+  double best_t = 1e300;
+  int best = 4;
+  for (int nw : {4, 2}) {
+    const long wgs = (long)((seq + 32 * nw - 1) / (32 * nw)) * heads * batch;
+    const long slots = 2L * cus * (4 / nw);  // same number of resident waves
+    const double t = (double)((wgs + slots - 1) / slots) * nw;
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best = nw;
+    }
+  }
+  return best;
+}
+
+hipError_t attention(int dtype, SeqView q, SeqView k, const void* vt, int64_t ld_vt, SeqView o,
+                     int batch, int seq, int heads, hipStream_t s) {
   if (seq <= 0 || batch <= 0) return hipSuccess;
+  const int dim = heads * kHD;
   if (dtype == DT_BF16) {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHD);
-    dim3 grid((seq + kBQ - 1) / kBQ, heads, batch);
-    hipLaunchKernelGGL(flash_attn_bf16_kernel, grid, dim3(256), 0, s, q, k, v, o, seq, heads,
-                       scale_log2);
+    const int nw = attn_waves(seq, heads, batch);
+    dim3 grid((seq + 32 * nw - 1) / (32 * nw), heads, batch);
+    if (nw == 4)
+      hipLaunchKernelGGL(flash_attn_bf16_kernel<4>, grid, dim3(256), 0, s, q, k,
+                         static_cast<const bf16*>(vt), ld_vt, dim, o, seq, scale_log2);
+    else
+      hipLaunchKernelGGL(flash_attn_bf16_kernel<2>, grid, dim3(128), 0, s, q, k,
+                         static_cast<const bf16*>(vt), ld_vt, dim, o, seq, scale_log2);
   } else {
     dim3 grid(seq, heads, batch);
-    hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(64), 0, s, q, k, v, o, seq, heads,
-                       1.f / sqrtf((float)kHD));
+    hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(64), 0, s, q, k, static_cast<const float*>(vt),
+                       ld_vt, dim, o, seq, 1.f / sqrtf((float)kHD));
   }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
+// V -> V^T (for callers that hold V token-major) and zeroing of the V^T row padding
+// ------------------------------------------------------------------------------------
+template <class T>
+__global__ void transpose_v_kernel(SeqView v, T* __restrict__ vt, int64_t ld_vt, int dim,
+                                   int seq) {
+  __shared__ T tile[32][33];
+  const int b = blockIdx.z;
+  const int j0 = blockIdx.x * 32, f0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8 threads
+  for (int r = ty; r < 32; r += 8) {
+    const int j = j0 + r, f = f0 + tx;
+    tile[r][tx] = (j < seq && f < dim) ? seq_cptr<T>(v, b, j)[f] : T(0.f);
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int f = f0 + r, j = j0 + tx;
+    if (f < dim && j < seq) vt[((int64_t)b * dim + f) * ld_vt + j] = tile[tx][r];
+  }
+}
+
+hipError_t transpose_v(int dtype, SeqView v, void* vt, int64_t ld_vt, int dim, int batch, int seq,
+                       hipStream_t s) {
+  dim3 grid((seq + 31) / 32, (dim + 31) / 32, batch), block(256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(transpose_v_kernel<bf16>, grid, block, 0, s, v, static_cast<bf16*>(vt),
+                       ld_vt, dim, seq);
+  else
+    hipLaunchKernelGGL(transpose_v_kernel<float>, grid, block, 0, s, v, static_cast<float*>(vt),
+                       ld_vt, dim, seq);
+  return hipGetLastError();
+}
+
+template <class T>
+__global__ void zero_cols_kernel(T* __restrict__ p, int64_t ld, int64_t rows, int c0, int c1) {
+  const int w = c1 - c0;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * w) return;
+  const int64_t r = idx / w;
+  p[r * ld + c0 + (idx % w)] = T(0.f);
+}
+
+hipError_t zero_cols(int dtype, void* p, int64_t ld, int64_t rows, int c0, int c1, hipStream_t s) {
+  const int64_t total = rows * (c1 - c0);
+  if (total <= 0) return hipSuccess;
+  dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(zero_cols_kernel<bf16>, grid, block, 0, s, static_cast<bf16*>(p), ld, rows,
+                       c0, c1);
+  else
+    hipLaunchKernelGGL(zero_cols_kernel<float>, grid, block, 0, s, static_cast<float*>(p), ld, rows,
+                       c0, c1);
   return hipGetLastError();
 }
 

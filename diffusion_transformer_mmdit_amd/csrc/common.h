@@ -37,10 +37,13 @@ FLUX_DEV void unpack8(uint4 v, float* f) {
   }
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
 FLUX_DEV uint32_t pack2(float a, float b) {
-  bf16 x = static_cast<bf16>(a), y = static_cast<bf16>(b);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, y)) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 FLUX_DEV uint4 pack8(const float* f) {

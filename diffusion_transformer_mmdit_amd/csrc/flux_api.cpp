@@ -183,12 +183,40 @@ static int lin(const flux_cfg* c, int epi, int m, int n, int k, const void* x, i
   return FLUX_OK;
 }
 
+// q | k row-major into qk [m, 2D]; v transposed into vt [B*D, ldvt] at token offset vt_off
+static int lin_qkv(const flux_cfg* c, int m, const void* x, const void* w, void* qk, void* vt,
+                   int64_t ldvt, int vt_off, int rpb, hipStream_t s) {
+  LinearArgs a{};
+  a.epilogue = EPI_QKV;
+  a.m = m;
+  a.n = 3 * c->dim;
+  a.k = c->dim;
+  a.x = x;
+  a.ldx = c->dim;
+  a.w = w;
+  a.ldw = c->dim;
+  a.y = qk;
+  a.ldy = 2 * c->dim;
+  a.y_dtype = c->dtype;
+  a.rows_per_batch = rpb;
+  a.vt = vt;
+  a.ldvt = ldvt;
+  a.vt_off = vt_off;
+  a.dim = c->dim;
+  HIP_TRY(linear(c->dtype, a, s));
+  return FLUX_OK;
+}
+
+// V^T row pitch: the sequence rounded up to the attention's 64-key tiles
+static int64_t vt_pitch(int L) { return ((int64_t)L + 63) / 64 * 64; }
+
 // ------------------------------------------------------------------------------------
 // double-stream block
 // ------------------------------------------------------------------------------------
 struct DoubleScratch {
   void* ln[2];    // [B*N_s, D] compute dtype       (0 = txt, 1 = img)
-  void* qkv[2];   // [B*N_s, 3D]
+  void* qk[2];    // [B*N_s, 2D] q | k
+  void* vt;       // [B*D, vt_pitch(L)] V^T of the joint sequence
   void* o[2];     // [B*N_s, D]
   float* mid[2];  // [B*N_s, D] residual after the attention branch
   void* mlp[2];   // [B*N_s, H]
@@ -202,11 +230,12 @@ static DoubleScratch carve_double(Carver& cv, const flux_cfg* c, int B, int Ni, 
   for (int i = 0; i < 2; ++i) {
     const size_t rows = (size_t)B * n[i];
     d.ln[i] = cv.take<char>(rows * D * es);
-    d.qkv[i] = cv.take<char>(rows * 3 * D * es);
+    d.qk[i] = cv.take<char>(rows * 2 * D * es);
     d.o[i] = cv.take<char>(rows * D * es);
     d.mid[i] = cv.take<float>(rows * D);
     d.mlp[i] = cv.take<char>(rows * H * es);
   }
+  d.vt = cv.take<char>((size_t)B * D * vt_pitch(Ni + Nt) * es);
   return d;
 }
 
@@ -235,16 +264,17 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
   const int D = c->dim, H = c->mlp_hidden, T = c->dtype;
   const int n[2] = {Nt, Ni};
   const int64_t mbs = 6 * (int64_t)D;
+  const int L = Nt + Ni;
+  const int64_t ldvt = vt_pitch(L);
   for (int i = 0; i < 2; ++i) {
     if (n[i] == 0) continue;
     const int rows = B * n[i];
     HIP_TRY(layernorm_modulate(in_dt, T, in[i], D, d.ln[i], D, rows, D, n[i], mods[i],
                                mods[i] + D, mbs, c->eps, s));
-    CHECK(lin(c, EPI_STORE, rows, 3 * D, D, d.ln[i], D, sw[i]->qkv, D, d.qkv[i], 3 * D, T,
-              nullptr, 0, 0, nullptr, 0, 1, s));
+    CHECK(lin_qkv(c, rows, d.ln[i], sw[i]->qkv, d.qk[i], d.vt, ldvt, i == 0 ? 0 : Nt, n[i], s));
   }
+  if (ldvt > L) HIP_TRY(zero_cols(T, d.vt, ldvt, (int64_t)B * D, L, (int)ldvt, s));
   // joint views: segment 0 = text rows, segment 1 = image rows
-  const int L = Nt + Ni;
   const int es = esize(T);
   auto view = [&](int col, void* const* bufs, int64_t ld) {
     SeqView v;
@@ -256,11 +286,11 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
     v.n0 = Nt;
     return v;
   };
-  SeqView qv = view(0, d.qkv, 3 * D), kv = view(D, d.qkv, 3 * D), vv = view(2 * D, d.qkv, 3 * D);
+  SeqView qv = view(0, d.qk, 2 * D), kv = view(D, d.qk, 2 * D);
   SeqView ov = view(0, d.o, D);
   HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, sw[0]->q_norm, sw[0]->k_norm, sw[1]->q_norm,
                        sw[1]->k_norm, cs, c->eps, s));
-  HIP_TRY(attention(T, qv, kv, vv, ov, B, L, c->heads, s));
+  HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, s));
   for (int i = 0; i < 2; ++i) {
     if (n[i] == 0) continue;
     const int rows = B * n[i];
@@ -340,7 +370,8 @@ extern "C" int flux_double_block_fwd(const flux_cfg* c, const flux_double_weight
 // ------------------------------------------------------------------------------------
 struct SingleScratch {
   void* ln;   // [B*L, D]
-  void* qkv;  // [B*L, 3D]
+  void* qk;   // [B*L, 2D] q | k
+  void* vt;   // [B*D, vt_pitch(L)] V^T
   void* cat;  // [B*L, D + H]  = [attention output | SwiGLU output]
 };
 
@@ -349,7 +380,8 @@ static SingleScratch carve_single(Carver& cv, const flux_cfg* c, int B, int L) {
   const int es = esize(c->dtype);
   const size_t rows = (size_t)B * L;
   d.ln = cv.take<char>(rows * c->dim * es);
-  d.qkv = cv.take<char>(rows * 3 * c->dim * es);
+  d.qk = cv.take<char>(rows * 2 * c->dim * es);
+  d.vt = cv.take<char>((size_t)B * c->dim * vt_pitch(L) * es);
   d.cat = cv.take<char>(rows * (c->dim + c->mlp_hidden) * es);
   return d;
 }
@@ -374,8 +406,9 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
   const int rows = B * L;
   const int64_t mbs = 3 * (int64_t)D, ldc = D + H;
   HIP_TRY(layernorm_modulate(in_dt, T, x, D, d.ln, D, rows, D, L, mod, mod + D, mbs, c->eps, s));
-  CHECK(lin(c, EPI_STORE, rows, 3 * D, D, d.ln, D, w->linear1, D, d.qkv, 3 * D, T, nullptr, 0, 0,
-            nullptr, 0, 1, s));
+  const int64_t ldvt = vt_pitch(L);
+  CHECK(lin_qkv(c, rows, d.ln, w->linear1, d.qk, d.vt, ldvt, 0, L, s));
+  if (ldvt > L) HIP_TRY(zero_cols(T, d.vt, ldvt, (int64_t)B * D, L, (int)ldvt, s));
   const char* w_mlp = static_cast<const char*>(w->linear1) + (size_t)3 * D * D * es;
   CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln, D, w_mlp, D,
             static_cast<char*>(d.cat) + (size_t)D * es, ldc, T, nullptr, 0, 0, nullptr, 0, 1, s));
@@ -387,11 +420,11 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
     v.n0 = L;
     return v;
   };
-  SeqView qv = view(d.qkv, 0, 3 * D), kv = view(d.qkv, D, 3 * D), vv = view(d.qkv, 2 * D, 3 * D);
+  SeqView qv = view(d.qk, 0, 2 * D), kv = view(d.qk, D, 2 * D);
   SeqView ov = view(d.cat, 0, ldc);
   HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, w->q_norm, w->k_norm, w->q_norm, w->k_norm, cs,
                        c->eps, s));
-  HIP_TRY(attention(T, qv, kv, vv, ov, B, L, c->heads, s));
+  HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, s));
   CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D + H, d.cat, ldc, w->linear2, D + H, out, D, out_dt,
             x, D, in_dt, mod + 2 * D, mbs, L, s));
   return FLUX_OK;
@@ -708,9 +741,16 @@ extern "C" int flux_qk_norm_rope(const flux_cfg* c, int B, int n_txt, int n_img,
   return FLUX_OK;
 }
 
+extern "C" size_t flux_attention_workspace_size(const flux_cfg* c, int B, int seq) {
+  if (check_cfg(c) != FLUX_OK || B <= 0 || seq <= 0) return 0;
+  Carver cv(nullptr);
+  cv.take<char>((size_t)B * c->dim * vt_pitch(seq) * esize(c->dtype));
+  return cv.off;
+}
+
 extern "C" int flux_attention(const flux_cfg* c, int B, int seq, const void* q, const void* k,
-                              const void* v, int64_t ld_in, void* o, int64_t ld_out,
-                              void* stream) {
+                              const void* v, int64_t ld_in, void* o, int64_t ld_out, void* ws,
+                              size_t ws_bytes, void* stream) {
   CHECK(check_cfg(c));
   if (B <= 0 || seq <= 0) return fail(FLUX_EINVAL, "batch and seq must be > 0");
   const int es = esize(c->dtype);
@@ -720,6 +760,7 @@ extern "C" int flux_attention(const flux_cfg* c, int B, int seq, const void* q, 
   CHECK(need(k, "k"));
   CHECK(need(v, "v"));
   CHECK(need(o, "o"));
+  CHECK(check_ws(ws, ws_bytes, flux_attention_workspace_size(c, B, seq)));
   auto mk = [&](const void* base, int64_t ld) {
     SeqView sv;
     sv.base0 = sv.base1 = const_cast<void*>(base);
@@ -728,8 +769,12 @@ extern "C" int flux_attention(const flux_cfg* c, int B, int seq, const void* q, 
     sv.n0 = seq;
     return sv;
   };
-  HIP_TRY(attention(c->dtype, mk(q, ld_in), mk(k, ld_in), mk(v, ld_in), mk(o, ld_out), B, seq,
-                    c->heads, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ldvt = vt_pitch(seq);
+  HIP_TRY(transpose_v(c->dtype, mk(v, ld_in), ws, ldvt, c->dim, B, seq, s));
+  if (ldvt > seq) HIP_TRY(zero_cols(c->dtype, ws, ldvt, (int64_t)B * c->dim, seq, (int)ldvt, s));
+  HIP_TRY(attention(c->dtype, mk(q, ld_in), mk(k, ld_in), ws, ldvt, mk(o, ld_out), B, seq,
+                    c->heads, s));
   return FLUX_OK;
 }
 

@@ -26,6 +26,7 @@ struct EpiStore {
   TY* y;
   int64_t ldy;
   static constexpr bool kPaired = false;
+  static constexpr bool kQuad = false;
   FLUX_DEV void operator()(int m, int n, float v) const { y[m * ldy + n] = from_f32<TY>(v); }
 };
 
@@ -35,6 +36,7 @@ struct EpiSwiGLU {
   int64_t ldy;
   int n_half;  // H
   static constexpr bool kPaired = true;
+  static constexpr bool kQuad = false;
   // logical column n of the interleaved [gate | up] tile -> physical W row
   FLUX_DEV static int phys_row(int n, int H) {
     const int j = ((n >> 6) << 5) + (n & 31);
@@ -55,9 +57,53 @@ struct EpiGatedResid {
   int64_t gate_bs;
   int rpb;
   static constexpr bool kPaired = false;
+  static constexpr bool kQuad = false;
   FLUX_DEV void operator()(int m, int n, float v) const {
     const int b = m / rpb;
     y[m * ldy + n] = from_f32<TY>(to_f32(r[m * ldr + n]) + gate[b * gate_bs + n] * v);
+  }
+};
+
+// q | k row-major, v transposed (V^T feeds the attention's PV product directly)
+template <class TY>
+struct EpiQKV {
+  TY* y;
+  int64_t ldy;
+  TY* vt;
+  int64_t ldvt;
+  int two_d, dim, rpb, vt_off;
+  static constexpr bool kPaired = false;
+  static constexpr bool kQuad = true;
+  FLUX_DEV void operator()(int m, int n, float v) const {
+    if (n < two_d) {
+      y[m * ldy + n] = from_f32<TY>(v);
+    } else {
+      const int b = m / rpb, i = m - b * rpb;
+      vt[((int64_t)b * dim + (n - two_d)) * ldvt + vt_off + i] = from_f32<TY>(v);
+    }
+  }
+  // rows m .. m+3 of column n (m % 4 == 0): the V^T part gets one 8-byte store when the
+  // four tokens are consecutive in one batch row and 8-byte aligned
+  FLUX_DEV void quad(int m, int n, float v0, float v1, float v2, float v3, int M) const {
+    if (n < two_d) {
+      TY* p = y + m * ldy + n;
+      p[0] = from_f32<TY>(v0);
+      if (m + 1 < M) p[ldy] = from_f32<TY>(v1);
+      if (m + 2 < M) p[2 * ldy] = from_f32<TY>(v2);
+      if (m + 3 < M) p[3 * ldy] = from_f32<TY>(v3);
+      return;
+    }
+    const int b = m / rpb, i = m - b * rpb;
+    TY* p = vt + ((int64_t)b * dim + (n - two_d)) * ldvt + vt_off + i;
+    if (sizeof(TY) == 2 && m + 3 < M && i + 3 < rpb && ((vt_off + i) & 3) == 0) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(pack2(v0, v1), pack2(v2, v3));
+      return;
+    }
+    // rows that cross a batch boundary or the end (not reached for 4-aligned shapes)
+    (*this)(m, n, v0);
+    if (m + 1 < M) (*this)(m + 1, n, v1);
+    if (m + 2 < M) (*this)(m + 2, n, v2);
+    if (m + 3 < M) (*this)(m + 3, n, v3);
   }
 };
 
@@ -67,8 +113,12 @@ struct EpiGatedResid {
 constexpr int kBK = 64;  // K slice
 constexpr int kThreads = 256;
 
-// element offset of (row, 16-byte chunk c) in a [rows][64] bf16 LDS tile
-FLUX_DEV int swz(int row, int c) { return row * kBK + ((c ^ (row & 7)) << 3); }
+// element offset of (row, 16-byte chunk c) in a [rows][64] bf16 LDS tile.  A row is
+// 128 bytes, half of the 64 x 4-byte banks, so rows 2r and 2r+1 share a bank row; XOR-ing
+// the chunk with (row >> 1) & 7 makes 16 consecutive rows at one logical chunk land on 16
+// distinct 16-byte bank groups (a conflict-free ds_read_b128 for every 16 lanes).
+FLUX_DEV int swz_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
+FLUX_DEV int swz(int row, int c) { return row * kBK + (swz_slot(row, c) << 3); }
 
 template <int BM, int BN, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restrict__ A,
@@ -227,6 +277,244 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
 }
 
 // ------------------------------------------------------------------------------------
+// bf16 MFMA kernel, large tiles, direct global->LDS loads (K % BK == 0)
+//
+// 4 waves in 2 x 2; each wave owns a (BM/2) x (BN/2) tile of 32x32 MFMA blocks.  ST LDS
+// stages of BK-wide K slices are filled by global_load_lds_dwordx4: one wave instruction
+// writes 1 KB of LDS contiguously (lane i at byte 16 i), so each lane fetches the global
+// chunk that belongs at its slot of the swizzled layout.  Slices are prefetched ST-1
+// ahead; each iteration waits only for the slice it is about to use (partial vmcnt).
+// Rows past M / N are clamped to valid rows (their results are never stored).
+// ------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+FLUX_DEV void lds_load16(const void* g, bf16* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+}
+
+// The same 16-byte global->LDS load issued through inline asm (M0 = wave-uniform LDS byte
+// address).  The compiler does not track these loads, so it does not add its own
+// conservative vmcnt(0) waits before LDS reads or barriers; the kernel waits explicitly.
+FLUX_DEV void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+FLUX_DEV uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int N>
+FLUX_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Tile order: the hardware dispatches workgroup i to XCD i % 8.  Give each XCD a
+// contiguous run of the logical order, and walk the logical order in bands of GROUP
+// M-tiles so concurrently running workgroups share A and W slices in their L2.
+FLUX_DEV void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  constexpr int GROUP = 8;
+  const int group_size = GROUP * tiles_n;
+  const int g = bid / group_size;
+  const int first_m = g * GROUP;
+  const int gm = min(tiles_m - first_m, GROUP);
+  const int r = bid - g * group_size;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
+// LDS layout of one operand slice: rows of BK bf16 (BK/8 chunks of 16 bytes).  With
+// 64 banks x 4 bytes (256 bytes) per bank row, 256/(2 BK) consecutive rows share a bank
+// row; XOR-ing the chunk index with (row / rows_per_bank_row) spreads the 16 rows read by
+// 16 lanes of a ds_read_b128 over 16 distinct 16-byte bank groups.
+template <int BK>
+struct Swz {
+  static constexpr int CPR = BK / 8;
+  static constexpr int RSH = (BK == 64) ? 1 : 2;
+  FLUX_DEV static int slot(int row, int c) { return c ^ ((row >> RSH) & (CPR - 1)); }
+  FLUX_DEV static int off(int row, int c) { return row * BK + (slot(row, c) << 3); }
+};
+
+template <int BM, int BN, int BK, int ST, int OCC, class Epi>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_lds_kernel(
+    const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw, int M,
+    int N, int K, int n_half, int tiles_m, int tiles_n, Epi epi) {
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(ST >= 2 && ST <= 4, "stages");
+  using S = Swz<BK>;
+  constexpr int CPR = BK / 8;         // chunks per row
+  constexpr int RPI = 64 / CPR;       // rows per wave load instruction
+  constexpr int AI = BM / (4 * RPI);  // A load instructions per wave per slice
+  constexpr int BI = BN / (4 * RPI);
+  constexpr int LOADS = AI + BI;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int KK = BK / 16;         // MFMA K sub-steps per slice
+  static_assert(AI >= 1 && BI >= 1, "tile too small for the load plan");
+  static_assert(!Epi::kPaired || (TN % 2 == 0), "SwiGLU needs gate/up tile pairs");
+
+  extern __shared__ __align__(16) bf16 smem[];
+  // stage s: A rows at smem + s * (BM + BN) * BK, B rows right after
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // direct-load sources: instruction j of wave w covers rows (w*AI + j)*RPI + [0, RPI);
+  // lane -> row lane / CPR, LDS slot lane % CPR, global chunk = the chunk of that slot
+  const bf16* a_src[AI];
+  const bf16* b_src[BI];
+#pragma unroll
+  for (int j = 0; j < AI; ++j) {
+    const int r = (wave * AI + j) * RPI + lane / CPR;
+    const int gr = min(m0 + r, M - 1);
+    a_src[j] = A + (int64_t)gr * lda + S::slot(r, lane % CPR) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < BI; ++j) {
+    const int r = (wave * BI + j) * RPI + lane / CPR;
+    int gn = n0 + r;
+    if constexpr (Epi::kPaired) {
+      const int jj = min(((gn >> 6) << 5) + (gn & 31), n_half - 1);
+      gn = ((gn >> 5) & 1) ? n_half + jj : jj;
+    } else {
+      gn = min(gn, N - 1);
+    }
+    b_src[j] = W + (int64_t)gn * ldw + S::slot(r, lane % CPR) * 8;
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_u32(smem));
+  auto issue = [&](int stage, int k0) {
+    const uint32_t abase = lds0 + (uint32_t)(stage * (BM + BN) * BK * 2);
+    const uint32_t bbase = abase + BM * BK * 2;
+#pragma unroll
+    for (int j = 0; j < AI; ++j)
+      dma16(a_src[j] + k0, __builtin_amdgcn_readfirstlane(abase + (wave * AI + j) * RPI * BK * 2));
+#pragma unroll
+    for (int j = 0; j < BI; ++j)
+      dma16(b_src[j] + k0, __builtin_amdgcn_readfirstlane(bbase + (wave * BI + j) * RPI * BK * 2));
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lrow = lane & 31, lk = lane >> 5;
+  bf16x8 af[2][TM], bfr[2][TN];
+  auto load_frags = [&](int set, const bf16* as, const bf16* bs, int kk) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      af[set][i] = *reinterpret_cast<const bf16x8*>(as + S::off(wm * WTM + i * 32 + lrow, kk * 2 + lk));
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bfr[set][j] = *reinterpret_cast<const bf16x8*>(bs + S::off(wn * WTN + j * 32 + lrow, kk * 2 + lk));
+  };
+
+  const int nk = K / BK;
+#pragma unroll
+  for (int p = 0; p < ST - 1; ++p)
+    if (p < nk) issue(p, p * BK);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // slice kt has landed once at most (slices issued after it) x LOADS loads are pending
+    if (kt + ST - 2 < nk)
+      wait_vmcnt<(ST - 2) * LOADS>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    // the stage of slice kt-1 is free now (every wave passed the barrier)
+    if (kt + ST - 1 < nk) issue((kt + ST - 1) % ST, (kt + ST - 1) * BK);
+    const bf16* as = smem + (kt % ST) * (BM + BN) * BK;
+    const bf16* bs = as + BM * BK;
+    load_frags(0, as, bs, 0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int c = kk & 1;
+      if (kk + 1 < KK) load_frags(c ^ 1, as, bs, kk + 1);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bfr[c][j], acc[i][j], 0, 0, 0);
+      if (kk + 1 < KK) {
+#pragma unroll
+        for (int q = 0; q < TM + TN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+      }
+    }
+  }
+
+  if constexpr (Epi::kQuad) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int m = m0 + wm * WTM + i * 32 + 8 * r4 + 4 * lk;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + wn * WTN + j * 32 + lrow;
+          if (n < N)
+            epi.quad(m, n, acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
+                     acc[i][j][4 * r4 + 3], M);
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+      if (m >= M) continue;
+      if constexpr (Epi::kPaired) {
+#pragma unroll
+        for (int j = 0; j < TN; j += 2) {
+          const int nl = n0 + wn * WTN + j * 32 + lrow;
+          const int jj = ((nl >> 6) << 5) + (nl & 31);
+          if (jj < n_half) epi.pair(m, jj, acc[i][j][r], acc[i][j + 1][r]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + wn * WTN + j * 32 + lrow;
+          if (n < N) epi(m, n, acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+// Launch one large-tile configuration (sets the dynamic LDS limit once per instance).
+template <int BM, int BN, int BK, int ST, int OCC, class Epi>
+static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N,
+                             int K, int n_half, const Epi& epi, hipStream_t s) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const size_t lds = (size_t)ST * (BM + BN) * BK * sizeof(bf16);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, Epi>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, Epi>), dim3(tiles_m * tiles_n),
+                     dim3(kThreads), lds, s, A, lda, W, ldw, M, N, K, n_half, tiles_m, tiles_n, epi);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
 // fp32 path (tiny fp32 workloads): LDS-tiled FMA, 64 x 64 tile, 4 x 4 per thread with
 // strided columns (tx + 16 jj) so the SwiGLU pairs (jj, jj+2) sit in one thread.
 // ------------------------------------------------------------------------------------
@@ -300,6 +588,28 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
                          int K, int n_half, const Epi& epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
+    if (K % kBK == 0) {
+      // choose the tile configuration with the smallest estimated time:
+      // rounds of resident workgroups x work per round / relative efficiency
+      const int cus = 256;
+      struct Cand { int bm, bn, occ; double eff; };
+      const Cand cands[3] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.85}, {128, 128, 2, 0.9}};
+      int best = 0;
+      double best_t = 1e300;
+      for (int c = 0; c < 3; ++c) {
+        const long tiles = (long)((M + cands[c].bm - 1) / cands[c].bm) *
+                           ((N + cands[c].bn - 1) / cands[c].bn);
+        const long slots = (long)cus * cands[c].occ;
+        const double t = (double)((tiles + slots - 1) / slots) * cands[c].bm * cands[c].bn *
+                         cands[c].occ / cands[c].eff;
+        if (t < best_t * 0.999) { best_t = t; best = c; }
+      }
+      auto* a = static_cast<const bf16*>(A);
+      auto* w = static_cast<const bf16*>(W);
+      if (best == 0) return launch_lds<256, 256, 64, 2, 1>(a, lda, w, ldw, M, N, K, n_half, epi, s);
+      if (best == 1) return launch_lds<256, 128, 64, 2, 1>(a, lda, w, ldw, M, N, K, n_half, epi, s);
+      return launch_lds<128, 128, 64, 2, 2>(a, lda, w, ldw, M, N, K, n_half, epi, s);
+    }
     constexpr int BM = 128, BN = 128;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const size_t lds = 2 * (BM + BN) * kBK * sizeof(bf16);
@@ -345,6 +655,11 @@ static hipError_t linear_t(const LinearArgs& a, hipStream_t s) {
                        EpiSwiGLU<T>{static_cast<T*>(a.y), a.ldy, a.n / 2}, s);
     case EPI_GATED_RESIDUAL:
       return gated<T>(a, s);
+    case EPI_QKV:
+      return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0,
+                       EpiQKV<T>{static_cast<T*>(a.y), a.ldy, static_cast<T*>(a.vt), a.ldvt,
+                                 2 * a.dim, a.dim, a.rows_per_batch, a.vt_off},
+                       s);
   }
   return hipErrorInvalidValue;
 }

@@ -8,7 +8,7 @@
 
 namespace flux {
 
-enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_GATED_RESIDUAL = 2 };
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_GATED_RESIDUAL = 2, EPI_QKV = 3 };
 
 struct LinearArgs {
   int epilogue;
@@ -26,6 +26,12 @@ struct LinearArgs {
   const float* gate;      // [batch, gate_bs]
   int64_t gate_bs;
   int rows_per_batch;
+  // EPI_QKV: columns [0, 2*dim) go to y (q | k, row-major, ldy); columns [2*dim, 3*dim)
+  // go transposed to vt[(b * dim + f) * ldvt + vt_off + i] for row m = b * rows_per_batch + i
+  void* vt;
+  int64_t ldvt;
+  int vt_off;
+  int dim;
 };
 
 // y = x W^T with epilogue; dtype = type of x and W (DT_BF16 -> MFMA path).
@@ -66,9 +72,19 @@ hipError_t qk_norm_rope(int dtype, SeqView q, SeqView k, int batch, int seq, int
                         const float* qg0, const float* kg0, const float* qg1, const float* kg1,
                         const float2* cs, float eps, hipStream_t s);
 
-// O = softmax(Q K^T / sqrt(128)) V per head; head_dim 128.
-hipError_t attention(int dtype, SeqView q, SeqView k, SeqView v, SeqView o, int batch, int seq,
-                     int heads, hipStream_t s);
+// O = softmax(Q K^T / sqrt(128)) V per head; head_dim 128.  q, k, o are joint-sequence
+// views (head h at columns [128 h, 128 h + 128)); V is given transposed:
+// vt[(b * heads * 128 + f) * ld_vt + j] = V[b, j, f], with ld_vt a multiple of 64 and the
+// columns [seq, ld_vt) finite (zero).
+hipError_t attention(int dtype, SeqView q, SeqView k, const void* vt, int64_t ld_vt, SeqView o,
+                     int batch, int seq, int heads, hipStream_t s);
+
+// vt[(b * dim + f) * ld_vt + j] = v(b, j)[f] for j < seq
+hipError_t transpose_v(int dtype, SeqView v, void* vt, int64_t ld_vt, int dim, int batch, int seq,
+                       hipStream_t s);
+
+// p[r * ld + c] = 0 for r < rows, c0 <= c < c1
+hipError_t zero_cols(int dtype, void* p, int64_t ld, int64_t rows, int c0, int c1, hipStream_t s);
 
 // Copy rows between two joint-sequence views (dtype conversion allowed).
 hipError_t copy_rows(int src_dtype, SeqView src, int dst_dtype, SeqView dst, int batch, int seq,

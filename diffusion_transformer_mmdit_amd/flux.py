@@ -100,7 +100,9 @@ _PROTOS = {
     "flux_qk_norm_rope_workspace_size": (c_size, [P(flux_cfg), c_int, c_int]),
     "flux_qk_norm_rope": (c_int, [P(flux_cfg), c_int, c_int, c_int, vp, vp, c_i64, vp, vp, vp, vp,
                                   vp, vp, vp, c_size, vp]),
-    "flux_attention": (c_int, [P(flux_cfg), c_int, c_int, vp, vp, vp, c_i64, vp, c_i64, vp]),
+    "flux_attention_workspace_size": (c_size, [P(flux_cfg), c_int, c_int]),
+    "flux_attention": (c_int, [P(flux_cfg), c_int, c_int, vp, vp, vp, c_i64, vp, c_i64, vp, c_size,
+                               vp]),
     "flux_linear": (c_int, [P(flux_cfg), c_int, c_int, c_int, c_int, vp, c_i64, vp, c_i64, vp,
                             c_i64, c_int, vp, c_i64, vp, c_int, vp]),
 }
@@ -295,9 +297,15 @@ def flux_qk_norm_rope(cfg, batch, n_txt, n_img, q, k, ld, q_norm_txt, k_norm_txt
                                    _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
-def flux_attention(cfg, batch, seq, q, k, v, ld_in, o, ld_out, stream=None):
+def flux_attention_workspace_size(cfg, batch, seq) -> int:
+    return lib().flux_attention_workspace_size(ctypes.byref(cfg), batch, seq)
+
+
+def flux_attention(cfg, batch, seq, q, k, v, ld_in, o, ld_out, workspace, workspace_bytes,
+                   stream=None):
     _check(lib().flux_attention(ctypes.byref(cfg), batch, seq, _ptr(q), _ptr(k), _ptr(v), ld_in,
-                                _ptr(o), ld_out, _stream(stream)))
+                                _ptr(o), ld_out, _ptr(workspace), workspace_bytes,
+                                _stream(stream)))
 
 
 def flux_linear(cfg, epilogue, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid=None, ldr=0,

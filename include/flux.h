@@ -213,9 +213,12 @@ int flux_qk_norm_rope(const flux_cfg* cfg, int batch, int n_txt, int n_img, void
 /* Joint attention O = softmax(Q K^T / sqrt(head_dim)) V per head over the whole
  * sequence, no mask ([SDPA]; [TRACE] Joint multi-head attention).
  * q, k, v: device [batch, seq, ld_in] (cfg->dtype), head h at columns
- * [h*head_dim, (h+1)*head_dim); o: device [batch, seq, ld_out]. */
+ * [h*head_dim, (h+1)*head_dim); o: device [batch, seq, ld_out].  The workspace (size from
+ * flux_attention_workspace_size) receives V transposed, the layout the kernel reads. */
+size_t flux_attention_workspace_size(const flux_cfg* cfg, int batch, int seq);
 int flux_attention(const flux_cfg* cfg, int batch, int seq, const void* q, const void* k,
-                   const void* v, int64_t ld_in, void* o, int64_t ld_out, void* stream);
+                   const void* v, int64_t ld_in, void* o, int64_t ld_out, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* Linear layer y = x W^T with an optional fused epilogue ([DIFF] 双流块 / 单流块 / 激活函数
  * 与 FFN):

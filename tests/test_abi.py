@@ -1,0 +1,165 @@
+"""The C-ABI library: it loads, exports every entry point include/flux.h declares, and its
+host-side validation rejects bad arguments before anything is enqueued (CPU only).
+
+The validation tests pass fake device addresses: every one of them must be rejected by the
+library's argument checks before any HIP call, so they are only run where no GPU is
+present (on a GPU the same paths are exercised with real buffers by the GPU tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from diffusion_transformer_mmdit_amd import flux as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flux.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(flux_[a-z0-9_]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+def test_header_declares_the_three_block_entry_points():
+    names = declared_functions()
+    for n in ("flux_double_block_fwd", "flux_single_block_fwd", "flux_denoiser_step"):
+        assert n in names
+    assert len(names) >= 15
+
+
+def test_library_exports_every_declared_symbol():
+    lib = F.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+    # and the binding wraps every one of them under the same name
+    assert sorted(F.EXPORTED) == declared_functions()
+    for n in declared_functions():
+        assert callable(getattr(F, n))
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in F.flux_version()
+    assert isinstance(F.flux_last_error(), str)
+
+
+def cfg9b():
+    return F.make_cfg(4096, 32, 12288, in_channels=128, context_dim=12288, n_double=8,
+                      n_single=24)
+
+
+def test_workspace_sizes_are_positive_and_reject_bad_configs():
+    c = cfg9b()
+    for fn in (F.flux_double_block_workspace_size, F.flux_single_block_workspace_size,
+               F.flux_denoiser_step_workspace_size):
+        n = fn(c, 1, 4096, 512)
+        assert 100 << 20 < n < 4 << 30
+        assert fn(c, 2, 4096, 512) > n
+    bad = cfg9b()
+    bad.dim = 4000
+    assert F.flux_double_block_workspace_size(bad, 1, 4096, 512) == 0
+    assert "dim" in F.flux_last_error()
+    bad = cfg9b()
+    bad.axes_dim[0] = 30
+    assert F.flux_single_block_workspace_size(bad, 1, 64, 16) == 0
+    assert "axes_dim" in F.flux_last_error()
+    assert F.flux_denoiser_step_workspace_size(c, 0, 64, 16) == 0
+
+
+FAKE = 1 << 40          # a 256-byte aligned fake device address (never dereferenced)
+
+
+def fake_double_weights():
+    w = F.flux_double_weights()
+    w.temb = F.flux_temb_weights(FAKE, FAKE)
+    w.mod_img = w.mod_txt = FAKE
+    w.img = F.flux_stream_weights(*([FAKE] * 6))
+    w.txt = F.flux_stream_weights(*([FAKE] * 6))
+    return w
+
+
+def call_double(cfg, w, ws_bytes=None, **over):
+    a = dict(t=FAKE, batch=1, n_img=64, n_txt=16, img=FAKE, txt=FAKE, img_ids=FAKE, txt_ids=FAKE,
+             img_out=FAKE, txt_out=FAKE, ws=FAKE)
+    a.update(over)
+    nb = ws_bytes if ws_bytes is not None else F.flux_double_block_workspace_size(cfg, 1, 64, 16)
+    L = F.lib()
+    return L.flux_double_block_fwd(ctypes.byref(cfg), ctypes.byref(w), a["t"], a["batch"],
+                                   a["n_img"], a["n_txt"], a["img"], a["txt"], a["img_ids"],
+                                   a["txt_ids"], a["img_out"], a["txt_out"], a["ws"], nb, None)
+
+
+@pytest.mark.skipif(not no_gpu(), reason="fake-pointer validation tests run only without a GPU")
+def test_double_block_validation_errors():
+    c = F.make_cfg(256, 2, 768)
+    w = fake_double_weights()
+    assert call_double(c, w, img=0) == F.FLUX_EINVAL
+    assert call_double(c, w, img=FAKE + 2) == F.FLUX_EALIGN
+    assert call_double(c, w, ws=0) == F.FLUX_EWORKSPACE
+    assert call_double(c, w, ws=FAKE + 16) == F.FLUX_EWORKSPACE
+    assert call_double(c, w, ws_bytes=1024) == F.FLUX_EWORKSPACE
+    assert call_double(c, w, batch=0) == F.FLUX_EINVAL
+    assert call_double(c, w, n_img=0) == F.FLUX_EINVAL
+    w2 = fake_double_weights()
+    w2.img.q_norm = 0
+    assert call_double(c, w2) == F.FLUX_EINVAL
+    assert "img.q_norm" in F.flux_last_error()
+    bad = F.make_cfg(256, 2, 768, dtype=7)
+    assert call_double(bad, w) == F.FLUX_EDTYPE
+    bad = F.make_cfg(256, 2, 768, head_dim=64)
+    assert call_double(bad, w) == F.FLUX_ESHAPE
+    bad = F.make_cfg(256, 2, 770)
+    assert call_double(bad, w) == F.FLUX_ESHAPE
+    L = F.lib()
+    assert L.flux_double_block_fwd(None, ctypes.byref(w), FAKE, 1, 64, 16, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, 1 << 30, None) == F.FLUX_EINVAL
+
+
+@pytest.mark.skipif(not no_gpu(), reason="fake-pointer validation tests run only without a GPU")
+def test_step_and_op_validation_errors():
+    c = F.make_cfg(256, 2, 768, in_channels=128, context_dim=384, n_double=1, n_single=1)
+    mw = F.flux_model_weights()
+    L = F.lib()
+    nb = F.flux_denoiser_step_workspace_size(c, 1, 64, 16)
+    # guidance is not supported (no guidance embedder)
+    st = L.flux_denoiser_step(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 1, 64, 16, FAKE,
+                              FAKE, FAKE, FAKE, FAKE, FAKE, nb, None)
+    assert st == F.FLUX_EINVAL and "guidance" in F.flux_last_error()
+    # missing weights
+    st = L.flux_denoiser_step(ctypes.byref(c), ctypes.byref(mw), FAKE, None, 1, 64, 16, FAKE, FAKE,
+                              FAKE, FAKE, FAKE, FAKE, nb, None)
+    assert st == F.FLUX_EINVAL
+    # linear: k must be a multiple of 8; bad epilogue
+    assert L.flux_linear(ctypes.byref(c), 0, 8, 8, 12, FAKE, 12, FAKE, 12, FAKE, 8, 0, None, 0,
+                         None, 1, None) == F.FLUX_ESHAPE
+    assert L.flux_linear(ctypes.byref(c), 9, 8, 8, 16, FAKE, 16, FAKE, 16, FAKE, 8, 0, None, 0,
+                         None, 1, None) == F.FLUX_EINVAL
+    assert L.flux_linear(ctypes.byref(c), 2, 8, 8, 16, FAKE, 16, FAKE, 16, FAKE, 8, 0, None, 0,
+                         None, 1, None) == F.FLUX_EINVAL
+    # attention: leading dimension smaller than dim
+    assert L.flux_attention(ctypes.byref(c), 1, 10, FAKE, FAKE, FAKE, 128, FAKE, 256, FAKE,
+                            1 << 20, None) == F.FLUX_EALIGN
+    # attention: workspace too small
+    assert L.flux_attention(ctypes.byref(c), 1, 10, FAKE, FAKE, FAKE, 256, FAKE, 256, FAKE,
+                            16, None) == F.FLUX_EWORKSPACE
+    # layernorm: bad x dtype
+    assert L.flux_layernorm_modulate(ctypes.byref(c), 4, 4, FAKE, 5, FAKE, FAKE, FAKE,
+                                     None) == F.FLUX_EDTYPE
+
+
+def test_binding_raises_when_library_missing(tmp_path, monkeypatch):
+    monkeypatch.setattr(F, "_lib", None)
+    with pytest.raises(F.FluxError):
+        F.lib(str(tmp_path / "nope.so"))
+    monkeypatch.setattr(F, "_lib", None)

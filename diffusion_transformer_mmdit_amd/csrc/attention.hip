@@ -233,21 +233,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(SeqView qv, SeqView kv,
 }
 
 static int attn_waves(int seq, int heads, int batch) {
-  // 2 resident workgroups per CU; pick the workgroup size (2 or 4 waves of 32 queries)
-  // that wastes the least of the last round of workgroups
+  // 64 KB of LDS per workgroup limits a CU to 2 resident workgroups, so 4-wave workgroups
+  // (2 waves per SIMD) are preferred; 2-wave workgroups only when 4-wave ones cannot
+  // give every CU two workgroups
   const int cus = 256;
-  double best_t = 1e300;
-  int best = 4;
-  for (int nw : {4, 2}) {
-    const long wgs = (long)((seq + 32 * nw - 1) / (32 * nw)) * heads * batch;
-    const long slots = 2L * cus * (4 / nw);  // same number of resident waves
-    const double t = (double)((wgs + slots - 1) / slots) * nw;
-    if (t < best_t * 0.999) {
-      best_t = t;
-      best = nw;
-    }
-  }
-  return best;
+  const long wg4 = (long)((seq + 127) / 128) * heads * batch;
+  return wg4 >= 2L * cus ? 4 : 2;
 }
 
 hipError_t attention(int dtype, SeqView q, SeqView k, const void* vt, int64_t ld_vt, SeqView o,

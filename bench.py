@@ -97,8 +97,11 @@ def dominant_kernel(F, wl, reps: int = 20):
     y = torch.empty((m, D + H), device="cuda", dtype=torch.bfloat16)
     cfg = F.make_cfg(D, wl.heads, H)
     s = torch.cuda.current_stream()
+    # the same split-K scratch the step gives its linear layers
+    lnb = F.flux_linear_workspace_size()
+    lws = torch.empty(lnb, dtype=torch.uint8, device="cuda")
     call = lambda: F.flux_linear(cfg, F.FLUX_EPI_SWIGLU, m, n, k, x, k, w, k, y[:, D:], D + H, 0,
-                                 stream=s)
+                                 workspace=lws, workspace_bytes=lnb, stream=s)
     for _ in range(3):
         call()
     ev = Events(s)

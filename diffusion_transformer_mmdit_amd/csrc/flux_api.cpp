@@ -160,8 +160,9 @@ static RopeBufs carve_rope(Carver& cv, int L) {
 static int lin(const flux_cfg* c, int epi, int m, int n, int k, const void* x, int64_t ldx,
                const void* w, int64_t ldw, void* y, int64_t ldy, int y_dtype,
                const void* resid = nullptr, int64_t ldr = 0, int r_dtype = FLUX_F32,
-               const float* gate = nullptr, int64_t gate_bs = 0, int rpb = 1, hipStream_t s = 0) {
-  LinearArgs a;
+               const float* gate = nullptr, int64_t gate_bs = 0, int rpb = 1, hipStream_t s = 0,
+               float* split_ws = nullptr) {
+  LinearArgs a{};
   a.epilogue = epi;
   a.m = m;
   a.n = n;
@@ -179,13 +180,14 @@ static int lin(const flux_cfg* c, int epi, int m, int n, int k, const void* x, i
   a.gate = gate;
   a.gate_bs = gate_bs;
   a.rows_per_batch = rpb;
+  a.split_ws = split_ws;
   HIP_TRY(linear(c->dtype, a, s));
   return FLUX_OK;
 }
 
 // q | k row-major into qk [m, 2D]; v transposed into vt [B*D, ldvt] at token offset vt_off
 static int lin_qkv(const flux_cfg* c, int m, const void* x, const void* w, void* qk, void* vt,
-                   int64_t ldvt, int vt_off, int rpb, hipStream_t s) {
+                   int64_t ldvt, int vt_off, int rpb, hipStream_t s, float* split_ws) {
   LinearArgs a{};
   a.epilogue = EPI_QKV;
   a.m = m;
@@ -203,6 +205,7 @@ static int lin_qkv(const flux_cfg* c, int m, const void* x, const void* w, void*
   a.ldvt = ldvt;
   a.vt_off = vt_off;
   a.dim = c->dim;
+  a.split_ws = split_ws;
   HIP_TRY(linear(c->dtype, a, s));
   return FLUX_OK;
 }
@@ -220,6 +223,7 @@ struct DoubleScratch {
   void* o[2];     // [B*N_s, D]
   float* mid[2];  // [B*N_s, D] residual after the attention branch
   void* mlp[2];   // [B*N_s, H]
+  float* split;   // split-K scratch of the linear layers
 };
 
 static DoubleScratch carve_double(Carver& cv, const flux_cfg* c, int B, int Ni, int Nt) {
@@ -236,6 +240,7 @@ static DoubleScratch carve_double(Carver& cv, const flux_cfg* c, int B, int Ni, 
     d.mlp[i] = cv.take<char>(rows * H * es);
   }
   d.vt = cv.take<char>((size_t)B * D * vt_pitch(Ni + Nt) * es);
+  d.split = cv.take<float>(linear_splitk_bytes() / sizeof(float));
   return d;
 }
 
@@ -271,7 +276,8 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
     const int rows = B * n[i];
     HIP_TRY(layernorm_modulate(in_dt, T, in[i], D, d.ln[i], D, rows, D, n[i], mods[i],
                                mods[i] + D, mbs, c->eps, s));
-    CHECK(lin_qkv(c, rows, d.ln[i], sw[i]->qkv, d.qk[i], d.vt, ldvt, i == 0 ? 0 : Nt, n[i], s));
+    CHECK(lin_qkv(c, rows, d.ln[i], sw[i]->qkv, d.qk[i], d.vt, ldvt, i == 0 ? 0 : Nt, n[i], s,
+                  d.split));
   }
   if (ldvt > L) HIP_TRY(zero_cols(T, d.vt, ldvt, (int64_t)B * D, L, (int)ldvt, s));
   // joint views: segment 0 = text rows, segment 1 = image rows
@@ -296,14 +302,14 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
     const int rows = B * n[i];
     // x + gate1 * (O W_o^T)  -> mid (f32)
     CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D, d.o[i], D, sw[i]->out, D, d.mid[i], D, FLUX_F32,
-              in[i], D, in_dt, mods[i] + 2 * D, mbs, n[i], s));
+              in[i], D, in_dt, mods[i] + 2 * D, mbs, n[i], s, d.split));
     HIP_TRY(layernorm_modulate(FLUX_F32, T, d.mid[i], D, d.ln[i], D, rows, D, n[i],
                                mods[i] + 3 * D, mods[i] + 4 * D, mbs, c->eps, s));
     CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln[i], D, sw[i]->mlp_in, D, d.mlp[i], H, T,
-              nullptr, 0, 0, nullptr, 0, 1, s));
+              nullptr, 0, 0, nullptr, 0, 1, s, d.split));
     // mid + gate2 * (M W_out^T) -> out
     CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, H, d.mlp[i], H, sw[i]->mlp_out, H, out[i], D,
-              out_dt, d.mid[i], D, FLUX_F32, mods[i] + 5 * D, mbs, n[i], s));
+              out_dt, d.mid[i], D, FLUX_F32, mods[i] + 5 * D, mbs, n[i], s, d.split));
   }
   return FLUX_OK;
 }
@@ -373,6 +379,7 @@ struct SingleScratch {
   void* qk;   // [B*L, 2D] q | k
   void* vt;   // [B*D, vt_pitch(L)] V^T
   void* cat;  // [B*L, D + H]  = [attention output | SwiGLU output]
+  float* split;  // split-K scratch of the linear layers
 };
 
 static SingleScratch carve_single(Carver& cv, const flux_cfg* c, int B, int L) {
@@ -383,6 +390,7 @@ static SingleScratch carve_single(Carver& cv, const flux_cfg* c, int B, int L) {
   d.qk = cv.take<char>(rows * 2 * c->dim * es);
   d.vt = cv.take<char>((size_t)B * c->dim * vt_pitch(L) * es);
   d.cat = cv.take<char>(rows * (c->dim + c->mlp_hidden) * es);
+  d.split = cv.take<float>(linear_splitk_bytes() / sizeof(float));
   return d;
 }
 
@@ -407,11 +415,12 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
   const int64_t mbs = 3 * (int64_t)D, ldc = D + H;
   HIP_TRY(layernorm_modulate(in_dt, T, x, D, d.ln, D, rows, D, L, mod, mod + D, mbs, c->eps, s));
   const int64_t ldvt = vt_pitch(L);
-  CHECK(lin_qkv(c, rows, d.ln, w->linear1, d.qk, d.vt, ldvt, 0, L, s));
+  CHECK(lin_qkv(c, rows, d.ln, w->linear1, d.qk, d.vt, ldvt, 0, L, s, d.split));
   if (ldvt > L) HIP_TRY(zero_cols(T, d.vt, ldvt, (int64_t)B * D, L, (int)ldvt, s));
   const char* w_mlp = static_cast<const char*>(w->linear1) + (size_t)3 * D * D * es;
   CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln, D, w_mlp, D,
-            static_cast<char*>(d.cat) + (size_t)D * es, ldc, T, nullptr, 0, 0, nullptr, 0, 1, s));
+            static_cast<char*>(d.cat) + (size_t)D * es, ldc, T, nullptr, 0, 0, nullptr, 0, 1, s,
+            d.split));
   auto view = [&](void* base, int col, int64_t ld) {
     SeqView v;
     v.base0 = v.base1 = static_cast<char*>(base) + (size_t)col * es;
@@ -426,7 +435,7 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
                        c->eps, s));
   HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, s));
   CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D + H, d.cat, ldc, w->linear2, D + H, out, D, out_dt,
-            x, D, in_dt, mod + 2 * D, mbs, L, s));
+            x, D, in_dt, mod + 2 * D, mbs, L, s, d.split));
   return FLUX_OK;
 }
 
@@ -778,10 +787,12 @@ extern "C" int flux_attention(const flux_cfg* c, int B, int seq, const void* q, 
   return FLUX_OK;
 }
 
+extern "C" size_t flux_linear_workspace_size(void) { return linear_splitk_bytes(); }
+
 extern "C" int flux_linear(const flux_cfg* c, int epi, int m, int n, int k, const void* x,
                            int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
                            int y_dtype, const void* resid, int64_t ldr, const float* gate,
-                           int rpb, void* stream) {
+                           int rpb, void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_cfg(c));
   if (m <= 0 || n <= 0 || k <= 0) return fail(FLUX_EINVAL, "m, n, k must be > 0");
   if (k % 8) return fail(FLUX_ESHAPE, "k must be a multiple of 8");
@@ -791,23 +802,33 @@ extern "C" int flux_linear(const flux_cfg* c, int epi, int m, int n, int k, cons
   CHECK(need(x, "x"));
   CHECK(need(w, "w"));
   if (!y) return fail(FLUX_EINVAL, "y is NULL");
+  float* split = nullptr;
+  if (ws) {
+    if (reinterpret_cast<uintptr_t>(ws) & 255u)
+      return fail(FLUX_EWORKSPACE, "workspace is not 256-byte aligned");
+    if (ws_bytes < linear_splitk_bytes())
+      return fail(FLUX_EWORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes,
+                  linear_splitk_bytes());
+    split = static_cast<float*>(ws);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
   if (epi == FLUX_EPI_SWIGLU) {
     if (n % 2) return fail(FLUX_ESHAPE, "SwiGLU needs an even n");
     if (ldy < n / 2) return fail(FLUX_ESHAPE, "ldy < n/2");
     return lin(c, EPI_SWIGLU, m, n, k, x, ldx, w, ldw, y, ldy, c->dtype, nullptr, 0, 0, nullptr,
-               0, 1, static_cast<hipStream_t>(stream));
+               0, 1, s, split);
   }
   if (y_dtype != FLUX_BF16 && y_dtype != FLUX_F32) return fail(FLUX_EDTYPE, "bad y_dtype");
   if (ldy < n) return fail(FLUX_ESHAPE, "ldy < n");
   if (epi == FLUX_EPI_STORE)
     return lin(c, EPI_STORE, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, nullptr, 0, 0, nullptr, 0,
-               1, static_cast<hipStream_t>(stream));
+               1, s, split);
   if (epi == FLUX_EPI_GATED_RESIDUAL) {
     if (!resid || !gate) return fail(FLUX_EINVAL, "resid and gate are required");
     if (rpb <= 0 || m % rpb) return fail(FLUX_ESHAPE, "m must be a multiple of rows_per_batch");
     if (ldr < n) return fail(FLUX_ESHAPE, "ldr < n");
     return lin(c, EPI_GATED_RESIDUAL, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid, ldr,
-               y_dtype, gate, n, rpb, static_cast<hipStream_t>(stream));
+               y_dtype, gate, n, rpb, s, split);
   }
   return fail(FLUX_EINVAL, "unknown epilogue %d", epi);
 }

@@ -279,7 +279,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
 // ------------------------------------------------------------------------------------
 // bf16 MFMA kernel, large tiles, direct global->LDS loads (K % BK == 0)
 //
-// 4 waves in 2 x 2; each wave owns a (BM/2) x (BN/2) tile of 32x32 MFMA blocks.  ST LDS
+// NWM x NWN waves; each owns a (BM/NWM) x (BN/NWN) tile of 32x32 MFMA blocks.  256x256
+// tiles use 8 waves (two per SIMD, so one wave's waits overlap the other's MFMAs); ST LDS
 // stages of BK-wide K slices are filled by global_load_lds_dwordx4: one wave instruction
 // writes 1 KB of LDS contiguously (lane i at byte 16 i), so each lane fetches the global
 // chunk that belongs at its slot of the swizzled layout.  Slices are prefetched ST-1
@@ -312,9 +313,10 @@ FLUX_DEV void wait_vmcnt() {
 // Tile order: the hardware dispatches workgroup i to XCD i % 8.  Give each XCD a
 // contiguous run of the logical order, and walk the logical order in bands of GROUP
 // M-tiles so concurrently running workgroups share A and W slices in their L2.
-FLUX_DEV void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+FLUX_DEV int xcd_remap(int bid, int total) {
+  return ((total & 7) == 0) ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
+}
+FLUX_DEV void logical_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int GROUP = 8;
   const int group_size = GROUP * tiles_n;
   const int g = bid / group_size;
@@ -323,6 +325,9 @@ FLUX_DEV void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int r = bid - g * group_size;
   tm = first_m + r % gm;
   tn = r / gm;
+}
+FLUX_DEV void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  logical_coords(xcd_remap(bid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 // LDS layout of one operand slice: rows of BK bf16 (BK/8 chunks of 16 bytes).  With
@@ -337,19 +342,21 @@ struct Swz {
   FLUX_DEV static int off(int row, int c) { return row * BK + (slot(row, c) << 3); }
 };
 
-template <int BM, int BN, int BK, int ST, int OCC, class Epi>
-__global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_lds_kernel(
+template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
+__global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw, int M,
-    int N, int K, int n_half, int tiles_m, int tiles_n, Epi epi) {
+    int N, int K, int n_half, int tiles_m, int tiles_n, int full_tiles, int splits,
+    float* __restrict__ partial, Epi epi) {
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(ST >= 2 && ST <= 4, "stages");
   using S = Swz<BK>;
-  constexpr int CPR = BK / 8;         // chunks per row
-  constexpr int RPI = 64 / CPR;       // rows per wave load instruction
-  constexpr int AI = BM / (4 * RPI);  // A load instructions per wave per slice
-  constexpr int BI = BN / (4 * RPI);
+  constexpr int NWV = NWM * NWN;        // waves per workgroup
+  constexpr int CPR = BK / 8;           // chunks per row
+  constexpr int RPI = 64 / CPR;         // rows per wave load instruction
+  constexpr int AI = BM / (NWV * RPI);  // A load instructions per wave per slice
+  constexpr int BI = BN / (NWV * RPI);
   constexpr int LOADS = AI + BI;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int WTM = BM / NWM, WTN = BN / NWN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int KK = BK / 16;         // MFMA K sub-steps per slice
   static_assert(AI >= 1 && BI >= 1, "tile too small for the load plan");
@@ -359,9 +366,22 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_lds_kernel(
   // stage s: A rows at smem + s * (BM + BN) * BK, B rows right after
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
+  // workgroups [0, full_tiles) own whole tiles (XCD-aware order); the rest split the
+  // remaining tiles along K into `splits` ranges and write fp32 partial tiles
+  const int nk_all = K / BK;
+  int logical, k_begin = 0, k_end = nk_all, unit = -1;
+  if ((int)blockIdx.x < full_tiles) {
+    logical = xcd_remap(blockIdx.x, full_tiles);
+  } else {
+    unit = blockIdx.x - full_tiles;
+    const int split = unit % splits;
+    logical = full_tiles + unit / splits;
+    k_begin = split * nk_all / splits;
+    k_end = (split + 1) * nk_all / splits;
+  }
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  logical_coords(logical, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // direct-load sources: instruction j of wave w covers rows (w*AI + j)*RPI + [0, RPI);
@@ -417,10 +437,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_lds_kernel(
       bfr[set][j] = *reinterpret_cast<const bf16x8*>(bs + S::off(wn * WTN + j * 32 + lrow, kk * 2 + lk));
   };
 
-  const int nk = K / BK;
+  const int nk = k_end - k_begin;
+  const int kb = k_begin * BK;
 #pragma unroll
   for (int p = 0; p < ST - 1; ++p)
-    if (p < nk) issue(p, p * BK);
+    if (p < nk) issue(p, kb + p * BK);
 
   for (int kt = 0; kt < nk; ++kt) {
     // slice kt has landed once at most (slices issued after it) x LOADS loads are pending
@@ -430,7 +451,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_lds_kernel(
       wait_vmcnt<0>();
     __syncthreads();
     // the stage of slice kt-1 is free now (every wave passed the barrier)
-    if (kt + ST - 1 < nk) issue((kt + ST - 1) % ST, (kt + ST - 1) * BK);
+    if (kt + ST - 1 < nk) issue((kt + ST - 1) % ST, kb + (kt + ST - 1) * BK);
     const bf16* as = smem + (kt % ST) * (BM + BN) * BK;
     const bf16* bs = as + BM * BK;
     load_frags(0, as, bs, 0);
@@ -454,6 +475,19 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_lds_kernel(
     }
   }
 
+  if (unit >= 0) {
+    // split-K unit: raw fp32 partial tile [BM][BN] (local coordinates)
+    float* pt = partial + (size_t)unit * BM * BN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ml = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) pt[ml * BN + wn * WTN + j * 32 + lrow] = acc[i][j][r];
+      }
+    return;
+  }
   if constexpr (Epi::kQuad) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -495,24 +529,98 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_lds_kernel(
   }
 }
 
+// Split-K tail: sum the `splits` partial tiles of each tail tile in a fixed order (so the
+// result is deterministic) and apply the fused epilogue.  grid = (tail tiles, chunks);
+// each thread owns 4 consecutive columns of one row (16-byte loads per partial).
+template <int BM, int BN, class Epi>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
+                                                            int splits, int full_tiles, int tiles_m,
+                                                            int tiles_n, int M, int N, int n_half,
+                                                            Epi epi) {
+  const int t = blockIdx.x;
+  int tm, tn;
+  logical_coords(full_tiles + t, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const float* p = partial + (size_t)t * splits * BM * BN;
+  const size_t stride = (size_t)BM * BN;
+  const int e = blockIdx.y * 256 + threadIdx.x;
+  if constexpr (Epi::kPaired) {
+    // logical columns come in 64-groups: 32 gate columns, then their 32 up columns
+    if (e >= BM * BN / 8) return;
+    const int ml = e / (BN / 8), q = e % (BN / 8);
+    const int nl = (q >> 3) * 64 + (q & 7) * 4;
+    const int m = m0 + ml;
+    if (m >= M) return;
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+    const float* pg = p + ml * BN + nl;
+#pragma unroll 4
+    for (int sp = 0; sp < splits; ++sp) {
+      const float4 a = *reinterpret_cast<const float4*>(pg + sp * stride);
+      const float4 b = *reinterpret_cast<const float4*>(pg + sp * stride + 32);
+      g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+      u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+    }
+    const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int nn = n0 + nl + c;
+      const int jj = ((nn >> 6) << 5) + (nn & 31);
+      if (jj < n_half) epi.pair(m, jj, gv[c], uv[c]);
+    }
+  } else {
+    if (e >= BM * BN / 4) return;
+    const int ml = e / (BN / 4), nl = (e % (BN / 4)) * 4;
+    const int m = m0 + ml;
+    if (m >= M) return;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* pp = p + ml * BN + nl;
+#pragma unroll 4
+    for (int sp = 0; sp < splits; ++sp) {
+      const float4 a = *reinterpret_cast<const float4*>(pp + sp * stride);
+      v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+    }
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (n0 + nl + c < N) epi(m, n0 + nl + c, vv[c]);
+  }
+}
+
 // Launch one large-tile configuration (sets the dynamic LDS limit once per instance).
-template <int BM, int BN, int BK, int ST, int OCC, class Epi>
+template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
 static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N,
-                             int K, int n_half, const Epi& epi, hipStream_t s) {
+                             int K, int n_half, const Epi& epi, int splits, float* partial,
+                             hipStream_t s) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int tiles = tiles_m * tiles_n;
+  const int slots = 256 * OCC;
+  const int tail = splits > 1 ? tiles % slots : 0;
+  const int full = tiles - tail;
+  if (tail == 0) splits = 1;
   const size_t lds = (size_t)ST * (BM + BN) * BK * sizeof(bf16);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, Epi>),
+        reinterpret_cast<const void*>(&gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, Epi>), dim3(tiles_m * tiles_n),
-                     dim3(kThreads), lds, s, A, lda, W, ldw, M, N, K, n_half, tiles_m, tiles_n, epi);
+  hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
+                     dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, A, lda, W, ldw, M, N,
+                     K, n_half, tiles_m, tiles_n, full, splits, partial, epi);
+  if (tail > 0) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int chunks = Epi::kPaired ? BM * BN / 8 / 256 : BM * BN / 4 / 256;
+    hipLaunchKernelGGL((splitk_reduce_kernel<BM, BN, Epi>), dim3(tail, chunks), dim3(256), 0, s,
+                       partial, splits, full, tiles_m, tiles_n, M, N, n_half, epi);
+  }
   return hipGetLastError();
 }
+
+// Bytes of split-K scratch the large-tile path may use (tail tiles x splits x tile).
+constexpr size_t kSplitkBytes = (size_t)256 * 256 * 256 * sizeof(float);
 
 // ------------------------------------------------------------------------------------
 // fp32 path (tiny fp32 workloads): LDS-tiled FMA, 64 x 64 tile, 4 x 4 per thread with
@@ -585,30 +693,52 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // ------------------------------------------------------------------------------------
 template <class T, class Epi>
 static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw, int M, int N,
-                         int K, int n_half, const Epi& epi, hipStream_t s) {
+                         int K, int n_half, const Epi& epi, hipStream_t s,
+                         float* split_ws = nullptr) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
     if (K % kBK == 0) {
-      // choose the tile configuration with the smallest estimated time:
-      // rounds of resident workgroups x work per round / relative efficiency
+      // choose the tile configuration (and split-K of the last partial round) with the
+      // smallest estimated time: rounds of resident workgroups x work per round /
+      // relative efficiency; a tail round split s ways along K costs 1/s of a round
       const int cus = 256;
       struct Cand { int bm, bn, occ; double eff; };
-      const Cand cands[3] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.85}, {128, 128, 2, 0.9}};
-      int best = 0;
+      const Cand cands[3] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.8}, {128, 128, 2, 0.85}};
+      const int nk = K / kBK;
+      int best = 0, best_split = 1;
       double best_t = 1e300;
       for (int c = 0; c < 3; ++c) {
         const long tiles = (long)((M + cands[c].bm - 1) / cands[c].bm) *
                            ((N + cands[c].bn - 1) / cands[c].bn);
         const long slots = (long)cus * cands[c].occ;
-        const double t = (double)((tiles + slots - 1) / slots) * cands[c].bm * cands[c].bn *
-                         cands[c].occ / cands[c].eff;
-        if (t < best_t * 0.999) { best_t = t; best = c; }
+        const double work = (double)cands[c].bm * cands[c].bn * cands[c].occ / cands[c].eff;
+        const long tail = tiles % slots;
+        // plain
+        double t = (double)((tiles + slots - 1) / slots) * work;
+        int split = 1;
+        // split the tail: s units per tail tile, at least 8 K-slices each
+        if (tail > 0 && split_ws != nullptr && 2 * tail <= slots &&
+            tail * cands[c].bm * cands[c].bn * sizeof(float) * 2 <= kSplitkBytes) {
+          int sp = (int)(slots / tail);
+          sp = sp < nk / 8 ? sp : nk / 8;
+          while (sp > 1 && (size_t)tail * sp * cands[c].bm * cands[c].bn * sizeof(float) > kSplitkBytes) --sp;
+          if (sp >= 2) {
+            const double ts = (double)(tiles / slots) * work + work / sp * 1.15;
+            if (ts < t) { t = ts; split = sp; }
+          }
+        }
+        if (t < best_t * 0.999) { best_t = t; best = c; best_split = split; }
       }
       auto* a = static_cast<const bf16*>(A);
       auto* w = static_cast<const bf16*>(W);
-      if (best == 0) return launch_lds<256, 256, 64, 2, 1>(a, lda, w, ldw, M, N, K, n_half, epi, s);
-      if (best == 1) return launch_lds<256, 128, 64, 2, 1>(a, lda, w, ldw, M, N, K, n_half, epi, s);
-      return launch_lds<128, 128, 64, 2, 2>(a, lda, w, ldw, M, N, K, n_half, epi, s);
+      if (best == 0)
+        return launch_lds<256, 256, 64, 2, 1, 4, 2>(a, lda, w, ldw, M, N, K, n_half, epi,
+                                                     best_split, split_ws, s);
+      if (best == 1)
+        return launch_lds<256, 128, 64, 2, 1, 4, 2>(a, lda, w, ldw, M, N, K, n_half, epi,
+                                                     best_split, split_ws, s);
+      return launch_lds<128, 128, 64, 2, 2, 2, 2>(a, lda, w, ldw, M, N, K, n_half, epi, best_split,
+                                                   split_ws, s);
     }
     constexpr int BM = 128, BN = 128;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -631,7 +761,7 @@ static hipError_t gated2(const LinearArgs& a, hipStream_t s) {
                    EpiGatedResid<TY, TR>{static_cast<TY*>(a.y), a.ldy,
                                          static_cast<const TR*>(a.resid), a.ldr, a.gate,
                                          a.gate_bs, a.rows_per_batch},
-                   s);
+                   s, a.split_ws);
 }
 
 template <class T>
@@ -647,22 +777,24 @@ static hipError_t linear_t(const LinearArgs& a, hipStream_t s) {
     case EPI_STORE:
       if (a.y_dtype == DT_F32)
         return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0,
-                         EpiStore<float>{static_cast<float*>(a.y), a.ldy}, s);
+                         EpiStore<float>{static_cast<float*>(a.y), a.ldy}, s, a.split_ws);
       return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0,
-                       EpiStore<bf16>{static_cast<bf16*>(a.y), a.ldy}, s);
+                       EpiStore<bf16>{static_cast<bf16*>(a.y), a.ldy}, s, a.split_ws);
     case EPI_SWIGLU:
       return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, a.n / 2,
-                       EpiSwiGLU<T>{static_cast<T*>(a.y), a.ldy, a.n / 2}, s);
+                       EpiSwiGLU<T>{static_cast<T*>(a.y), a.ldy, a.n / 2}, s, a.split_ws);
     case EPI_GATED_RESIDUAL:
       return gated<T>(a, s);
     case EPI_QKV:
       return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0,
                        EpiQKV<T>{static_cast<T*>(a.y), a.ldy, static_cast<T*>(a.vt), a.ldvt,
                                  2 * a.dim, a.dim, a.rows_per_batch, a.vt_off},
-                       s);
+                       s, a.split_ws);
   }
   return hipErrorInvalidValue;
 }
+
+size_t linear_splitk_bytes() { return kSplitkBytes; }
 
 hipError_t linear(int dtype, const LinearArgs& a, hipStream_t s) {
   return dtype == DT_BF16 ? linear_t<bf16>(a, s) : linear_t<float>(a, s);

@@ -32,7 +32,13 @@ struct LinearArgs {
   int64_t ldvt;
   int vt_off;
   int dim;
+  // optional scratch of linear_splitk_bytes() bytes: lets the large-tile path split the
+  // last partial round of tiles along K (nullptr: never split)
+  float* split_ws;
 };
+
+// scratch size that enables every split-K choice of linear()
+size_t linear_splitk_bytes();
 
 // y = x W^T with epilogue; dtype = type of x and W (DT_BF16 -> MFMA path).
 hipError_t linear(int dtype, const LinearArgs& a, hipStream_t s);

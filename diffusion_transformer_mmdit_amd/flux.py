@@ -103,8 +103,9 @@ _PROTOS = {
     "flux_attention_workspace_size": (c_size, [P(flux_cfg), c_int, c_int]),
     "flux_attention": (c_int, [P(flux_cfg), c_int, c_int, vp, vp, vp, c_i64, vp, c_i64, vp, c_size,
                                vp]),
+    "flux_linear_workspace_size": (c_size, []),
     "flux_linear": (c_int, [P(flux_cfg), c_int, c_int, c_int, c_int, vp, c_i64, vp, c_i64, vp,
-                            c_i64, c_int, vp, c_i64, vp, c_int, vp]),
+                            c_i64, c_int, vp, c_i64, vp, c_int, vp, c_size, vp]),
 }
 
 EXPORTED = tuple(_PROTOS)
@@ -308,8 +309,12 @@ def flux_attention(cfg, batch, seq, q, k, v, ld_in, o, ld_out, workspace, worksp
                                 _stream(stream)))
 
 
+def flux_linear_workspace_size() -> int:
+    return lib().flux_linear_workspace_size()
+
+
 def flux_linear(cfg, epilogue, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid=None, ldr=0,
-                gate=None, rows_per_batch=1, stream=None):
+                gate=None, rows_per_batch=1, workspace=None, workspace_bytes=0, stream=None):
     _check(lib().flux_linear(ctypes.byref(cfg), epilogue, m, n, k, _ptr(x), ldx, _ptr(w), ldw,
                              _ptr(y), ldy, y_dtype, _ptr(resid), ldr, _ptr(gate), rows_per_batch,
-                             _stream(stream)))
+                             _ptr(workspace), workspace_bytes, _stream(stream)))

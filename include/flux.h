@@ -234,10 +234,14 @@ typedef enum {
   FLUX_EPI_SWIGLU = 1,
   FLUX_EPI_GATED_RESIDUAL = 2
 } flux_epilogue;
+/* workspace: NULL, or flux_linear_workspace_size() bytes (256-byte aligned) of scratch that
+ * lets the large-tile path split the last partial round of output tiles along K (fp32
+ * partials reduced in a fixed order, so results stay deterministic). */
+size_t flux_linear_workspace_size(void);
 int flux_linear(const flux_cfg* cfg, int epilogue, int m, int n, int k, const void* x,
                 int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy, int y_dtype,
                 const void* resid, int64_t ldr, const float* gate, int rows_per_batch,
-                void* stream);
+                void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

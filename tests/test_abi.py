@@ -142,11 +142,14 @@ def test_step_and_op_validation_errors():
     assert st == F.FLUX_EINVAL
     # linear: k must be a multiple of 8; bad epilogue
     assert L.flux_linear(ctypes.byref(c), 0, 8, 8, 12, FAKE, 12, FAKE, 12, FAKE, 8, 0, None, 0,
-                         None, 1, None) == F.FLUX_ESHAPE
+                         None, 1, None, 0, None) == F.FLUX_ESHAPE
     assert L.flux_linear(ctypes.byref(c), 9, 8, 8, 16, FAKE, 16, FAKE, 16, FAKE, 8, 0, None, 0,
-                         None, 1, None) == F.FLUX_EINVAL
+                         None, 1, None, 0, None) == F.FLUX_EINVAL
     assert L.flux_linear(ctypes.byref(c), 2, 8, 8, 16, FAKE, 16, FAKE, 16, FAKE, 8, 0, None, 0,
-                         None, 1, None) == F.FLUX_EINVAL
+                         None, 1, None, 0, None) == F.FLUX_EINVAL
+    # split-K workspace smaller than flux_linear_workspace_size()
+    assert L.flux_linear(ctypes.byref(c), 0, 8, 8, 16, FAKE, 16, FAKE, 16, FAKE, 8, 0, None, 0,
+                         None, 1, FAKE, 1024, None) == F.FLUX_EWORKSPACE
     # attention: leading dimension smaller than dim
     assert L.flux_attention(ctypes.byref(c), 1, 10, FAKE, FAKE, FAKE, 128, FAKE, 256, FAKE,
                             1 << 20, None) == F.FLUX_EALIGN

@@ -166,8 +166,17 @@ def _sample_rows(m, k=64, seed=0):
     return np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, size=k)]))
 
 
+def _lin_ws(use_ws):
+    """Split-K scratch (None: the kernels never split along K)."""
+    if not use_ws:
+        return None, 0
+    nb = F().flux_linear_workspace_size()
+    return G.workspace(nb), nb
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
 @pytest.mark.parametrize("m,n,k,dtype", LIN_CASES)
-def test_linear_store(m, n, k, dtype):
+def test_linear_store(m, n, k, dtype, use_ws):
     t = G.torch()
     seed = m + n + k
     x = fs.normal(seed, "x", (m, k), dtype=dtype)
@@ -175,8 +184,10 @@ def test_linear_store(m, n, k, dtype):
     f = F()
     for y_dtype in ("f32", dtype):
         y = t.empty((m, n), dtype=G.dt(y_dtype), device="cuda")
+        ws, nb = _lin_ws(use_ws)
         f.flux_linear(cfg(256, dtype), f.FLUX_EPI_STORE, m, n, k, G.dev(x, dtype), k, G.dev(w, dtype),
-                      k, y, n, f.FLUX_F32 if y_dtype == "f32" else f.FLUX_BF16, stream=G.stream())
+                      k, y, n, f.FLUX_F32 if y_dtype == "f32" else f.FLUX_BF16, workspace=ws,
+                      workspace_bytes=nb, stream=G.stream())
         t.cuda.synchronize()
         rows = _sample_rows(m) if m * n * k > 2e9 else np.arange(m)
         ref = O.linear(x[rows].astype(np.float64), w.astype(np.float64))
@@ -186,8 +197,9 @@ def test_linear_store(m, n, k, dtype):
             G.assert_close(G.host(y)[rows], ref, dtype, f"linear {m}x{n}x{k} -> f32")
 
 
+@pytest.mark.parametrize("use_ws", [False, True])
 @pytest.mark.parametrize("m,n,k,dtype", LIN_CASES)
-def test_linear_swiglu(m, n, k, dtype):
+def test_linear_swiglu(m, n, k, dtype, use_ws):
     t = G.torch()
     seed = 3 * m + n + k
     n2 = 2 * n
@@ -195,8 +207,9 @@ def test_linear_swiglu(m, n, k, dtype):
     w = fs.normal(seed, "w", (n2, k), std=0.02, dtype=dtype)
     f = F()
     y = t.empty((m, n), dtype=G.dt(dtype), device="cuda")
+    ws, nb = _lin_ws(use_ws)
     f.flux_linear(cfg(256, dtype), f.FLUX_EPI_SWIGLU, m, n2, k, G.dev(x, dtype), k, G.dev(w, dtype), k,
-                  y, n, 0, stream=G.stream())
+                  y, n, 0, workspace=ws, workspace_bytes=nb, stream=G.stream())
     t.cuda.synchronize()
     rows = _sample_rows(m) if m * n2 * k > 2e9 else np.arange(m)
     ref = O.swiglu(O.linear(x[rows].astype(np.float64), w.astype(np.float64)))
@@ -206,8 +219,9 @@ def test_linear_swiglu(m, n, k, dtype):
         G.assert_close(G.host(y)[rows], ref, dtype, f"linear+SwiGLU {m}x{n2}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k,dtype", LIN_CASES)
-def test_linear_gated_residual(m, n, k, dtype):
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("m,n,k,dtype", LIN_CASES + [(4608, 4096, 16384, "bf16")])
+def test_linear_gated_residual(m, n, k, dtype, use_ws):
     t = G.torch()
     seed = 5 * m + n + k
     rpb = m // 2 if m % 2 == 0 else m
@@ -220,7 +234,8 @@ def test_linear_gated_residual(m, n, k, dtype):
     rd = G.dev(r, dtype)
     f.flux_linear(cfg(256, dtype), f.FLUX_EPI_GATED_RESIDUAL, m, n, k, G.dev(x, dtype), k,
                   G.dev(w, dtype), k, rd, n, f.FLUX_BF16 if dtype == "bf16" else f.FLUX_F32,
-                  resid=rd, ldr=n, gate=G.dev(gate), rows_per_batch=rpb, stream=G.stream())
+                  resid=rd, ldr=n, gate=G.dev(gate), rows_per_batch=rpb, workspace=_lin_ws(use_ws)[0],
+                  workspace_bytes=_lin_ws(use_ws)[1], stream=G.stream())
     t.cuda.synchronize()
     rows = _sample_rows(m) if m * n * k > 2e9 else np.arange(m)
     ref = r[rows].astype(np.float64) + gate[rows // rpb].astype(np.float64) * O.linear(

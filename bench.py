@@ -2,6 +2,7 @@
 MI355X through the C ABI.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --probe dominant|copy      # a few bare launches, for counter runs
 
 Prints ONE JSON line: step throughput (algorithmic TFLOP/s, whole step), ms per step, the
 roofline of the dominant kernel (timed live with HIP events on the stream it runs on), and
@@ -85,10 +86,51 @@ class Events:
 
 
 # ------------------------------------------------------------------------------------
+# HBM traffic of the dominant kernel from committed rocprofv3 counter runs.  The summary
+# records a hash of the GEMM sources it was taken with; once those sources change the
+# figure no longer describes the kernel and is reported as null.
+# ------------------------------------------------------------------------------------
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_swiglu_4608x24576x4096_hbm_counters.md")
+KERNEL_SOURCES = ("diffusion_transformer_mmdit_amd/csrc/gemm.hip",
+                  "diffusion_transformer_mmdit_amd/csrc/kernels.h",
+                  "diffusion_transformer_mmdit_amd/csrc/common.h")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when absent or stale."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if ":" in line and line.split(":", 1)[0].strip() in ("traffic_bytes_per_launch",
+                                                             "kernel_source_sha256"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------------------------
 # dominant kernel: the bf16 MFMA GEMM with the fused SwiGLU epilogue, at the single-block
 # MLP-in shape (the largest launch of the step), launched exactly as the step launches it
 # ------------------------------------------------------------------------------------
-def dominant_kernel(F, wl, reps: int = 20):
+def dominant_kernel(F, wl, reps: int = 20, probe: bool = False):
     import torch
     D, H, L = wl.dim, wl.mlp_hidden, wl.seq
     m, n, k = wl.batch * L, 2 * H, D
@@ -104,6 +146,9 @@ def dominant_kernel(F, wl, reps: int = 20):
                                  workspace=lws, workspace_bytes=lnb, stream=s)
     for _ in range(3):
         call()
+    if probe:
+        torch.cuda.synchronize()
+        return None
     ev = Events(s)
     ev.start()
     for _ in range(reps):
@@ -111,18 +156,31 @@ def dominant_kernel(F, wl, reps: int = 20):
     ms = ev.stop_ms() / reps
     flops = 2.0 * m * n * k
     achieved = flops / (ms * 1e-3) / 1e12
+    algo_bytes = 2 * (m * k + n * k + m * (n // 2))   # A, W once; bf16 h once
     return {
-        "kernel": "gemm_bf16_kernel<EpiSwiGLU> (single-block linear1 MLP part)",
+        "kernel": "gemm_bf16_lds_kernel<256,256,64,2,1,4,2,EpiSwiGLU<bf16>> (single-block linear1 MLP part)",
         "shape": [m, n, k],
         "bound": "mfma",
         "achieved": round(achieved, 1),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
+        "traffic": measured_traffic(),
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
+        "algorithmic_bytes_per_launch": algo_bytes,
         "avg_launch_us": round(ms * 1e3, 1),
         "algorithmic_flops_per_launch": flops,
     }
+
+
+def copy_probe(mib: int = 1024):
+    """A plain 1 GiB device copy: the reference that scales the HBM byte counters."""
+    import torch
+    a = torch.full((mib << 20,), 1, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 # ------------------------------------------------------------------------------------
@@ -170,6 +228,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="klein9b_step_1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", choices=("dominant", "copy"), default=None,
+                    help="only launch the dominant kernel (or a 1 GiB copy) 3 times and exit")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -186,6 +246,14 @@ def main(argv=None) -> int:
         return 1
     wl = fs.workload(args.workload)
     assert wl.kind == "step"
+    if args.probe == "dominant":
+        dominant_kernel(F, wl, probe=True)
+        print("[bench] probe: dominant kernel launched 3 times", file=sys.stderr, flush=True)
+        return 0
+    if args.probe == "copy":
+        copy_probe()
+        print("[bench] probe: 1 GiB copy launched 3 times", file=sys.stderr, flush=True)
+        return 0
     dtype = torch.bfloat16
     print(f"[bench] {wl.name}: generating {fs.param_count(fs.step_weight_specs(wl)) / 1e9:.3f} B "
           "params on device", file=sys.stderr, flush=True)

@@ -16,6 +16,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace flux {
 
 // ------------------------------------------------------------------------------------
@@ -280,28 +282,36 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
 // bf16 MFMA kernel, large tiles, direct global->LDS loads (K % BK == 0)
 //
 // NWM x NWN waves; each owns a (BM/NWM) x (BN/NWN) tile of 32x32 MFMA blocks.  256x256
-// tiles use 8 waves (two per SIMD, so one wave's waits overlap the other's MFMAs); ST LDS
+// tiles use 8 waves (two per SIMD, so one wave's waits overlap the other's MFMAs).  ST LDS
 // stages of BK-wide K slices are filled by global_load_lds_dwordx4: one wave instruction
 // writes 1 KB of LDS contiguously (lane i at byte 16 i), so each lane fetches the global
-// chunk that belongs at its slot of the swizzled layout.  Slices are prefetched ST-1
-// ahead; each iteration waits only for the slice it is about to use (partial vmcnt).
-// Rows past M / N are clamped to valid rows (their results are never stored).
+// chunk that belongs at its slot of the swizzled layout.  The loads use the scalar-base
+// form (SGPR pointer advanced per slice + a fixed 32-bit per-lane byte offset) so a load
+// costs two instructions.
+//
+// Schedule of one slice (KK = BK/16 MFMA k-steps, fragments double buffered in registers):
+//   k-steps 0 .. KK-2:  MFMAs of step kk, each followed by one fragment read of step kk+1
+//   k-step  KK-1:       wait for slice kt+1 and barrier (every wave is then done reading
+//                       this stage), then MFMAs of the last step interleaved with the
+//                       fragment reads of the next slice's step 0 and the loads of slice
+//                       kt+ST into the stage just freed
+// so the barrier is the only point where the MFMA pipe can drain, and the first fragments
+// of a slice are read under the MFMAs of the previous one.  The K loop is peeled so the
+// steady state carries no branches.  Rows past M / N are clamped to valid rows (their
+// results are never stored).
 // ------------------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-FLUX_DEV void lds_load16(const void* g, bf16* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
-}
-
-// The same 16-byte global->LDS load issued through inline asm (M0 = wave-uniform LDS byte
-// address).  The compiler does not track these loads, so it does not add its own
-// conservative vmcnt(0) waits before LDS reads or barriers; the kernel waits explicitly.
-FLUX_DEV void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
-               : "memory", "m0");
-}
 FLUX_DEV uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16-byte global->LDS load through inline asm: M0 = wave-uniform LDS byte address, global
+// address = scalar base + per-lane 32-bit byte offset.  The compiler does not track these
+// loads, so it adds no conservative vmcnt(0) before LDS reads or barriers; the kernel
+// waits explicitly with wait_vmcnt.
+FLUX_DEV void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff),
+               "s"(base)
+               : "memory", "m0");
 }
 
 template <int N>
@@ -358,14 +368,18 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
   constexpr int LOADS = AI + BI;
   constexpr int WTM = BM / NWM, WTN = BN / NWN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int KK = BK / 16;         // MFMA K sub-steps per slice
+  constexpr int KK = BK / 16;           // MFMA k-steps per slice
+  constexpr int NF = TM + TN;           // fragments per k-step
+  constexpr uint32_t STAGE_B = (BM + BN) * BK * 2;
   static_assert(AI >= 1 && BI >= 1, "tile too small for the load plan");
+  static_assert(KK % 2 == 0, "fragment sets alternate with the k-step parity");
   static_assert(!Epi::kPaired || (TN % 2 == 0), "SwiGLU needs gate/up tile pairs");
 
   extern __shared__ __align__(16) bf16 smem[];
   // stage s: A rows at smem + s * (BM + BN) * BK, B rows right after
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / NWN, wn = wave % NWN;
   // workgroups [0, full_tiles) own whole tiles (XCD-aware order); the rest split the
   // remaining tiles along K into `splits` ranges and write fp32 partial tiles
@@ -384,15 +398,15 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
   logical_coords(logical, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // direct-load sources: instruction j of wave w covers rows (w*AI + j)*RPI + [0, RPI);
-  // lane -> row lane / CPR, LDS slot lane % CPR, global chunk = the chunk of that slot
-  const bf16* a_src[AI];
-  const bf16* b_src[BI];
+  // load plan: instruction j of wave w covers rows (w*AI + j)*RPI + [0, RPI); lane ->
+  // row lane / CPR, LDS slot lane % CPR, global chunk = the chunk of that slot.  Byte
+  // offsets from the operand base fit 32 bits (checked by the launcher).
+  uint32_t a_off[AI], b_off[BI];
 #pragma unroll
   for (int j = 0; j < AI; ++j) {
     const int r = (wave * AI + j) * RPI + lane / CPR;
     const int gr = min(m0 + r, M - 1);
-    a_src[j] = A + (int64_t)gr * lda + S::slot(r, lane % CPR) * 8;
+    a_off[j] = (uint32_t)(((int64_t)gr * lda + S::slot(r, lane % CPR) * 8) * 2);
   }
 #pragma unroll
   for (int j = 0; j < BI; ++j) {
@@ -404,18 +418,15 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
     } else {
       gn = min(gn, N - 1);
     }
-    b_src[j] = W + (int64_t)gn * ldw + S::slot(r, lane % CPR) * 8;
+    b_off[j] = (uint32_t)(((int64_t)gn * ldw + S::slot(r, lane % CPR) * 8) * 2);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_u32(smem));
-  auto issue = [&](int stage, int k0) {
-    const uint32_t abase = lds0 + (uint32_t)(stage * (BM + BN) * BK * 2);
-    const uint32_t bbase = abase + BM * BK * 2;
-#pragma unroll
-    for (int j = 0; j < AI; ++j)
-      dma16(a_src[j] + k0, __builtin_amdgcn_readfirstlane(abase + (wave * AI + j) * RPI * BK * 2));
-#pragma unroll
-    for (int j = 0; j < BI; ++j)
-      dma16(b_src[j] + k0, __builtin_amdgcn_readfirstlane(bbase + (wave * BI + j) * RPI * BK * 2));
+  auto dma = [&](int q, int stage, int k0) {  // q-th load instruction of this wave's share
+    const uint32_t sb = lds0 + (uint32_t)stage * STAGE_B;
+    if (q < AI)
+      dma16s(A + k0, a_off[q], sb + (uint32_t)((wave * AI + q) * RPI * BK * 2));
+    else
+      dma16s(W + k0, b_off[q - AI], sb + (uint32_t)(BM * BK * 2 + (wave * BI + q - AI) * RPI * BK * 2));
   };
 
   f32x16 acc[TM][TN];
@@ -427,53 +438,78 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int lrow = lane & 31, lk = lane >> 5;
-  bf16x8 af[2][TM], bfr[2][TN];
-  auto load_frags = [&](int set, const bf16* as, const bf16* bs, int kk) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-      af[set][i] = *reinterpret_cast<const bf16x8*>(as + S::off(wm * WTM + i * 32 + lrow, kk * 2 + lk));
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      bfr[set][j] = *reinterpret_cast<const bf16x8*>(bs + S::off(wn * WTN + j * 32 + lrow, kk * 2 + lk));
+  bf16x8 fr[2][NF];  // [set][A fragments | B fragments]
+  auto rd = [&](int set, int q, int stage, int kk) {
+    const bf16* base = smem + stage * (BM + BN) * BK;
+    if (q < TM)
+      fr[set][q] = *reinterpret_cast<const bf16x8*>(base + S::off(wm * WTM + q * 32 + lrow, kk * 2 + lk));
+    else
+      fr[set][q] = *reinterpret_cast<const bf16x8*>(base + BM * BK +
+                                                     S::off(wn * WTN + (q - TM) * 32 + lrow, kk * 2 + lk));
   };
 
   const int nk = k_end - k_begin;
   const int kb = k_begin * BK;
+  // prologue: fill every stage, wait for slice 0, read its first fragments
 #pragma unroll
-  for (int p = 0; p < ST - 1; ++p)
-    if (p < nk) issue(p, kb + p * BK);
+  for (int p = 0; p < ST; ++p)
+    if (p < nk)
+#pragma unroll
+      for (int q = 0; q < LOADS; ++q) dma(q, p, kb + p * BK);
+  if (nk >= ST)
+    wait_vmcnt<(ST - 1) * LOADS>();
+  else
+    wait_vmcnt<0>();
+  __syncthreads();
+  if (nk > 0)
+#pragma unroll
+    for (int q = 0; q < NF; ++q) rd(0, q, 0, 0);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // slice kt has landed once at most (slices issued after it) x LOADS loads are pending
-    if (kt + ST - 2 < nk)
-      wait_vmcnt<(ST - 2) * LOADS>();
-    else
-      wait_vmcnt<0>();
-    __syncthreads();
-    // the stage of slice kt-1 is free now (every wave passed the barrier)
-    if (kt + ST - 1 < nk) issue((kt + ST - 1) % ST, kb + (kt + ST - 1) * BK);
-    const bf16* as = smem + (kt % ST) * (BM + BN) * BK;
-    const bf16* bs = as + BM * BK;
-    load_frags(0, as, bs, 0);
+  // one slice; DMA_ON: load slice kt+ST, RD_ON: read the next slice's first fragments
+  auto slice = [&](int kt, auto dma_on, auto rd_on) {
+    constexpr bool DMA_ON = decltype(dma_on)::value, RD_ON = decltype(rd_on)::value;
+    const int st = kt % ST;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int c = kk & 1;
-      if (kk + 1 < KK) load_frags(c ^ 1, as, bs, kk + 1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bfr[c][j], acc[i][j], 0, 0, 0);
-      if (kk + 1 < KK) {
-#pragma unroll
-        for (int q = 0; q < TM + TN; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+      const int cur = kk & 1, nxt = cur ^ 1;
+      const bool last = kk == KK - 1;
+      if (last) {
+        // slice kt+1 landed (later slices may still be in flight) and, after the barrier,
+        // every wave is done reading stage st
+        if (DMA_ON)
+          wait_vmcnt<(ST - 2) * LOADS>();
+        else
+          wait_vmcnt<0>();
+        __syncthreads();
       }
+      const bool do_rd = !last || RD_ON;
+      const bool do_dma = last && DMA_ON;
+      const int rst = last ? (kt + 1) % ST : st, rkk = last ? 0 : kk + 1;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < TM * TN; ++q) {
+        const int i = q / TN, j = q % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (do_rd && q < NF) rd(nxt, q, rst, rkk);
+        if (do_dma && q < LOADS) dma(q, st, kb + (kt + ST) * BK);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // any loads not yet issued (fewer MFMAs than loads)
+      if (do_dma)
+#pragma unroll
+        for (int q = TM * TN; q < LOADS; ++q) dma(q, st, kb + (kt + ST) * BK);
+      if (do_rd)
+#pragma unroll
+        for (int q = TM * TN; q < NF; ++q) rd(nxt, q, rst, rkk);
     }
-  }
+  };
+  using On = std::true_type;
+  using Off = std::false_type;
+  int kt = 0;
+  for (; kt + ST < nk; ++kt) slice(kt, On{}, On{});
+  for (; kt + 1 < nk; ++kt) slice(kt, Off{}, On{});
+  if (kt < nk) slice(kt, Off{}, Off{});
 
   if (unit >= 0) {
     // split-K unit: raw fp32 partial tile [BM][BN] (local coordinates)
@@ -697,11 +733,17 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
                          float* split_ws = nullptr) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    if (K % kBK == 0) {
+    // the large-tile kernel addresses operands with 32-bit byte offsets from their base
+    const bool off32 = (int64_t)M * lda * 2 < (int64_t{1} << 32) &&
+                       (int64_t)N * ldw * 2 < (int64_t{1} << 32);
+    if (K % kBK == 0 && off32) {
       // choose the tile configuration (and split-K of the last partial round) with the
-      // smallest estimated time: rounds of resident workgroups x work per round /
-      // relative efficiency; a tail round split s ways along K costs 1/s of a round
+      // smallest estimated time.  A round of resident workgroups costs its MACs at about
+      // 1 PFLOP/s over the chip, scaled by the configuration's relative efficiency; a tail
+      // round split s ways along K costs 1/s of a round plus the fp32 partial tiles'
+      // round trip through HBM and the reduce launch.
       const int cus = 256;
+      constexpr double kFlopPerCu = 4.0e12, kHbm = 5.0e12, kReduceLaunch = 3e-6;
       struct Cand { int bm, bn, occ; double eff; };
       const Cand cands[3] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.8}, {128, 128, 2, 0.85}};
       const int nk = K / kBK;
@@ -711,19 +753,20 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
         const long tiles = (long)((M + cands[c].bm - 1) / cands[c].bm) *
                            ((N + cands[c].bn - 1) / cands[c].bn);
         const long slots = (long)cus * cands[c].occ;
-        const double work = (double)cands[c].bm * cands[c].bn * cands[c].occ / cands[c].eff;
+        const double round = 2.0 * cands[c].bm * cands[c].bn * cands[c].occ * (double)K /
+                             cands[c].eff / kFlopPerCu;
         const long tail = tiles % slots;
-        // plain
-        double t = (double)((tiles + slots - 1) / slots) * work;
+        const size_t tile_bytes = (size_t)cands[c].bm * cands[c].bn * sizeof(float);
+        double t = (double)((tiles + slots - 1) / slots) * round;
         int split = 1;
         // split the tail: s units per tail tile, at least 8 K-slices each
-        if (tail > 0 && split_ws != nullptr && 2 * tail <= slots &&
-            tail * cands[c].bm * cands[c].bn * sizeof(float) * 2 <= kSplitkBytes) {
+        if (tail > 0 && split_ws != nullptr && 2 * tail <= slots) {
           int sp = (int)(slots / tail);
           sp = sp < nk / 8 ? sp : nk / 8;
-          while (sp > 1 && (size_t)tail * sp * cands[c].bm * cands[c].bn * sizeof(float) > kSplitkBytes) --sp;
+          while (sp > 1 && (size_t)tail * sp * tile_bytes > kSplitkBytes) --sp;
           if (sp >= 2) {
-            const double ts = (double)(tiles / slots) * work + work / sp * 1.15;
+            const double ts = (double)(tiles / slots) * round + round / sp +
+                              2.0 * tail * sp * tile_bytes / kHbm + kReduceLaunch;
             if (ts < t) { t = ts; split = sp; }
           }
         }

@@ -293,8 +293,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
 //   k-steps 0 .. KK-2:  MFMAs of step kk, each followed by one fragment read of step kk+1
 //   k-step  KK-1:       wait for slice kt+1 and barrier (every wave is then done reading
 //                       this stage), then MFMAs of the last step interleaved with the
-//                       fragment reads of the next slice's step 0 and the loads of slice
-//                       kt+ST into the stage just freed
+//                       fragment reads of the next slice's step 0 and half the loads of
+//                       slice kt+ST into the stage just freed (the other half goes with
+//                       step 0 of the next slice)
 // so the barrier is the only point where the MFMA pipe can drain, and the first fragments
 // of a slice are read under the MFMAs of the previous one.  The K loop is peeled so the
 // steady state carries no branches.  Rows past M / N are clamped to valid rows (their
@@ -465,9 +466,15 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
 #pragma unroll
     for (int q = 0; q < NF; ++q) rd(0, q, 0, 0);
 
-  // one slice; DMA_ON: load slice kt+ST, RD_ON: read the next slice's first fragments
-  auto slice = [&](int kt, auto dma_on, auto rd_on) {
+  // One slice.  The loads of slice kt+ST go into stage kt%ST, which the barrier of the last
+  // k-step of slice kt frees; they are split over that k-step and the first k-step of
+  // slice kt+1 (fewer loads in flight at once), and land before the barrier of slice kt+1.
+  // DMA_ON: start loading slice kt+ST; CONT: finish the loads begun in slice kt-1;
+  // RD_ON: read the next slice's first fragments.
+  constexpr int PER = (LOADS + 1) / 2;  // loads per k-step
+  auto slice = [&](int kt, auto dma_on, auto rd_on, auto cont_on) {
     constexpr bool DMA_ON = decltype(dma_on)::value, RD_ON = decltype(rd_on)::value;
+    constexpr bool CONT = decltype(cont_on)::value;
     const int st = kt % ST;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -483,8 +490,20 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
         __syncthreads();
       }
       const bool do_rd = !last || RD_ON;
-      const bool do_dma = last && DMA_ON;
       const int rst = last ? (kt + 1) % ST : st, rkk = last ? 0 : kk + 1;
+      // loads [q0, q1) of slice `ds` into stage `dst` in this k-step
+      int q0 = 0, q1 = 0, dst = 0, ds = 0;
+      if (last && DMA_ON) {
+        q1 = PER;
+        dst = st;
+        ds = kt + ST;
+      } else if (kk == 0 && CONT) {
+        q0 = PER;
+        q1 = LOADS;
+        dst = (kt + ST - 1) % ST;
+        ds = kt + ST - 1;
+      }
+      const int dk = kb + ds * BK;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < TM * TN; ++q) {
@@ -492,13 +511,13 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (do_rd && q < NF) rd(nxt, q, rst, rkk);
-        if (do_dma && q < LOADS) dma(q, st, kb + (kt + ST) * BK);
+        if (q0 + q < q1) dma(q0 + q, dst, dk);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // any loads not yet issued (fewer MFMAs than loads)
-      if (do_dma)
+      // leftovers when a k-step has fewer MFMAs than reads or loads
 #pragma unroll
-        for (int q = TM * TN; q < LOADS; ++q) dma(q, st, kb + (kt + ST) * BK);
+      for (int q = TM * TN; q < PER; ++q)
+        if (q0 + q < q1) dma(q0 + q, dst, dk);
       if (do_rd)
 #pragma unroll
         for (int q = TM * TN; q < NF; ++q) rd(nxt, q, rst, rkk);
@@ -507,9 +526,17 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
   using On = std::true_type;
   using Off = std::false_type;
   int kt = 0;
-  for (; kt + ST < nk; ++kt) slice(kt, On{}, On{});
-  for (; kt + 1 < nk; ++kt) slice(kt, Off{}, On{});
-  if (kt < nk) slice(kt, Off{}, Off{});
+  if (kt + ST < nk) slice(kt++, On{}, On{}, Off{});
+  for (; kt + ST < nk; ++kt) slice(kt, On{}, On{}, On{});
+  // kt >= 1 here only if slice kt-1 started loading slice kt+ST-1 (< nk)
+  if (kt >= 1 && kt + 1 < nk) slice(kt++, Off{}, On{}, On{});
+  for (; kt + 1 < nk; ++kt) slice(kt, Off{}, On{}, Off{});
+  if (kt < nk) {
+    if (kt >= 1 && kt - 1 + ST < nk)
+      slice(kt, Off{}, Off{}, On{});
+    else
+      slice(kt, Off{}, Off{}, Off{});
+  }
 
   if (unit >= 0) {
     // split-K unit: raw fp32 partial tile [BM][BN] (local coordinates)

@@ -158,7 +158,10 @@ def test_qk_norm_rope(D, n_txt, n_img, batch, dtype):
 # ------------------------------------------------------------------------------------
 LIN_CASES = [  # m, n, k, dtype
     (80, 768, 256, "f32"), (77, 200, 136, "bf16"), (300, 390, 520, "bf16"),
-    (1536, 3072, 3072, "bf16"), (4096, 12288, 4096, "bf16"), (512, 4096, 12288, "bf16")]
+    (1536, 3072, 3072, "bf16"), (4096, 12288, 4096, "bf16"), (512, 4096, 12288, "bf16"),
+    # 1, 2, 3 and 5 K slices of 64: every branch of the peeled K loop, ragged M and N tails
+    (300, 520, 64, "bf16"), (600, 1100, 128, "bf16"), (513, 700, 192, "bf16"),
+    (1030, 2050, 320, "bf16")]
 
 
 def _sample_rows(m, k=64, seed=0):

@@ -17,7 +17,12 @@
 //     lazy running maximum: O and the row sum are rescaled only when a row's maximum
 //     grows by more than 2^8, which keeps p <= 256 and skips almost all rescales;
 //   * two workgroups per CU (<= 256 registers per wave) so one workgroup's softmax
-//     overlaps the other's MFMAs.
+//     overlaps the other's MFMAs;
+//   * work units are (query block, head, batch).  Units that fill whole rounds of resident
+//     workgroups run whole; each unit of a partial last round is split along the keys into
+//     `splits` ranges whose unnormalised fp32 partial outputs, running maxima and sums a
+//     second kernel merges in a fixed order (the usual rescale-and-sum of flash-attention
+//     partials), so the last round is not left mostly idle.
 #include "common.h"
 #include "kernels.h"
 
@@ -50,19 +55,39 @@ FLUX_DEV int key_perm(int m) {
   return 16 * (q >> 1) + 8 * g + 4 * (q & 1) + t;
 }
 
+// Unit u = (b * heads + head) * nqb + qb (query blocks of one head are consecutive, so a
+// run of units on one XCD shares that head's K and V in L2).
+FLUX_DEV int attn_xcd_remap(int bid, int total) {
+  return ((total & 7) == 0) ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
+}
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     SeqView qv, SeqView kv, const bf16* __restrict__ vt, int64_t ld_vt, int dim, SeqView ov,
-    int seq, float scale_log2) {
+    int seq, float scale_log2, int nqb, int heads, int full_units, int splits,
+    float* __restrict__ partial) {
   constexpr int NT = 64 * NW;
   __shared__ __align__(16) bf16 Ks[2][kBKV * kHD];
   __shared__ __align__(16) bf16 Vs[2][kHD * kBKV];
 
+  const int ntiles = (seq + kBKV - 1) / kBKV;
+  int unit, t_begin = 0, t_end = ntiles, part = -1;
+  if ((int)blockIdx.x < full_units) {
+    unit = attn_xcd_remap(blockIdx.x, full_units);
+  } else {
+    part = blockIdx.x - full_units;
+    unit = full_units + part / splits;
+    const int sp = part % splits;
+    t_begin = sp * ntiles / splits;
+    t_end = (sp + 1) * ntiles / splits;
+  }
+  const int qb = unit % nqb;
+  const int head = (unit / nqb) % heads, b = unit / (nqb * heads);
+
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int head = blockIdx.y, b = blockIdx.z;
-  const int q0 = blockIdx.x * (32 * NW) + wave * 32;
+  const int q0 = qb * (32 * NW) + wave * 32;
   const int hoff = head * kHD;
 
   // ---- Q fragments (B operand of S^T = K Q^T): query l32, dims 16 kk + 8 g .. + 8
@@ -106,15 +131,14 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   const int krow0 = key_perm(l32), krow1 = 32 + key_perm(l32);
 
-  const int ntiles = (seq + kBKV - 1) / kBKV;
-  issue(0, 0);
+  issue(t_begin & 1, t_begin * kBKV);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  for (int it = t_begin; it < t_end; ++it) {
     const int cur = it & 1;
     const int kv0 = it * kBKV;
-    if (it + 1 < ntiles) issue(cur ^ 1, kv0 + kBKV);
+    if (it + 1 < t_end) issue(cur ^ 1, kv0 + kBKV);
 
     // S^T = K Q^T: s[h] covers MFMA rows of key block h (keys 32 h + key_perm(row))
     f32x16 s[2];
@@ -187,10 +211,30 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     __syncthreads();
   }
 
-  // normalise and write O[query][d]: lane owns query l32, dims 32 dt + 8 (r/4) + 4 g + r%4
+  // lane owns query l32 and dims 32 dt + 8 (r/4) + 4 g + r%4
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.f / l_tot;
   const int qi = q0 + l32;
+  if (part >= 0) {
+    // split unit: unnormalised O, running maximum (log2 domain) and sum for the merge
+    const int ql = wave * 32 + l32;
+    float* op = partial + ((int64_t)part * NT / 2 + ql) * kHD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(op + 32 * dt + 8 * r4 + 4 * g) =
+            make_float4(o[dt][4 * r4], o[dt][4 * r4 + 1], o[dt][4 * r4 + 2], o[dt][4 * r4 + 3]);
+    if (g == 0) {
+      // (maximum, sum) pairs follow the O rows of all split units
+      const int n_parts = gridDim.x - full_units;
+      float* ml = partial + (int64_t)n_parts * (NT / 2) * kHD + ((int64_t)part * NT / 2 + ql) * 2;
+      ml[0] = m_run;
+      ml[1] = l_tot;
+    }
+    return;
+  }
+  // normalise and write O[query][d]
+  const float inv = 1.f / l_tot;
   if (qi < seq) {
     bf16* op = seq_mptr<bf16>(ov, b, qi) + hoff;
 #pragma unroll
@@ -203,6 +247,44 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
         *reinterpret_cast<uint2*>(op + d) = pk;
       }
   }
+}
+
+// Merge of the split units: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s, splits taken in order.  One thread per (query, 4 dims); grid.x walks the
+// split units' queries, QPU = queries per unit.
+template <int QPU>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ partial,
+                                                         int64_t ml_offset, int splits,
+                                                         int n_units, int full_units, int nqb,
+                                                         int heads, int seq, SeqView ov) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int d4 = (int)(idx & 31);
+  const int64_t uq = idx >> 5;  // split unit * QPU + query
+  if (uq >= (int64_t)n_units * QPU) return;
+  const int tu = (int)(uq / QPU), ql = (int)(uq % QPU);
+  const int unit = full_units + tu;
+  const int qb = unit % nqb, head = (unit / nqb) % heads, b = unit / (nqb * heads);
+  const int qi = qb * QPU + ql;
+  if (qi >= seq) return;
+  const float* ml = partial + ml_offset;
+  float mmax = -INFINITY;
+  for (int sp = 0; sp < splits; ++sp)
+    mmax = fmaxf(mmax, ml[(((int64_t)tu * splits + sp) * QPU + ql) * 2]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lsum = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const int64_t row = ((int64_t)tu * splits + sp) * QPU + ql;
+    const float w = exp2f(ml[row * 2] - mmax);
+    lsum += w * ml[row * 2 + 1];
+    const float4 v = *reinterpret_cast<const float4*>(partial + row * kHD + 4 * d4);
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  const float inv = 1.f / lsum;
+  bf16* op = seq_mptr<bf16>(ov, b, qi) + head * kHD + 4 * d4;
+  *reinterpret_cast<uint2*>(op) = make_uint2(pack2(acc.x * inv, acc.y * inv), pack2(acc.z * inv, acc.w * inv));
 }
 
 // fp32 path (tiny fp32 workloads): one wave per (query, head); each lane owns 2 dims.
@@ -241,20 +323,54 @@ static int attn_waves(int seq, int heads, int batch) {
   return wg4 >= 2L * cus ? 4 : 2;
 }
 
+// Largest partial-output footprint: at most one round of resident workgroups (2 per CU)
+// of split units, 128 queries each, 128 dims + (maximum, sum) per query.
+constexpr int kAttnSlots = 2 * 256;
+size_t attention_split_bytes() { return (size_t)kAttnSlots * 128 * (kHD + 2) * sizeof(float); }
+
+template <int NW>
+static hipError_t launch_flash(SeqView q, SeqView k, const bf16* vt, int64_t ld_vt, int dim,
+                               SeqView o, int batch, int seq, int heads, float* split_ws,
+                               hipStream_t s) {
+  constexpr int QPU = 32 * NW;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHD);
+  const int nqb = (seq + QPU - 1) / QPU;
+  const int units = nqb * heads * batch;
+  const int ntiles = (seq + kBKV - 1) / kBKV;
+  // split the partial last round along the keys (at least 4 key tiles per range)
+  int tail = units % kAttnSlots, splits = 1;
+  if (split_ws != nullptr && tail > 0 && 2 * tail <= kAttnSlots) {
+    splits = kAttnSlots / tail;
+    if (splits > ntiles / 4) splits = ntiles / 4;
+  }
+  if (splits < 2) {
+    splits = 1;
+    tail = 0;
+  }
+  const int full = units - tail;
+  const int grid = full + tail * splits;
+  hipLaunchKernelGGL(flash_attn_bf16_kernel<NW>, dim3(grid), dim3(64 * NW), 0, s, q, k, vt, ld_vt,
+                     dim, o, seq, scale_log2, nqb, heads, full, splits, split_ws);
+  if (tail > 0) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t ml_offset = (int64_t)tail * splits * QPU * kHD;  // after the split units' O rows
+    const int64_t threads = (int64_t)tail * QPU * 32;
+    hipLaunchKernelGGL(attn_merge_kernel<QPU>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       s, split_ws, ml_offset, splits, tail, full, nqb, heads, seq, o);
+  }
+  return hipGetLastError();
+}
+
 hipError_t attention(int dtype, SeqView q, SeqView k, const void* vt, int64_t ld_vt, SeqView o,
-                     int batch, int seq, int heads, hipStream_t s) {
+                     int batch, int seq, int heads, float* split_ws, hipStream_t s) {
   if (seq <= 0 || batch <= 0) return hipSuccess;
   const int dim = heads * kHD;
   if (dtype == DT_BF16) {
-    const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHD);
-    const int nw = attn_waves(seq, heads, batch);
-    dim3 grid((seq + 32 * nw - 1) / (32 * nw), heads, batch);
-    if (nw == 4)
-      hipLaunchKernelGGL(flash_attn_bf16_kernel<4>, grid, dim3(256), 0, s, q, k,
-                         static_cast<const bf16*>(vt), ld_vt, dim, o, seq, scale_log2);
-    else
-      hipLaunchKernelGGL(flash_attn_bf16_kernel<2>, grid, dim3(128), 0, s, q, k,
-                         static_cast<const bf16*>(vt), ld_vt, dim, o, seq, scale_log2);
+    const bf16* v = static_cast<const bf16*>(vt);
+    if (attn_waves(seq, heads, batch) == 4)
+      return launch_flash<4>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, s);
+    return launch_flash<2>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, s);
   } else {
     dim3 grid(seq, heads, batch);
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(64), 0, s, q, k, static_cast<const float*>(vt),

@@ -210,6 +210,13 @@ static int lin_qkv(const flux_cfg* c, int m, const void* x, const void* w, void*
   return FLUX_OK;
 }
 
+// Scratch shared, one after the other on the stream, by the linear layers' split-K tails
+// and the attention's key-split units.
+static size_t split_scratch_bytes() {
+  const size_t a = linear_splitk_bytes(), b = attention_split_bytes();
+  return a > b ? a : b;
+}
+
 // V^T row pitch: the sequence rounded up to the attention's 64-key tiles
 static int64_t vt_pitch(int L) { return ((int64_t)L + 63) / 64 * 64; }
 
@@ -240,7 +247,7 @@ static DoubleScratch carve_double(Carver& cv, const flux_cfg* c, int B, int Ni, 
     d.mlp[i] = cv.take<char>(rows * H * es);
   }
   d.vt = cv.take<char>((size_t)B * D * vt_pitch(Ni + Nt) * es);
-  d.split = cv.take<float>(linear_splitk_bytes() / sizeof(float));
+  d.split = cv.take<float>(split_scratch_bytes() / sizeof(float));
   return d;
 }
 
@@ -296,7 +303,7 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
   SeqView ov = view(0, d.o, D);
   HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, sw[0]->q_norm, sw[0]->k_norm, sw[1]->q_norm,
                        sw[1]->k_norm, cs, c->eps, s));
-  HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, s));
+  HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, d.split, s));
   for (int i = 0; i < 2; ++i) {
     if (n[i] == 0) continue;
     const int rows = B * n[i];
@@ -390,7 +397,7 @@ static SingleScratch carve_single(Carver& cv, const flux_cfg* c, int B, int L) {
   d.qk = cv.take<char>(rows * 2 * c->dim * es);
   d.vt = cv.take<char>((size_t)B * c->dim * vt_pitch(L) * es);
   d.cat = cv.take<char>(rows * (c->dim + c->mlp_hidden) * es);
-  d.split = cv.take<float>(linear_splitk_bytes() / sizeof(float));
+  d.split = cv.take<float>(split_scratch_bytes() / sizeof(float));
   return d;
 }
 
@@ -433,7 +440,7 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
   SeqView ov = view(d.cat, 0, ldc);
   HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, w->q_norm, w->k_norm, w->q_norm, w->k_norm, cs,
                        c->eps, s));
-  HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, s));
+  HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, d.split, s));
   CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D + H, d.cat, ldc, w->linear2, D + H, out, D, out_dt,
             x, D, in_dt, mod + 2 * D, mbs, L, s, d.split));
   return FLUX_OK;
@@ -750,10 +757,22 @@ extern "C" int flux_qk_norm_rope(const flux_cfg* c, int B, int n_txt, int n_img,
   return FLUX_OK;
 }
 
+// workspace: V^T [B*D, vt_pitch(seq)], then the partial outputs of key-split units
+struct AttnScratch {
+  void* vt;
+  float* split;
+};
+static AttnScratch carve_attention(Carver& cv, const flux_cfg* c, int B, int seq) {
+  AttnScratch a;
+  a.vt = cv.take<char>((size_t)B * c->dim * vt_pitch(seq) * esize(c->dtype));
+  a.split = cv.take<float>(attention_split_bytes() / sizeof(float));
+  return a;
+}
+
 extern "C" size_t flux_attention_workspace_size(const flux_cfg* c, int B, int seq) {
   if (check_cfg(c) != FLUX_OK || B <= 0 || seq <= 0) return 0;
   Carver cv(nullptr);
-  cv.take<char>((size_t)B * c->dim * vt_pitch(seq) * esize(c->dtype));
+  carve_attention(cv, c, B, seq);
   return cv.off;
 }
 
@@ -779,11 +798,13 @@ extern "C" int flux_attention(const flux_cfg* c, int B, int seq, const void* q, 
     return sv;
   };
   hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  const AttnScratch a = carve_attention(cv, c, B, seq);
   const int64_t ldvt = vt_pitch(seq);
-  HIP_TRY(transpose_v(c->dtype, mk(v, ld_in), ws, ldvt, c->dim, B, seq, s));
-  if (ldvt > seq) HIP_TRY(zero_cols(c->dtype, ws, ldvt, (int64_t)B * c->dim, seq, (int)ldvt, s));
-  HIP_TRY(attention(c->dtype, mk(q, ld_in), mk(k, ld_in), ws, ldvt, mk(o, ld_out), B, seq,
-                    c->heads, s));
+  HIP_TRY(transpose_v(c->dtype, mk(v, ld_in), a.vt, ldvt, c->dim, B, seq, s));
+  if (ldvt > seq) HIP_TRY(zero_cols(c->dtype, a.vt, ldvt, (int64_t)B * c->dim, seq, (int)ldvt, s));
+  HIP_TRY(attention(c->dtype, mk(q, ld_in), mk(k, ld_in), a.vt, ldvt, mk(o, ld_out), B, seq,
+                    c->heads, a.split, s));
   return FLUX_OK;
 }
 

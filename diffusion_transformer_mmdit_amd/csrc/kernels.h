@@ -81,9 +81,11 @@ hipError_t qk_norm_rope(int dtype, SeqView q, SeqView k, int batch, int seq, int
 // O = softmax(Q K^T / sqrt(128)) V per head; head_dim 128.  q, k, o are joint-sequence
 // views (head h at columns [128 h, 128 h + 128)); V is given transposed:
 // vt[(b * heads * 128 + f) * ld_vt + j] = V[b, j, f], with ld_vt a multiple of 64 and the
-// columns [seq, ld_vt) finite (zero).
+// columns [seq, ld_vt) finite (zero).  split_ws (attention_split_bytes() of device memory,
+// or null to run every unit whole) holds the partial outputs of key-split units.
 hipError_t attention(int dtype, SeqView q, SeqView k, const void* vt, int64_t ld_vt, SeqView o,
-                     int batch, int seq, int heads, hipStream_t s);
+                     int batch, int seq, int heads, float* split_ws, hipStream_t s);
+size_t attention_split_bytes();
 
 // vt[(b * dim + f) * ld_vt + j] = v(b, j)[f] for j < seq
 hipError_t transpose_v(int dtype, SeqView v, void* vt, int64_t ld_vt, int dim, int batch, int seq,

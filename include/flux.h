@@ -214,7 +214,9 @@ int flux_qk_norm_rope(const flux_cfg* cfg, int batch, int n_txt, int n_img, void
  * sequence, no mask ([SDPA]; [TRACE] Joint multi-head attention).
  * q, k, v: device [batch, seq, ld_in] (cfg->dtype), head h at columns
  * [h*head_dim, (h+1)*head_dim); o: device [batch, seq, ld_out].  The workspace (size from
- * flux_attention_workspace_size) receives V transposed, the layout the kernel reads. */
+ * flux_attention_workspace_size) receives V transposed, the layout the kernel reads, and
+ * the fp32 partial outputs of query blocks whose keys are split over several workgroups
+ * (merged in a fixed order, so results are deterministic). */
 size_t flux_attention_workspace_size(const flux_cfg* cfg, int batch, int seq);
 int flux_attention(const flux_cfg* cfg, int batch, int seq, const void* q, const void* k,
                    const void* v, int64_t ld_in, void* o, int64_t ld_out, void* workspace,

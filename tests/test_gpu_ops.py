@@ -254,7 +254,10 @@ def test_linear_gated_residual(m, n, k, dtype, use_ws):
 # ------------------------------------------------------------------------------------
 @pytest.mark.parametrize("seq,heads,batch,dtype,n_q", [
     (80, 2, 1, "f32", None), (80, 2, 1, "bf16", None), (200, 3, 2, "bf16", None),
-    (1, 1, 1, "bf16", None), (1536, 24, 1, "bf16", 96), (4608, 32, 1, "bf16", 48)])
+    (1, 1, 1, "bf16", None), (1536, 24, 1, "bf16", 96), (4608, 32, 1, "bf16", 48),
+    # query blocks of a partial last round split along the keys and merged: 2-wave blocks
+    # with 2 key ranges, 4-wave blocks with 4 ranges and a ragged last tile, batch 2
+    (600, 3, 1, "bf16", None), (1100, 64, 1, "bf16", 64), (700, 6, 2, "bf16", None)])
 def test_attention(seq, heads, batch, dtype, n_q):
     t = G.torch()
     seed = seq + heads

@@ -26,6 +26,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace flux {
 
 template <class T>
@@ -38,8 +40,6 @@ FLUX_DEV T* seq_mptr(const SeqView& v, int b, int j) {
   return (j < v.n0) ? static_cast<T*>(v.base0) + b * v.bs0 + (int64_t)j * v.ld
                     : static_cast<T*>(v.base1) + b * v.bs1 + (int64_t)(j - v.n0) * v.ld;
 }
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kHD = 128;   // head dim
 constexpr int kBKV = 64;   // keys per tile
@@ -97,30 +97,57 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     const bf16* qp = seq_cptr<bf16>(qv, b, qi) + hoff + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+    // compiler-visible vmcnt(0): the compiler does not count the asm K/V loads, so a wait
+    // it derived for these Q loads inside the key loop would also stall on those
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
   // ---- direct-load plan.  K: one wave instruction = 4 rows x 256 B; lane -> row
   // (lane >> 4), slot (lane & 15).  V^T: one instruction = 8 rows x 128 B; lane -> row
-  // (lane >> 3), slot (lane & 7).  Each lane fetches the logical chunk of its slot.
+  // (lane >> 3), slot (lane & 7).  Each lane fetches the logical chunk of its slot.  A key
+  // tile that lies inside one segment of the key view and inside the sequence is addressed
+  // as a scalar base (per tile) + a fixed per-lane byte offset, so issuing it costs no
+  // vector instructions; other tiles (the last one, one straddling the txt/img boundary)
+  // take per-lane addresses with the key clamped to the sequence.
   constexpr int KI = 16 / NW;  // K instructions per wave per tile (64 rows / 4)
   constexpr int VI = 16 / NW;  // V instructions per wave per tile (128 rows / 8)
   const bf16* vt_head = vt + ((int64_t)b * dim + hoff) * ld_vt;
+  uint32_t k_voff[KI], v_voff[VI];
+#pragma unroll
+  for (int j = 0; j < KI; ++j) {
+    const int row = (wave * KI + j) * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 15);
+    k_voff[j] = (uint32_t)(((int64_t)row * kv.ld + hoff + c * 8) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < VI; ++j) {
+    const int d = (wave * VI + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((d >> 1) & 7);
+    v_voff[j] = (uint32_t)(((int64_t)d * ld_vt + c * 8) * 2);
+  }
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t ks0 = __builtin_amdgcn_readfirstlane(lds_u32(&Ks[0][0])) + wv * KI * 4 * kHD * 2;
+  const uint32_t vs0 = __builtin_amdgcn_readfirstlane(lds_u32(&Vs[0][0])) + wv * VI * 8 * kBKV * 2;
+  constexpr uint32_t KBUF = kBKV * kHD * 2, VBUF = kHD * kBKV * 2;
   auto issue = [&](int buf, int kv0) {
+    const bool in0 = kv0 + kBKV <= kv.n0, in1 = kv0 >= kv.n0;
+    if ((in0 || in1) && kv0 + kBKV <= seq) {
+      const bf16* kb = in0 ? static_cast<const bf16*>(kv.base0) + b * kv.bs0 + (int64_t)kv0 * kv.ld
+                           : static_cast<const bf16*>(kv.base1) + b * kv.bs1 +
+                                 (int64_t)(kv0 - kv.n0) * kv.ld;
 #pragma unroll
-    for (int j = 0; j < KI; ++j) {
-      const int row = (wave * KI + j) * 4 + (lane >> 4);
-      const int key = min(kv0 + row, seq - 1);  // past the end: a valid row, masked later
-      const int c = (lane & 15) ^ (row & 15);
-      const bf16* src = seq_cptr<bf16>(kv, b, key) + hoff + c * 8;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&Ks[buf][(wave * KI + j) * 4 * kHD], 16, 0, 0);
+      for (int j = 0; j < KI; ++j) dma16s(kb, k_voff[j], ks0 + buf * KBUF + j * 4 * kHD * 2);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KI; ++j) {
+        const int row = (wave * KI + j) * 4 + (lane >> 4);
+        const int key = min(kv0 + row, seq - 1);  // past the end: a valid row, masked later
+        const int c = (lane & 15) ^ (row & 15);
+        dma16v(seq_cptr<bf16>(kv, b, key) + hoff + c * 8, ks0 + buf * KBUF + j * 4 * kHD * 2);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < VI; ++j) {
-      const int d = (wave * VI + j) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((d >> 1) & 7);
-      const bf16* src = vt_head + (int64_t)d * ld_vt + kv0 + c * 8;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&Vs[buf][(wave * VI + j) * 8 * kBKV], 16, 0, 0);
-    }
+    for (int j = 0; j < VI; ++j) dma16s(vt_head + kv0, v_voff[j], vs0 + buf * VBUF + j * 8 * kBKV * 2);
   };
 
   f32x16 o[4];
@@ -130,13 +157,12 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const int krow0 = key_perm(l32), krow1 = 32 + key_perm(l32);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-  issue(t_begin & 1, t_begin * kBKV);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int it = t_begin; it < t_end; ++it) {
-    const int cur = it & 1;
+  // one key tile; CUR = its LDS buffer (compile time, so every LDS offset is immediate)
+  auto tile = [&](int it, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
     const int kv0 = it * kBKV;
     if (it + 1 < t_end) issue(cur ^ 1, kv0 + kBKV);
 
@@ -162,12 +188,25 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
           if (kv0 + 32 * h + 16 * (r >> 3) + 8 * g + (r & 7) >= seq) s[h][r] = -INFINITY;
     }
 
-    // online softmax with a lazily updated maximum (log2 domain)
-    float mx = s[0][0];
+    // online softmax in the log2 domain with a lazily updated maximum: the exponentials
+    // are taken against the running maximum while the tile maximum is found; only when
+    // some row's maximum grows by more than 2^8 are O and the sum rescaled and the
+    // exponentials redone (every row on the first tile, rarely afterwards)
+    float p[2][16];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h][r]);
+      for (int r = 0; r < 16; ++r)
+        // raw v_exp_f32: arguments are <= 8, results below 2^-126 may flush to zero
+        p[h][r] = __builtin_amdgcn_exp2f(fmaf(s[h][r], scale_log2, -m_run));
+    float mx4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx4[i] = fmaxf(s[0][i], s[1][i]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 4 * (1 - h); r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[h][r]);
+    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
     const bool grow = mx > m_run + 8.f;
     if (__any(grow)) {
@@ -179,26 +218,27 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
       m_run = m_new;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[h][r] = __builtin_amdgcn_exp2f(fmaf(s[h][r], scale_log2, -m_run));
     }
-    float psum = 0.f;
+
+    // P in bf16 (the PV product's operand); the row sum is taken over the same rounded
+    // values with bf16 dot products against (1, 1)
+    uint32_t pw[16];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int i = 0; i < 16; ++i) pw[i] = pack2(p[i >> 3][2 * (i & 7)], p[i >> 3][2 * (i & 7) + 1]);
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // raw v_exp_f32: arguments are <= 8, results below 2^-126 may flush to zero
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[h][r], scale_log2, -m_run));
-        s[h][r] = p;
-        psum += p;
-      }
-    l_run += psum;
+    for (int i = 0; i < 16; ++i)
+      ls[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[i]), ones, ls[i & 3], false);
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
     // O^T += V^T P^T over 4 chunks of 16 keys; lane group g owns keys 16 c + 8 g .. + 8
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int h = c >> 1, r0 = 8 * (c & 1);
-      const uint4 pw = make_uint4(pack2(s[h][r0], s[h][r0 + 1]), pack2(s[h][r0 + 2], s[h][r0 + 3]),
-                                  pack2(s[h][r0 + 4], s[h][r0 + 5]), pack2(s[h][r0 + 6], s[h][r0 + 7]));
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const bf16x8 vf =
@@ -209,7 +249,20 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  issue(t_begin & 1, t_begin * kBKV);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  using Buf0 = std::integral_constant<int, 0>;
+  using Buf1 = std::integral_constant<int, 1>;
+  int it = t_begin;
+  if (it < t_end && (it & 1)) tile(it++, Buf1{});
+  for (; it + 1 < t_end; it += 2) {
+    tile(it, Buf0{});
+    tile(it + 1, Buf1{});
   }
+  if (it < t_end) tile(it, Buf0{});
 
   // lane owns query l32 and dims 32 dt + 8 (r/4) + 4 g + r%4
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

@@ -65,5 +65,27 @@ FLUX_DEV float group_sum16(float v) {  // sum over aligned groups of 16 lanes
 
 FLUX_DEV float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
+// ---- direct global->LDS loads ---------------------------------------------------------
+// Byte address of an LDS object (wave-uniform when the object is).
+FLUX_DEV uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16-byte global->LDS loads issued through inline asm (M0 = wave-uniform LDS byte address;
+// lane i writes LDS bytes [16 i, 16 i + 16)).  The compiler does not track these loads, so
+// it adds no conservative vmcnt(0) before later LDS reads or barriers; callers wait
+// explicitly (s_waitcnt vmcnt) before they read the data.
+//   dma16s: global address = scalar base + per-lane 32-bit byte offset
+//   dma16v: per-lane 64-bit global address
+FLUX_DEV void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff),
+               "s"(base)
+               : "memory", "m0");
+}
+FLUX_DEV void dma16v(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // ---- dtype tags shared with the host -------------------------------------------------
 enum { DT_BF16 = 0, DT_F32 = 1 };

@@ -301,20 +301,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
 // steady state carries no branches.  Rows past M / N are clamped to valid rows (their
 // results are never stored).
 // ------------------------------------------------------------------------------------
-FLUX_DEV uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 16-byte global->LDS load through inline asm: M0 = wave-uniform LDS byte address, global
-// address = scalar base + per-lane 32-bit byte offset.  The compiler does not track these
-// loads, so it adds no conservative vmcnt(0) before LDS reads or barriers; the kernel
-// waits explicitly with wait_vmcnt.
-FLUX_DEV void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff),
-               "s"(base)
-               : "memory", "m0");
-}
-
 template <int N>
 FLUX_DEV void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -3,6 +3,8 @@ MI355X through the C ABI.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --probe dominant|copy      # a few bare launches, for counter runs
+    python bench.py --per-config               # one JSON line per traced workload: ms per
+                                               # block, LN+modulate and RMSNorm+RoPE GB/s
 
 Prints ONE JSON line: step throughput (algorithmic TFLOP/s, whole step), ms per step, the
 roofline of the dominant kernel (timed live with HIP events on the stream it runs on), and
@@ -221,6 +223,90 @@ def cpu_baseline(wl, flops_step: float):
     }
 
 
+# ------------------------------------------------------------------------------------
+# per-workload block timings and bandwidth-kernel rates
+# ------------------------------------------------------------------------------------
+PER_CONFIG = ("tiny_single_f32", "klein4b_single_512", "klein9b_double_1024",
+              "klein9b_step_1024", "dev_pair_2048")
+
+
+def _time_ms(fn, s, warmup=3, reps=10):
+    import torch
+    for _ in range(warmup):
+        fn()
+    ev = Events(s)
+    torch.cuda.synchronize()
+    ev.start()
+    for _ in range(reps):
+        fn()
+    return ev.stop_ms() / reps
+
+
+def per_config_line(F, fs, name: str) -> dict:
+    import torch
+    wl = fs.workload(name)
+    dtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    fdt = F.FLUX_BF16 if wl.dtype == "bf16" else F.FLUX_F32
+    D, H, B = wl.dim, wl.mlp_hidden, wl.batch
+    Nt, Ni, L = wl.n_txt, wl.n_img, wl.seq
+    cfg = F.make_cfg(D, wl.heads, H, dtype=fdt)
+    s = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed)
+    img = torch.randn((B, Ni, D), generator=g, device="cuda").to(dtype)
+    txt = torch.randn((B, Nt, D), generator=g, device="cuda").to(dtype)
+    t = torch.rand((B,), generator=g, device="cuda")
+    img_ids = torch.from_numpy(fs.image_ids(Ni)).cuda()
+    txt_ids = torch.from_numpy(fs.text_ids(Nt)).cuda()
+    img_o, txt_o = torch.empty_like(img), torch.empty_like(txt)
+    kinds = {"single": ("single",), "double": ("double",), "step": ("double", "single"),
+             "pair": ("double", "single")}[wl.kind]
+    res = {"workload": name, "dtype": wl.dtype, "dim": D, "heads": wl.heads, "mlp_hidden": H,
+           "n_txt": Nt, "n_img": Ni, "batch": B}
+    for kind in kinds:
+        if kind == "double":
+            w = device_weights(fs.double_block_weight_specs(D, H), wl.seed, dtype)
+            nb = F.flux_double_block_workspace_size(cfg, B, Ni, Nt)
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            bw = F.double_weights(w)
+            fn = lambda: F.flux_double_block_fwd(cfg, bw, t, B, Ni, Nt, img, txt, img_ids, txt_ids,
+                                                 img_o, txt_o, ws, nb, s)
+        else:
+            w = device_weights(fs.single_block_weight_specs(D, H), wl.seed, dtype)
+            nb = F.flux_single_block_workspace_size(cfg, B, Ni, Nt)
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            bw = F.single_weights(w)
+            fn = lambda: F.flux_single_block_fwd(cfg, bw, t, B, Ni, Nt, img, txt, img_ids, txt_ids,
+                                                 img_o, txt_o, ws, nb, s)
+        ms = _time_ms(fn, s)
+        fl = block_flops(kind, D, H, Ni, Nt, B)
+        res[f"{kind}_block_ms"] = round(ms, 4)
+        res[f"{kind}_block_tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
+        del w, ws, bw
+    # LN + modulate over the joint sequence: fp32 residual in, model dtype out (as the step)
+    x32 = torch.randn((B * L, D), generator=g, device="cuda")
+    y = torch.empty((B * L, D), device="cuda", dtype=dtype)
+    sh = torch.randn((B, D), generator=g, device="cuda")
+    sc = torch.randn((B, D), generator=g, device="cuda")
+    ms = _time_ms(lambda: F.flux_layernorm_modulate(cfg, B * L, L, x32, F.FLUX_F32, sh, sc, y, s), s)
+    nbytes = B * L * D * (4 + y.element_size())
+    res["ln_modulate_us"] = round(ms * 1e3, 2)
+    res["ln_modulate_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    res["ln_modulate_pct_hbm"] = round(100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+    # RMSNorm + RoPE on q and k in place, inside a [B, L, 3D] QKV buffer
+    qkv = torch.randn((B, L, 3 * D), generator=g, device="cuda").to(dtype)
+    gam = torch.ones(128, device="cuda")
+    nb = F.flux_qk_norm_rope_workspace_size(cfg, Nt, Ni)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    ms = _time_ms(lambda: F.flux_qk_norm_rope(cfg, B, Nt, Ni, qkv, qkv[..., D:], 3 * D, gam, gam,
+                                              gam, gam, txt_ids, img_ids, ws, nb, s), s)
+    nbytes = 2 * 2 * B * L * D * qkv.element_size()
+    res["qk_norm_rope_us"] = round(ms * 1e3, 2)
+    res["qk_norm_rope_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    res["qk_norm_rope_pct_hbm"] = round(100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +314,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="klein9b_step_1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-config", action="store_true",
+                    help="time the blocks and bandwidth kernels of every traced workload")
     ap.add_argument("--probe", choices=("dominant", "copy"), default=None,
                     help="only launch the dominant kernel (or a 1 GiB copy) 3 times and exit")
     args = ap.parse_args(argv)
@@ -244,6 +332,11 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
         return 1
+    if args.per_config:
+        for name in PER_CONFIG:
+            print(json.dumps(per_config_line(F, fs, name)), flush=True)
+            torch.cuda.empty_cache()
+        return 0
     wl = fs.workload(args.workload)
     assert wl.kind == "step"
     if args.probe == "dominant":

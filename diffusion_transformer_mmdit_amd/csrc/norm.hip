@@ -3,9 +3,9 @@
 //
 // LayerNorm + modulate ("双流块" AdaLN pre-norm of the Diffusers walk-through, eps 1e-6):
 //   y = (1 + scale) * (x - mean) / sqrt(var + eps) + shift   (biased variance, no affine)
-// One wave per row: the row is held in registers (16-byte loads, 8 elements per lane per
-// chunk), mean and variance are two exact passes over the registers with wave64 shuffle
-// reductions, and the output is written with 16-byte stores.
+// One wave per row: the row is held in registers (each lane moves 16 bytes of the input
+// per chunk, so a wave instruction reads 1 KB contiguously), mean and variance are two
+// exact passes over the registers with wave64 shuffle reductions.
 //
 // QK RMSNorm + RoPE ("双流块" norm_q / norm_k; "位置 id 的维度" per-axis rotary embedding,
 // theta 2000, axes 32/32/32/32): 16 lanes own one (token, head) vector of 128 values;
@@ -45,27 +45,59 @@ FLUX_DEV void store8<float>(float* p, const float* f) {
 // ------------------------------------------------------------------------------------
 // LayerNorm + modulate
 // ------------------------------------------------------------------------------------
-template <class TX, class TY, int MAXI>
+// CW-element chunk I/O: a lane moves 16 bytes of the input type per chunk (CW = 4 fp32 or
+// 8 bf16), so each wave instruction reads 1 KB contiguously.
+template <class T, int CW>
+FLUX_DEV void load_cw(const T* p, float* f) {
+  if constexpr (CW == 8) {
+    load8(p, f);
+  } else {
+    static_assert(sizeof(T) == 4 && CW == 4, "fp32 chunks of 4");
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  }
+}
+template <class T, int CW>
+FLUX_DEV void store_cw(T* p, const float* f) {
+  if constexpr (CW == 8) {
+    store8(p, f);
+  } else if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack2(f[0], f[1]), pack2(f[2], f[3]));
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  }
+}
+FLUX_DEV void load_mod(const float* p, float* f, int n) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  if (n == 8) {
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+}
+
+template <class TX, class TY, int MAXI, bool EXACT>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(const TX* __restrict__ x, int64_t ldx,
                                                           TY* __restrict__ y, int64_t ldy,
                                                           int rows, int dim, int rpb,
                                                           const float* __restrict__ shift,
                                                           const float* __restrict__ scale,
                                                           int64_t mod_bs, float eps) {
+  constexpr int CW = 16 / sizeof(TX);  // elements per lane chunk
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const int nch = dim >> 3;
+  const int nch = dim / CW;
   const TX* xr = x + (int64_t)row * ldx;
-  float v[MAXI][8];
+  float v[MAXI][CW];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     const int c = lane + 64 * i;
-    if (c < nch) {
-      load8(xr + c * 8, v[i]);
+    if (EXACT || c < nch) {
+      load_cw<TX, CW>(xr + c * CW, v[i]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[i][e];
+      for (int e = 0; e < CW; ++e) s += v[i][e];
     }
   }
   const float mean = wave_sum(s) / dim;
@@ -73,9 +105,9 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const TX* __restrict__
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     const int c = lane + 64 * i;
-    if (c < nch) {
+    if (EXACT || c < nch) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < CW; ++e) {
         v[i][e] -= mean;
         q += v[i][e] * v[i][e];
       }
@@ -89,14 +121,62 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const TX* __restrict__
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     const int c = lane + 64 * i;
-    if (c < nch) {
-      float a[8], m[8], o[8];
-      load8(sh + c * 8, a);
-      load8(sc + c * 8, m);
+    if (EXACT || c < nch) {
+      float a[CW], m[CW], o[CW];
+      load_mod(sh + c * CW, a, CW);
+      load_mod(sc + c * CW, m, CW);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (1.f + m[e]) * (v[i][e] * rstd) + a[e];
-      store8(yr + c * 8, o);
+      for (int e = 0; e < CW; ++e) o[e] = (1.f + m[e]) * (v[i][e] * rstd) + a[e];
+      store_cw<TY, CW>(yr + c * CW, o);
     }
+  }
+}
+
+// fp32 rows of exactly 256 J values (the residual stream): lane l holds the float4s
+// 4 (l + 64 j), j < J, so every load instruction reads 1 KB contiguously.
+template <class TY, int J>
+__global__ __launch_bounds__(256) void ln_modulate_f32_kernel(const float* __restrict__ x,
+                                                              int64_t ldx, TY* __restrict__ y,
+                                                              int64_t ldy, int rows, int rpb,
+                                                              const float* __restrict__ shift,
+                                                              const float* __restrict__ scale,
+                                                              int64_t mod_bs, float eps) {
+  constexpr int D = 256 * J;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)min(row, rows - 1) * ldx);
+  float4 v[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) v[j] = xr[lane + 64 * j];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+  const float mean = wave_sum(s) * (1.f / D);
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    v[j].x -= mean;
+    v[j].y -= mean;
+    v[j].z -= mean;
+    v[j].w -= mean;
+    q += (v[j].x * v[j].x + v[j].y * v[j].y) + (v[j].z * v[j].z + v[j].w * v[j].w);
+  }
+  const float rstd = rsqrtf(wave_sum(q) * (1.f / D) + eps);
+  if (row >= rows) return;
+  const int b = row / rpb;
+  const float4* sh = reinterpret_cast<const float4*>(shift + b * mod_bs);
+  const float4* sc = reinterpret_cast<const float4*>(scale + b * mod_bs);
+  TY* yr = y + (int64_t)row * ldy;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = lane + 64 * j;
+    const float4 a = sh[c], m = sc[c];
+    float o[4] = {(1.f + m.x) * (v[j].x * rstd) + a.x, (1.f + m.y) * (v[j].y * rstd) + a.y,
+                  (1.f + m.z) * (v[j].z * rstd) + a.z, (1.f + m.w) * (v[j].w * rstd) + a.w};
+    store_cw<TY, 4>(yr + 4 * c, o);
+    // the modulation vectors' loads are issued 4 chunks at a time, not all hoisted ahead
+    // of the loop (that doubles the registers and halves the waves in flight)
+    if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -104,20 +184,40 @@ template <class TX, class TY>
 static hipError_t ln_dispatch(const void* x, int64_t ldx, void* y, int64_t ldy, int rows, int dim,
                               int rpb, const float* shift, const float* scale, int64_t mod_bs,
                               float eps, hipStream_t s) {
-  const int per_lane = (dim / 8 + 63) / 64;
+  constexpr int CW = 16 / sizeof(TX);
+  const int per_lane = (dim / CW + 63) / 64;
   dim3 grid((rows + 3) / 4), block(256);
   auto* xp = static_cast<const TX*>(x);
   auto* yp = static_cast<TY*>(y);
-#define FLUX_LN(N)                                                                          \
-  hipLaunchKernelGGL((ln_modulate_kernel<TX, TY, N>), grid, block, 0, s, xp, ldx, yp, ldy, \
-                     rows, dim, rpb, shift, scale, mod_bs, eps)
+  if constexpr (sizeof(TX) == 4) {
+#define FLUX_LN32(J)                                                                          \
+  if (dim == 256 * J) {                                                                      \
+    hipLaunchKernelGGL((ln_modulate_f32_kernel<TY, J>), grid, block, 0, s, xp, ldx, yp, ldy, \
+                       rows, rpb, shift, scale, mod_bs, eps);                               \
+    return hipGetLastError();                                                               \
+  }
+    FLUX_LN32(12) FLUX_LN32(16) FLUX_LN32(24) FLUX_LN32(32)
+#undef FLUX_LN32
+  }
+  // rows that fill whole sets of 64 chunks (every traced width) take the unguarded kernel
+  const bool exact = (dim / CW) % 64 == 0;
+#define FLUX_LN(N)                                                                           \
+  do {                                                                                      \
+    if (exact && (dim / CW) == 64 * N)                                                      \
+      hipLaunchKernelGGL((ln_modulate_kernel<TX, TY, N, true>), grid, block, 0, s, xp, ldx, \
+                         yp, ldy, rows, dim, rpb, shift, scale, mod_bs, eps);               \
+    else                                                                                    \
+      hipLaunchKernelGGL((ln_modulate_kernel<TX, TY, N, false>), grid, block, 0, s, xp,     \
+                         ldx, yp, ldy, rows, dim, rpb, shift, scale, mod_bs, eps);          \
+  } while (0)
   if (per_lane <= 1) FLUX_LN(1);
   else if (per_lane <= 2) FLUX_LN(2);
   else if (per_lane <= 4) FLUX_LN(4);
-  else if (per_lane <= 6) FLUX_LN(6);
   else if (per_lane <= 8) FLUX_LN(8);
   else if (per_lane <= 12) FLUX_LN(12);
   else if (per_lane <= 16) FLUX_LN(16);
+  else if (per_lane <= 24) FLUX_LN(24);
+  else if (per_lane <= 32) FLUX_LN(32);
   else return hipErrorInvalidValue;
 #undef FLUX_LN
   return hipGetLastError();
@@ -230,11 +330,65 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(SeqView q, SeqView k,
   store8(p, o);
 }
 
+// One workgroup per token: thread t owns chunks c = t + 256 i of the token's [q | k] (8
+// values each); c % 16 == t % 16, so the thread's (cos, sin) slice of the token and its
+// position in every head are fixed, and the angle table row is read once per token.
+template <class T>
+__global__ __launch_bounds__(256) void qk_norm_rope_token_kernel(
+    SeqView q, SeqView k, int batch, int seq, int heads, const float* __restrict__ qg0,
+    const float* __restrict__ kg0, const float* __restrict__ qg1, const float* __restrict__ kg1,
+    const float2* __restrict__ cs, float eps) {
+  const int l16 = threadIdx.x & 15;
+  const int qchunks = heads * 16, nch = 2 * qchunks;
+  const int64_t token = blockIdx.x;
+  const int j = token % seq, b = token / seq;
+  const float4* c4 = reinterpret_cast<const float4*>(cs + (int64_t)j * 64 + l16 * 4);
+  const float4 c01 = c4[0], c23 = c4[1];
+  const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
+  const float sn[4] = {c01.y, c01.w, c23.y, c23.w};
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    const int which = c >= qchunks;
+    const int head = (c - which * qchunks) >> 4;
+    const SeqView& v = which ? k : q;
+    const bool seg1 = j >= v.n0;
+    const float* g = which ? (seg1 ? kg1 : kg0) : (seg1 ? qg1 : qg0);
+    T* p = seq_ptr<T>(v, b, j) + head * 128 + l16 * 8;
+    float x[8], gm[8];
+    load8(p, x);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    const float r = rsqrtf(group_sum16(ss) * (1.f / 128.f) + eps);
+    load8(g + l16 * 8, gm);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * r * gm[e];
+    float o[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      o[2 * t] = x[2 * t] * cc[t] - x[2 * t + 1] * sn[t];
+      o[2 * t + 1] = x[2 * t] * sn[t] + x[2 * t + 1] * cc[t];
+    }
+    store8(p, o);
+  }
+}
+
 hipError_t qk_norm_rope(int dtype, SeqView q, SeqView k, int batch, int seq, int heads,
                         const float* qg0, const float* kg0, const float* qg1, const float* kg1,
                         const float2* cs, float eps, hipStream_t s) {
   const int64_t units = (int64_t)batch * seq * heads * 2;
   if (units <= 0) return hipSuccess;
+  // measured on MI355X: the per-token kernel is faster up to 32 heads (4 chunks per
+  // thread), the per-(token, head) one above
+  if (heads <= 32) {
+    dim3 grid((unsigned)((int64_t)batch * seq)), block(256);
+    if (dtype == DT_BF16)
+      hipLaunchKernelGGL(qk_norm_rope_token_kernel<bf16>, grid, block, 0, s, q, k, batch, seq,
+                         heads, qg0, kg0, qg1, kg1, cs, eps);
+    else
+      hipLaunchKernelGGL(qk_norm_rope_token_kernel<float>, grid, block, 0, s, q, k, batch, seq,
+                         heads, qg0, kg0, qg1, kg1, cs, eps);
+    return hipGetLastError();
+  }
   dim3 grid((units + 15) / 16), block(256);
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(qk_norm_rope_kernel<bf16>, grid, block, 0, s, q, k, batch, seq, heads, qg0,

@@ -27,6 +27,7 @@ from __future__ import annotations
 import math
 import os
 import zlib
+from collections.abc import Mapping
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 
@@ -266,6 +267,57 @@ def make_weights(specs: dict, seed: int, dtype: str, names=None,
         return dict(one(n) for n in names)
     with ThreadPoolExecutor(threads) as ex:
         return dict(ex.map(one, names))
+
+
+class LazyWeights(Mapping):
+    """Step weights generated on first use, one block at a time.
+
+    Names "double.{i}.*" / "single.{i}.*" form one group per block: the first access to a
+    name of a block generates the whole block and drops the previously generated block;
+    other names are generated once and kept.  Values equal make_weights(specs, ...)[name]
+    (each tensor has its own named random stream), so a consumer that walks the blocks in
+    order holds one block's weights at a time.
+    """
+
+    def __init__(self, specs: dict, seed: int, dtype: str, threads: int | None = None):
+        self._specs, self._seed, self._dtype, self._threads = specs, seed, dtype, threads
+        self._groups: dict[str, list] = {}
+        for n in specs:
+            self._groups.setdefault(self._group(n), []).append(n)
+        self._block_key, self._block = None, {}
+        self._kept: dict = {}
+
+    @staticmethod
+    def _group(name: str) -> str:
+        parts = name.split(".")
+        return ".".join(parts[:2]) if parts[0] in ("double", "single") and len(parts) > 2 else name
+
+    def __getitem__(self, name):
+        g = self._group(name)
+        if g == name:
+            if name not in self._kept:
+                self._kept[name] = make_weights(self._specs, self._seed, self._dtype, [name])[name]
+            return self._kept[name]
+        if g != self._block_key:
+            self._block = {}
+            self._block = make_weights(self._specs, self._seed, self._dtype, self._groups[g],
+                                       threads=self._threads)
+            self._block_key = g
+        return self._block[name]
+
+    def __iter__(self):
+        return iter(self._specs)
+
+    def __len__(self):
+        return len(self._specs)
+
+    def groups(self) -> list:
+        """Group keys in the order the step uses them (globals, then blocks)."""
+        return list(self._groups)
+
+    def group_names(self, group: str) -> list:
+        """Tensor names of one group."""
+        return list(self._groups[group])
 
 
 # ----------------------------------------------------------------------------------

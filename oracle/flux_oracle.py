@@ -309,6 +309,91 @@ def single_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: Sequence | Non
 
 
 # ----------------------------------------------------------------------------------
+# Blocks evaluated at a subset of output rows (large workloads)
+#
+# Every step of a block except the attention's mixing over keys acts on one token at a
+# time, so the outputs of selected rows need only the keys and values of all tokens and
+# everything else for the selected rows.  These functions compute exactly that, with the
+# same steps as double_block / single_block; tests pin them to those on small inputs.
+# ----------------------------------------------------------------------------------
+def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """attention() for a subset of queries: q [B, R, h, d] (already rotated), k and v
+    [B, L, h, d] -> [B, R, h*d]."""
+    B, R, h, d = q.shape
+    out = np.empty((B, R, h, d), dtype=np.float64)
+    for b in range(B):
+        for head in range(h):
+            p = attention_weights(q[b, :, head, :], k[b, :, head, :])
+            out[b, :, head, :] = np.matmul(p, v[b, :, head, :])
+    return out.reshape(B, R, h * d)
+
+
+def double_block_rows(img, txt, t, w: Mapping, img_ids, txt_ids, rows_img, rows_txt,
+                      mods: dict | None = None):
+    """double_block() outputs at image rows `rows_img` and text rows `rows_txt` only.
+
+    Returns (img_out [B, len(rows_img), D], txt_out [B, len(rows_txt), D]), float64."""
+    streams = {"txt": f64(txt), "img": f64(img)}
+    rows = {"txt": np.asarray(rows_txt, dtype=np.int64), "img": np.asarray(rows_img, dtype=np.int64)}
+    if mods is None:
+        mods = double_block_mods(t, w)
+    D = streams["img"].shape[-1]
+    n_txt = streams["txt"].shape[1]
+    pos = rope_positions(txt_ids, img_ids)
+    qs, ks, vs = {}, {}, {}
+    for s in ("txt", "img"):
+        shift1, scale1 = mods[s][0], mods[s][1]
+        wqkv = f64(w[f"{s}.qkv"])
+        a = layernorm_modulate(streams[s], shift1, scale1)
+        kv = linear(a, wqkv[D:])                                 # keys, values: all tokens
+        ks[s] = rms_norm(_heads(kv[..., :D]), f64(w[f"{s}.k_norm"]))
+        vs[s] = _heads(kv[..., D:])
+        q = linear(a[:, rows[s]], wqkv[:D])                      # queries: selected rows
+        qs[s] = rms_norm(_heads(q), f64(w[f"{s}.q_norm"]))
+    k = apply_rope(np.concatenate([ks["txt"], ks["img"]], axis=1), pos)
+    v = np.concatenate([vs["txt"], vs["img"]], axis=1)
+    out = {}
+    for s, off in (("txt", 0), ("img", n_txt)):
+        q = apply_rope(qs[s], pos[rows[s] + off])
+        o = attention_rows(q, k, v)
+        _, _, gate1, shift2, scale2, gate2 = mods[s]
+        x = streams[s][:, rows[s]] + gate1[:, None, :] * linear(o, f64(w[f"{s}.out"]))
+        u = linear(layernorm_modulate(x, shift2, scale2), f64(w[f"{s}.mlp_in"]))
+        out[s] = x + gate2[:, None, :] * linear(swiglu(u), f64(w[f"{s}.mlp_out"]))
+    return out["img"], out["txt"]
+
+
+def single_block_rows(img, txt, t, w: Mapping, img_ids, txt_ids, rows_img, rows_txt,
+                      mods: Sequence | None = None):
+    """single_block() outputs at image rows `rows_img` and text rows `rows_txt` only.
+
+    Returns (img_out [B, len(rows_img), D], txt_out [B, len(rows_txt), D]), float64."""
+    txt = f64(txt)
+    img = f64(img)
+    n_txt = txt.shape[1]
+    x = np.concatenate([txt, img], axis=1)
+    D = x.shape[-1]
+    if mods is None:
+        mods = single_block_mods(t, w)
+    shift, scale, gate = mods
+    w1 = f64(w["linear1"])
+    a = layernorm_modulate(x, shift, scale)
+    kv = linear(a, w1[D:3 * D])                                  # keys, values: all tokens
+    pos = rope_positions(txt_ids, img_ids)
+    k = apply_rope(rms_norm(_heads(kv[..., :D]), f64(w["k_norm"])), pos)
+    v = _heads(kv[..., D:])
+    sel = np.concatenate([np.asarray(rows_txt, dtype=np.int64),
+                          n_txt + np.asarray(rows_img, dtype=np.int64)])
+    y = linear(a[:, sel], w1[np.r_[0:D, 3 * D:w1.shape[0]]])     # q and [gate | up]
+    q = apply_rope(rms_norm(_heads(y[..., :D]), f64(w["q_norm"])), pos[sel])
+    o = attention_rows(q, k, v)
+    out = x[:, sel] + gate[:, None, :] * linear(np.concatenate([o, swiglu(y[..., D:])], axis=-1),
+                                                f64(w["linear2"]))
+    nt = len(rows_txt)
+    return out[:, nt:], out[:, :nt]
+
+
+# ----------------------------------------------------------------------------------
 # Denoiser step
 # ----------------------------------------------------------------------------------
 class _Prefixed(Mapping):

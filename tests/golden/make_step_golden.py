@@ -1,0 +1,65 @@
+"""Write the sampled fp64 oracle output of one full Klein-9B 1024² denoiser step.
+
+    python tests/golden/make_step_golden.py [--workload klein9b_step_1024] [--rows 16]
+
+Calls only oracle/ (the fp64 definition) and the seeded input generator: the weights are
+generated block by block (flux_synth.LazyWeights), the step runs in fp64 on the host (a
+few minutes), and the output rows of a seeded sample of image tokens (always the first and
+the last) are written to tests/golden/<workload>.txt, all 128 channels each, for the GPU
+test that runs the same step through flux_denoiser_step.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import flux_synth as fs  # noqa: E402
+from oracle import flux_oracle as O  # noqa: E402
+
+
+def sample_rows(n_img: int, k: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng([seed, 7])
+    mid = rng.choice(np.arange(1, n_img - 1), size=k - 2, replace=False)
+    return np.sort(np.concatenate([[0, n_img - 1], mid])).astype(np.int64)
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="klein9b_step_1024")
+    ap.add_argument("--rows", type=int, default=16)
+    args = ap.parse_args(argv)
+    wl = fs.workload(args.workload)
+    assert wl.kind == "step" and wl.batch == 1
+    inp = fs.step_inputs(wl, with_weights=False)
+    w = fs.LazyWeights(fs.step_weight_specs(wl), wl.seed, wl.dtype)
+    t0 = time.time()
+
+    def progress(kind, i):
+        print(f"[golden] {kind} block {i} done at {time.time() - t0:.0f} s", flush=True)
+
+    out = O.denoiser_step(inp["x"], inp["ctx"], inp["t"], w, inp["img_ids"], inp["txt_ids"],
+                          wl.n_double, wl.n_single, on_block=progress)
+    rows = sample_rows(wl.n_img, args.rows, wl.seed)
+    path = os.path.join(HERE, f"{wl.name}.txt")
+    with open(path, "w") as f:
+        f.write(f"# fp64 oracle output of one {wl.name} denoiser step (flux_synth seed {wl.seed},"
+                f" t = {float(inp['t'][0]):.9g})\n")
+        f.write("# written by tests/golden/make_step_golden.py (oracle/ + flux_synth only)\n")
+        f.write(f"# output rms over all rows: {np.sqrt(np.mean(out[0] ** 2)):.17g}\n")
+        f.write("# each line: image token index, then its 128 output channels\n")
+        for r in rows:
+            f.write(" ".join([str(int(r))] + [f"{v:.17g}" for v in out[0, r]]) + "\n")
+    print(f"[golden] wrote {path} ({len(rows)} rows) in {time.time() - t0:.0f} s", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

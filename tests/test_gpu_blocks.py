@@ -88,6 +88,38 @@ def test_klein9b_double_block_1024():
     check_block("double", wl, inp, "Klein-9B double 1024^2")
 
 
+def _sample(n, k, seed):
+    if n == 0:
+        return np.array([], dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(n), size=min(k, n), replace=False)
+    return np.unique(np.concatenate([[0, n - 1], mid])).astype(np.int64)
+
+
+@pytest.mark.parametrize("kind", ["double", "single"])
+def test_dev_pair_block_2048_sampled_rows(kind):
+    """FLUX.2-dev shapes at 2048² (D 6144, 48 heads, 512 + 16384 tokens): the whole block
+    on the GPU, the oracle at sampled output rows (keys and values from every token)."""
+    wl = fs.workload("dev_pair_2048")
+    inp = fs.block_inputs(wl, kind=kind)
+    img, txt = run(kind, wl, inp)
+    ri, rt = _sample(wl.n_img, 40, 11), _sample(wl.n_txt, 10, 12)
+    fn = O.double_block_rows if kind == "double" else O.single_block_rows
+    ref_img, ref_txt = fn(inp["img"], inp["txt"], inp["t"], inp["weights"], inp["img_ids"],
+                          inp["txt_ids"], ri, rt)
+    got_img, got_txt = G.host(img)[:, ri], G.host(txt)[:, rt]
+    G.assert_close(got_img, ref_img, wl.dtype, f"dev {kind} 2048^2 img rows")
+    G.assert_close(got_txt, ref_txt, wl.dtype, f"dev {kind} 2048^2 txt rows")
+    # the block's own update at those rows, against the rounding floor of the output
+    d_got = got_img - inp["img"][:, ri].astype(np.float64)
+    d_ref = ref_img - inp["img"][:, ri].astype(np.float64)
+    _, nl = G.errors(d_got, d_ref)
+    floor = np.linalg.norm(inp["img"][:, ri].astype(np.float64)) * 2.0 ** -9 / np.linalg.norm(d_ref)
+    print(f"[parity] dev {kind} img update at sampled rows: nL2={nl:.3e} (floor {floor:.1e})",
+          flush=True)
+    assert nl <= 2e-2 + 2 * floor, (nl, floor)
+
+
 # ------------------------------------------------------------------------------------
 # identities and determinism
 # ------------------------------------------------------------------------------------

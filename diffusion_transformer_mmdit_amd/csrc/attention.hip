@@ -160,9 +160,20 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-  // one key tile; CUR = its LDS buffer (compile time, so every LDS offset is immediate)
-  auto tile = [&](int it, auto cur_c) {
+  // per-lane LDS element offsets of the fragments: K rows krow0 (krow1 = krow0 + 32 has
+  // the same swizzle, so its fragments sit 32 rows further) for each of the 8 k-steps;
+  // V^T rows 32 dt + l32 (the swizzle depends only on l32) for each 16-key chunk c
+  int koff[8], voff[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = k_off(krow0, 2 * kk + g);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) voff[c] = v_off(l32, 2 * c + g);
+
+  // one key tile; CUR = its LDS buffer (compile time, so every LDS offset is immediate);
+  // MASK: the tile reaches past the sequence (only the last tile of the sequence can)
+  auto tile = [&](int it, auto cur_c, auto mask_c) {
     constexpr int cur = decltype(cur_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
     const int kv0 = it * kBKV;
     if (it + 1 < t_end) issue(cur ^ 1, kv0 + kBKV);
 
@@ -174,13 +185,13 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
       for (int r = 0; r < 16; ++r) s[h][r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[cur][k_off(krow0, 2 * kk + g)]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[cur][k_off(krow1, 2 * kk + g)]);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[cur][koff[kk]]);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[cur][koff[kk] + 32 * kHD]);
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[kk], s[1], 0, 0, 0);
     }
     // register r of block h holds key 32 h + 16 (r >> 3) + 8 g + (r & 7)
-    if (kv0 + kBKV > seq) {
+    if (MASK) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -241,8 +252,7 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
       const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(&Vs[cur][v_off(32 * dt + l32, 2 * c + g)]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vs[cur][voff[c] + 32 * dt * kBKV]);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[dt], 0, 0, 0);
       }
     }
@@ -256,13 +266,22 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
   __syncthreads();
   using Buf0 = std::integral_constant<int, 0>;
   using Buf1 = std::integral_constant<int, 1>;
+  using NoMask = std::false_type;
+  // tiles [t_begin, t_full) lie inside the sequence; a partial last tile is masked
+  const int t_full = min(t_end, seq / kBKV);
   int it = t_begin;
-  if (it < t_end && (it & 1)) tile(it++, Buf1{});
-  for (; it + 1 < t_end; it += 2) {
-    tile(it, Buf0{});
-    tile(it + 1, Buf1{});
+  if (it < t_full && (it & 1)) tile(it++, Buf1{}, NoMask{});
+  for (; it + 1 < t_full; it += 2) {
+    tile(it, Buf0{}, NoMask{});
+    tile(it + 1, Buf1{}, NoMask{});
   }
-  if (it < t_end) tile(it, Buf0{});
+  if (it < t_full) tile(it++, Buf0{}, NoMask{});
+  if (it < t_end) {
+    if (it & 1)
+      tile(it, Buf1{}, std::true_type{});
+    else
+      tile(it, Buf0{}, std::true_type{});
+  }
 
   // lane owns query l32 and dims 32 dt + 8 (r/4) + 4 g + r%4
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

@@ -68,6 +68,24 @@ def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------------
 # Conditioning: timestep embedding and modulation
 # ----------------------------------------------------------------------------------
+def bf16_storage(x) -> np.ndarray:
+    """Value of x after it is computed in fp32 and stored as bf16 (round to nearest, ties
+    to even, at each step: fp64 -> fp32 -> bf16), returned as float64.
+
+    Used only through the `storage` argument of the blocks and the step, which applies it
+    where a bf16 pipeline stores an intermediate (GEMM operands, attention probabilities
+    and outputs); the definition itself (storage=None) keeps every value in fp64.
+    """
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32)).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)) << np.uint32(16)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _keep(x):
+    return x
+
+
 def timestep_embedding(t) -> np.ndarray:
     """256-channel sinusoid of 1000*t.  [DIFF] 时间步缩放; [KLEIN] 条件注入.
 
@@ -198,18 +216,25 @@ def attention_weights(q: np.ndarray, k: np.ndarray) -> np.ndarray:
     return softmax_rows(np.matmul(q, k.T) / np.sqrt(q.shape[-1]))
 
 
-def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, storage=None) -> np.ndarray:
     """Multi-head attention over the full joint sequence, no mask.
 
     q, k, v: [B, L, h, d] -> [B, L, h*d] (heads concatenated in head order).
     [TRACE] Joint multi-head attention (separate QKV, shared attention); [SDPA].
+    With `storage`, the unnormalised probabilities exp(s - max) are stored through it and
+    normalised by the sum of the stored values.
     """
     B, L, h, d = q.shape
     out = np.empty((B, L, h, d), dtype=np.float64)
     for b in range(B):
         for head in range(h):
-            p = attention_weights(q[b, :, head, :], k[b, :, head, :])
-            out[b, :, head, :] = np.matmul(p, v[b, :, head, :])
+            if storage is None:
+                p = attention_weights(q[b, :, head, :], k[b, :, head, :])
+                out[b, :, head, :] = np.matmul(p, v[b, :, head, :])
+            else:
+                sc = np.matmul(q[b, :, head, :], k[b, :, head, :].T) / np.sqrt(d)
+                e = storage(np.exp(sc - sc.max(axis=-1, keepdims=True)))
+                out[b, :, head, :] = np.matmul(e, v[b, :, head, :]) / e.sum(axis=-1, keepdims=True)
     return out.reshape(B, L, h * d)
 
 
@@ -236,7 +261,8 @@ def double_block_mods(t, w: Mapping) -> dict:
             "txt": modulation(temb, f64(w["mod_txt"]), 6)}
 
 
-def double_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: dict | None = None):
+def double_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: dict | None = None,
+                 storage=None):
     """Double-stream block.  Returns (img_out, txt_out), float64.
 
     [TRACE] section 4 (Double-stream block: modulate image + text streams, joint
@@ -245,32 +271,36 @@ def double_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: dict | None = 
     img: [B, N_img, D]; txt: [B, N_txt, D]; w keys "img.qkv", "img.out", "img.mlp_in",
     "img.mlp_out", "img.q_norm", "img.k_norm" and the same for "txt."; mods: per stream
     the six [B, D] chunks (shift1, scale1, gate1, shift2, scale2, gate2), computed from
-    t with "temb.*", "mod_img", "mod_txt" when not given.
+    t with "temb.*", "mod_img", "mod_txt" when not given.  `storage` (e.g. bf16_storage)
+    is applied where a bf16 pipeline stores a value: the normalised-and-modulated inputs
+    of the linears, q / k / v, q and k after RMSNorm + RoPE, the attention probabilities
+    and output, and the SwiGLU output; the residual stream is not rounded.
     """
+    st = storage or _keep
     streams = {"txt": f64(txt), "img": f64(img)}
     if mods is None:
         mods = double_block_mods(t, w)
     qs, ks, vs = {}, {}, {}
     for s in ("txt", "img"):
         shift1, scale1 = mods[s][0], mods[s][1]
-        a = layernorm_modulate(streams[s], shift1, scale1)
-        q, k, v = np.split(linear(a, f64(w[f"{s}.qkv"])), 3, axis=-1)
+        a = st(layernorm_modulate(streams[s], shift1, scale1))
+        q, k, v = (st(y) for y in np.split(linear(a, f64(w[f"{s}.qkv"])), 3, axis=-1))
         qs[s] = rms_norm(_heads(q), f64(w[f"{s}.q_norm"]))
         ks[s] = rms_norm(_heads(k), f64(w[f"{s}.k_norm"]))
         vs[s] = _heads(v)
     pos = rope_positions(txt_ids, img_ids)
-    q = apply_rope(np.concatenate([qs["txt"], qs["img"]], axis=1), pos)
-    k = apply_rope(np.concatenate([ks["txt"], ks["img"]], axis=1), pos)
+    q = st(apply_rope(np.concatenate([qs["txt"], qs["img"]], axis=1), pos))
+    k = st(apply_rope(np.concatenate([ks["txt"], ks["img"]], axis=1), pos))
     v = np.concatenate([vs["txt"], vs["img"]], axis=1)
-    o = attention(q, k, v)
+    o = st(attention(q, k, v, storage))
     n_txt = streams["txt"].shape[1]
     o_s = {"txt": o[:, :n_txt], "img": o[:, n_txt:]}
     out = {}
     for s in ("txt", "img"):
         _, _, gate1, shift2, scale2, gate2 = mods[s]
         x = streams[s] + gate1[:, None, :] * linear(o_s[s], f64(w[f"{s}.out"]))
-        u = linear(layernorm_modulate(x, shift2, scale2), f64(w[f"{s}.mlp_in"]))
-        x = x + gate2[:, None, :] * linear(swiglu(u), f64(w[f"{s}.mlp_out"]))
+        u = linear(st(layernorm_modulate(x, shift2, scale2)), f64(w[f"{s}.mlp_in"]))
+        x = x + gate2[:, None, :] * linear(st(swiglu(u)), f64(w[f"{s}.mlp_out"]))
         out[s] = x
     return out["img"], out["txt"]
 
@@ -279,7 +309,8 @@ def single_block_mods(t, w: Mapping) -> list:
     return modulation(conditioning(t, w), f64(w["mod"]), 3)
 
 
-def single_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: Sequence | None = None):
+def single_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: Sequence | None = None,
+                 storage=None):
     """Single-stream (parallel) block.  Returns (img_out, txt_out), float64.
 
     [TRACE] section 4 (merge image + text sequence, attention + gated MLP);
@@ -287,8 +318,10 @@ def single_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: Sequence | Non
     fused to_qkv_mlp_proj (D -> 3D + 2H), attention and SwiGLU in parallel, fused
     to_out ((D + H) -> D), gated residual.
     w keys "linear1" [3D+2H, D], "linear2" [D, D+H], "q_norm", "k_norm" (and "temb.*",
-    "mod" when mods is not given); mods = (shift, scale, gate), each [B, D].
+    "mod" when mods is not given); mods = (shift, scale, gate), each [B, D].  `storage`
+    as for double_block (the linear1 MLP part feeds SwiGLU unrounded).
     """
+    st = storage or _keep
     txt = f64(txt)
     img = f64(img)
     n_txt = txt.shape[1]
@@ -297,13 +330,13 @@ def single_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: Sequence | Non
     if mods is None:
         mods = single_block_mods(t, w)
     shift, scale, gate = mods
-    y = linear(layernorm_modulate(x, shift, scale), f64(w["linear1"]))
-    q, k, v, u = y[..., :D], y[..., D:2 * D], y[..., 2 * D:3 * D], y[..., 3 * D:]
+    y = linear(st(layernorm_modulate(x, shift, scale)), f64(w["linear1"]))
+    q, k, v, u = st(y[..., :D]), st(y[..., D:2 * D]), st(y[..., 2 * D:3 * D]), y[..., 3 * D:]
     pos = rope_positions(txt_ids, img_ids)
-    q = apply_rope(rms_norm(_heads(q), f64(w["q_norm"])), pos)
-    k = apply_rope(rms_norm(_heads(k), f64(w["k_norm"])), pos)
-    o = attention(q, k, _heads(v))
-    x = x + gate[:, None, :] * linear(np.concatenate([o, swiglu(u)], axis=-1),
+    q = st(apply_rope(rms_norm(_heads(q), f64(w["q_norm"])), pos))
+    k = st(apply_rope(rms_norm(_heads(k), f64(w["k_norm"])), pos))
+    o = st(attention(q, k, _heads(v), storage))
+    x = x + gate[:, None, :] * linear(np.concatenate([o, st(swiglu(u))], axis=-1),
                                       f64(w["linear2"]))
     return x[:, n_txt:], x[:, :n_txt]
 
@@ -427,7 +460,7 @@ def step_mods(t, w: Mapping) -> dict:
 
 
 def denoiser_step(x, ctx, t, w: Mapping, img_ids, txt_ids, n_double: int, n_single: int,
-                  on_block=None):
+                  on_block=None, storage=None):
     """One denoiser forward: [B, N_img, in_ch] -> [B, N_img, in_ch], float64.
 
     [TRACE] section 3 (packed image tokens width 128 -> hidden; text condition joint dim;
@@ -435,20 +468,22 @@ def denoiser_step(x, ctx, t, w: Mapping, img_ids, txt_ids, n_double: int, n_sing
     image tokens -> [1, 4096, 128]); [DIFF] 前向传播输入输出约定.
     Block weights are read as "double.{i}.<key>" and "single.{i}.<key>" so `w` may be a
     lazy mapping that materialises one block at a time.  `on_block(kind, i)` is called
-    after each block (progress reporting).
+    after each block (progress reporting).  `storage` as for the blocks, plus the final
+    LayerNorm+modulate output; the residual stream and the output are not rounded.
     """
+    st = storage or _keep
     mods = step_mods(t, w)
     img = linear(f64(x), f64(w["img_in"]))
     txt = linear(f64(ctx), f64(w["txt_in"]))
     for i in range(n_double):
         img, txt = double_block(img, txt, None, _Prefixed(w, f"double.{i}."),
-                                img_ids, txt_ids, mods=mods["double"])
+                                img_ids, txt_ids, mods=mods["double"], storage=storage)
         if on_block:
             on_block("double", i)
     for i in range(n_single):
         img, txt = single_block(img, txt, None, _Prefixed(w, f"single.{i}."),
-                                img_ids, txt_ids, mods=mods["single"])
+                                img_ids, txt_ids, mods=mods["single"], storage=storage)
         if on_block:
             on_block("single", i)
     shift_f, scale_f = mods["final"]
-    return linear(layernorm_modulate(img, shift_f, scale_f), f64(w["proj_out"]))
+    return linear(st(layernorm_modulate(img, shift_f, scale_f)), f64(w["proj_out"]))

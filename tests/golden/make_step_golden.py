@@ -1,12 +1,15 @@
 """Write the sampled fp64 oracle output of one full Klein-9B 1024² denoiser step.
 
     python tests/golden/make_step_golden.py [--workload klein9b_step_1024] [--rows 16]
+                                            [--storage bf16]
 
 Calls only oracle/ (the fp64 definition) and the seeded input generator: the weights are
 generated block by block (flux_synth.LazyWeights), the step runs in fp64 on the host (a
 few minutes), and the output rows of a seeded sample of image tokens (always the first and
 the last) are written to tests/golden/<workload>.txt, all 128 channels each, for the GPU
-test that runs the same step through flux_denoiser_step.
+test that runs the same step through flux_denoiser_step.  With --storage bf16 the step is
+the oracle's bf16 storage mode (the definition with values rounded to bf16 where a bf16
+pipeline stores them) and the file is tests/golden/<workload>_bf16_storage.txt.
 """
 from __future__ import annotations
 
@@ -35,6 +38,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="klein9b_step_1024")
     ap.add_argument("--rows", type=int, default=16)
+    ap.add_argument("--storage", choices=("fp64", "bf16"), default="fp64")
     args = ap.parse_args(argv)
     wl = fs.workload(args.workload)
     assert wl.kind == "step" and wl.batch == 1
@@ -45,12 +49,15 @@ def main(argv=None) -> int:
     def progress(kind, i):
         print(f"[golden] {kind} block {i} done at {time.time() - t0:.0f} s", flush=True)
 
+    storage = O.bf16_storage if args.storage == "bf16" else None
     out = O.denoiser_step(inp["x"], inp["ctx"], inp["t"], w, inp["img_ids"], inp["txt_ids"],
-                          wl.n_double, wl.n_single, on_block=progress)
+                          wl.n_double, wl.n_single, on_block=progress, storage=storage)
     rows = sample_rows(wl.n_img, args.rows, wl.seed)
-    path = os.path.join(HERE, f"{wl.name}.txt")
+    suffix = "_bf16_storage" if storage else ""
+    what = "fp64 oracle, bf16 storage mode," if storage else "fp64 oracle"
+    path = os.path.join(HERE, f"{wl.name}{suffix}.txt")
     with open(path, "w") as f:
-        f.write(f"# fp64 oracle output of one {wl.name} denoiser step (flux_synth seed {wl.seed},"
+        f.write(f"# {what} output of one {wl.name} denoiser step (flux_synth seed {wl.seed},"
                 f" t = {float(inp['t'][0]):.9g})\n")
         f.write("# written by tests/golden/make_step_golden.py (oracle/ + flux_synth only)\n")
         f.write(f"# output rms over all rows: {np.sqrt(np.mean(out[0] ** 2)):.17g}\n")

@@ -1,0 +1,67 @@
+"""Pins of the oracle's bf16 storage mode (the definition with values rounded where a
+bf16 pipeline stores them): the rounding itself against an independent conversion, worked
+ties, identities that survive it, and the size of its effect."""
+import numpy as np
+import pytest
+
+import flux_synth as fs
+from oracle import flux_oracle as O
+
+
+def test_bf16_storage_matches_torch_conversion():
+    import torch
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(200_000) * np.exp(rng.uniform(-12, 12, 200_000))).astype(np.float64)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_storage(x), ref)
+
+
+@pytest.mark.parametrize("x,want", [
+    (1.0, 1.0),
+    (1.0 + 2.0 ** -8, 1.0),                     # halfway, ties to the even neighbour 1.0
+    (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),     # halfway, ties to the even 1 + 2^-6
+    (1.0 + 2.0 ** -8 + 2.0 ** -30, 1.0),        # rounded to fp32 first: becomes a tie
+    (-1.5, -1.5),
+    (1.0 / 3.0, 0.333984375),
+    (65504.0, 65536.0),
+])
+def test_bf16_storage_worked_values(x, want):
+    assert O.bf16_storage(np.array([x]))[0] == want
+
+
+@pytest.mark.parametrize("kind", ["double", "single"])
+def test_zero_gate_identity_survives_storage_rounding(kind):
+    wl = fs.workload("tiny_single_f32", dtype="bf16", t_fixed=None)
+    inp = fs.block_inputs(wl, kind=kind)
+    D = wl.dim
+    w = dict(inp["weights"])
+    if kind == "double":
+        for s in ("img", "txt"):
+            m = w[f"mod_{s}"].copy()
+            m[2 * D:3 * D] = 0.0
+            m[5 * D:6 * D] = 0.0
+            w[f"mod_{s}"] = m
+        img, txt = O.double_block(inp["img"], inp["txt"], inp["t"], w, inp["img_ids"],
+                                  inp["txt_ids"], storage=O.bf16_storage)
+    else:
+        m = w["mod"].copy()
+        m[2 * D:3 * D] = 0.0
+        w["mod"] = m
+        img, txt = O.single_block(inp["img"], inp["txt"], inp["t"], w, inp["img_ids"],
+                                  inp["txt_ids"], storage=O.bf16_storage)
+    np.testing.assert_array_equal(img, inp["img"].astype(np.float64))
+    np.testing.assert_array_equal(txt, inp["txt"].astype(np.float64))
+
+
+@pytest.mark.parametrize("kind", ["double", "single"])
+def test_storage_rounding_effect_is_bf16_sized(kind):
+    wl = fs.workload("tiny_single_f32", dtype="bf16", t_fixed=None)
+    inp = fs.block_inputs(wl, kind=kind)
+    fn = O.double_block if kind == "double" else O.single_block
+    args = (inp["img"], inp["txt"], inp["t"], inp["weights"], inp["img_ids"], inp["txt_ids"])
+    exact, _ = fn(*args)
+    rounded, _ = fn(*args, storage=O.bf16_storage)
+    upd = exact - inp["img"].astype(np.float64)
+    rel = np.linalg.norm(rounded - exact) / np.linalg.norm(upd)
+    # a few bf16 roundings (relative 2^-9 each) in the update's inputs
+    assert 1e-4 < rel < 2e-2, rel

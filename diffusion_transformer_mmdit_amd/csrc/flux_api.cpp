@@ -624,12 +624,13 @@ extern "C" int flux_denoiser_step(const flux_cfg* c, const flux_model_weights* w
   HIP_TRY(gemv(T, w->mod_final, 2 * D, D, sb.cb.stemb, B, false, false, sb.mod_final, s));
   HIP_TRY(rope_table(txt_ids, img_ids, Nt, Ni, c->axes_dim, c->rope_theta, sb.rb.pos, sb.rb.cs, s));
 
-  // stems (fp32 residual stream)
+  // stems (fp32 residual stream); the block scratch is idle until the first block, so its
+  // split-K area serves their tails
   CHECK(lin(c, EPI_STORE, B * Ni, D, c->in_channels, x, c->in_channels, w->img_in, c->in_channels,
-            sb.res_img, D, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s));
+            sb.res_img, D, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s, sb.d.split));
   if (Nt > 0)
     CHECK(lin(c, EPI_STORE, B * Nt, D, c->context_dim, ctx, c->context_dim, w->txt_in,
-              c->context_dim, sb.res_txt, D, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s));
+              c->context_dim, sb.res_txt, D, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s, sb.d.split));
 
   // double-stream blocks
   const void* in[2] = {sb.res_txt, sb.res_img};
@@ -656,7 +657,7 @@ extern "C" int flux_denoiser_step(const flux_cfg* c, const flux_model_weights* w
                                2 * D, c->eps, s));
   }
   CHECK(lin(c, EPI_STORE, B * Ni, c->in_channels, D, sb.ln_head, D, w->proj_out, D, out,
-            c->in_channels, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s));
+            c->in_channels, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s, sb.sg.split));
   return FLUX_OK;
 }
 

@@ -23,13 +23,52 @@ namespace flux {
 // ------------------------------------------------------------------------------------
 // Epilogue functors: called once per output element (m < M, n < N checked by caller)
 // ------------------------------------------------------------------------------------
+// Row-vector access (kRow4): vec4(m, n, v, N) handles columns n .. n+3 (n % 4 == 0, columns
+// at or past N skipped) of row m.  `vec` says the rows start on 4-element boundaries so
+// the columns move as one 8- or 16-byte access; it is set on the host by set_vec().
+template <class T>
+inline bool row4_aligned(const T* p, int64_t ld) {
+  return (reinterpret_cast<uintptr_t>(p) % (4 * sizeof(T))) == 0 && ld % 4 == 0;
+}
+template <class T>
+FLUX_DEV void store4(T* p, float4 v);
+template <>
+FLUX_DEV void store4<float>(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+template <>
+FLUX_DEV void store4<bf16>(bf16* p, float4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack2(v.x, v.y), pack2(v.z, v.w));
+}
+template <class T>
+FLUX_DEV float4 load4(const T* p);
+template <>
+FLUX_DEV float4 load4<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
+template <>
+FLUX_DEV float4 load4<bf16>(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
 template <class TY>
 struct EpiStore {
   TY* y;
   int64_t ldy;
+  bool vec = false;
   static constexpr bool kPaired = false;
   static constexpr bool kQuad = false;
+  static constexpr bool kRow4 = true;
+  void set_vec() { vec = row4_aligned(y, ldy); }
   FLUX_DEV void operator()(int m, int n, float v) const { y[m * ldy + n] = from_f32<TY>(v); }
+  FLUX_DEV void vec4(int m, int n, float4 v, int N) const {
+    if (vec && n + 3 < N) {
+      store4<TY>(y + m * ldy + n, v);
+      return;
+    }
+    const float a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (n + c < N) (*this)(m, n + c, a[c]);
+  }
 };
 
 template <class TY>
@@ -39,6 +78,7 @@ struct EpiSwiGLU {
   int n_half;  // H
   static constexpr bool kPaired = true;
   static constexpr bool kQuad = false;
+  static constexpr bool kRow4 = false;
   // logical column n of the interleaved [gate | up] tile -> physical W row
   FLUX_DEV static int phys_row(int n, int H) {
     const int j = ((n >> 6) << 5) + (n & 31);
@@ -58,11 +98,28 @@ struct EpiGatedResid {
   const float* gate;
   int64_t gate_bs;
   int rpb;
+  bool vec = false;
   static constexpr bool kPaired = false;
   static constexpr bool kQuad = false;
+  static constexpr bool kRow4 = true;
+  void set_vec() { vec = row4_aligned(y, ldy) && row4_aligned(r, ldr) && row4_aligned(gate, gate_bs); }
   FLUX_DEV void operator()(int m, int n, float v) const {
     const int b = m / rpb;
-    y[m * ldy + n] = from_f32<TY>(to_f32(r[m * ldr + n]) + gate[b * gate_bs + n] * v);
+    y[m * ldy + n] = from_f32<TY>(fmaf(gate[b * gate_bs + n], v, to_f32(r[m * ldr + n])));
+  }
+  FLUX_DEV void vec4(int m, int n, float4 v, int N) const {
+    const int b = m / rpb;
+    if (vec && n + 3 < N) {
+      const float4 x = load4<TR>(r + m * ldr + n);
+      const float4 g = *reinterpret_cast<const float4*>(gate + b * gate_bs + n);
+      store4<TY>(y + m * ldy + n, make_float4(fmaf(g.x, v.x, x.x), fmaf(g.y, v.y, x.y),
+                                              fmaf(g.z, v.z, x.z), fmaf(g.w, v.w, x.w)));
+      return;
+    }
+    const float a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (n + c < N) (*this)(m, n + c, a[c]);
   }
 };
 
@@ -76,6 +133,7 @@ struct EpiQKV {
   int two_d, dim, rpb, vt_off;
   static constexpr bool kPaired = false;
   static constexpr bool kQuad = true;
+  static constexpr bool kRow4 = false;
   FLUX_DEV void operator()(int m, int n, float v) const {
     if (n < two_d) {
       y[m * ldy + n] = from_f32<TY>(v);
@@ -537,6 +595,45 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
       }
     return;
   }
+  if constexpr (Epi::kRow4) {
+    // Row-vector epilogue through the (now idle) LDS stages.  Pass p = (i, h) stages the 16
+    // rows i*32 + 16h + [0, 16) of every wave's tile: PR = 16*NWM rows of BN fp32 (two
+    // buffers, alternating), then each wave moves whole staged rows with 16-byte LDS reads
+    // and row-contiguous global accesses (the residual / gate loads of a pass are all in
+    // flight together).  Staged row sr holds tile row (sr/16)*WTM + i*32 + 16h + sr%16;
+    // its 32-column halves of each 64 are swapped when bit 2 of sr is set, so the two
+    // half-waves of a ds_write (rows 4 apart) hit different banks.
+    constexpr int PR = 16 * NWM, NT = 64 * NWV, CPO = BN / 4;
+    constexpr int PER_T = PR * CPO / NT;
+    static_assert(PR * CPO % NT == 0 && BN % 64 == 0, "staged epilogue shape");
+    static_assert(2 * PR * BN * 4 <= ST * STAGE_B, "staging buffers fit in the LDS stages");
+    float* stg = reinterpret_cast<float*>(smem);
+    __syncthreads();  // every wave is done reading the last slice
+#pragma unroll
+    for (int p = 0; p < 2 * TM; ++p) {
+      const int i = p >> 1, h = p & 1;
+      float* buf = stg + (p & 1) * PR * BN;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int sr = wm * 16 + 8 * (rr >> 2) + 4 * lk + (rr & 3);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          buf[sr * BN + ((wn * WTN + j * 32 + lrow) ^ (lk << 5))] = acc[i][j][8 * h + rr];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < PER_T; ++u) {
+        const int e = tid + u * NT;
+        const int sr = e / CPO, c = e % CPO;
+        const int m = m0 + (sr >> 4) * WTM + i * 32 + 16 * h + (sr & 15);
+        const int n = n0 + 4 * c;
+        const float4 v =
+            *reinterpret_cast<const float4*>(buf + sr * BN + ((4 * c) ^ (((sr >> 2) & 1) << 5)));
+        if (m < M && n < N) epi.vec4(m, n, v, N);
+      }
+    }
+    return;
+  }
   if constexpr (Epi::kQuad) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -628,10 +725,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
       const float4 a = *reinterpret_cast<const float4*>(pp + sp * stride);
       v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
     }
-    const float vv[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (Epi::kRow4) {
+      if (n0 + nl < N) epi.vec4(m, n0 + nl, v, N);
+    } else {
+      const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (n0 + nl + c < N) epi(m, n0 + nl + c, vv[c]);
+      for (int c = 0; c < 4; ++c)
+        if (n0 + nl + c < N) epi(m, n0 + nl + c, vv[c]);
+    }
   }
 }
 
@@ -813,11 +914,10 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
 
 template <class T, class TY, class TR>
 static hipError_t gated2(const LinearArgs& a, hipStream_t s) {
-  return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0,
-                   EpiGatedResid<TY, TR>{static_cast<TY*>(a.y), a.ldy,
-                                         static_cast<const TR*>(a.resid), a.ldr, a.gate,
-                                         a.gate_bs, a.rows_per_batch},
-                   s, a.split_ws);
+  EpiGatedResid<TY, TR> epi{static_cast<TY*>(a.y), a.ldy, static_cast<const TR*>(a.resid),
+                            a.ldr, a.gate, a.gate_bs, a.rows_per_batch};
+  epi.set_vec();
+  return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws);
 }
 
 template <class T>
@@ -831,11 +931,15 @@ template <class T>
 static hipError_t linear_t(const LinearArgs& a, hipStream_t s) {
   switch (a.epilogue) {
     case EPI_STORE:
-      if (a.y_dtype == DT_F32)
-        return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0,
-                         EpiStore<float>{static_cast<float*>(a.y), a.ldy}, s, a.split_ws);
-      return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0,
-                       EpiStore<bf16>{static_cast<bf16*>(a.y), a.ldy}, s, a.split_ws);
+      if (a.y_dtype == DT_F32) {
+        EpiStore<float> epi{static_cast<float*>(a.y), a.ldy};
+        epi.set_vec();
+        return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws);
+      } else {
+        EpiStore<bf16> epi{static_cast<bf16*>(a.y), a.ldy};
+        epi.set_vec();
+        return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws);
+      }
     case EPI_SWIGLU:
       return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, a.n / 2,
                        EpiSwiGLU<T>{static_cast<T*>(a.y), a.ldy, a.n / 2}, s, a.split_ws);

@@ -16,6 +16,7 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <climits>
 #include <type_traits>
 
 namespace flux {
@@ -58,6 +59,7 @@ struct EpiStore {
   static constexpr bool kQuad = false;
   static constexpr bool kRow4 = true;
   void set_vec() { vec = row4_aligned(y, ldy); }
+  FLUX_DEV int col_major_from() const { return INT_MAX; }
   FLUX_DEV void operator()(int m, int n, float v) const { y[m * ldy + n] = from_f32<TY>(v); }
   FLUX_DEV void vec4(int m, int n, float4 v, int N) const {
     if (vec && n + 3 < N) {
@@ -103,6 +105,7 @@ struct EpiGatedResid {
   static constexpr bool kQuad = false;
   static constexpr bool kRow4 = true;
   void set_vec() { vec = row4_aligned(y, ldy) && row4_aligned(r, ldr) && row4_aligned(gate, gate_bs); }
+  FLUX_DEV int col_major_from() const { return INT_MAX; }
   FLUX_DEV void operator()(int m, int n, float v) const {
     const int b = m / rpb;
     y[m * ldy + n] = from_f32<TY>(fmaf(gate[b * gate_bs + n], v, to_f32(r[m * ldr + n])));
@@ -131,9 +134,23 @@ struct EpiQKV {
   TY* vt;
   int64_t ldvt;
   int two_d, dim, rpb, vt_off;
+  bool vec = false;
   static constexpr bool kPaired = false;
   static constexpr bool kQuad = true;
-  static constexpr bool kRow4 = false;
+  static constexpr bool kRow4 = true;
+  void set_vec() { vec = row4_aligned(y, ldy); }
+  // first column of the transposed (V) part: tiles at or past it take the column path
+  FLUX_DEV int col_major_from() const { return two_d; }
+  FLUX_DEV void vec4(int m, int n, float4 v, int N) const {
+    if (vec && n + 3 < two_d) {
+      store4<TY>(y + m * ldy + n, v);
+      return;
+    }
+    const float a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (n + c < N) (*this)(m, n + c, a[c]);
+  }
   FLUX_DEV void operator()(int m, int n, float v) const {
     if (n < two_d) {
       y[m * ldy + n] = from_f32<TY>(v);
@@ -621,15 +638,30 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
           buf[sr * BN + ((wn * WTN + j * 32 + lrow) ^ (lk << 5))] = acc[i][j][8 * h + rr];
       }
       __syncthreads();
+      if (n0 < epi.col_major_from()) {
 #pragma unroll
-      for (int u = 0; u < PER_T; ++u) {
-        const int e = tid + u * NT;
-        const int sr = e / CPO, c = e % CPO;
-        const int m = m0 + (sr >> 4) * WTM + i * 32 + 16 * h + (sr & 15);
-        const int n = n0 + 4 * c;
-        const float4 v =
-            *reinterpret_cast<const float4*>(buf + sr * BN + ((4 * c) ^ (((sr >> 2) & 1) << 5)));
-        if (m < M && n < N) epi.vec4(m, n, v, N);
+        for (int u = 0; u < PER_T; ++u) {
+          const int e = tid + u * NT;
+          const int sr = e / CPO, c = e % CPO;
+          const int m = m0 + (sr >> 4) * WTM + i * 32 + 16 * h + (sr & 15);
+          const int n = n0 + 4 * c;
+          const float4 v = *reinterpret_cast<const float4*>(buf + sr * BN +
+                                                            ((4 * c) ^ (((sr >> 2) & 1) << 5)));
+          if (m < M && n < N) epi.vec4(m, n, v, N);
+        }
+      } else if constexpr (Epi::kQuad) {
+        // column-major output: item = 4 consecutive rows (staged rows 4q .. 4q+3 of a wave
+        // block, same bit 2) of one column; 4 lanes in a row cover 16 contiguous rows
+#pragma unroll 2
+        for (int u = 0; u < PER_T; ++u) {
+          const int e = tid + u * NT;
+          const int q = e & 3, col = (e >> 2) % BN, wb = (e >> 2) / BN;
+          const int sr = wb * 16 + 4 * q;
+          const float* src = buf + sr * BN + (col ^ ((q & 1) << 5));
+          const int m = m0 + wb * WTM + i * 32 + 16 * h + 4 * q;
+          const int n = n0 + col;
+          if (m < M && n < N) epi.quad(m, n, src[0], src[BN], src[2 * BN], src[3 * BN], M);
+        }
       }
     }
     return;
@@ -945,11 +977,12 @@ static hipError_t linear_t(const LinearArgs& a, hipStream_t s) {
                        EpiSwiGLU<T>{static_cast<T*>(a.y), a.ldy, a.n / 2}, s, a.split_ws);
     case EPI_GATED_RESIDUAL:
       return gated<T>(a, s);
-    case EPI_QKV:
-      return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0,
-                       EpiQKV<T>{static_cast<T*>(a.y), a.ldy, static_cast<T*>(a.vt), a.ldvt,
-                                 2 * a.dim, a.dim, a.rows_per_batch, a.vt_off},
-                       s, a.split_ws);
+    case EPI_QKV: {
+      EpiQKV<T> epi{static_cast<T*>(a.y), a.ldy, static_cast<T*>(a.vt), a.ldvt,
+                    2 * a.dim, a.dim, a.rows_per_batch, a.vt_off};
+      epi.set_vec();
+      return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws);
+    }
   }
   return hipErrorInvalidValue;
 }

@@ -6,10 +6,13 @@
 // 前向传播输入输出约定) and the FLUX.2 Klein 9B shape trace (sections 3 and 4).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "flux.h"
 #include "kernels.h"
@@ -40,6 +43,102 @@ static int fail(int code, const char* fmt, ...) {
 
 extern "C" const char* flux_last_error(void) { return g_err.c_str(); }
 extern "C" const char* flux_version(void) { return "libflux 0.1 (gfx950)"; }
+
+// ------------------------------------------------------------------------------------
+// measurement hook: event pairs around the launches of one site, created up front
+// ------------------------------------------------------------------------------------
+namespace {
+struct Timing {
+  std::mutex mu;
+  std::atomic<int> site{0};
+  std::vector<hipEvent_t> ev;  // start, end, start, end, ...
+  int used = 0;                // pairs handed out
+  int dropped = 0;             // launches past the armed capacity
+};
+Timing g_timing;
+
+void timing_release() {
+  for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+  g_timing.ev.clear();
+  g_timing.used = g_timing.dropped = 0;
+}
+
+// Records the start event on construction and the end event on destruction when `site` is
+// the armed one; costs one relaxed atomic load otherwise.
+class TimedSite {
+ public:
+  TimedSite(int site, hipStream_t s) : s_(s) {
+    if (g_timing.site.load(std::memory_order_relaxed) != site) return;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.site.load(std::memory_order_relaxed) != site) return;
+    if ((size_t)(2 * g_timing.used + 2) > g_timing.ev.size()) {
+      ++g_timing.dropped;
+      return;
+    }
+    const int i = g_timing.used++;
+    if (hipEventRecord(g_timing.ev[2 * i], s) == hipSuccess) end_ = g_timing.ev[2 * i + 1];
+  }
+  ~TimedSite() {
+    if (end_) (void)hipEventRecord(end_, s_);
+  }
+  TimedSite(const TimedSite&) = delete;
+  TimedSite& operator=(const TimedSite&) = delete;
+
+ private:
+  hipStream_t s_;
+  hipEvent_t end_ = nullptr;
+};
+}  // namespace
+
+extern "C" int flux_timing_begin(int site, int max_launches) {
+  if (site < FLUX_SITE_SINGLE_QKV || site > FLUX_SITE_SINGLE_LINEAR2)
+    return fail(FLUX_EINVAL, "unknown timing site %d", site);
+  if (max_launches <= 0 || max_launches > (1 << 16))
+    return fail(FLUX_EINVAL, "max_launches must be in [1, 65536] (got %d)", max_launches);
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.site.store(0);
+  timing_release();
+  g_timing.ev.reserve(2 * (size_t)max_launches);
+  for (int i = 0; i < 2 * max_launches; ++i) {
+    hipEvent_t e;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      timing_release();
+      return fail(FLUX_EHIP, "hipEventCreate failed: %s", hipGetErrorString(r));
+    }
+    g_timing.ev.push_back(e);
+  }
+  g_timing.site.store(site);
+  return FLUX_OK;
+}
+
+extern "C" int flux_timing_end(int* launches, double* mean_us) {
+  if (!launches || !mean_us) return fail(FLUX_EINVAL, "launches and mean_us are required");
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.site.store(0);
+  *launches = 0;
+  *mean_us = 0.0;
+  if (g_timing.dropped > 0) {
+    const int d = g_timing.dropped;
+    timing_release();
+    return fail(FLUX_EINVAL, "%d launches exceeded the armed capacity", d);
+  }
+  double sum = 0.0;
+  for (int i = 0; i < g_timing.used; ++i) {
+    hipError_t r = hipEventSynchronize(g_timing.ev[2 * i + 1]);
+    float ms = 0.f;
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]);
+    if (r != hipSuccess) {
+      timing_release();
+      return fail(FLUX_EHIP, "timing event %d: %s", i, hipGetErrorString(r));
+    }
+    sum += ms;
+  }
+  *launches = g_timing.used;
+  if (g_timing.used > 0) *mean_us = 1e3 * sum / g_timing.used;
+  timing_release();
+  return FLUX_OK;
+}
 
 // ------------------------------------------------------------------------------------
 // validation helpers
@@ -422,12 +521,18 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
   const int64_t mbs = 3 * (int64_t)D, ldc = D + H;
   HIP_TRY(layernorm_modulate(in_dt, T, x, D, d.ln, D, rows, D, L, mod, mod + D, mbs, c->eps, s));
   const int64_t ldvt = vt_pitch(L);
-  CHECK(lin_qkv(c, rows, d.ln, w->linear1, d.qk, d.vt, ldvt, 0, L, s, d.split));
+  {
+    TimedSite ts(FLUX_SITE_SINGLE_QKV, s);
+    CHECK(lin_qkv(c, rows, d.ln, w->linear1, d.qk, d.vt, ldvt, 0, L, s, d.split));
+  }
   if (ldvt > L) HIP_TRY(zero_cols(T, d.vt, ldvt, (int64_t)B * D, L, (int)ldvt, s));
   const char* w_mlp = static_cast<const char*>(w->linear1) + (size_t)3 * D * D * es;
-  CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln, D, w_mlp, D,
-            static_cast<char*>(d.cat) + (size_t)D * es, ldc, T, nullptr, 0, 0, nullptr, 0, 1, s,
-            d.split));
+  {
+    TimedSite ts(FLUX_SITE_SINGLE_MLP_IN, s);
+    CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln, D, w_mlp, D,
+              static_cast<char*>(d.cat) + (size_t)D * es, ldc, T, nullptr, 0, 0, nullptr, 0, 1,
+              s, d.split));
+  }
   auto view = [&](void* base, int col, int64_t ld) {
     SeqView v;
     v.base0 = v.base1 = static_cast<char*>(base) + (size_t)col * es;
@@ -440,7 +545,11 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
   SeqView ov = view(d.cat, 0, ldc);
   HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, w->q_norm, w->k_norm, w->q_norm, w->k_norm, cs,
                        c->eps, s));
-  HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, d.split, s));
+  {
+    TimedSite ts(FLUX_SITE_SINGLE_ATTENTION, s);
+    HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, d.split, s));
+  }
+  TimedSite ts(FLUX_SITE_SINGLE_LINEAR2, s);
   CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D + H, d.cat, ldc, w->linear2, D + H, out, D, out_dt,
             x, D, in_dt, mod + 2 * D, mbs, L, s, d.split));
   return FLUX_OK;

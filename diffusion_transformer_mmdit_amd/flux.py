@@ -83,6 +83,8 @@ P = ctypes.POINTER
 _PROTOS = {
     "flux_last_error": (ctypes.c_char_p, []),
     "flux_version": (ctypes.c_char_p, []),
+    "flux_timing_begin": (c_int, [c_int, c_int]),
+    "flux_timing_end": (c_int, [P(c_int), P(ctypes.c_double)]),
     "flux_double_block_workspace_size": (c_size, [P(flux_cfg), c_int, c_int, c_int]),
     "flux_double_block_fwd": (c_int, [P(flux_cfg), P(flux_double_weights), vp, c_int, c_int, c_int,
                                       vp, vp, vp, vp, vp, vp, vp, c_size, vp]),
@@ -156,6 +158,22 @@ def flux_last_error() -> str:
 
 def flux_version() -> str:
     return lib().flux_version().decode()
+
+
+FLUX_SITE_SINGLE_QKV, FLUX_SITE_SINGLE_MLP_IN = 1, 2
+FLUX_SITE_SINGLE_ATTENTION, FLUX_SITE_SINGLE_LINEAR2 = 3, 4
+
+
+def flux_timing_begin(site: int, max_launches: int) -> None:
+    _check(lib().flux_timing_begin(site, max_launches))
+
+
+def flux_timing_end() -> tuple[int, float]:
+    """(number of timed launches, their mean duration in microseconds)."""
+    n = c_int(0)
+    us = ctypes.c_double(0.0)
+    _check(lib().flux_timing_end(ctypes.byref(n), ctypes.byref(us)))
+    return n.value, us.value
 
 
 # ------------------------------------------------------------------------------------

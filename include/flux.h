@@ -131,6 +131,29 @@ const char* flux_last_error(void);
 const char* flux_version(void);
 
 /* ---------------------------------------------------------------------------------
+ * Measurement hook (per-launch kernel durations inside a running workload)
+ *
+ * flux_timing_begin(site, max_launches) creates 2*max_launches HIP events and arms `site`:
+ * from then on every launch of that site that this process enqueues (from any block or
+ * step call) is bracketed by an event pair recorded on the launch's own stream, so the
+ * timed calls create nothing.  flux_timing_end waits for the recorded events, returns the
+ * number of timed launches and their mean duration in microseconds, disarms the site and
+ * destroys the events.  One site is armed at a time per process; begin while armed
+ * discards the previous arming.  Errors: FLUX_EINVAL for an unknown site, a capacity
+ * outside [1, 65536], NULL outputs, or more launches than the capacity (then nothing is
+ * returned); FLUX_EHIP if event creation or timing fails.
+ * ------------------------------------------------------------------------------- */
+typedef enum {
+  FLUX_SITE_SINGLE_QKV = 1,       /* single block: linear1 q|k|v part (QKV epilogue) */
+  FLUX_SITE_SINGLE_MLP_IN = 2,    /* single block: linear1 gate|up part (SwiGLU epilogue) */
+  FLUX_SITE_SINGLE_ATTENTION = 3, /* single block: joint attention (with its key-split merge) */
+  FLUX_SITE_SINGLE_LINEAR2 = 4    /* single block: linear2 + gated residual (with its split-K
+                                     reduce) */
+} flux_timing_site;
+int flux_timing_begin(int site, int max_launches);
+int flux_timing_end(int* launches, double* mean_us);
+
+/* ---------------------------------------------------------------------------------
  * Blocks and step
  * ------------------------------------------------------------------------------- */
 

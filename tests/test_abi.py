@@ -161,6 +161,20 @@ def test_step_and_op_validation_errors():
                                      None) == F.FLUX_EDTYPE
 
 
+def test_timing_hook_validation():
+    L = F.lib()
+    n, us = ctypes.c_int(7), ctypes.c_double(1.0)
+    # unknown site, capacity out of range, NULL outputs: rejected before any HIP call
+    assert L.flux_timing_begin(0, 4) == F.FLUX_EINVAL
+    assert L.flux_timing_begin(5, 4) == F.FLUX_EINVAL
+    assert L.flux_timing_begin(F.FLUX_SITE_SINGLE_MLP_IN, 0) == F.FLUX_EINVAL
+    assert L.flux_timing_begin(F.FLUX_SITE_SINGLE_MLP_IN, (1 << 16) + 1) == F.FLUX_EINVAL
+    assert L.flux_timing_end(None, None) == F.FLUX_EINVAL
+    # not armed: nothing was timed
+    assert L.flux_timing_end(ctypes.byref(n), ctypes.byref(us)) == F.FLUX_OK
+    assert (n.value, us.value) == (0, 0.0)
+
+
 def test_binding_raises_when_library_missing(tmp_path, monkeypatch):
     monkeypatch.setattr(F, "_lib", None)
     with pytest.raises(F.FluxError):

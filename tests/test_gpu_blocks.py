@@ -152,3 +152,37 @@ def test_block_is_deterministic(kind):
     a = fn(wl, inp, wd)
     b = fn(wl, inp, wd)
     assert G.torch().equal(a[0], b[0]) and G.torch().equal(a[1], b[1])
+
+
+def test_timing_hook_times_only_the_armed_site():
+    """The measurement hook brackets exactly the armed site's launches (one per single block,
+    none from a double block) and refuses more launches than it was armed for."""
+    from diffusion_transformer_mmdit_amd import flux as F
+    wl = fs.workload("tiny_single_f32", dtype="bf16", n_txt=64, n_img=256, t_fixed=None,
+                     dim=512, heads=4, mlp_hidden=1536)
+    single = fs.block_inputs(wl, kind="single")
+    double = fs.block_inputs(wl, kind="double")
+    ws_single = G.upload_weights(single["weights"], "bf16")
+    ws_double = G.upload_weights(double["weights"], "bf16")
+    for site in (F.FLUX_SITE_SINGLE_QKV, F.FLUX_SITE_SINGLE_MLP_IN, F.FLUX_SITE_SINGLE_ATTENTION,
+                 F.FLUX_SITE_SINGLE_LINEAR2):
+        F.flux_timing_begin(site, 4)
+        G.run_single_block(wl, single, ws_single)
+        G.run_double_block(wl, double, ws_double)
+        G.run_single_block(wl, single, ws_single)
+        n, us = F.flux_timing_end()
+        assert n == 2 and 0.0 < us < 1e5, (site, n, us)
+    # capacity exceeded: an error, and the hook is disarmed afterwards
+    F.flux_timing_begin(F.FLUX_SITE_SINGLE_MLP_IN, 1)
+    G.run_single_block(wl, single, ws_single)
+    G.run_single_block(wl, single, ws_single)
+    with pytest.raises(F.FluxError):
+        F.flux_timing_end()
+    G.run_single_block(wl, single, ws_single)
+    assert F.flux_timing_end() == (0, 0.0)
+    # the timed launches still compute the same result
+    F.flux_timing_begin(F.FLUX_SITE_SINGLE_MLP_IN, 1)
+    a = G.run_single_block(wl, single, ws_single)
+    F.flux_timing_end()
+    b = G.run_single_block(wl, single, ws_single)
+    assert G.torch().equal(a[0], b[0]) and G.torch().equal(a[1], b[1])

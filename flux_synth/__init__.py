@@ -367,3 +367,21 @@ def step_inputs(wl: Workload, with_weights: bool = True) -> dict:
     if with_weights:
         out["weights"] = make_weights(step_weight_specs(wl), wl.seed, wl.dtype)
     return out
+
+
+def sample_inputs(wl: Workload, latent_h: int, latent_w: int, with_uncond: bool = False,
+                  with_weights: bool = True) -> dict:
+    """Inputs of a sampling run: fp32 noise latent [B, in_channels / 4, latent_h, latent_w],
+    text condition (and an unconditional one for guidance) in the workload dtype."""
+    B = wl.batch
+    out = {
+        "noise": normal(wl.seed, "noise", (B, wl.in_channels // 4, latent_h, latent_w),
+                        dtype="f32"),
+        "ctx": normal(wl.seed, "ctx", (B, wl.n_txt, wl.context_dim), dtype=wl.dtype),
+    }
+    if with_uncond:
+        out["ctx_uncond"] = normal(wl.seed, "ctx_uncond", (B, wl.n_txt, wl.context_dim),
+                                   dtype=wl.dtype)
+    if with_weights:
+        out["weights"] = make_weights(step_weight_specs(wl), wl.seed, wl.dtype)
+    return out

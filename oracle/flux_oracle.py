@@ -27,9 +27,13 @@ Readings of points the pages leave open (each also listed in the design doc):
   * single block: linear1 output order [q | k | v | gate | up]; linear2 input [attn | mlp]
   * joint sequence order: text tokens first, then image tokens
   * no biases anywhere
+  * sampling: latent 2x2 patches -> token channels in (c, ph, pw) order, patches row-major;
+    noise levels on the uniform grid 1 - i/n; Euler step x += (sigma_next - sigma) v with
+    v taken at sigma; guidance v_u + g (v_c - v_u)
 
-Parity pins for every function live in tests/test_oracle_pins.py (closed forms,
-invariants and brute force); none is "parity unpinned".
+Parity pins for every function live in tests/test_oracle_pins.py and, for the sampling
+loop, tests/test_oracle_sampler.py (closed forms, invariants, brute force and an
+independent library routine); none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -487,3 +491,97 @@ def denoiser_step(x, ctx, t, w: Mapping, img_ids, txt_ids, n_double: int, n_sing
             on_block("single", i)
     shift_f, scale_f = mods["final"]
     return linear(st(layernorm_modulate(img, shift_f, scale_f)), f64(w["proj_out"]))
+
+
+# ----------------------------------------------------------------------------------
+# Sampling loop around the denoiser step
+#
+# [KLEIN] 训练方法: latent rectified flow / flow matching; the distilled model samples in
+# 4 steps with guidance folded into its weights, the base model in 50 steps with the two
+# forwards of classifier-free guidance.  [DIFF] Flux2 管线 call chain: the VAE latent is
+# packed into tokens with their 4-D ids, a flow-matching Euler scheduler calls the
+# transformer once per step.  [KLEIN] Visual tokenizer / VAE: 32-channel latent, 2x2
+# patchify -> in_channels 128 (32 x 2 x 2).
+# ----------------------------------------------------------------------------------
+def pack_latents(z) -> np.ndarray:
+    """[B, C, H, W] latent -> [B, (H/2)(W/2), 4C] tokens: one token per 2x2 patch, patches
+    in row-major order of the (H/2) x (W/2) grid, channel index 4c + 2 ph + pw (reading:
+    the pages give only the 32 x 2 x 2 product; this is that factor order)."""
+    z = f64(z)
+    B, C, H, W = z.shape
+    if H % 2 or W % 2:
+        raise ValueError("latent height and width must be even")
+    p = z.reshape(B, C, H // 2, 2, W // 2, 2)          # b, c, r, ph, col, pw
+    return p.transpose(0, 2, 4, 1, 3, 5).reshape(B, (H // 2) * (W // 2), 4 * C)
+
+
+def unpack_latents(x, H: int, W: int) -> np.ndarray:
+    """Inverse of pack_latents: [B, (H/2)(W/2), 4C] -> [B, C, H, W]."""
+    x = f64(x)
+    B, N, C4 = x.shape
+    if H % 2 or W % 2 or N != (H // 2) * (W // 2) or C4 % 4:
+        raise ValueError("token count / channels do not match the latent shape")
+    p = x.reshape(B, H // 2, W // 2, C4 // 4, 2, 2)     # b, r, col, c, ph, pw
+    return p.transpose(0, 3, 1, 4, 2, 5).reshape(B, C4 // 4, H, W)
+
+
+def generation_ids(grid_h: int, grid_w: int, n_txt: int):
+    """(img_ids [grid_h * grid_w, 4], txt_ids [n_txt, 4]) int32: image token (r, c) of the
+    packed grid has id (0, r, c, 0) in row-major order, text token i has (0, 0, 0, i).
+    [DIFF] 位置 id (4-D (T, H, W, L) ids shared by the batch); the tiny shape example's
+    (0, row, col, 0) image ids on an 8 x 8 grid."""
+    img = np.zeros((grid_h * grid_w, 4), dtype=np.int32)
+    for r in range(grid_h):
+        img[r * grid_w:(r + 1) * grid_w, 1] = r
+        img[r * grid_w:(r + 1) * grid_w, 2] = np.arange(grid_w)
+    txt = np.zeros((n_txt, 4), dtype=np.int32)
+    txt[:, 3] = np.arange(n_txt)
+    return img, txt
+
+
+def uniform_sigmas(n_steps: int) -> np.ndarray:
+    """n_steps + 1 noise levels 1 - i / n_steps (fp32), from pure noise (t = 1) to data
+    (t = 0).  Reading: the pages name the flow-matching Euler scheduler but neither its
+    schedule nor a shift; this is the plain uniform grid."""
+    if n_steps <= 0:
+        raise ValueError("n_steps must be > 0")
+    return (1.0 - np.arange(n_steps + 1, dtype=np.float64) / n_steps).astype(np.float32)
+
+
+def cfg_combine(v_cond, v_uncond, scale: float) -> np.ndarray:
+    """v_u + scale (v_c - v_u).  Reading: the pages say the base model needs the two
+    forwards of classifier-free guidance (and that distillation removes them) but not how
+    they are combined; this is the standard combination."""
+    v_u = f64(v_uncond)
+    return v_u + float(scale) * (f64(v_cond) - v_u)
+
+
+def denoise(noise, ctx, w: Mapping, sigmas, n_double: int, n_single: int, ctx_uncond=None,
+            guidance: float = 1.0, model_input=None, storage=None, on_step=None) -> np.ndarray:
+    """Rectified-flow Euler sampling: [B, C, H, W] noise latent -> [B, C, H, W] latent.
+
+    x_0 = pack(noise); for i < n: v_i = velocity of the denoiser step at x_i, t = sigma_i;
+    x_{i+1} = x_i + (sigma_{i+1} - sigma_i) v_i; result unpack(x_n).  With ctx_uncond the
+    velocity is cfg_combine(step(ctx), step(ctx_uncond), guidance).  Position ids are
+    generation_ids of the packed grid and the text length.  `model_input(x)` maps the
+    state to the values the step reads (e.g. bf16 rounding for a bf16 model; default:
+    the state itself); `storage` is passed to the step.  `on_step(i)` reports progress.
+    """
+    sig = np.asarray(sigmas, dtype=np.float32).astype(np.float64)
+    noise = f64(noise)
+    B, C, H, W = noise.shape
+    img_ids, txt_ids = generation_ids(H // 2, W // 2, np.shape(ctx)[1])
+    feed = model_input or (lambda a: a)
+    x = pack_latents(noise)
+    for i in range(len(sig) - 1):
+        t = np.full((B,), sig[i], dtype=np.float32)
+        xi = feed(x)
+        v = denoiser_step(xi, ctx, t, w, img_ids, txt_ids, n_double, n_single, storage=storage)
+        if ctx_uncond is not None:
+            vu = denoiser_step(xi, ctx_uncond, t, w, img_ids, txt_ids, n_double, n_single,
+                               storage=storage)
+            v = cfg_combine(v, vu, guidance)
+        x = x + (sig[i + 1] - sig[i]) * v
+        if on_step:
+            on_step(i)
+    return unpack_latents(x, H, W)

@@ -154,3 +154,100 @@ def test_mutation_is_caught(name, monkeypatch):
         if failed:
             break
     assert failed, f"no pin caught mutation {name}"
+
+
+# ----------------------------------------------------------------------------------
+# Sampling loop: each planted mistake must fail a pin of tests/test_oracle_sampler.py
+# ----------------------------------------------------------------------------------
+import tests.test_oracle_sampler as spins  # noqa: E402
+
+
+def _sampler_pins():
+    out = []
+    for n, f in inspect.getmembers(spins, inspect.isfunction):
+        if not n.startswith("test_"):
+            continue
+        if "shape" in inspect.signature(f).parameters:
+            out.append(lambda f=f: f((2, 8, 6, 10)))
+        else:
+            out.append(f)
+    return out
+
+
+def _mut_pack_channels_last(z):
+    z = np.asarray(z, dtype=np.float64)
+    B, C, H, W = z.shape
+    p = z.reshape(B, C, H // 2, 2, W // 2, 2)
+    return p.transpose(0, 2, 4, 3, 5, 1).reshape(B, (H // 2) * (W // 2), 4 * C)
+
+
+def _mut_pack_column_major(z):
+    z = np.asarray(z, dtype=np.float64)
+    B, C, H, W = z.shape
+    p = z.reshape(B, C, H // 2, 2, W // 2, 2)
+    return p.transpose(0, 4, 2, 1, 3, 5).reshape(B, (H // 2) * (W // 2), 4 * C)
+
+
+def _mut_ids_transposed(gh, gw, n_txt):
+    img, txt = _sorig["generation_ids"](gh, gw, n_txt)
+    return img[:, [0, 2, 1, 3]], txt
+
+
+def _mut_sigmas_reversed(n):
+    return _sorig["uniform_sigmas"](n)[::-1].copy()
+
+
+def _mut_cfg_swapped(v_cond, v_uncond, scale):
+    return _sorig["cfg_combine"](v_uncond, v_cond, scale)
+
+
+def _denoise_variant(noise, ctx, w, sigmas, n_double, n_single, ctx_uncond=None, guidance=1.0,
+                     model_input=None, storage=None, on_step=None, t_next=False, flip=False,
+                     restart=False):
+    sig = np.asarray(sigmas, dtype=np.float32).astype(np.float64)
+    noise = np.asarray(noise, dtype=np.float64)
+    B, C, H, W = noise.shape
+    img_ids, txt_ids = O.generation_ids(H // 2, W // 2, np.shape(ctx)[1])
+    x0 = O.pack_latents(noise)
+    x = x0
+    for i in range(len(sig) - 1):
+        t = np.full((B,), sig[i + 1] if t_next else sig[i], dtype=np.float32)
+        src = x0 if restart else x
+        v = O.denoiser_step(src, ctx, t, w, img_ids, txt_ids, n_double, n_single)
+        if ctx_uncond is not None:
+            v = O.cfg_combine(v, O.denoiser_step(src, ctx_uncond, t, w, img_ids, txt_ids,
+                                                 n_double, n_single), guidance)
+        d = (sig[i] - sig[i + 1]) if flip else (sig[i + 1] - sig[i])
+        x = src + d * v
+    return O.unpack_latents(x, H, W)
+
+
+_sorig = {}
+
+SAMPLER_MUTATIONS = {
+    "pack_channel_factor_last": ("pack_latents", _mut_pack_channels_last),
+    "pack_patches_column_major": ("pack_latents", _mut_pack_column_major),
+    "ids_rows_and_columns_swapped": ("generation_ids", _mut_ids_transposed),
+    "sigmas_increasing": ("uniform_sigmas", _mut_sigmas_reversed),
+    "cfg_branches_swapped": ("cfg_combine", _mut_cfg_swapped),
+    "euler_velocity_at_next_level": ("denoise", lambda *a, **k: _denoise_variant(*a, t_next=True, **k)),
+    "euler_step_sign_flipped": ("denoise", lambda *a, **k: _denoise_variant(*a, flip=True, **k)),
+    "euler_restarts_from_noise": ("denoise", lambda *a, **k: _denoise_variant(*a, restart=True, **k)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SAMPLER_MUTATIONS))
+def test_sampler_mutation_is_caught(name, monkeypatch):
+    attr, fn = SAMPLER_MUTATIONS[name]
+    _sorig.clear()
+    _sorig.update({k: getattr(O, k) for k in ("generation_ids", "uniform_sigmas", "cfg_combine")})
+    monkeypatch.setattr(O, attr, fn)
+    failed = False
+    for f in _sampler_pins():
+        try:
+            with np.errstate(all="ignore"):
+                f()
+        except (AssertionError, ValueError, IndexError):
+            failed = True
+            break
+    assert failed, f"no pin caught mutation {name}"

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -16,6 +17,7 @@
 
 #include "flux.h"
 #include "kernels.h"
+#include "sampler.h"
 
 using namespace flux;
 
@@ -680,16 +682,11 @@ extern "C" size_t flux_denoiser_step_workspace_size(const flux_cfg* c, int B, in
   return cv.off;
 }
 
-extern "C" int flux_denoiser_step(const flux_cfg* c, const flux_model_weights* w, const float* t,
-                                  const float* guidance, int B, int Ni, int Nt, const void* x,
-                                  const void* ctx, const int32_t* img_ids,
-                                  const int32_t* txt_ids, float* out, void* ws, size_t ws_bytes,
-                                  void* stream) {
+// configuration and weights of a denoiser step (everything but the per-call buffers)
+static int check_model(const flux_cfg* c, const flux_model_weights* w, int B, int Ni, int Nt) {
   CHECK(check_cfg(c));
   CHECK(check_sizes(B, Ni, Nt));
-  if (guidance) return fail(FLUX_EINVAL, "guidance must be NULL (no guidance embedder)");
   if (!w) return fail(FLUX_EINVAL, "weights is NULL");
-  if (!t) return fail(FLUX_EINVAL, "t is NULL");
   if (c->in_channels <= 0 || c->in_channels % 8)
     return fail(FLUX_ESHAPE, "in_channels must be a positive multiple of 8");
   if (Nt > 0 && (c->context_dim <= 0 || c->context_dim % 8))
@@ -709,19 +706,15 @@ extern "C" int flux_denoiser_step(const flux_cfg* c, const flux_model_weights* w
     CHECK(check_stream(&w->double_blocks[i].txt, "double.txt"));
   }
   for (int i = 0; i < c->n_single; ++i) CHECK(check_single_w(&w->single_blocks[i], false));
-  CHECK(need(x, "x"));
-  CHECK(need(out, "out"));
-  if (!img_ids) return fail(FLUX_EINVAL, "img_ids is NULL");
-  if (Nt > 0) {
-    CHECK(need(w->txt_in, "txt_in"));
-    CHECK(need(ctx, "ctx"));
-    if (!txt_ids) return fail(FLUX_EINVAL, "txt_ids is NULL");
-  }
-  const size_t want = flux_denoiser_step_workspace_size(c, B, Ni, Nt);
-  CHECK(check_ws(ws, ws_bytes, want));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int D = c->dim, L = Ni + Nt, T = c->dtype;
+  if (Nt > 0) CHECK(need(w->txt_in, "txt_in"));
+  return FLUX_OK;
+}
 
+// launch sequence of one validated step; ws holds flux_denoiser_step_workspace_size bytes
+static int run_step(const flux_cfg* c, const flux_model_weights* w, const float* t, int B,
+                    int Ni, int Nt, const void* x, const void* ctx, const int32_t* img_ids,
+                    const int32_t* txt_ids, float* out, void* ws, hipStream_t s) {
+  const int D = c->dim, L = Ni + Nt, T = c->dtype;
   Carver cv(ws);
   StepBufs sb = carve_step(cv, c, B, Ni, Nt);
 
@@ -767,6 +760,167 @@ extern "C" int flux_denoiser_step(const flux_cfg* c, const flux_model_weights* w
   }
   CHECK(lin(c, EPI_STORE, B * Ni, c->in_channels, D, sb.ln_head, D, w->proj_out, D, out,
             c->in_channels, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s, sb.sg.split));
+  return FLUX_OK;
+}
+
+extern "C" int flux_denoiser_step(const flux_cfg* c, const flux_model_weights* w, const float* t,
+                                  const float* guidance, int B, int Ni, int Nt, const void* x,
+                                  const void* ctx, const int32_t* img_ids,
+                                  const int32_t* txt_ids, float* out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  if (guidance) return fail(FLUX_EINVAL, "guidance must be NULL (no guidance embedder)");
+  CHECK(check_model(c, w, B, Ni, Nt));
+  if (!t) return fail(FLUX_EINVAL, "t is NULL");
+  CHECK(need(x, "x"));
+  CHECK(need(out, "out"));
+  if (!img_ids) return fail(FLUX_EINVAL, "img_ids is NULL");
+  if (Nt > 0) {
+    CHECK(need(ctx, "ctx"));
+    if (!txt_ids) return fail(FLUX_EINVAL, "txt_ids is NULL");
+  }
+  CHECK(check_ws(ws, ws_bytes, flux_denoiser_step_workspace_size(c, B, Ni, Nt)));
+  return run_step(c, w, t, B, Ni, Nt, x, ctx, img_ids, txt_ids, out, ws,
+                  static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------------------------
+// sampling loop ([KLEIN] 训练方法: rectified flow, 4 distilled steps or 50 base steps with
+// classifier-free guidance; [DIFF] pipeline call chain: packed latents and ids, a
+// flow-matching Euler scheduler calling the transformer once per step)
+// ------------------------------------------------------------------------------------
+struct SampleBufs {
+  float* x;        // state [B, Ni, in_ch] fp32
+  void* xin;       // model input [Bm, Ni, in_ch] (model dtype)
+  float* v;        // velocity [Bm, Ni, in_ch] fp32
+  void* ctx2;      // [cond ; uncond] condition [2B, Nt, ctx_dim] (guided only)
+  float* t;        // [Bm]
+  int32_t* img_ids;
+  int32_t* txt_ids;
+  void* step_ws;
+};
+
+static SampleBufs carve_sample(Carver& cv, const flux_cfg* c, int B, int Ni, int Nt, bool guided) {
+  SampleBufs sb;
+  const int Bm = guided ? 2 * B : B, es = esize(c->dtype);
+  const size_t tok = (size_t)Ni * c->in_channels;
+  sb.x = cv.take<float>((size_t)B * tok);
+  sb.xin = cv.take<char>((size_t)Bm * tok * es);
+  sb.v = cv.take<float>((size_t)Bm * tok);
+  sb.ctx2 = guided ? cv.take<char>((size_t)Bm * Nt * c->context_dim * es) : nullptr;
+  sb.t = cv.take<float>((size_t)Bm);
+  sb.img_ids = cv.take<int32_t>((size_t)Ni * 4);
+  sb.txt_ids = cv.take<int32_t>((size_t)(Nt > 0 ? Nt : 1) * 4);
+  sb.step_ws = cv.take<char>(flux_denoiser_step_workspace_size(c, Bm, Ni, Nt));
+  return sb;
+}
+
+static int check_latent(int B, int C, int H, int W) {
+  if (B <= 0 || C <= 0 || H <= 0 || W <= 0) return fail(FLUX_EINVAL, "sizes must be > 0");
+  if (H % 2 || W % 2) return fail(FLUX_ESHAPE, "latent height and width must be even");
+  if ((int64_t)B * C * H * W >= (int64_t{1} << 31))
+    return fail(FLUX_ESHAPE, "latent has 2^31 or more elements");
+  return FLUX_OK;
+}
+
+extern "C" size_t flux_denoise_workspace_size(const flux_cfg* c, int B, int latent_h,
+                                              int latent_w, int Nt, int guided) {
+  if (check_cfg(c) != FLUX_OK || c->in_channels <= 0 || c->in_channels % 8) return 0;
+  if (check_latent(B, c->in_channels / 4, latent_h, latent_w) != FLUX_OK) return 0;
+  const int Ni = (latent_h / 2) * (latent_w / 2);
+  if (check_sizes(guided ? 2 * B : B, Ni, Nt) != FLUX_OK) return 0;
+  Carver cv(nullptr);
+  carve_sample(cv, c, B, Ni, Nt, guided != 0);
+  return cv.off;
+}
+
+extern "C" int flux_denoise(const flux_cfg* c, const flux_model_weights* w, int n_steps,
+                            const float* sigmas, float guidance_scale, int B, int latent_h,
+                            int latent_w, int Nt, const float* noise, const void* ctx,
+                            const void* ctx_uncond, float* latents_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(c));
+  if (c->in_channels <= 0 || c->in_channels % 8)
+    return fail(FLUX_ESHAPE, "in_channels must be a positive multiple of 8");
+  const int C = c->in_channels / 4;
+  CHECK(check_latent(B, C, latent_h, latent_w));
+  if (n_steps <= 0 || n_steps > 10000) return fail(FLUX_EINVAL, "n_steps must be in [1, 10000]");
+  std::vector<float> sig(n_steps + 1);
+  for (int i = 0; i <= n_steps; ++i)
+    sig[i] = sigmas ? sigmas[i] : (float)(1.0 - (double)i / n_steps);
+  for (int i = 0; i <= n_steps; ++i) {
+    if (!std::isfinite(sig[i])) return fail(FLUX_EINVAL, "sigmas[%d] is not finite", i);
+    if (i > 0 && !(sig[i] < sig[i - 1]))
+      return fail(FLUX_EINVAL, "sigmas must decrease strictly (sigmas[%d] >= sigmas[%d])", i,
+                  i - 1);
+  }
+  const bool guided = ctx_uncond != nullptr;
+  if (guided && !std::isfinite(guidance_scale))
+    return fail(FLUX_EINVAL, "guidance_scale is not finite");
+  const int Ni = (latent_h / 2) * (latent_w / 2), Bm = guided ? 2 * B : B;
+  CHECK(check_model(c, w, Bm, Ni, Nt));
+  CHECK(need(noise, "noise"));
+  CHECK(need(latents_out, "latents_out"));
+  if (Nt > 0) CHECK(need(ctx, "ctx"));
+  if (guided && Nt == 0) return fail(FLUX_EINVAL, "guidance needs a text condition (n_txt > 0)");
+  if (guided) CHECK(need(ctx_uncond, "ctx_uncond"));
+  CHECK(check_ws(ws, ws_bytes, flux_denoise_workspace_size(c, B, latent_h, latent_w, Nt, guided)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = c->dtype;
+  Carver cv(ws);
+  SampleBufs sb = carve_sample(cv, c, B, Ni, Nt, guided);
+  const int64_t n = (int64_t)B * Ni * c->in_channels;
+
+  HIP_TRY(generation_ids(sb.img_ids, latent_h / 2, latent_w / 2, sb.txt_ids, Nt, s));
+  const void* cond = ctx;
+  if (guided) {
+    const size_t bytes = (size_t)B * Nt * c->context_dim * esize(T);
+    HIP_TRY(hipMemcpyAsync(sb.ctx2, ctx, bytes, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(hipMemcpyAsync(static_cast<char*>(sb.ctx2) + bytes, ctx_uncond, bytes,
+                           hipMemcpyDeviceToDevice, s));
+    cond = sb.ctx2;
+  }
+  HIP_TRY(pack_latents(noise, sb.x, B, C, latent_h, latent_w, s));
+  for (int i = 0; i < n_steps; ++i) {
+    // x_i = x_{i-1} + (sigma_i - sigma_{i-1}) v_{i-1}, then the model input in its dtype
+    HIP_TRY(sampler_update(T, sb.x, i ? sb.v : nullptr, n, i ? sig[i] - sig[i - 1] : 0.f,
+                           guidance_scale, guided, sb.xin, s));
+    HIP_TRY(fill_f32(sb.t, Bm, sig[i], s));
+    CHECK(run_step(c, w, sb.t, Bm, Ni, Nt, sb.xin, cond, sb.img_ids, sb.txt_ids, sb.v,
+                   sb.step_ws, s));
+  }
+  HIP_TRY(sampler_update(T, sb.x, sb.v, n, sig[n_steps] - sig[n_steps - 1], guidance_scale,
+                         guided, nullptr, s));
+  HIP_TRY(unpack_latents(sb.x, latents_out, B, C, latent_h, latent_w, s));
+  return FLUX_OK;
+}
+
+extern "C" int flux_pack_latents(int B, int C, int H, int W, const float* z, float* tokens,
+                                 void* stream) {
+  CHECK(check_latent(B, C, H, W));
+  CHECK(need(z, "z"));
+  CHECK(need(tokens, "tokens"));
+  HIP_TRY(pack_latents(z, tokens, B, C, H, W, static_cast<hipStream_t>(stream)));
+  return FLUX_OK;
+}
+
+extern "C" int flux_unpack_latents(int B, int C, int H, int W, const float* tokens, float* z,
+                                   void* stream) {
+  CHECK(check_latent(B, C, H, W));
+  CHECK(need(tokens, "tokens"));
+  CHECK(need(z, "z"));
+  HIP_TRY(unpack_latents(tokens, z, B, C, H, W, static_cast<hipStream_t>(stream)));
+  return FLUX_OK;
+}
+
+extern "C" int flux_generation_ids(int grid_h, int grid_w, int n_txt, int32_t* img_ids,
+                                   int32_t* txt_ids, void* stream) {
+  if (grid_h <= 0 || grid_w <= 0 || n_txt < 0)
+    return fail(FLUX_EINVAL, "need grid_h, grid_w > 0 and n_txt >= 0");
+  if ((int64_t)grid_h * grid_w + n_txt >= (int64_t{1} << 30))
+    return fail(FLUX_ESHAPE, "too many tokens");
+  CHECK(need(img_ids, "img_ids"));
+  if (n_txt > 0) CHECK(need(txt_ids, "txt_ids"));
+  HIP_TRY(generation_ids(img_ids, grid_h, grid_w, txt_ids, n_txt, static_cast<hipStream_t>(stream)));
   return FLUX_OK;
 }
 

@@ -94,6 +94,12 @@ _PROTOS = {
     "flux_denoiser_step_workspace_size": (c_size, [P(flux_cfg), c_int, c_int, c_int]),
     "flux_denoiser_step": (c_int, [P(flux_cfg), P(flux_model_weights), vp, vp, c_int, c_int, c_int,
                                    vp, vp, vp, vp, vp, vp, c_size, vp]),
+    "flux_denoise_workspace_size": (c_size, [P(flux_cfg), c_int, c_int, c_int, c_int, c_int]),
+    "flux_denoise": (c_int, [P(flux_cfg), P(flux_model_weights), c_int, vp, ctypes.c_float, c_int,
+                             c_int, c_int, c_int, vp, vp, vp, vp, vp, c_size, vp]),
+    "flux_pack_latents": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp]),
+    "flux_unpack_latents": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp]),
+    "flux_generation_ids": (c_int, [c_int, c_int, c_int, vp, vp, vp]),
     "flux_rope_positions": (c_int, [P(flux_cfg), vp, vp, c_int, c_int, vp, vp]),
     "flux_modulation_workspace_size": (c_size, [P(flux_cfg), c_int]),
     "flux_modulation": (c_int, [P(flux_cfg), P(flux_temb_weights), vp, c_int, vp, c_int, vp, vp,
@@ -280,6 +286,42 @@ def flux_denoiser_step(cfg, w, t, guidance, batch, n_img, n_txt, x, ctx, img_ids
                                     batch, n_img, n_txt, _ptr(x), _ptr(ctx), _ptr(img_ids),
                                     _ptr(txt_ids), _ptr(out), _ptr(workspace), workspace_bytes,
                                     _stream(stream)))
+
+
+def flux_denoise_workspace_size(cfg, batch, latent_h, latent_w, n_txt, guided) -> int:
+    return lib().flux_denoise_workspace_size(ctypes.byref(cfg), batch, latent_h, latent_w, n_txt,
+                                             int(bool(guided)))
+
+
+def flux_denoise(cfg, w, n_steps, sigmas, guidance_scale, batch, latent_h, latent_w, n_txt,
+                 noise, ctx, ctx_uncond, latents_out, workspace, workspace_bytes, stream=None):
+    """sigmas: host sequence of n_steps + 1 floats, or None for the uniform grid."""
+    ws = w.struct if isinstance(w, ModelWeights) else w
+    sig = None
+    if sigmas is not None:
+        vals = [float(v) for v in sigmas]
+        if len(vals) != n_steps + 1:
+            raise FluxError(FLUX_EINVAL, f"need {n_steps + 1} sigmas, got {len(vals)}")
+        sig = (ctypes.c_float * len(vals))(*vals)
+    _check(lib().flux_denoise(ctypes.byref(cfg), ctypes.byref(ws), n_steps,
+                              ctypes.cast(sig, ctypes.c_void_p) if sig is not None else None,
+                              float(guidance_scale), batch, latent_h, latent_w, n_txt, _ptr(noise),
+                              _ptr(ctx), _ptr(ctx_uncond), _ptr(latents_out), _ptr(workspace),
+                              workspace_bytes, _stream(stream)))
+
+
+def flux_pack_latents(batch, channels, h, w, z, tokens, stream=None):
+    _check(lib().flux_pack_latents(batch, channels, h, w, _ptr(z), _ptr(tokens), _stream(stream)))
+
+
+def flux_unpack_latents(batch, channels, h, w, tokens, z, stream=None):
+    _check(lib().flux_unpack_latents(batch, channels, h, w, _ptr(tokens), _ptr(z),
+                                     _stream(stream)))
+
+
+def flux_generation_ids(grid_h, grid_w, n_txt, img_ids, txt_ids, stream=None):
+    _check(lib().flux_generation_ids(grid_h, grid_w, n_txt, _ptr(img_ids), _ptr(txt_ids),
+                                     _stream(stream)))
 
 
 def flux_rope_positions(cfg, txt_ids, img_ids, n_txt, n_img, pos_out, stream=None):

@@ -193,6 +193,53 @@ int flux_denoiser_step(const flux_cfg* cfg, const flux_model_weights* w, const f
                        const void* ctx, const int32_t* img_ids, const int32_t* txt_ids,
                        float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Sampling loop: rectified-flow Euler steps of the denoiser from a noise latent
+ * ([KLEIN] 训练方法: latent rectified flow, 4 steps for the distilled model, 50 steps with
+ * the two forwards of classifier-free guidance for the base model; [DIFF] pipeline call
+ * chain: packed latents with 4-D ids, a flow-matching Euler scheduler calling the
+ * transformer once per step; [KLEIN] Visual tokenizer / VAE: 2x2 patchify of the latent).
+ *
+ *   x_0 = pack(noise);  x_{i+1} = x_i + (sigmas[i+1] - sigmas[i]) * v_i;  out = unpack(x_n)
+ *
+ * v_i is the step's output at x_i (rounded to cfg->dtype as the step's input) with
+ * t = sigmas[i].  With ctx_uncond, each step is one batch-2*batch forward over
+ * [ctx ; ctx_uncond] and v_i = v_u + guidance_scale * (v_c - v_u); without it the scale is
+ * ignored.  Position ids are generated: image token (r, c) of the (latent_h/2) x
+ * (latent_w/2) grid -> (0, r, c, 0) row-major, text token i -> (0, 0, 0, i).
+ *   sigmas      HOST float[n_steps + 1], finite and strictly decreasing (t of each level;
+ *               the step multiplies by 1000); NULL: the uniform grid 1 - i / n_steps
+ *   noise       device fp32 [batch, in_channels/4, latent_h, latent_w] (latent_h, latent_w
+ *               even); the state stays fp32 between steps
+ *   ctx, ctx_uncond  device [batch, n_txt, context_dim] (cfg->dtype); ctx_uncond may be NULL
+ *   latents_out device fp32 [batch, in_channels/4, latent_h, latent_w]; may alias noise
+ *   workspace   flux_denoise_workspace_size(cfg, batch, latent_h, latent_w, n_txt,
+ *               ctx_uncond != NULL) bytes, 256-byte aligned
+ * The weights are those of flux_denoiser_step.  Errors (nothing enqueued): FLUX_EINVAL
+ * (NULL pointers, n_steps outside [1, 10000], sigmas not finite or not decreasing,
+ * guidance without text, non-finite scale), FLUX_ESHAPE (odd latent sides, in_channels not
+ * a multiple of 8), FLUX_EALIGN, FLUX_EWORKSPACE, and the step's own errors. */
+size_t flux_denoise_workspace_size(const flux_cfg* cfg, int batch, int latent_h, int latent_w,
+                                   int n_txt, int guided);
+int flux_denoise(const flux_cfg* cfg, const flux_model_weights* w, int n_steps,
+                 const float* sigmas, float guidance_scale, int batch, int latent_h, int latent_w,
+                 int n_txt, const float* noise, const void* ctx, const void* ctx_uncond,
+                 float* latents_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* 2x2 latent packing used by flux_denoise ([KLEIN] Visual tokenizer / VAE):
+ * tokens[b, r * (W/2) + c, 4 ch + 2 ph + pw] = z[b, ch, 2 r + ph, 2 c + pw].
+ *   z       device fp32 [batch, channels, H, W] (H, W even);  tokens device fp32
+ *           [batch, (H/2)(W/2), 4 channels].  Errors: FLUX_EINVAL, FLUX_ESHAPE, FLUX_EALIGN. */
+int flux_pack_latents(int batch, int channels, int H, int W, const float* z, float* tokens,
+                      void* stream);
+int flux_unpack_latents(int batch, int channels, int H, int W, const float* tokens, float* z,
+                        void* stream);
+
+/* Position ids of a generation ([DIFF] 位置 id): img_ids device int32 [grid_h * grid_w, 4]
+ * = (0, r, c, 0) row-major; txt_ids device int32 [n_txt, 4] = (0, 0, 0, i) (may be NULL
+ * when n_txt == 0).  Errors: FLUX_EINVAL, FLUX_ESHAPE, FLUX_EALIGN. */
+int flux_generation_ids(int grid_h, int grid_w, int n_txt, int32_t* img_ids, int32_t* txt_ids,
+                        void* stream);
+
 /* ---------------------------------------------------------------------------------
  * Single operations of the hot path (each is one kernel, or a short fixed sequence,
  * of the blocks above; exported so each can be checked and timed on its own).

@@ -161,6 +161,40 @@ def test_step_and_op_validation_errors():
                                      None) == F.FLUX_EDTYPE
 
 
+def test_sampler_validation_errors():
+    L = F.lib()
+    c = F.make_cfg(256, 2, 768, in_channels=32, context_dim=48, n_double=1, n_single=1)
+    mw = F.flux_model_weights()
+    args = lambda n, sig, h, w, nt, unc, ws=FAKE, nb=1 << 30: (
+        ctypes.byref(c), ctypes.byref(mw), n, sig, ctypes.c_float(2.0), 1, h, w, nt, FAKE, FAKE,
+        unc, FAKE, ws, nb, None)
+    assert L.flux_denoise(*args(0, None, 8, 8, 5, None)) == F.FLUX_EINVAL
+    assert L.flux_denoise(*args(4, None, 7, 8, 5, None)) == F.FLUX_ESHAPE
+    up = (ctypes.c_float * 3)(1.0, 0.5, 0.5)
+    assert L.flux_denoise(*args(2, ctypes.cast(up, ctypes.c_void_p), 8, 8, 5, None)) == F.FLUX_EINVAL
+    assert "decrease" in F.flux_last_error()
+    nan = (ctypes.c_float * 2)(1.0, float("nan"))
+    assert L.flux_denoise(*args(1, ctypes.cast(nan, ctypes.c_void_p), 8, 8, 5, None)) == F.FLUX_EINVAL
+    # missing weights are reported before anything is enqueued
+    assert L.flux_denoise(*args(2, None, 8, 8, 5, None)) == F.FLUX_EINVAL
+    # workspace queries: 0 for bad shapes, guided needs more than unguided
+    assert F.flux_denoise_workspace_size(c, 1, 7, 8, 5, False) == 0
+    assert F.flux_denoise_workspace_size(c, 0, 8, 8, 5, False) == 0
+    a = F.flux_denoise_workspace_size(c, 1, 8, 8, 5, False)
+    b = F.flux_denoise_workspace_size(c, 1, 8, 8, 5, True)
+    assert 0 < a < b
+    # binding: wrong number of levels
+    with pytest.raises(F.FluxError):
+        F.flux_denoise(c, mw, 2, [1.0, 0.0], 1.0, 1, 8, 8, 5, FAKE, FAKE, None, FAKE, FAKE, 1 << 30)
+    # packing and ids
+    assert L.flux_pack_latents(1, 4, 6, 5, FAKE, FAKE, None) == F.FLUX_ESHAPE
+    assert L.flux_pack_latents(1, 4, 6, 6, None, FAKE, None) == F.FLUX_EINVAL
+    assert L.flux_unpack_latents(1, 4, 6, 6, FAKE + 4, FAKE, None) == F.FLUX_EALIGN
+    assert L.flux_unpack_latents(0, 4, 6, 6, FAKE, FAKE, None) == F.FLUX_EINVAL
+    assert L.flux_generation_ids(0, 4, 2, FAKE, FAKE, None) == F.FLUX_EINVAL
+    assert L.flux_generation_ids(4, 4, 2, FAKE, None, None) == F.FLUX_EINVAL
+
+
 def test_timing_hook_validation():
     L = F.lib()
     n, us = ctypes.c_int(7), ctypes.c_double(1.0)

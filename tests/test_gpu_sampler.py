@@ -1,0 +1,173 @@
+"""Sampling loop through the C ABI: latent packing and generation ids bit-exact against the
+oracle, the Euler / guidance loop against the fp64 oracle at sizes it runs in seconds, and
+at the Klein-9B 1024^2 size the properties that hold at any size (zero velocity leaves
+the latent unchanged, bitwise; repeated runs agree bitwise)."""
+import numpy as np
+import pytest
+
+import flux_synth as fs
+from oracle import flux_oracle as O
+from tests import flux_gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from diffusion_transformer_mmdit_amd import flux as F
+    F.lib()
+
+
+def F_():
+    from diffusion_transformer_mmdit_amd import flux as F
+    return F
+
+
+@pytest.mark.parametrize("shape", [(1, 32, 16, 16), (2, 8, 6, 10), (1, 3, 2, 2),
+                                   (1, 32, 128, 128)])
+def test_pack_unpack_bit_exact(shape):
+    F, t = F_(), G.torch()
+    B, C, H, W = shape
+    print(f"[sampler] pack/unpack {shape}", flush=True)
+    z = fs.normal(77, "z", shape, dtype="f32")
+    zd = G.dev(z, "f32")
+    tok = t.empty((B, (H // 2) * (W // 2), 4 * C), device="cuda")
+    F.flux_pack_latents(B, C, H, W, zd, tok, G.stream())
+    back = t.empty_like(zd)
+    F.flux_unpack_latents(B, C, H, W, tok, back, G.stream())
+    t.cuda.synchronize()
+    assert np.array_equal(G.host(tok), O.pack_latents(z))
+    assert t.equal(back, zd)
+
+
+@pytest.mark.parametrize("gh,gw,nt", [(8, 8, 16), (3, 5, 0), (64, 64, 512), (7, 1, 3)])
+def test_generation_ids_bit_exact(gh, gw, nt):
+    F, t = F_(), G.torch()
+    img = t.full((gh * gw, 4), -1, dtype=t.int32, device="cuda")
+    txt = t.full((max(nt, 1), 4), -1, dtype=t.int32, device="cuda")
+    F.flux_generation_ids(gh, gw, nt, img, txt if nt else None, G.stream())
+    t.cuda.synchronize()
+    ri, rt = O.generation_ids(gh, gw, nt)
+    assert np.array_equal(img.cpu().numpy(), ri)
+    if nt:
+        assert np.array_equal(txt.cpu().numpy(), rt)
+
+
+def run_denoise(wl, inp, n_steps, sigmas=None, guidance=1.0, guided=False, w_dev=None, lat=None):
+    F, t = F_(), G.torch()
+    cfg = G.cfg_for(wl)
+    w_dev = w_dev or G.upload_weights(inp["weights"], wl.dtype)
+    mw = F.ModelWeights(w_dev, wl.n_double, wl.n_single)
+    B, C, H, W = inp["noise"].shape if lat is None else lat
+    noise = inp["noise_dev"] if "noise_dev" in inp else G.dev(inp["noise"], "f32")
+    ctx = G.dev(inp["ctx"], wl.dtype) if "ctx" in inp else inp["ctx_dev"]
+    unc = None
+    if guided:
+        unc = G.dev(inp["ctx_uncond"], wl.dtype) if "ctx_uncond" in inp else inp["ctx_uncond_dev"]
+    out = t.empty((B, C, H, W), device="cuda")
+    nb = F.flux_denoise_workspace_size(cfg, B, H, W, wl.n_txt, guided)
+    ws = G.workspace(nb)
+    F.flux_denoise(cfg, mw, n_steps, sigmas, guidance, B, H, W, wl.n_txt, noise, ctx, unc, out,
+                   ws, nb, G.stream())
+    t.cuda.synchronize()
+    return out
+
+
+def tiny_step_workload(**kw):
+    return fs.workload("tiny_single_f32", kind="step", in_channels=32, context_dim=48,
+                       n_double=1, n_single=2, n_img=16, n_txt=5, **kw)
+
+
+def test_denoise_tiny_fp32_four_uniform_steps():
+    wl = tiny_step_workload()
+    inp = fs.sample_inputs(wl, 8, 8)
+    print("[sampler] tiny fp32, 4 uniform steps", flush=True)
+    got = G.host(run_denoise(wl, inp, 4))
+    ref = O.denoise(inp["noise"], inp["ctx"], inp["weights"], O.uniform_sigmas(4), 1, 2)
+    G.assert_close(got, ref, "f32", "tiny fp32 denoise (4 steps)")
+
+
+def small_bf16(batch):
+    return fs.workload("tiny_single_f32", dtype="bf16", kind="step", dim=512, heads=4,
+                       mlp_hidden=1536, in_channels=128, context_dim=64, n_double=2, n_single=2,
+                       n_img=60, n_txt=24, t_fixed=None, batch=batch, seed=1011)
+
+
+@pytest.mark.parametrize("batch,guided", [(1, False), (1, True), (2, True)])
+def test_denoise_small_bf16(batch, guided):
+    # non-square 6 x 10 token grid, explicit levels, guidance 3.5
+    wl = small_bf16(batch)
+    inp = fs.sample_inputs(wl, 12, 20, with_uncond=guided)
+    sig = [1.0, 0.7, 0.35, 0.0]
+    print(f"[sampler] small bf16 batch {batch} guided {guided}", flush=True)
+    got = G.host(run_denoise(wl, inp, 3, sigmas=sig, guidance=3.5, guided=guided))
+    ref = O.denoise(inp["noise"], inp["ctx"], inp["weights"], sig, 2, 2,
+                    ctx_uncond=inp.get("ctx_uncond"), guidance=3.5,
+                    model_input=O.bf16_storage)
+    G.assert_close(got, ref, "bf16", f"small bf16 denoise (batch {batch}, guided {guided})")
+
+
+def test_denoise_guidance_with_equal_conditions_is_unguided():
+    wl = small_bf16(1)
+    inp = fs.sample_inputs(wl, 12, 20)
+    w_dev = G.upload_weights(inp["weights"], wl.dtype)
+    plain = G.host(run_denoise(wl, inp, 2, guidance=5.0, w_dev=w_dev))
+    same = dict(inp, ctx_uncond=inp["ctx"])
+    guided = G.host(run_denoise(wl, same, 2, guidance=5.0, guided=True, w_dev=w_dev))
+    G.assert_close(guided, plain, "bf16", "guided run with equal conditions vs unguided")
+
+
+def klein9b_device_weights(wl, zero_proj_out):
+    """Seeded device weights of the Klein-9B manifest (torch's generator on the GPU: the
+    properties below hold for any weights)."""
+    t = G.torch()
+    g = t.Generator(device="cuda")
+    g.manual_seed(wl.seed)
+    w = {}
+    for name, (shape, kind) in fs.step_weight_specs(wl).items():
+        if kind == "g":
+            w[name] = 1.0 + 0.02 * t.randn(shape, generator=g, device="cuda")
+        else:
+            w[name] = (0.02 * t.randn(shape, generator=g, device="cuda")).to(t.bfloat16)
+    if zero_proj_out:
+        w["proj_out"].zero_()
+    return w
+
+
+@pytest.fixture(scope="module")
+def klein9b_sampling():
+    wl = fs.workload("klein9b_step_1024")
+    t = G.torch()
+    g = t.Generator(device="cuda")
+    g.manual_seed(wl.seed + 1)
+    inp = {"noise_dev": t.randn((1, 32, 128, 128), generator=g, device="cuda"),
+           "ctx_dev": t.randn((1, wl.n_txt, wl.context_dim), generator=g,
+                              device="cuda").to(t.bfloat16)}
+    inp["ctx_uncond_dev"] = t.randn((1, wl.n_txt, wl.context_dim), generator=g,
+                                    device="cuda").to(t.bfloat16)
+    return wl, inp
+
+
+def test_klein9b_zero_velocity_keeps_the_latent_bitwise(klein9b_sampling):
+    wl, inp = klein9b_sampling
+    print("[sampler] Klein-9B 1024^2, proj_out = 0, 4 steps guided", flush=True)
+    w = klein9b_device_weights(wl, zero_proj_out=True)
+    out = run_denoise(wl, inp, 4, guidance=4.0, guided=True, w_dev=w, lat=(1, 32, 128, 128))
+    assert G.torch().equal(out, inp["noise_dev"])
+    del w
+
+
+def test_klein9b_four_steps_deterministic_and_finite(klein9b_sampling):
+    wl, inp = klein9b_sampling
+    print("[sampler] Klein-9B 1024^2, 4 distilled steps twice", flush=True)
+    w = klein9b_device_weights(wl, zero_proj_out=False)
+    a = run_denoise(wl, inp, 4, w_dev=w, lat=(1, 32, 128, 128))
+    b = run_denoise(wl, inp, 4, w_dev=w, lat=(1, 32, 128, 128))
+    t = G.torch()
+    assert t.isfinite(a).all() and t.equal(a, b)
+    # the latent moved away from the noise (a non-zero velocity was integrated)
+    assert (a - inp["noise_dev"]).abs().max().item() > 1e-3
+    del w

@@ -234,7 +234,7 @@ def cpu_baseline(wl, flops_step: float):
 # per-workload block timings and bandwidth-kernel rates
 # ------------------------------------------------------------------------------------
 PER_CONFIG = ("tiny_single_f32", "klein4b_single_512", "klein9b_double_1024",
-              "klein9b_step_1024", "dev_pair_2048")
+              "klein9b_step_1024", "dev_pair_2048", "klein9b_generate_1024")
 
 
 def _time_ms(fn, s, warmup=3, reps=10):
@@ -249,9 +249,60 @@ def _time_ms(fn, s, warmup=3, reps=10):
     return ev.stop_ms() / reps
 
 
+def generate_line(F, fs, wl) -> dict:
+    """Sampling loop at the step's shapes: a 4-step distilled generation and guided steps
+    (one batch-2 forward each), against the plain step; all on device-resident inputs."""
+    import torch
+    dtype = torch.bfloat16
+    w = device_weights(fs.step_weight_specs(wl), wl.seed, dtype)
+    mw = F.ModelWeights(w, wl.n_double, wl.n_single)
+    cfg = F.make_cfg(wl.dim, wl.heads, wl.mlp_hidden, in_channels=wl.in_channels,
+                     context_dim=wl.context_dim, n_double=wl.n_double, n_single=wl.n_single)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed)
+    lat = 2 * wl.grid
+    C = wl.in_channels // 4
+    noise = torch.randn((1, C, lat, lat), generator=g, device="cuda")
+    ctx = torch.randn((1, wl.n_txt, wl.context_dim), generator=g, device="cuda").to(dtype)
+    unc = torch.randn((1, wl.n_txt, wl.context_dim), generator=g, device="cuda").to(dtype)
+    out = torch.empty_like(noise)
+    s = torch.cuda.current_stream()
+    res = {"workload": wl.name, "dtype": wl.dtype, "latent": [1, C, lat, lat], "n_txt": wl.n_txt}
+    # the plain step on the same shapes
+    x = torch.randn((1, wl.n_img, wl.in_channels), generator=g, device="cuda").to(dtype)
+    t = torch.rand((1,), generator=g, device="cuda")
+    img_ids = torch.from_numpy(fs.image_ids(wl.n_img)).cuda()
+    txt_ids = torch.from_numpy(fs.text_ids(wl.n_txt)).cuda()
+    vout = torch.empty((1, wl.n_img, wl.in_channels), device="cuda")
+    nb = F.flux_denoiser_step_workspace_size(cfg, 1, wl.n_img, wl.n_txt)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    step_ms = _time_ms(lambda: F.flux_denoiser_step(cfg, mw, t, None, 1, wl.n_img, wl.n_txt, x, ctx,
+                                                    img_ids, txt_ids, vout, ws, nb, s), s)
+    del ws
+    res["step_ms"] = round(step_ms, 3)
+    fl = step_flops(wl)
+    for guided, n, key in ((False, 4, "generate_4step"), (True, 4, "guided_4step")):
+        nb = F.flux_denoise_workspace_size(cfg, 1, lat, lat, wl.n_txt, guided)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        fn = lambda: F.flux_denoise(cfg, mw, n, None, 4.0, 1, lat, lat, wl.n_txt, noise, ctx,
+                                    unc if guided else None, out, ws, nb, s)
+        ms = _time_ms(fn, s, warmup=1, reps=3)
+        flops = n * (2 if guided else 1) * fl
+        res[f"{key}_ms"] = round(ms, 3)
+        res[f"{key}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        # time outside the n (or 2n batch rows of) denoiser steps: packing, ids, updates
+        res[f"{key}_ms_per_step"] = round(ms / n, 3)
+        del ws
+    res["sampler_overhead_ms"] = round(res["generate_4step_ms"] - 4 * step_ms, 3)
+    del w, mw
+    return res
+
+
 def per_config_line(F, fs, name: str) -> dict:
     import torch
     wl = fs.workload(name)
+    if wl.kind == "generate":
+        return generate_line(F, fs, wl)
     dtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     fdt = F.FLUX_BF16 if wl.dtype == "bf16" else F.FLUX_F32
     D, H, B = wl.dim, wl.mlp_hidden, wl.batch
@@ -323,6 +374,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-config", action="store_true",
                     help="time the blocks and bandwidth kernels of every traced workload")
+    ap.add_argument("--only", default=None, choices=PER_CONFIG,
+                    help="with --per-config: just this workload")
     ap.add_argument("--probe", choices=("dominant", "copy"), default=None,
                     help="only launch the dominant kernel (or a 1 GiB copy) 3 times and exit")
     args = ap.parse_args(argv)
@@ -340,7 +393,7 @@ def main(argv=None) -> int:
         print("no GPU available", file=sys.stderr)
         return 1
     if args.per_config:
-        for name in PER_CONFIG:
+        for name in PER_CONFIG if args.only is None else (args.only,):
             print(json.dumps(per_config_line(F, fs, name)), flush=True)
             torch.cuda.empty_cache()
         return 0

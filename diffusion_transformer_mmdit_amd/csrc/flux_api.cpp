@@ -883,13 +883,12 @@ extern "C" int flux_denoise(const flux_cfg* c, const flux_model_weights* w, int 
   for (int i = 0; i < n_steps; ++i) {
     // x_i = x_{i-1} + (sigma_i - sigma_{i-1}) v_{i-1}, then the model input in its dtype
     HIP_TRY(sampler_update(T, sb.x, i ? sb.v : nullptr, n, i ? sig[i] - sig[i - 1] : 0.f,
-                           guidance_scale, guided, sb.xin, s));
-    HIP_TRY(fill_f32(sb.t, Bm, sig[i], s));
+                           guidance_scale, guided, sb.xin, sb.t, Bm, sig[i], s));
     CHECK(run_step(c, w, sb.t, Bm, Ni, Nt, sb.xin, cond, sb.img_ids, sb.txt_ids, sb.v,
                    sb.step_ws, s));
   }
   HIP_TRY(sampler_update(T, sb.x, sb.v, n, sig[n_steps] - sig[n_steps - 1], guidance_scale,
-                         guided, nullptr, s));
+                         guided, nullptr, nullptr, 0, 0.f, s));
   HIP_TRY(unpack_latents(sb.x, latents_out, B, C, latent_h, latent_w, s));
   return FLUX_OK;
 }

@@ -12,11 +12,12 @@ hipError_t unpack_latents(const float* x, float* z, int B, int C, int H, int W, 
 // img_ids [gh * gw, 4] = (0, r, c, 0) row-major; txt_ids [n_txt, 4] = (0, 0, 0, i)
 hipError_t generation_ids(int32_t* img_ids, int gh, int gw, int32_t* txt_ids, int n_txt,
                           hipStream_t s);
-hipError_t fill_f32(float* p, int n, float v, hipStream_t s);
 // x[0 .. n) += dt * v_eff (n % 4 == 0, 16-byte aligned), v_eff = v or, guided,
 // v[i] for the conditional half and v[n + i] for the unconditional: v_u + g (v_c - v_u).
 // v == nullptr leaves x unchanged.  xin (optional, xin_dtype): model input = new x, written
-// to xin[0 .. n) and, guided, also to xin[n .. 2n).
+// to xin[0 .. n) and, guided, also to xin[n .. 2n).  t_out (optional): t_out[0 .. nt) =
+// t_val, the timestep of the next step.
 hipError_t sampler_update(int xin_dtype, float* x, const float* v, int64_t n, float dt, float g,
-                          bool guided, void* xin, hipStream_t s);
+                          bool guided, void* xin, float* t_out, int nt, float t_val,
+                          hipStream_t s);
 }  // namespace flux

@@ -15,23 +15,26 @@
 namespace flux {
 
 // tokens[b, r*gw + c, 4 ch + 2 ph + pw] = z[b, ch, 2r + ph, 2c + pw]; one thread per
-// (b, token, ch): two 8-byte reads (the patch's rows), one 16-byte write.
+// (b, ch, patch row r, patch column c), consecutive threads along c: two contiguous 8-byte
+// reads (the patch's rows), one 16-byte write.
 __global__ void pack_latents_kernel(const float* __restrict__ z, float* __restrict__ x, int B,
                                     int C, int H, int W) {
-  const int gw = W / 2, n = (H / 2) * gw;
+  const int gw = W / 2, gh = H / 2;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)B * n * C) return;
-  const int ch = (int)(idx % C);
-  const int64_t bt = idx / C;
-  const int tok = (int)(bt % n), b = (int)(bt / n);
-  const int r = tok / gw, c = tok % gw;
-  const float* src = z + (((int64_t)b * C + ch) * H + 2 * r) * W + 2 * c;
+  if (idx >= (int64_t)B * C * gh * gw) return;
+  const int c = (int)(idx % gw);
+  const int64_t q = idx / gw;
+  const int r = (int)(q % gh);
+  const int64_t bc = q / gh;
+  const int ch = (int)(bc % C), b = (int)(bc / C);
+  const float* src = z + (bc * H + 2 * r) * W + 2 * c;
   const float2 top = *reinterpret_cast<const float2*>(src);
   const float2 bot = *reinterpret_cast<const float2*>(src + W);
-  *reinterpret_cast<float4*>(x + bt * 4 * C + 4 * ch) = make_float4(top.x, top.y, bot.x, bot.y);
+  *reinterpret_cast<float4*>(x + ((int64_t)b * gh * gw + (int64_t)r * gw + c) * 4 * C + 4 * ch) =
+      make_float4(top.x, top.y, bot.x, bot.y);
 }
 
-// inverse of pack_latents_kernel, one thread per (b, ch, patch row r, patch column c)
+// inverse of pack_latents_kernel, same thread mapping
 __global__ void unpack_latents_kernel(const float* __restrict__ x, float* __restrict__ z, int B,
                                       int C, int H, int W) {
   const int gw = W / 2, gh = H / 2;
@@ -62,11 +65,6 @@ __global__ void generation_ids_kernel(int32_t* __restrict__ img_ids, int gh, int
   }
 }
 
-__global__ void fill_f32_kernel(float* __restrict__ p, int n, float v) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx < n) p[idx] = v;
-}
-
 template <class T>
 FLUX_DEV void store4_as(T* p, float4 v);
 template <>
@@ -81,12 +79,15 @@ FLUX_DEV void store4_as<bf16>(bf16* p, float4 v) {
 // x += dt * v_eff over n4 groups of 4 elements; v_eff = v, or with guidance v_u + g (v_c -
 // v_u) where group i of the conditional half is v[i] and of the unconditional half
 // v[half4 + i].  Without v the state is left as is.  xin (optional) receives the model
-// input: the new state in the model dtype, written to both halves with guidance.
+// input: the new state in the model dtype, written to both halves with guidance.  The
+// first nt threads also write the next level's timestep t_val to t_out.
 template <class T>
 __global__ void sampler_update_kernel(float* __restrict__ x, const float* __restrict__ v,
                                       int64_t n4, int64_t half4, float dt, float g, int guided,
-                                      T* __restrict__ xin) {
+                                      T* __restrict__ xin, float* __restrict__ t_out, int nt,
+                                      float t_val) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nt) t_out[i] = t_val;
   if (i >= n4) return;
   float4 s = reinterpret_cast<float4*>(x)[i];
   if (v) {
@@ -135,21 +136,20 @@ hipError_t generation_ids(int32_t* img_ids, int gh, int gw, int32_t* txt_ids, in
   return hipGetLastError();
 }
 
-hipError_t fill_f32(float* p, int n, float v, hipStream_t s) {
-  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, p, n, v);
-  return hipGetLastError();
-}
-
 hipError_t sampler_update(int xin_dtype, float* x, const float* v, int64_t n, float dt, float g,
-                          bool guided, void* xin, hipStream_t s) {
+                          bool guided, void* xin, float* t_out, int nt, float t_val,
+                          hipStream_t s) {
   const int64_t n4 = n / 4;
-  if (n4 == 0) return hipSuccess;
+  const int64_t threads = n4 > nt ? n4 : nt;
+  if (threads == 0) return hipSuccess;
   if (xin_dtype == DT_BF16)
-    hipLaunchKernelGGL(sampler_update_kernel<bf16>, dim3(blocks_for(n4, 256)), dim3(256), 0, s, x,
-                       v, n4, n4, dt, g, guided ? 1 : 0, static_cast<bf16*>(xin));
+    hipLaunchKernelGGL(sampler_update_kernel<bf16>, dim3(blocks_for(threads, 256)), dim3(256), 0,
+                       s, x, v, n4, n4, dt, g, guided ? 1 : 0, static_cast<bf16*>(xin), t_out,
+                       t_out ? nt : 0, t_val);
   else
-    hipLaunchKernelGGL(sampler_update_kernel<float>, dim3(blocks_for(n4, 256)), dim3(256), 0, s,
-                       x, v, n4, n4, dt, g, guided ? 1 : 0, static_cast<float*>(xin));
+    hipLaunchKernelGGL(sampler_update_kernel<float>, dim3(blocks_for(threads, 256)), dim3(256), 0,
+                       s, x, v, n4, n4, dt, g, guided ? 1 : 0, static_cast<float*>(xin), t_out,
+                       t_out ? nt : 0, t_val);
   return hipGetLastError();
 }
 

@@ -30,9 +30,11 @@ Readings of points the pages leave open (each also listed in the design doc):
   * sampling: latent 2x2 patches -> token channels in (c, ph, pw) order, patches row-major;
     noise levels on the uniform grid 1 - i/n; Euler step x += (sigma_next - sigma) v with
     v taken at sigma; guidance v_u + g (v_c - v_u)
+  * reference K/V cache: reference image j has ids (1 + j, r, c, 0); all reference tokens
+    attend to all reference tokens (one segment); the fixed reference timestep is 0
 
 Parity pins for every function live in tests/test_oracle_pins.py and, for the sampling
-loop, tests/test_oracle_sampler.py (closed forms, invariants, brute force and an
+loop and the reference K/V cache, tests/test_oracle_sampler.py and tests/test_oracle_refkv.py (closed forms, invariants, brute force and an
 independent library routine); none is "parity unpinned".
 """
 from __future__ import annotations
@@ -581,6 +583,214 @@ def denoise(noise, ctx, w: Mapping, sigmas, n_double: int, n_single: int, ctx_un
             vu = denoiser_step(xi, ctx_uncond, t, w, img_ids, txt_ids, n_double, n_single,
                                storage=storage)
             v = cfg_combine(v, vu, guidance)
+        x = x + (sig[i + 1] - sig[i]) * v
+        if on_step:
+            on_step(i)
+    return unpack_latents(x, H, W)
+
+
+# ----------------------------------------------------------------------------------
+# Reference-image K/V cache
+#
+# [DIFF] 参考图 KV 缓存机制: a per-layer cache (Flux2KVLayerCache) keeps the reference
+# tokens' K and V after RoPE, for every double and single block.  Extract mode (first
+# denoising step): sequence [txt, ref, img]; reference tokens attend only to reference
+# tokens, text and image tokens attend to every token; reference tokens are modulated at a
+# fixed timestep (ref_fixed_timestep, default 0.0), placed by position beside the image
+# modulation; the reference K/V are stored.  Cached mode (later steps): sequence
+# [txt, img]; the cached reference K/V are inserted between the text and image keys.
+# [KLEIN] Infra (KV 缓存): step 0 extracts, later steps reuse the reference K/V.
+# Reading: reference image j (0-based) has ids (1 + j, r, c, 0) on its own packed grid.
+# ----------------------------------------------------------------------------------
+def attention_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray, allowed=None,
+                     storage=None) -> np.ndarray:
+    """softmax(q k^T / sqrt(d)) v per head, each query over the keys `allowed[q, :]` marks
+    (all keys when None).  q [B, Lq, h, d], k and v [B, Lk, h, d] -> [B, Lq, h*d].
+    `storage` as for attention()."""
+    B, Lq, h, d = q.shape
+    out = np.empty((B, Lq, h, d), dtype=np.float64)
+    for b in range(B):
+        for head in range(h):
+            sc = np.matmul(q[b, :, head, :], k[b, :, head, :].T) / np.sqrt(d)
+            if allowed is not None:
+                sc = np.where(allowed, sc, -np.inf)
+            e = np.exp(sc - sc.max(axis=-1, keepdims=True))
+            if storage is not None:
+                e = storage(e)
+            out[b, :, head, :] = np.matmul(e, v[b, :, head, :]) / e.sum(axis=-1, keepdims=True)
+    return out.reshape(B, Lq, h * d)
+
+
+def reference_ids(n_refs: int, grid_h: int, grid_w: int) -> np.ndarray:
+    """[n_refs * grid_h * grid_w, 4] int32: token (r, c) of reference j -> (1 + j, r, c, 0)."""
+    img, _ = generation_ids(grid_h, grid_w, 0)
+    out = np.concatenate([img] * n_refs) if n_refs else np.zeros((0, 4), np.int32)
+    out[:, 0] = np.repeat(np.arange(1, n_refs + 1, dtype=np.int32), grid_h * grid_w)
+    return out
+
+
+def _ln_rows(x, segments, shift_idx, scale_idx):
+    """LayerNorm + modulate where consecutive row segments [(n_rows, mods), ...] use their own
+    modulation set."""
+    parts, r0 = [], 0
+    for n, m in segments:
+        parts.append(layernorm_modulate(x[:, r0:r0 + n], m[shift_idx], m[scale_idx]))
+        r0 += n
+    return np.concatenate(parts, axis=1)
+
+
+def _gate_rows(y, segments, gate_idx):
+    parts, r0 = [], 0
+    for n, m in segments:
+        parts.append(m[gate_idx][:, None, :] * y[:, r0:r0 + n])
+        r0 += n
+    return np.concatenate(parts, axis=1)
+
+
+def step_extract(x, ref_x, ctx, t, w: Mapping, img_ids, ref_ids, txt_ids, n_double: int,
+                 n_single: int, t_ref: float = 0.0, storage=None):
+    """Extract-mode denoiser step over [txt, ref, img] -> (out [B, N_img, in_ch], cache).
+
+    cache[l] = (K, V) of the reference tokens at block l (double blocks first, then single
+    blocks): K after RMSNorm + RoPE and V, each [B, N_ref, h, 128].  `storage` as for
+    denoiser_step.
+    """
+    st = storage or _keep
+    B = np.shape(x)[0]
+    mods = step_mods(t, w)
+    mods_r = step_mods(np.full((B,), t_ref, dtype=np.float32), w)
+    txt = linear(f64(ctx), f64(w["txt_in"]))
+    ref = linear(f64(ref_x), f64(w["img_in"]))
+    img = linear(f64(x), f64(w["img_in"]))
+    Nt, Nr, Ni = txt.shape[1], ref.shape[1], img.shape[1]
+    L = Nt + Nr + Ni
+    pos = rope_positions(txt_ids, np.concatenate([_ids2d(ref_ids), _ids2d(img_ids)]))
+    allowed = np.ones((L, L), dtype=bool)
+    allowed[Nt:Nt + Nr, :] = False
+    allowed[Nt:Nt + Nr, Nt:Nt + Nr] = True
+    cache = []
+    for i in range(n_double):
+        wd = _Prefixed(w, f"double.{i}.")
+        # text stream alone; image stream = [ref ; img] rows with per-segment modulation
+        seg = {"txt": [(Nt, mods["double"]["txt"])],
+               "img": [(Nr, mods_r["double"]["img"]), (Ni, mods["double"]["img"])]}
+        xs = {"txt": txt, "img": np.concatenate([ref, img], axis=1)}
+        qs, ks, vs = {}, {}, {}
+        for s in ("txt", "img"):
+            a = st(_ln_rows(xs[s], seg[s], 0, 1))
+            q, k, v = (st(y) for y in np.split(linear(a, f64(wd[f"{s}.qkv"])), 3, axis=-1))
+            qs[s] = rms_norm(_heads(q), f64(wd[f"{s}.q_norm"]))
+            ks[s] = rms_norm(_heads(k), f64(wd[f"{s}.k_norm"]))
+            vs[s] = _heads(v)
+        q = st(apply_rope(np.concatenate([qs["txt"], qs["img"]], axis=1), pos))
+        k = st(apply_rope(np.concatenate([ks["txt"], ks["img"]], axis=1), pos))
+        v = np.concatenate([vs["txt"], vs["img"]], axis=1)
+        cache.append((k[:, Nt:Nt + Nr], v[:, Nt:Nt + Nr]))
+        o = st(attention_masked(q, k, v, allowed, storage))
+        o_s = {"txt": o[:, :Nt], "img": o[:, Nt:]}
+        for s in ("txt", "img"):
+            xx = xs[s] + _gate_rows(linear(o_s[s], f64(wd[f"{s}.out"])), seg[s], 2)
+            u = linear(st(_ln_rows(xx, seg[s], 3, 4)), f64(wd[f"{s}.mlp_in"]))
+            xs[s] = xx + _gate_rows(linear(st(swiglu(u)), f64(wd[f"{s}.mlp_out"])), seg[s], 5)
+        txt, ref, img = xs["txt"], xs["img"][:, :Nr], xs["img"][:, Nr:]
+    seg = [(Nt, mods["single"]), (Nr, mods_r["single"]), (Ni, mods["single"])]
+    h = np.concatenate([txt, ref, img], axis=1)
+    D = h.shape[-1]
+    for i in range(n_single):
+        ws = _Prefixed(w, f"single.{i}.")
+        y = linear(st(_ln_rows(h, seg, 0, 1)), f64(ws["linear1"]))
+        q, k, v, u = st(y[..., :D]), st(y[..., D:2 * D]), st(y[..., 2 * D:3 * D]), y[..., 3 * D:]
+        q = st(apply_rope(rms_norm(_heads(q), f64(ws["q_norm"])), pos))
+        k = st(apply_rope(rms_norm(_heads(k), f64(ws["k_norm"])), pos))
+        v = _heads(v)
+        cache.append((k[:, Nt:Nt + Nr], v[:, Nt:Nt + Nr]))
+        o = st(attention_masked(q, k, v, allowed, storage))
+        h = h + _gate_rows(linear(np.concatenate([o, st(swiglu(u))], axis=-1),
+                                  f64(ws["linear2"])), seg, 2)
+    shift_f, scale_f = mods["final"]
+    out = linear(st(layernorm_modulate(h[:, Nt + Nr:], shift_f, scale_f)), f64(w["proj_out"]))
+    return out, cache
+
+
+def step_cached(x, ctx, t, w: Mapping, img_ids, txt_ids, cache, n_double: int, n_single: int,
+                storage=None) -> np.ndarray:
+    """Cached-mode denoiser step over [txt, img]: at block l the keys and values are
+    [txt ; cached reference ; img] (cache[l] as returned by step_extract)."""
+    st = storage or _keep
+    mods = step_mods(t, w)
+    txt = linear(f64(ctx), f64(w["txt_in"]))
+    img = linear(f64(x), f64(w["img_in"]))
+    Nt = txt.shape[1]
+    pos = rope_positions(txt_ids, img_ids)
+
+    def inject(kv, l):
+        return tuple(np.concatenate([a[:, :Nt], f64(c), a[:, Nt:]], axis=1)
+                     for a, c in zip(kv, cache[l]))
+
+    for i in range(n_double):
+        wd = _Prefixed(w, f"double.{i}.")
+        xs = {"txt": txt, "img": img}
+        qs, ks, vs = {}, {}, {}
+        for s in ("txt", "img"):
+            m = mods["double"][s]
+            a = st(layernorm_modulate(xs[s], m[0], m[1]))
+            q, k, v = (st(y) for y in np.split(linear(a, f64(wd[f"{s}.qkv"])), 3, axis=-1))
+            qs[s] = rms_norm(_heads(q), f64(wd[f"{s}.q_norm"]))
+            ks[s] = rms_norm(_heads(k), f64(wd[f"{s}.k_norm"]))
+            vs[s] = _heads(v)
+        q = st(apply_rope(np.concatenate([qs["txt"], qs["img"]], axis=1), pos))
+        k = st(apply_rope(np.concatenate([ks["txt"], ks["img"]], axis=1), pos))
+        v = np.concatenate([vs["txt"], vs["img"]], axis=1)
+        k, v = inject((k, v), i)
+        o = st(attention_masked(q, k, v, None, storage))
+        o_s = {"txt": o[:, :Nt], "img": o[:, Nt:]}
+        for s in ("txt", "img"):
+            _, _, g1, s2, c2, g2 = mods["double"][s]
+            xx = xs[s] + g1[:, None, :] * linear(o_s[s], f64(wd[f"{s}.out"]))
+            u = linear(st(layernorm_modulate(xx, s2, c2)), f64(wd[f"{s}.mlp_in"]))
+            xs[s] = xx + g2[:, None, :] * linear(st(swiglu(u)), f64(wd[f"{s}.mlp_out"]))
+        txt, img = xs["txt"], xs["img"]
+    shift, scale, gate = mods["single"]
+    h = np.concatenate([txt, img], axis=1)
+    D = h.shape[-1]
+    for i in range(n_single):
+        ws = _Prefixed(w, f"single.{i}.")
+        y = linear(st(layernorm_modulate(h, shift, scale)), f64(ws["linear1"]))
+        q, k, v, u = st(y[..., :D]), st(y[..., D:2 * D]), st(y[..., 2 * D:3 * D]), y[..., 3 * D:]
+        q = st(apply_rope(rms_norm(_heads(q), f64(ws["q_norm"])), pos))
+        k = st(apply_rope(rms_norm(_heads(k), f64(ws["k_norm"])), pos))
+        k, v = inject((k, _heads(v)), n_double + i)
+        o = st(attention_masked(q, k, v, None, storage))
+        h = h + gate[:, None, :] * linear(np.concatenate([o, st(swiglu(u))], axis=-1),
+                                          f64(ws["linear2"]))
+    shift_f, scale_f = mods["final"]
+    return linear(st(layernorm_modulate(h[:, Nt:], shift_f, scale_f)), f64(w["proj_out"]))
+
+
+def denoise_with_refs(noise, refs, ctx, w: Mapping, sigmas, n_double: int, n_single: int,
+                      use_cache: bool = True, model_input=None, on_step=None) -> np.ndarray:
+    """denoise() conditioned on reference latents refs [B, R, C, Hr, Wr]: the first step
+    runs in extract mode, later steps in cached mode (use_cache) or again in extract mode
+    (every step recomputes the references).  Reference j has ids (1 + j, r, c, 0)."""
+    sig = np.asarray(sigmas, dtype=np.float32).astype(np.float64)
+    noise = f64(noise)
+    refs = f64(refs)
+    B, C, H, W = noise.shape
+    R, Hr, Wr = refs.shape[1], refs.shape[3], refs.shape[4]
+    ref_x = np.concatenate([pack_latents(refs[:, j]) for j in range(R)], axis=1)
+    ref_ids = reference_ids(R, Hr // 2, Wr // 2)
+    img_ids, txt_ids = generation_ids(H // 2, W // 2, np.shape(ctx)[1])
+    feed = model_input or (lambda a: a)
+    rin = feed(ref_x)
+    x = pack_latents(noise)
+    cache = None
+    for i in range(len(sig) - 1):
+        t = np.full((B,), sig[i], dtype=np.float32)
+        if cache is None or not use_cache:
+            v, cache = step_extract(feed(x), rin, ctx, t, w, img_ids, ref_ids, txt_ids,
+                                    n_double, n_single)
+        else:
+            v = step_cached(feed(x), ctx, t, w, img_ids, txt_ids, cache, n_double, n_single)
         x = x + (sig[i + 1] - sig[i]) * v
         if on_step:
             on_step(i)

@@ -251,3 +251,57 @@ def test_sampler_mutation_is_caught(name, monkeypatch):
             failed = True
             break
     assert failed, f"no pin caught mutation {name}"
+
+
+# ----------------------------------------------------------------------------------
+# Reference K/V cache: each planted mistake must fail a pin of tests/test_oracle_refkv.py
+# ----------------------------------------------------------------------------------
+import tests.test_oracle_refkv as rpins  # noqa: E402
+
+_rorig = {}
+
+
+def _mut_mask_ignored(q, k, v, allowed=None, storage=None):
+    return _rorig["attention_masked"](q, k, v, None, storage)
+
+
+def _mut_ref_ids_same_plane(n_refs, gh, gw):
+    ids = _rorig["reference_ids"](n_refs, gh, gw)
+    ids[:, 0] -= 1
+    return ids
+
+
+def _mut_ln_rows_first_set(x, segments, shift_idx, scale_idx):
+    m0 = segments[0][1]
+    return O.layernorm_modulate(x, m0[shift_idx], m0[scale_idx])
+
+
+def _mut_gate_rows_last_set(y, segments, gate_idx):
+    return segments[-1][1][gate_idx][:, None, :] * y
+
+
+REFKV_MUTATIONS = {
+    "reference_queries_see_every_key": ("attention_masked", _mut_mask_ignored),
+    "reference_ids_on_the_image_plane": ("reference_ids", _mut_ref_ids_same_plane),
+    "one_modulation_set_for_all_rows": ("_ln_rows", _mut_ln_rows_first_set),
+    "one_gate_set_for_all_rows": ("_gate_rows", _mut_gate_rows_last_set),
+}
+
+
+@pytest.mark.parametrize("name", sorted(REFKV_MUTATIONS))
+def test_refkv_mutation_is_caught(name, monkeypatch):
+    attr, fn = REFKV_MUTATIONS[name]
+    _rorig.clear()
+    _rorig.update({k: getattr(O, k) for k in ("attention_masked", "reference_ids")})
+    monkeypatch.setattr(O, attr, fn)
+    failed = False
+    for n, f in inspect.getmembers(rpins, inspect.isfunction):
+        if not n.startswith("test_"):
+            continue
+        try:
+            with np.errstate(all="ignore"):
+                f()
+        except (AssertionError, ValueError, IndexError):
+            failed = True
+            break
+    assert failed, f"no pin caught mutation {name}"

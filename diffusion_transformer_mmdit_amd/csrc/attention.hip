@@ -61,16 +61,18 @@ FLUX_DEV int attn_xcd_remap(int bid, int total) {
   return ((total & 7) == 0) ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
 }
 
-template <int NW>
+// EXTRA: key tiles past the sequence's own come from the extra source `xkv` (see KvExtra).
+template <int NW, bool EXTRA>
 __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     SeqView qv, SeqView kv, const bf16* __restrict__ vt, int64_t ld_vt, int dim, SeqView ov,
     int seq, float scale_log2, int nqb, int heads, int full_units, int splits,
-    float* __restrict__ partial) {
+    float* __restrict__ partial, KvExtra xkv) {
   constexpr int NT = 64 * NW;
   __shared__ __align__(16) bf16 Ks[2][kBKV * kHD];
   __shared__ __align__(16) bf16 Vs[2][kHD * kBKV];
 
-  const int ntiles = (seq + kBKV - 1) / kBKV;
+  const int nm = (seq + kBKV - 1) / kBKV;  // tiles of the sequence's own keys
+  const int ntiles = nm + (EXTRA ? (xkv.n + kBKV - 1) / kBKV : 0);
   int unit, t_begin = 0, t_end = ntiles, part = -1;
   if ((int)blockIdx.x < full_units) {
     unit = attn_xcd_remap(blockIdx.x, full_units);
@@ -129,7 +131,62 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
   const uint32_t ks0 = __builtin_amdgcn_readfirstlane(lds_u32(&Ks[0][0])) + wv * KI * 4 * kHD * 2;
   const uint32_t vs0 = __builtin_amdgcn_readfirstlane(lds_u32(&Vs[0][0])) + wv * VI * 8 * kBKV * 2;
   constexpr uint32_t KBUF = kBKV * kHD * 2, VBUF = kHD * kBKV * 2;
-  auto issue = [&](int buf, int kv0) {
+  // tile of the extra source at key x0: scalar base + per-lane offsets while the tile lies
+  // inside the extra keys, else per-lane addresses with the key clamped to the last one.
+  // The extra source's fields are read into scalars once (a by-reference capture of the
+  // argument struct would place it in per-lane memory).
+  const bf16* xk = nullptr;
+  const bf16* xvt = nullptr;
+  int64_t xld = 0, xldv = 0;
+  int xn = 0;
+  if constexpr (EXTRA) {
+    const int bx = b % xkv.nb;
+    xk = static_cast<const bf16*>(xkv.k) + bx * xkv.bs;
+    xvt = static_cast<const bf16*>(xkv.vt) + ((int64_t)bx * dim + hoff) * xkv.ld_vt;
+    xld = xkv.ld;
+    xldv = xkv.ld_vt;
+    xn = xkv.n;
+  }
+  auto uni = [](const bf16* p) {  // a wave-uniform pointer, in scalar registers
+    const uint64_t u = reinterpret_cast<uintptr_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return reinterpret_cast<const bf16*>(((uint64_t)hi << 32) | lo);
+  };
+  auto issue_extra = [&](int buf, int x0) {
+    if (x0 + kBKV <= xn) {
+      const bf16* kb = uni(xk + (int64_t)x0 * xld);
+#pragma unroll
+      for (int j = 0; j < KI; ++j) {
+        const int row = (wave * KI + j) * 4 + (lane >> 4);
+        const int c = (lane & 15) ^ (row & 15);
+        dma16s(kb, (uint32_t)(((int64_t)row * xld + hoff + c * 8) * 2),
+               __builtin_amdgcn_readfirstlane(ks0 + buf * KBUF + j * 4 * kHD * 2));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KI; ++j) {
+        const int row = (wave * KI + j) * 4 + (lane >> 4);
+        const int key = min(x0 + row, xn - 1);
+        const int c = (lane & 15) ^ (row & 15);
+        dma16v(xk + (int64_t)key * xld + hoff + c * 8,
+               __builtin_amdgcn_readfirstlane(ks0 + buf * KBUF + j * 4 * kHD * 2));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VI; ++j) {
+      const int d = (wave * VI + j) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((d >> 1) & 7);
+      dma16s(uni(xvt + x0), (uint32_t)(((int64_t)d * xldv + c * 8) * 2),
+             __builtin_amdgcn_readfirstlane(vs0 + buf * VBUF + j * 8 * kBKV * 2));
+    }
+  };
+  auto issue = [&](int buf, int it) {
+    if (EXTRA && it >= nm) {
+      issue_extra(buf, (it - nm) * kBKV);
+      return;
+    }
+    const int kv0 = it * kBKV;
     const bool in0 = kv0 + kBKV <= kv.n0, in1 = kv0 >= kv.n0;
     if ((in0 || in1) && kv0 + kBKV <= seq) {
       const bf16* kb = in0 ? static_cast<const bf16*>(kv.base0) + b * kv.bs0 + (int64_t)kv0 * kv.ld
@@ -170,12 +227,13 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
   for (int c = 0; c < 4; ++c) voff[c] = v_off(l32, 2 * c + g);
 
   // one key tile; CUR = its LDS buffer (compile time, so every LDS offset is immediate);
-  // MASK: the tile reaches past the sequence (only the last tile of the sequence can)
+  // MASK: the tile reaches past its keys (the last tile of the sequence, and of the extra
+  // keys), whose count in the tile is `lim`
   auto tile = [&](int it, auto cur_c, auto mask_c) {
     constexpr int cur = decltype(cur_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
-    const int kv0 = it * kBKV;
-    if (it + 1 < t_end) issue(cur ^ 1, kv0 + kBKV);
+    const int lim = (EXTRA && it >= nm) ? xn - (it - nm) * kBKV : seq - it * kBKV;
+    if (it + 1 < t_end) issue(cur ^ 1, it + 1);
 
     // S^T = K Q^T: s[h] covers MFMA rows of key block h (keys 32 h + key_perm(row))
     f32x16 s[2];
@@ -196,7 +254,7 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kv0 + 32 * h + 16 * (r >> 3) + 8 * g + (r & 7) >= seq) s[h][r] = -INFINITY;
+          if (32 * h + 16 * (r >> 3) + 8 * g + (r & 7) >= lim) s[h][r] = -INFINITY;
     }
 
     // online softmax in the log2 domain with a lazily updated maximum: the exponentials
@@ -261,26 +319,42 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     __syncthreads();
   };
 
-  issue(t_begin & 1, t_begin * kBKV);
+  issue(t_begin & 1, t_begin);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   using Buf0 = std::integral_constant<int, 0>;
   using Buf1 = std::integral_constant<int, 1>;
   using NoMask = std::false_type;
-  // tiles [t_begin, t_full) lie inside the sequence; a partial last tile is masked
-  const int t_full = min(t_end, seq / kBKV);
-  int it = t_begin;
-  if (it < t_full && (it & 1)) tile(it++, Buf1{}, NoMask{});
-  for (; it + 1 < t_full; it += 2) {
-    tile(it, Buf0{}, NoMask{});
-    tile(it + 1, Buf1{}, NoMask{});
-  }
-  if (it < t_full) tile(it++, Buf0{}, NoMask{});
-  if (it < t_end) {
-    if (it & 1)
-      tile(it, Buf1{}, std::true_type{});
-    else
-      tile(it, Buf0{}, std::true_type{});
+  using Mask = std::true_type;
+  if constexpr (EXTRA) {
+    // up to two partial tiles: the sequence's last and the extra keys' last
+    for (int it = t_begin; it < t_end; ++it) {
+      const bool mk = (it == nm - 1 && (seq % kBKV) != 0) ||
+                      (it == ntiles - 1 && (xn % kBKV) != 0);
+      if (it & 1) {
+        if (mk) tile(it, Buf1{}, Mask{});
+        else tile(it, Buf1{}, NoMask{});
+      } else {
+        if (mk) tile(it, Buf0{}, Mask{});
+        else tile(it, Buf0{}, NoMask{});
+      }
+    }
+  } else {
+    // tiles [t_begin, t_full) lie inside the sequence; a partial last tile is masked
+    const int t_full = min(t_end, seq / kBKV);
+    int it = t_begin;
+    if (it < t_full && (it & 1)) tile(it++, Buf1{}, NoMask{});
+    for (; it + 1 < t_full; it += 2) {
+      tile(it, Buf0{}, NoMask{});
+      tile(it + 1, Buf1{}, NoMask{});
+    }
+    if (it < t_full) tile(it++, Buf0{}, NoMask{});
+    if (it < t_end) {
+      if (it & 1)
+        tile(it, Buf1{}, Mask{});
+      else
+        tile(it, Buf0{}, Mask{});
+    }
   }
 
   // lane owns query l32 and dims 32 dt + 8 (r/4) + 4 g + r%4
@@ -362,7 +436,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
 // fp32 path (tiny fp32 workloads): one wave per (query, head); each lane owns 2 dims.
 __global__ __launch_bounds__(64) void attn_f32_kernel(SeqView qv, SeqView kv,
                                                       const float* __restrict__ vt, int64_t ld_vt,
-                                                      int dim, SeqView ov, int seq, float scale) {
+                                                      int dim, SeqView ov, int seq, float scale,
+                                                      KvExtra xkv) {
   const int lane = threadIdx.x;
   const int qi = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const int d = head * kHD + 2 * lane;
@@ -380,6 +455,22 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(SeqView qv, SeqView kv,
     o0 = o0 * a + p * v0[j];
     o1 = o1 * a + p * v1[j];
     m = m_new;
+  }
+  if (xkv.n > 0) {
+    const int bx = b % xkv.nb;
+    const float* xk = static_cast<const float*>(xkv.k) + bx * xkv.bs + d;
+    const float* xv0 = static_cast<const float*>(xkv.vt) + ((int64_t)bx * dim + d) * xkv.ld_vt;
+    const float* xv1 = xv0 + xkv.ld_vt;
+    for (int j = 0; j < xkv.n; ++j) {
+      const float* kp = xk + (int64_t)j * xkv.ld;
+      const float s = wave_sum(q0 * kp[0] + q1 * kp[1]) * scale;
+      const float m_new = fmaxf(m, s);
+      const float a = expf(m - m_new), p = expf(s - m_new);
+      l = l * a + p;
+      o0 = o0 * a + p * xv0[j];
+      o1 = o1 * a + p * xv1[j];
+      m = m_new;
+    }
   }
   float* op = seq_mptr<float>(ov, b, qi) + d;
   op[0] = o0 / l;
@@ -400,15 +491,15 @@ static int attn_waves(int seq, int heads, int batch) {
 constexpr int kAttnSlots = 2 * 256;
 size_t attention_split_bytes() { return (size_t)kAttnSlots * 128 * (kHD + 2) * sizeof(float); }
 
-template <int NW>
+template <int NW, bool EXTRA>
 static hipError_t launch_flash(SeqView q, SeqView k, const bf16* vt, int64_t ld_vt, int dim,
                                SeqView o, int batch, int seq, int heads, float* split_ws,
-                               hipStream_t s) {
+                               const KvExtra& x, hipStream_t s) {
   constexpr int QPU = 32 * NW;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHD);
   const int nqb = (seq + QPU - 1) / QPU;
   const int units = nqb * heads * batch;
-  const int ntiles = (seq + kBKV - 1) / kBKV;
+  const int ntiles = (seq + kBKV - 1) / kBKV + (EXTRA ? (x.n + kBKV - 1) / kBKV : 0);
   // split the partial last round along the keys (at least 4 key tiles per range)
   int tail = units % kAttnSlots, splits = 1;
   if (split_ws != nullptr && tail > 0 && 2 * tail <= kAttnSlots) {
@@ -421,8 +512,8 @@ static hipError_t launch_flash(SeqView q, SeqView k, const bf16* vt, int64_t ld_
   }
   const int full = units - tail;
   const int grid = full + tail * splits;
-  hipLaunchKernelGGL(flash_attn_bf16_kernel<NW>, dim3(grid), dim3(64 * NW), 0, s, q, k, vt, ld_vt,
-                     dim, o, seq, scale_log2, nqb, heads, full, splits, split_ws);
+  hipLaunchKernelGGL((flash_attn_bf16_kernel<NW, EXTRA>), dim3(grid), dim3(64 * NW), 0, s, q, k, vt,
+                     ld_vt, dim, o, seq, scale_log2, nqb, heads, full, splits, split_ws, x);
   if (tail > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -435,18 +526,26 @@ static hipError_t launch_flash(SeqView q, SeqView k, const bf16* vt, int64_t ld_
 }
 
 hipError_t attention(int dtype, SeqView q, SeqView k, const void* vt, int64_t ld_vt, SeqView o,
-                     int batch, int seq, int heads, float* split_ws, hipStream_t s) {
+                     int batch, int seq, int heads, float* split_ws, hipStream_t s,
+                     const KvExtra* extra) {
   if (seq <= 0 || batch <= 0) return hipSuccess;
   const int dim = heads * kHD;
+  KvExtra x{};
+  x.nb = 1;
+  if (extra != nullptr && extra->n > 0) x = *extra;
   if (dtype == DT_BF16) {
     const bf16* v = static_cast<const bf16*>(vt);
+    // extra keys: 4-wave workgroups only (the 2-wave variant of the extra-source path does
+    // not fit the register budget)
+    if (x.n > 0)
+      return launch_flash<4, true>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, x, s);
     if (attn_waves(seq, heads, batch) == 4)
-      return launch_flash<4>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, s);
-    return launch_flash<2>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, s);
+      return launch_flash<4, false>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, x, s);
+    return launch_flash<2, false>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, x, s);
   } else {
     dim3 grid(seq, heads, batch);
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(64), 0, s, q, k, static_cast<const float*>(vt),
-                       ld_vt, dim, o, seq, 1.f / sqrtf((float)kHD));
+                       ld_vt, dim, o, seq, 1.f / sqrtf((float)kHD), x);
   }
   return hipGetLastError();
 }

@@ -324,6 +324,18 @@ static int64_t vt_pitch(int L) { return ((int64_t)L + 63) / 64 * 64; }
 // ------------------------------------------------------------------------------------
 // double-stream block
 // ------------------------------------------------------------------------------------
+// One block's slot of the reference K/V cache: the reference tokens' q | k rows (k after
+// RMSNorm + RoPE; q is only used while the cache is filled) and their V^T.
+struct RefSlot {
+  void* qk;       // [B * n, 2D]
+  void* vt;       // [B * D, vt_pitch(n)]
+  int n;          // reference tokens per batch item
+};
+// How a block call uses its slot: not at all; it computes the reference tokens themselves
+// (writes the slot; the block's image stream / sequence IS the references); it attends to
+// them as extra keys.
+enum RefUse { REF_NONE = 0, REF_FILL = 1, REF_KEYS = 2 };
+
 struct DoubleScratch {
   void* ln[2];    // [B*N_s, D] compute dtype       (0 = txt, 1 = img)
   void* qk[2];    // [B*N_s, 2D] q | k
@@ -370,24 +382,44 @@ static int check_stream(const flux_stream_weights* w, const char* nm) {
 }
 
 // in[s] / out[s]: stream residuals [B*N_s, D] of in_dt / out_dt; mods[s]: [B, 6D] f32
+// Slot of the reference cache as extra attention keys
+static KvExtra extra_keys(const flux_cfg* c, const RefSlot* ref, int B) {
+  KvExtra x{};
+  const int D = c->dim, es = esize(c->dtype);
+  x.k = static_cast<const char*>(ref->qk) + (size_t)D * es;  // k columns of the q | k rows
+  x.bs = (int64_t)ref->n * 2 * D;
+  x.ld = 2 * D;
+  x.vt = ref->vt;
+  x.ld_vt = vt_pitch(ref->n);
+  x.n = ref->n;
+  x.nb = B;
+  return x;
+}
+
+// ref_use == REF_FILL: Nt must be 0 and the image stream is the reference tokens; their
+// q | k and V^T go to the slot.  REF_KEYS: the slot's tokens are extra keys of the
+// attention.
 static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B, int Ni, int Nt,
                       const void* in[2], int in_dt, void* out[2], int out_dt,
                       const float* mods[2], const float2* cs, const DoubleScratch& d,
-                      hipStream_t s) {
+                      hipStream_t s, const RefSlot* ref = nullptr, int ref_use = REF_NONE) {
   const int D = c->dim, H = c->mlp_hidden, T = c->dtype;
   const int n[2] = {Nt, Ni};
   const int64_t mbs = 6 * (int64_t)D;
   const int L = Nt + Ni;
   const int64_t ldvt = vt_pitch(L);
+  const bool fill = ref_use == REF_FILL;
+  void* qk[2] = {d.qk[0], fill ? ref->qk : d.qk[1]};
+  void* vtb = fill ? ref->vt : d.vt;
   for (int i = 0; i < 2; ++i) {
     if (n[i] == 0) continue;
     const int rows = B * n[i];
     HIP_TRY(layernorm_modulate(in_dt, T, in[i], D, d.ln[i], D, rows, D, n[i], mods[i],
                                mods[i] + D, mbs, c->eps, s));
-    CHECK(lin_qkv(c, rows, d.ln[i], sw[i]->qkv, d.qk[i], d.vt, ldvt, i == 0 ? 0 : Nt, n[i], s,
+    CHECK(lin_qkv(c, rows, d.ln[i], sw[i]->qkv, qk[i], vtb, ldvt, i == 0 ? 0 : Nt, n[i], s,
                   d.split));
   }
-  if (ldvt > L) HIP_TRY(zero_cols(T, d.vt, ldvt, (int64_t)B * D, L, (int)ldvt, s));
+  if (ldvt > L) HIP_TRY(zero_cols(T, vtb, ldvt, (int64_t)B * D, L, (int)ldvt, s));
   // joint views: segment 0 = text rows, segment 1 = image rows
   const int es = esize(T);
   auto view = [&](int col, void* const* bufs, int64_t ld) {
@@ -400,11 +432,14 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
     v.n0 = Nt;
     return v;
   };
-  SeqView qv = view(0, d.qk, 2 * D), kv = view(D, d.qk, 2 * D);
+  SeqView qv = view(0, qk, 2 * D), kv = view(D, qk, 2 * D);
   SeqView ov = view(0, d.o, D);
   HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, sw[0]->q_norm, sw[0]->k_norm, sw[1]->q_norm,
                        sw[1]->k_norm, cs, c->eps, s));
-  HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, d.split, s));
+  KvExtra xk{};
+  if (ref_use == REF_KEYS) xk = extra_keys(c, ref, B);
+  HIP_TRY(attention(T, qv, kv, vtb, ldvt, ov, B, L, c->heads, d.split, s,
+                    ref_use == REF_KEYS ? &xk : nullptr));
   for (int i = 0; i < 2; ++i) {
     if (n[i] == 0) continue;
     const int rows = B * n[i];
@@ -515,20 +550,38 @@ static int check_single_w(const flux_single_weights* w, bool with_mod) {
 }
 
 // x: merged [B*L, D] of in_dt; out: [B*L, D] of out_dt (may alias x); mod [B, 3D]
+// ref_use == REF_FILL: the sequence is the reference tokens; their q | k and V^T go to the
+// slot, and with kv_only the block stops there (the last block: its output is not needed).
+// REF_KEYS: the slot's tokens are extra keys of the attention.
 static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, int L, const void* x,
                       int in_dt, void* out, int out_dt, const float* mod, const float2* cs,
-                      const SingleScratch& d, hipStream_t s) {
+                      const SingleScratch& d, hipStream_t s, const RefSlot* ref = nullptr,
+                      int ref_use = REF_NONE, bool kv_only = false) {
   const int D = c->dim, H = c->mlp_hidden, T = c->dtype, es = esize(T);
   const int rows = B * L;
   const int64_t mbs = 3 * (int64_t)D, ldc = D + H;
+  const bool fill = ref_use == REF_FILL;
+  void* qkb = fill ? ref->qk : d.qk;
+  void* vtb = fill ? ref->vt : d.vt;
   HIP_TRY(layernorm_modulate(in_dt, T, x, D, d.ln, D, rows, D, L, mod, mod + D, mbs, c->eps, s));
   const int64_t ldvt = vt_pitch(L);
   {
     TimedSite ts(FLUX_SITE_SINGLE_QKV, s);
-    CHECK(lin_qkv(c, rows, d.ln, w->linear1, d.qk, d.vt, ldvt, 0, L, s, d.split));
+    CHECK(lin_qkv(c, rows, d.ln, w->linear1, qkb, vtb, ldvt, 0, L, s, d.split));
   }
-  if (ldvt > L) HIP_TRY(zero_cols(T, d.vt, ldvt, (int64_t)B * D, L, (int)ldvt, s));
+  if (ldvt > L) HIP_TRY(zero_cols(T, vtb, ldvt, (int64_t)B * D, L, (int)ldvt, s));
   const char* w_mlp = static_cast<const char*>(w->linear1) + (size_t)3 * D * D * es;
+  if (kv_only) {
+    SeqView qv, kv;
+    qv.base0 = qv.base1 = qkb;
+    kv.base0 = kv.base1 = static_cast<char*>(qkb) + (size_t)D * es;
+    qv.bs0 = qv.bs1 = kv.bs0 = kv.bs1 = (int64_t)L * 2 * D;
+    qv.ld = kv.ld = 2 * D;
+    qv.n0 = kv.n0 = L;
+    HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, w->q_norm, w->k_norm, w->q_norm, w->k_norm,
+                         cs, c->eps, s));
+    return FLUX_OK;
+  }
   {
     TimedSite ts(FLUX_SITE_SINGLE_MLP_IN, s);
     CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln, D, w_mlp, D,
@@ -543,13 +596,16 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
     v.n0 = L;
     return v;
   };
-  SeqView qv = view(d.qk, 0, 2 * D), kv = view(d.qk, D, 2 * D);
+  SeqView qv = view(qkb, 0, 2 * D), kv = view(qkb, D, 2 * D);
   SeqView ov = view(d.cat, 0, ldc);
   HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, w->q_norm, w->k_norm, w->q_norm, w->k_norm, cs,
                        c->eps, s));
   {
     TimedSite ts(FLUX_SITE_SINGLE_ATTENTION, s);
-    HIP_TRY(attention(T, qv, kv, d.vt, ldvt, ov, B, L, c->heads, d.split, s));
+    KvExtra xk{};
+    if (ref_use == REF_KEYS) xk = extra_keys(c, ref, B);
+    HIP_TRY(attention(T, qv, kv, vtb, ldvt, ov, B, L, c->heads, d.split, s,
+                      ref_use == REF_KEYS ? &xk : nullptr));
   }
   TimedSite ts(FLUX_SITE_SINGLE_LINEAR2, s);
   CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D + H, d.cat, ldc, w->linear2, D + H, out, D, out_dt,
@@ -711,9 +767,15 @@ static int check_model(const flux_cfg* c, const flux_model_weights* w, int B, in
 }
 
 // launch sequence of one validated step; ws holds flux_denoiser_step_workspace_size bytes
+static RefSlot ref_slot(const flux_cfg* c, const void* cache, int B, int Nr, int layer);
+
+// launch sequence of one validated step; ws holds flux_denoiser_step_workspace_size bytes.
+// With a reference cache (Nr > 0), every block also attends to its slot's reference keys.
 static int run_step(const flux_cfg* c, const flux_model_weights* w, const float* t, int B,
                     int Ni, int Nt, const void* x, const void* ctx, const int32_t* img_ids,
-                    const int32_t* txt_ids, float* out, void* ws, hipStream_t s) {
+                    const int32_t* txt_ids, float* out, void* ws, hipStream_t s,
+                    const void* cache = nullptr, int Nr = 0) {
+  const int use = (cache != nullptr && Nr > 0) ? REF_KEYS : REF_NONE;
   const int D = c->dim, L = Ni + Nt, T = c->dtype;
   Carver cv(ws);
   StepBufs sb = carve_step(cv, c, B, Ni, Nt);
@@ -740,16 +802,20 @@ static int run_step(const flux_cfg* c, const flux_model_weights* w, const float*
   const float* md[2] = {sb.mod_dtxt, sb.mod_dimg};
   for (int i = 0; i < c->n_double; ++i) {
     const flux_stream_weights* sw[2] = {&w->double_blocks[i].txt, &w->double_blocks[i].img};
-    CHECK(run_double(c, sw, B, Ni, Nt, in, FLUX_F32, io, FLUX_F32, md, sb.rb.cs, sb.d, s));
+    const RefSlot slot = use ? ref_slot(c, cache, B, Nr, i) : RefSlot{};
+    CHECK(run_double(c, sw, B, Ni, Nt, in, FLUX_F32, io, FLUX_F32, md, sb.rb.cs, sb.d, s, &slot,
+                     use));
   }
   // merge [txt ; img] (already merged when B == 1)
   if (B > 1)
     HIP_TRY(copy_rows(FLUX_F32, stream_view(sb.res_txt, sb.res_img, Nt, Ni, D), FLUX_F32,
                       merged_view(sb.res, L, D), B, L, D, s));
   // single-stream blocks
-  for (int i = 0; i < c->n_single; ++i)
+  for (int i = 0; i < c->n_single; ++i) {
+    const RefSlot slot = use ? ref_slot(c, cache, B, Nr, c->n_double + i) : RefSlot{};
     CHECK(run_single(c, &w->single_blocks[i], B, L, sb.res, FLUX_F32, sb.res, FLUX_F32,
-                     sb.mod_single, sb.rb.cs, sb.sg, s));
+                     sb.mod_single, sb.rb.cs, sb.sg, s, &slot, use));
+  }
   // head: keep image tokens, final LayerNorm + modulate, proj_out
   for (int b = 0; b < B; ++b) {
     const float* rows = sb.res + ((size_t)b * L + Nt) * D;
@@ -920,6 +986,222 @@ extern "C" int flux_generation_ids(int grid_h, int grid_w, int n_txt, int32_t* i
   CHECK(need(img_ids, "img_ids"));
   if (n_txt > 0) CHECK(need(txt_ids, "txt_ids"));
   HIP_TRY(generation_ids(img_ids, grid_h, grid_w, txt_ids, n_txt, static_cast<hipStream_t>(stream)));
+  return FLUX_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// reference-image K/V cache ([DIFF] 参考图 KV 缓存机制: Flux2KVLayerCache per block,
+// extract / cached modes; [KLEIN] Infra, KV 缓存).  Reference tokens attend only to
+// reference tokens and are modulated at the fixed timestep 0, so their K/V do not depend
+// on the noisy image, the text or t: the extract step is the reference-only forward that
+// fills the cache (flux_ref_cache_fill) followed by the cached step.
+// ------------------------------------------------------------------------------------
+static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+static void ref_slot_bytes(const flux_cfg* c, int B, int Nr, size_t& qk, size_t& vt) {
+  const int es = esize(c->dtype);
+  qk = align256((size_t)B * Nr * 2 * c->dim * es);
+  vt = align256((size_t)B * c->dim * vt_pitch(Nr) * es);
+}
+
+static RefSlot ref_slot(const flux_cfg* c, const void* cache, int B, int Nr, int layer) {
+  size_t qk, vt;
+  ref_slot_bytes(c, B, Nr, qk, vt);
+  char* base = const_cast<char*>(static_cast<const char*>(cache)) + (size_t)layer * (qk + vt);
+  return RefSlot{base, base + qk, Nr};
+}
+
+extern "C" size_t flux_ref_cache_size(const flux_cfg* c, int B, int Nr) {
+  if (check_cfg(c) != FLUX_OK || B <= 0 || Nr <= 0 || c->n_double < 0 || c->n_single < 0)
+    return 0;
+  size_t qk, vt;
+  ref_slot_bytes(c, B, Nr, qk, vt);
+  return (size_t)(c->n_double + c->n_single) * (qk + vt);
+}
+
+static int check_cache(const flux_cfg* c, const void* cache, size_t bytes, int B, int Nr) {
+  const size_t want = flux_ref_cache_size(c, B, Nr);
+  if (!cache) return fail(FLUX_EINVAL, "cache is NULL");
+  if (reinterpret_cast<uintptr_t>(cache) & 255u)
+    return fail(FLUX_EALIGN, "cache is not 256-byte aligned");
+  if (bytes < want) return fail(FLUX_EWORKSPACE, "cache has %zu bytes, need %zu", bytes, want);
+  return FLUX_OK;
+}
+
+extern "C" size_t flux_ref_cache_fill_workspace_size(const flux_cfg* c, int B, int Nr) {
+  if (check_cfg(c) != FLUX_OK || check_sizes(B, Nr, 0) != FLUX_OK) return 0;
+  Carver cv(nullptr);
+  carve_step(cv, c, B, Nr, 0);
+  cv.take<float>((size_t)B);
+  return cv.off;
+}
+
+static int run_ref_fill(const flux_cfg* c, const flux_model_weights* w, int B, int Nr,
+                        const void* ref_x, const int32_t* ref_ids, void* cache, void* ws,
+                        hipStream_t s) {
+  const int D = c->dim, T = c->dtype;
+  Carver cv(ws);
+  StepBufs sb = carve_step(cv, c, B, Nr, 0);
+  float* t0 = cv.take<float>((size_t)B);
+  HIP_TRY(sampler_update(T, nullptr, nullptr, 0, 0.f, 0.f, false, nullptr, t0, B, 0.f, s));
+  CHECK(run_cond(c, &w->temb, t0, B, sb.cb, s));
+  HIP_TRY(gemv(T, w->mod_double_img, 6 * D, D, sb.cb.stemb, B, false, false, sb.mod_dimg, s));
+  HIP_TRY(gemv(T, w->mod_single, 3 * D, D, sb.cb.stemb, B, false, false, sb.mod_single, s));
+  HIP_TRY(rope_table(ref_ids, ref_ids, 0, Nr, c->axes_dim, c->rope_theta, sb.rb.pos, sb.rb.cs, s));
+  CHECK(lin(c, EPI_STORE, B * Nr, D, c->in_channels, ref_x, c->in_channels, w->img_in,
+            c->in_channels, sb.res_img, D, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s, sb.d.split));
+  const void* in[2] = {sb.res_txt, sb.res_img};
+  void* io[2] = {sb.res_txt, sb.res_img};
+  const float* md[2] = {sb.mod_dimg, sb.mod_dimg};
+  for (int i = 0; i < c->n_double; ++i) {
+    const flux_stream_weights* sw[2] = {&w->double_blocks[i].txt, &w->double_blocks[i].img};
+    const RefSlot slot = ref_slot(c, cache, B, Nr, i);
+    CHECK(run_double(c, sw, B, Nr, 0, in, FLUX_F32, io, FLUX_F32, md, sb.rb.cs, sb.d, s, &slot,
+                     REF_FILL));
+  }
+  if (B > 1)
+    HIP_TRY(copy_rows(FLUX_F32, stream_view(sb.res_txt, sb.res_img, 0, Nr, D), FLUX_F32,
+                      merged_view(sb.res, Nr, D), B, Nr, D, s));
+  for (int i = 0; i < c->n_single; ++i) {
+    const RefSlot slot = ref_slot(c, cache, B, Nr, c->n_double + i);
+    CHECK(run_single(c, &w->single_blocks[i], B, Nr, sb.res, FLUX_F32, sb.res, FLUX_F32,
+                     sb.mod_single, sb.rb.cs, sb.sg, s, &slot, REF_FILL, i == c->n_single - 1));
+  }
+  return FLUX_OK;
+}
+
+extern "C" int flux_ref_cache_fill(const flux_cfg* c, const flux_model_weights* w, int B, int Nr,
+                                   const void* ref_x, const int32_t* ref_ids, void* cache,
+                                   size_t cache_bytes, void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_model(c, w, B, Nr, 0));
+  CHECK(need(ref_x, "ref_x"));
+  CHECK(need(ref_ids, "ref_ids"));
+  CHECK(check_cache(c, cache, cache_bytes, B, Nr));
+  CHECK(check_ws(ws, ws_bytes, flux_ref_cache_fill_workspace_size(c, B, Nr)));
+  return run_ref_fill(c, w, B, Nr, ref_x, ref_ids, cache, ws, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int flux_denoiser_step_cached(const flux_cfg* c, const flux_model_weights* w,
+                                         const float* t, int B, int Ni, int Nt, int Nr,
+                                         const void* x, const void* ctx, const int32_t* img_ids,
+                                         const int32_t* txt_ids, const void* cache,
+                                         size_t cache_bytes, float* out, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  CHECK(check_model(c, w, B, Ni, Nt));
+  if (Nr <= 0) return fail(FLUX_EINVAL, "n_ref must be > 0 (got %d)", Nr);
+  if (!t) return fail(FLUX_EINVAL, "t is NULL");
+  CHECK(need(x, "x"));
+  CHECK(need(out, "out"));
+  if (!img_ids) return fail(FLUX_EINVAL, "img_ids is NULL");
+  if (Nt > 0) {
+    CHECK(need(ctx, "ctx"));
+    if (!txt_ids) return fail(FLUX_EINVAL, "txt_ids is NULL");
+  }
+  CHECK(check_cache(c, cache, cache_bytes, B, Nr));
+  CHECK(check_ws(ws, ws_bytes, flux_denoiser_step_workspace_size(c, B, Ni, Nt)));
+  return run_step(c, w, t, B, Ni, Nt, x, ctx, img_ids, txt_ids, out, ws,
+                  static_cast<hipStream_t>(stream), cache, Nr);
+}
+
+// sampling with reference latents [B, R, C, ref_h, ref_w]: packed references (ids
+// (1 + j, r, c, 0)), the cache filled once (use_cache) or before every step
+struct RefSampleBufs {
+  float* ref_f;     // packed references [B, Nr, in_ch] fp32
+  void* ref_in;     // the same in the model dtype
+  int32_t* ref_ids;
+  void* cache;
+  void* run_ws;     // step / fill workspace (never used at the same time)
+};
+
+static RefSampleBufs carve_ref_sample(Carver& cv, const flux_cfg* c, int B, int Ni, int Nt,
+                                      int Nr) {
+  RefSampleBufs r;
+  const size_t tok = (size_t)B * Nr * c->in_channels;
+  r.ref_f = cv.take<float>(tok);
+  r.ref_in = cv.take<char>(tok * esize(c->dtype));
+  r.ref_ids = cv.take<int32_t>((size_t)Nr * 4);
+  r.cache = cv.take<char>(flux_ref_cache_size(c, B, Nr));
+  const size_t a = flux_denoiser_step_workspace_size(c, B, Ni, Nt);
+  const size_t f = flux_ref_cache_fill_workspace_size(c, B, Nr);
+  r.run_ws = cv.take<char>(a > f ? a : f);
+  return r;
+}
+
+extern "C" size_t flux_denoise_refs_workspace_size(const flux_cfg* c, int B, int latent_h,
+                                                   int latent_w, int Nt, int n_refs, int ref_h,
+                                                   int ref_w) {
+  if (check_cfg(c) != FLUX_OK || c->in_channels <= 0 || c->in_channels % 8) return 0;
+  const int C = c->in_channels / 4;
+  if (check_latent(B, C, latent_h, latent_w) != FLUX_OK || n_refs <= 0 ||
+      check_latent(B * n_refs, C, ref_h, ref_w) != FLUX_OK)
+    return 0;
+  const int Ni = (latent_h / 2) * (latent_w / 2), Nr = n_refs * (ref_h / 2) * (ref_w / 2);
+  if (check_sizes(B, Ni, Nt) != FLUX_OK) return 0;
+  Carver cv(nullptr);
+  SampleBufs sb = carve_sample(cv, c, B, Ni, Nt, false);
+  (void)sb;
+  carve_ref_sample(cv, c, B, Ni, Nt, Nr);
+  return cv.off;
+}
+
+extern "C" int flux_denoise_refs(const flux_cfg* c, const flux_model_weights* w, int n_steps,
+                                 const float* sigmas, int B, int latent_h, int latent_w, int Nt,
+                                 const float* noise, const void* ctx, int n_refs, int ref_h,
+                                 int ref_w, const float* refs, int use_cache, float* latents_out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(c));
+  if (c->in_channels <= 0 || c->in_channels % 8)
+    return fail(FLUX_ESHAPE, "in_channels must be a positive multiple of 8");
+  const int C = c->in_channels / 4;
+  CHECK(check_latent(B, C, latent_h, latent_w));
+  if (n_refs <= 0) return fail(FLUX_EINVAL, "n_refs must be > 0 (use flux_denoise without)");
+  CHECK(check_latent(B * n_refs, C, ref_h, ref_w));
+  if (n_steps <= 0 || n_steps > 10000) return fail(FLUX_EINVAL, "n_steps must be in [1, 10000]");
+  std::vector<float> sig(n_steps + 1);
+  for (int i = 0; i <= n_steps; ++i)
+    sig[i] = sigmas ? sigmas[i] : (float)(1.0 - (double)i / n_steps);
+  for (int i = 0; i <= n_steps; ++i) {
+    if (!std::isfinite(sig[i])) return fail(FLUX_EINVAL, "sigmas[%d] is not finite", i);
+    if (i > 0 && !(sig[i] < sig[i - 1]))
+      return fail(FLUX_EINVAL, "sigmas must decrease strictly (sigmas[%d] >= sigmas[%d])", i,
+                  i - 1);
+  }
+  const int gh = ref_h / 2, gw = ref_w / 2;
+  const int Ni = (latent_h / 2) * (latent_w / 2), Nr = n_refs * gh * gw;
+  CHECK(check_model(c, w, B, Ni, Nt));
+  CHECK(check_sizes(B, Nr, 0));
+  CHECK(need(noise, "noise"));
+  CHECK(need(refs, "refs"));
+  CHECK(need(latents_out, "latents_out"));
+  if (Nt > 0) CHECK(need(ctx, "ctx"));
+  CHECK(check_ws(ws, ws_bytes, flux_denoise_refs_workspace_size(c, B, latent_h, latent_w, Nt,
+                                                                 n_refs, ref_h, ref_w)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = c->dtype;
+  Carver cv(ws);
+  SampleBufs sb = carve_sample(cv, c, B, Ni, Nt, false);
+  RefSampleBufs rb = carve_ref_sample(cv, c, B, Ni, Nt, Nr);
+  const int64_t n = (int64_t)B * Ni * c->in_channels;
+
+  HIP_TRY(generation_ids(sb.img_ids, latent_h / 2, latent_w / 2, sb.txt_ids, Nt, s));
+  for (int j = 0; j < n_refs; ++j)
+    HIP_TRY(generation_ids(rb.ref_ids + (size_t)j * gh * gw * 4, gh, gw, nullptr, 0, s, 1 + j));
+  // references as [B * R] latents -> [B, R * gh * gw] tokens, then the model dtype
+  HIP_TRY(pack_latents(refs, rb.ref_f, B * n_refs, C, ref_h, ref_w, s));
+  HIP_TRY(sampler_update(T, rb.ref_f, nullptr, (int64_t)B * Nr * c->in_channels, 0.f, 0.f,
+                         false, rb.ref_in, nullptr, 0, 0.f, s));
+  HIP_TRY(pack_latents(noise, sb.x, B, C, latent_h, latent_w, s));
+  for (int i = 0; i < n_steps; ++i) {
+    if (i == 0 || !use_cache)
+      CHECK(run_ref_fill(c, w, B, Nr, rb.ref_in, rb.ref_ids, rb.cache, rb.run_ws, s));
+    HIP_TRY(sampler_update(T, sb.x, i ? sb.v : nullptr, n, i ? sig[i] - sig[i - 1] : 0.f, 1.f,
+                           false, sb.xin, sb.t, B, sig[i], s));
+    CHECK(run_step(c, w, sb.t, B, Ni, Nt, sb.xin, ctx, sb.img_ids, sb.txt_ids, sb.v, rb.run_ws,
+                   s, rb.cache, Nr));
+  }
+  HIP_TRY(sampler_update(T, sb.x, sb.v, n, sig[n_steps] - sig[n_steps - 1], 1.f, false, nullptr,
+                         nullptr, 0, 0.f, s));
+  HIP_TRY(unpack_latents(sb.x, latents_out, B, C, latent_h, latent_w, s));
   return FLUX_OK;
 }
 

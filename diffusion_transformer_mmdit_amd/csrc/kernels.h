@@ -83,8 +83,20 @@ hipError_t qk_norm_rope(int dtype, SeqView q, SeqView k, int batch, int seq, int
 // vt[(b * heads * 128 + f) * ld_vt + j] = V[b, j, f], with ld_vt a multiple of 64 and the
 // columns [seq, ld_vt) finite (zero).  split_ws (attention_split_bytes() of device memory,
 // or null to run every unit whole) holds the partial outputs of key-split units.
+// Optional extra keys and values appended after the `seq` keys of the view (a reference
+// K/V cache): key j (< n) of batch b is k + bb * bs + j * ld (head h at columns
+// [128 h, 128 h + 128)), its values column j of the rows bb * dim + f of vt (ld_vt a
+// multiple of 64, columns [n, ld_vt) finite), with bb = b % nb.
+struct KvExtra {
+  const void* k;
+  int64_t bs, ld;
+  const void* vt;
+  int64_t ld_vt;
+  int n, nb;
+};
 hipError_t attention(int dtype, SeqView q, SeqView k, const void* vt, int64_t ld_vt, SeqView o,
-                     int batch, int seq, int heads, float* split_ws, hipStream_t s);
+                     int batch, int seq, int heads, float* split_ws, hipStream_t s,
+                     const KvExtra* extra = nullptr);
 size_t attention_split_bytes();
 
 // vt[(b * dim + f) * ld_vt + j] = v(b, j)[f] for j < seq

@@ -9,9 +9,9 @@ namespace flux {
 // channel 4 ch + 2 ph + pw of patch (r, c) in row-major patch order.
 hipError_t pack_latents(const float* z, float* x, int B, int C, int H, int W, hipStream_t s);
 hipError_t unpack_latents(const float* x, float* z, int B, int C, int H, int W, hipStream_t s);
-// img_ids [gh * gw, 4] = (0, r, c, 0) row-major; txt_ids [n_txt, 4] = (0, 0, 0, i)
+// img_ids [gh * gw, 4] = (t_axis, r, c, 0) row-major; txt_ids [n_txt, 4] = (0, 0, 0, i)
 hipError_t generation_ids(int32_t* img_ids, int gh, int gw, int32_t* txt_ids, int n_txt,
-                          hipStream_t s);
+                          hipStream_t s, int t_axis = 0);
 // x[0 .. n) += dt * v_eff (n % 4 == 0, 16-byte aligned), v_eff = v or, guided,
 // v[i] for the conditional half and v[n + i] for the unconditional: v_u + g (v_c - v_u).
 // v == nullptr leaves x unchanged.  xin (optional, xin_dtype): model input = new x, written

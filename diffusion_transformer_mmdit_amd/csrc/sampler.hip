@@ -52,13 +52,13 @@ __global__ void unpack_latents_kernel(const float* __restrict__ x, float* __rest
   *reinterpret_cast<float2*>(dst + W) = make_float2(v.z, v.w);
 }
 
-// image token (r, c) -> (0, r, c, 0) row-major; text token i -> (0, 0, 0, i)
+// image token (r, c) -> (t_axis, r, c, 0) row-major; text token i -> (0, 0, 0, i)
 __global__ void generation_ids_kernel(int32_t* __restrict__ img_ids, int gh, int gw,
-                                      int32_t* __restrict__ txt_ids, int n_txt) {
+                                      int32_t* __restrict__ txt_ids, int n_txt, int t_axis) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int n_img = gh * gw;
   if (idx < n_img) {
-    *reinterpret_cast<int4*>(img_ids + 4 * idx) = make_int4(0, idx / gw, idx % gw, 0);
+    *reinterpret_cast<int4*>(img_ids + 4 * idx) = make_int4(t_axis, idx / gw, idx % gw, 0);
   } else if (idx < n_img + n_txt) {
     const int i = idx - n_img;
     *reinterpret_cast<int4*>(txt_ids + 4 * i) = make_int4(0, 0, 0, i);
@@ -128,11 +128,11 @@ hipError_t unpack_latents(const float* x, float* z, int B, int C, int H, int W, 
 }
 
 hipError_t generation_ids(int32_t* img_ids, int gh, int gw, int32_t* txt_ids, int n_txt,
-                          hipStream_t s) {
+                          hipStream_t s, int t_axis) {
   const int n = gh * gw + n_txt;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(generation_ids_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, img_ids,
-                     gh, gw, txt_ids, n_txt);
+                     gh, gw, txt_ids, n_txt, t_axis);
   return hipGetLastError();
 }
 

@@ -97,6 +97,18 @@ _PROTOS = {
     "flux_denoise_workspace_size": (c_size, [P(flux_cfg), c_int, c_int, c_int, c_int, c_int]),
     "flux_denoise": (c_int, [P(flux_cfg), P(flux_model_weights), c_int, vp, ctypes.c_float, c_int,
                              c_int, c_int, c_int, vp, vp, vp, vp, vp, c_size, vp]),
+    "flux_ref_cache_size": (c_size, [P(flux_cfg), c_int, c_int]),
+    "flux_ref_cache_fill_workspace_size": (c_size, [P(flux_cfg), c_int, c_int]),
+    "flux_ref_cache_fill": (c_int, [P(flux_cfg), P(flux_model_weights), c_int, c_int, vp, vp, vp,
+                                    c_size, vp, c_size, vp]),
+    "flux_denoiser_step_cached": (c_int, [P(flux_cfg), P(flux_model_weights), vp, c_int, c_int,
+                                          c_int, c_int, vp, vp, vp, vp, vp, c_size, vp, vp,
+                                          c_size, vp]),
+    "flux_denoise_refs_workspace_size": (c_size, [P(flux_cfg), c_int, c_int, c_int, c_int, c_int,
+                                                  c_int, c_int]),
+    "flux_denoise_refs": (c_int, [P(flux_cfg), P(flux_model_weights), c_int, vp, c_int, c_int,
+                                  c_int, c_int, vp, vp, c_int, c_int, c_int, vp, c_int, vp, vp,
+                                  c_size, vp]),
     "flux_pack_latents": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp]),
     "flux_unpack_latents": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp]),
     "flux_generation_ids": (c_int, [c_int, c_int, c_int, vp, vp, vp]),
@@ -308,6 +320,55 @@ def flux_denoise(cfg, w, n_steps, sigmas, guidance_scale, batch, latent_h, laten
                               float(guidance_scale), batch, latent_h, latent_w, n_txt, _ptr(noise),
                               _ptr(ctx), _ptr(ctx_uncond), _ptr(latents_out), _ptr(workspace),
                               workspace_bytes, _stream(stream)))
+
+
+def flux_ref_cache_size(cfg, batch, n_ref) -> int:
+    return lib().flux_ref_cache_size(ctypes.byref(cfg), batch, n_ref)
+
+
+def flux_ref_cache_fill_workspace_size(cfg, batch, n_ref) -> int:
+    return lib().flux_ref_cache_fill_workspace_size(ctypes.byref(cfg), batch, n_ref)
+
+
+def flux_ref_cache_fill(cfg, w, batch, n_ref, ref_x, ref_ids, cache, cache_bytes, workspace,
+                        workspace_bytes, stream=None):
+    ws = w.struct if isinstance(w, ModelWeights) else w
+    _check(lib().flux_ref_cache_fill(ctypes.byref(cfg), ctypes.byref(ws), batch, n_ref,
+                                     _ptr(ref_x), _ptr(ref_ids), _ptr(cache), cache_bytes,
+                                     _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def flux_denoiser_step_cached(cfg, w, t, batch, n_img, n_txt, n_ref, x, ctx, img_ids, txt_ids,
+                              cache, cache_bytes, out, workspace, workspace_bytes, stream=None):
+    ws = w.struct if isinstance(w, ModelWeights) else w
+    _check(lib().flux_denoiser_step_cached(ctypes.byref(cfg), ctypes.byref(ws), _ptr(t), batch,
+                                           n_img, n_txt, n_ref, _ptr(x), _ptr(ctx), _ptr(img_ids),
+                                           _ptr(txt_ids), _ptr(cache), cache_bytes, _ptr(out),
+                                           _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def flux_denoise_refs_workspace_size(cfg, batch, latent_h, latent_w, n_txt, n_refs, ref_h,
+                                     ref_w) -> int:
+    return lib().flux_denoise_refs_workspace_size(ctypes.byref(cfg), batch, latent_h, latent_w,
+                                                  n_txt, n_refs, ref_h, ref_w)
+
+
+def flux_denoise_refs(cfg, w, n_steps, sigmas, batch, latent_h, latent_w, n_txt, noise, ctx,
+                      n_refs, ref_h, ref_w, refs, use_cache, latents_out, workspace,
+                      workspace_bytes, stream=None):
+    ws = w.struct if isinstance(w, ModelWeights) else w
+    sig = None
+    if sigmas is not None:
+        vals = [float(v) for v in sigmas]
+        if len(vals) != n_steps + 1:
+            raise FluxError(FLUX_EINVAL, f"need {n_steps + 1} sigmas, got {len(vals)}")
+        sig = (ctypes.c_float * len(vals))(*vals)
+    _check(lib().flux_denoise_refs(ctypes.byref(cfg), ctypes.byref(ws), n_steps,
+                                   ctypes.cast(sig, ctypes.c_void_p) if sig is not None else None,
+                                   batch, latent_h, latent_w, n_txt, _ptr(noise), _ptr(ctx),
+                                   n_refs, ref_h, ref_w, _ptr(refs), int(bool(use_cache)),
+                                   _ptr(latents_out), _ptr(workspace), workspace_bytes,
+                                   _stream(stream)))
 
 
 def flux_pack_latents(batch, channels, h, w, z, tokens, stream=None):

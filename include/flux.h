@@ -225,6 +225,57 @@ int flux_denoise(const flux_cfg* cfg, const flux_model_weights* w, int n_steps,
                  int n_txt, const float* noise, const void* ctx, const void* ctx_uncond,
                  float* latents_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Reference-image K/V cache ([DIFF] 参考图 KV 缓存机制: per-block cache of the reference
+ * tokens' K/V after RoPE; extract mode runs [txt, ref, img] with reference tokens attending
+ * only to reference tokens, modulated at the fixed timestep 0; cached mode runs [txt, img]
+ * with the cached reference K/V among the keys; [KLEIN] Infra, KV 缓存: step 0 extracts,
+ * later steps reuse).  Since reference tokens see only reference tokens at a fixed
+ * timestep, their K/V do not depend on the noisy image, the text or t, so the extract step
+ * is flux_ref_cache_fill followed by flux_denoiser_step_cached, with identical results.
+ *
+ * cache: device memory of flux_ref_cache_size(cfg, batch, n_ref) bytes, 256-byte aligned,
+ * owned by the caller; one slot per block (double blocks, then single blocks), each holding
+ * the reference tokens' q | k rows [batch * n_ref, 2 * dim] (k after RMSNorm + RoPE) and
+ * their values transposed [batch * dim, n_ref rounded up to 64] (cfg->dtype).
+ *
+ * flux_ref_cache_fill: the reference-only forward.
+ *   ref_x   device [batch, n_ref, in_channels] (cfg->dtype): packed reference latents
+ *   ref_ids device int32 [n_ref, 4] (shared by the batch; flux_denoise_refs uses
+ *           (1 + j, r, c, 0) for reference j)
+ *   workspace flux_ref_cache_fill_workspace_size(cfg, batch, n_ref) bytes, 256-byte aligned
+ * flux_denoiser_step_cached: flux_denoiser_step (same arguments and workspace size, without
+ *   guidance) whose attention in every block also covers the cache's n_ref reference keys.
+ * Errors (nothing enqueued): FLUX_EINVAL, FLUX_ESHAPE, FLUX_EALIGN, FLUX_EWORKSPACE (also for
+ * a cache smaller than flux_ref_cache_size), and the step's own errors. */
+size_t flux_ref_cache_size(const flux_cfg* cfg, int batch, int n_ref);
+size_t flux_ref_cache_fill_workspace_size(const flux_cfg* cfg, int batch, int n_ref);
+int flux_ref_cache_fill(const flux_cfg* cfg, const flux_model_weights* w, int batch, int n_ref,
+                        const void* ref_x, const int32_t* ref_ids, void* cache, size_t cache_bytes,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int flux_denoiser_step_cached(const flux_cfg* cfg, const flux_model_weights* w, const float* t,
+                              int batch, int n_img, int n_txt, int n_ref, const void* x,
+                              const void* ctx, const int32_t* img_ids, const int32_t* txt_ids,
+                              const void* cache, size_t cache_bytes, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Sampling conditioned on reference latents (the editing path of the pages' KV variant):
+ * flux_denoise without guidance, where every step also attends to the reference tokens.
+ *   refs  device fp32 [batch, n_refs, in_channels/4, ref_h, ref_w] (ref_h, ref_w even);
+ *         reference j is packed like the noise and gets ids (1 + j, r, c, 0)
+ *   use_cache  1: the cache is filled once, before the first step (extract, then cached);
+ *              0: it is filled again before every step (the references recomputed each step;
+ *              same result, bit for bit)
+ *   workspace flux_denoise_refs_workspace_size(...) bytes (it holds the cache)
+ * Errors as flux_denoise, and FLUX_EINVAL for n_refs <= 0. */
+size_t flux_denoise_refs_workspace_size(const flux_cfg* cfg, int batch, int latent_h,
+                                        int latent_w, int n_txt, int n_refs, int ref_h,
+                                        int ref_w);
+int flux_denoise_refs(const flux_cfg* cfg, const flux_model_weights* w, int n_steps,
+                      const float* sigmas, int batch, int latent_h, int latent_w, int n_txt,
+                      const float* noise, const void* ctx, int n_refs, int ref_h, int ref_w,
+                      const float* refs, int use_cache, float* latents_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* 2x2 latent packing used by flux_denoise ([KLEIN] Visual tokenizer / VAE):
  * tokens[b, r * (W/2) + c, 4 ch + 2 ph + pw] = z[b, ch, 2 r + ph, 2 c + pw].
  *   z       device fp32 [batch, channels, H, W] (H, W even);  tokens device fp32

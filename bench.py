@@ -234,7 +234,9 @@ def cpu_baseline(wl, flops_step: float):
 # per-workload block timings and bandwidth-kernel rates
 # ------------------------------------------------------------------------------------
 PER_CONFIG = ("tiny_single_f32", "klein4b_single_512", "klein9b_double_1024",
-              "klein9b_step_1024", "dev_pair_2048", "klein9b_generate_1024")
+              "klein9b_step_1024", "dev_pair_2048", "klein9b_generate_1024", "klein9b_edit_1024")
+# editing cells (reference images, output side in pixels) of the pages' K/V cache table
+EDIT_CELLS = ((1, 512), (1, 1024), (2, 1024), (4, 1024))
 
 
 def _time_ms(fn, s, warmup=3, reps=10):
@@ -298,11 +300,64 @@ def generate_line(F, fs, wl) -> dict:
     return res
 
 
+def edit_line(F, fs, wl) -> dict:
+    """4-step generations conditioned on 1024^2 reference latents: the reference K/V cache
+    filled once (extract, then cached steps) against filled before every step (the
+    references recomputed each step); the cached steps' single-block attention (joint
+    sequence + reference keys) timed with the library's event hook."""
+    import torch
+    dtype = torch.bfloat16
+    w = device_weights(fs.step_weight_specs(wl), wl.seed, dtype)
+    mw = F.ModelWeights(w, wl.n_double, wl.n_single)
+    cfg = F.make_cfg(wl.dim, wl.heads, wl.mlp_hidden, in_channels=wl.in_channels,
+                     context_dim=wl.context_dim, n_double=wl.n_double, n_single=wl.n_single)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed)
+    C = wl.in_channels // 4
+    ctx = torch.randn((1, wl.n_txt, wl.context_dim), generator=g, device="cuda").to(dtype)
+    s = torch.cuda.current_stream()
+    res = {"workload": wl.name, "dtype": wl.dtype, "n_steps": 4, "reference_side": 1024,
+           "cells": []}
+    for n_refs, side in EDIT_CELLS:
+        lat = side // 8                      # 8x VAE downsampling: latent side
+        ref_lat = 1024 // 8
+        noise = torch.randn((1, C, lat, lat), generator=g, device="cuda")
+        refs = torch.randn((1, n_refs, C, ref_lat, ref_lat), generator=g, device="cuda")
+        out = torch.empty_like(noise)
+        nb = F.flux_denoise_refs_workspace_size(cfg, 1, lat, lat, wl.n_txt, n_refs, ref_lat,
+                                                ref_lat)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        cell = {"refs": n_refs, "output": side}
+        for use_cache, key in ((True, "cached"), (False, "recomputed")):
+            fn = lambda: F.flux_denoise_refs(cfg, mw, 4, None, 1, lat, lat, wl.n_txt, noise, ctx,
+                                             n_refs, ref_lat, ref_lat, refs, use_cache, out, ws,
+                                             nb, s)
+            if use_cache:
+                fn()
+                F.flux_timing_begin(F.FLUX_SITE_SINGLE_ATTENTION, 4 * wl.n_single)
+                fn()
+                n_att, att_us = F.flux_timing_end()
+                Lq = wl.n_txt + (lat // 2) ** 2
+                Lk = Lq + n_refs * (ref_lat // 2) ** 2
+                cell["attention_us"] = round(att_us, 1)
+                cell["attention_tflops"] = round(4.0 * Lq * Lk * wl.dim / (att_us * 1e-6) / 1e12,
+                                                 1)
+            cell[f"{key}_ms"] = round(_time_ms(fn, s, warmup=1, reps=2), 2)
+        cell["speedup"] = round(cell["recomputed_ms"] / cell["cached_ms"], 3)
+        res["cells"].append(cell)
+        del ws, noise, refs, out
+        torch.cuda.empty_cache()
+    del w, mw
+    return res
+
+
 def per_config_line(F, fs, name: str) -> dict:
     import torch
     wl = fs.workload(name)
     if wl.kind == "generate":
         return generate_line(F, fs, wl)
+    if wl.kind == "edit":
+        return edit_line(F, fs, wl)
     dtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     fdt = F.FLUX_BF16 if wl.dtype == "bf16" else F.FLUX_F32
     D, H, B = wl.dim, wl.mlp_hidden, wl.batch

@@ -55,6 +55,30 @@ FLUX_DEV int key_perm(int m) {
   return 16 * (q >> 1) + 8 * g + 4 * (q & 1) + t;
 }
 
+// Direct loads with operands forced into scalar registers (readfirstlane; a no-op for
+// values the compiler already holds there).  The extra-key variant of the kernel uses them:
+// with its second key source the compiler no longer proves these operands uniform itself.
+FLUX_DEV const void* uniform_ptr(const void* p) {
+  const uint64_t u = reinterpret_cast<uintptr_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+template <bool U>
+FLUX_DEV void dma_s(const void* base, uint32_t voff, uint32_t lds) {
+  if constexpr (U)
+    dma16s(uniform_ptr(base), voff, __builtin_amdgcn_readfirstlane(lds));
+  else
+    dma16s(base, voff, lds);
+}
+template <bool U>
+FLUX_DEV void dma_v(const void* g, uint32_t lds) {
+  if constexpr (U)
+    dma16v(g, __builtin_amdgcn_readfirstlane(lds));
+  else
+    dma16v(g, lds);
+}
+
 // Unit u = (b * heads + head) * nqb + qb (query blocks of one head are consecutive, so a
 // run of units on one XCD shares that head's K and V in L2).
 FLUX_DEV int attn_xcd_remap(int bid, int total) {
@@ -114,19 +138,34 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
   constexpr int KI = 16 / NW;  // K instructions per wave per tile (64 rows / 4)
   constexpr int VI = 16 / NW;  // V instructions per wave per tile (128 rows / 8)
   const bf16* vt_head = vt + ((int64_t)b * dim + hoff) * ld_vt;
-  uint32_t k_voff[KI], v_voff[VI];
-#pragma unroll
-  for (int j = 0; j < KI; ++j) {
+  // per-lane byte offsets of load j of a K tile (row stride ld) and a V^T tile (ld_v)
+  auto k_lane_off = [&](int j, int64_t ld) __attribute__((always_inline)) {
     const int row = (wave * KI + j) * 4 + (lane >> 4);
     const int c = (lane & 15) ^ (row & 15);
-    k_voff[j] = (uint32_t)(((int64_t)row * kv.ld + hoff + c * 8) * 2);
-  }
-#pragma unroll
-  for (int j = 0; j < VI; ++j) {
+    return (uint32_t)(((int64_t)row * ld + hoff + c * 8) * 2);
+  };
+  auto v_lane_off = [&](int j, int64_t ld_v) __attribute__((always_inline)) {
     const int d = (wave * VI + j) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((d >> 1) & 7);
-    v_voff[j] = (uint32_t)(((int64_t)d * ld_vt + c * 8) * 2);
+    return (uint32_t)(((int64_t)d * ld_v + c * 8) * 2);
+  };
+  // the plain kernel keeps them in registers; the extra-key variant, short of registers,
+  // recomputes them per tile
+  uint32_t k_voff[EXTRA ? 1 : KI], v_voff[EXTRA ? 1 : VI];
+  if constexpr (!EXTRA) {
+#pragma unroll
+    for (int j = 0; j < KI; ++j) k_voff[j] = k_lane_off(j, kv.ld);
+#pragma unroll
+    for (int j = 0; j < VI; ++j) v_voff[j] = v_lane_off(j, ld_vt);
   }
+  auto kvo = [&](int j) __attribute__((always_inline)) {
+    if constexpr (EXTRA) return k_lane_off(j, kv.ld);
+    else return k_voff[j];
+  };
+  auto vvo = [&](int j) __attribute__((always_inline)) {
+    if constexpr (EXTRA) return v_lane_off(j, ld_vt);
+    else return v_voff[j];
+  };
   const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ks0 = __builtin_amdgcn_readfirstlane(lds_u32(&Ks[0][0])) + wv * KI * 4 * kHD * 2;
   const uint32_t vs0 = __builtin_amdgcn_readfirstlane(lds_u32(&Vs[0][0])) + wv * VI * 8 * kBKV * 2;
@@ -147,41 +186,26 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     xldv = xkv.ld_vt;
     xn = xkv.n;
   }
-  auto uni = [](const bf16* p) {  // a wave-uniform pointer, in scalar registers
-    const uint64_t u = reinterpret_cast<uintptr_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-    return reinterpret_cast<const bf16*>(((uint64_t)hi << 32) | lo);
-  };
-  auto issue_extra = [&](int buf, int x0) {
+  auto issue_extra = [&](int buf, int x0) __attribute__((always_inline)) {
     if (x0 + kBKV <= xn) {
-      const bf16* kb = uni(xk + (int64_t)x0 * xld);
+      const bf16* kb = xk + (int64_t)x0 * xld;
 #pragma unroll
-      for (int j = 0; j < KI; ++j) {
-        const int row = (wave * KI + j) * 4 + (lane >> 4);
-        const int c = (lane & 15) ^ (row & 15);
-        dma16s(kb, (uint32_t)(((int64_t)row * xld + hoff + c * 8) * 2),
-               __builtin_amdgcn_readfirstlane(ks0 + buf * KBUF + j * 4 * kHD * 2));
-      }
+      for (int j = 0; j < KI; ++j)
+        dma_s<true>(kb, k_lane_off(j, xld), ks0 + buf * KBUF + j * 4 * kHD * 2);
     } else {
 #pragma unroll
       for (int j = 0; j < KI; ++j) {
         const int row = (wave * KI + j) * 4 + (lane >> 4);
         const int key = min(x0 + row, xn - 1);
         const int c = (lane & 15) ^ (row & 15);
-        dma16v(xk + (int64_t)key * xld + hoff + c * 8,
-               __builtin_amdgcn_readfirstlane(ks0 + buf * KBUF + j * 4 * kHD * 2));
+        dma_v<true>(xk + (int64_t)key * xld + hoff + c * 8, ks0 + buf * KBUF + j * 4 * kHD * 2);
       }
     }
 #pragma unroll
-    for (int j = 0; j < VI; ++j) {
-      const int d = (wave * VI + j) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((d >> 1) & 7);
-      dma16s(uni(xvt + x0), (uint32_t)(((int64_t)d * xldv + c * 8) * 2),
-             __builtin_amdgcn_readfirstlane(vs0 + buf * VBUF + j * 8 * kBKV * 2));
-    }
+    for (int j = 0; j < VI; ++j)
+      dma_s<true>(xvt + x0, v_lane_off(j, xldv), vs0 + buf * VBUF + j * 8 * kBKV * 2);
   };
-  auto issue = [&](int buf, int it) {
+  auto issue = [&](int buf, int it) __attribute__((always_inline)) {
     if (EXTRA && it >= nm) {
       issue_extra(buf, (it - nm) * kBKV);
       return;
@@ -193,18 +217,19 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
                            : static_cast<const bf16*>(kv.base1) + b * kv.bs1 +
                                  (int64_t)(kv0 - kv.n0) * kv.ld;
 #pragma unroll
-      for (int j = 0; j < KI; ++j) dma16s(kb, k_voff[j], ks0 + buf * KBUF + j * 4 * kHD * 2);
+      for (int j = 0; j < KI; ++j) dma_s<EXTRA>(kb, kvo(j), ks0 + buf * KBUF + j * 4 * kHD * 2);
     } else {
 #pragma unroll
       for (int j = 0; j < KI; ++j) {
         const int row = (wave * KI + j) * 4 + (lane >> 4);
         const int key = min(kv0 + row, seq - 1);  // past the end: a valid row, masked later
         const int c = (lane & 15) ^ (row & 15);
-        dma16v(seq_cptr<bf16>(kv, b, key) + hoff + c * 8, ks0 + buf * KBUF + j * 4 * kHD * 2);
+        dma_v<EXTRA>(seq_cptr<bf16>(kv, b, key) + hoff + c * 8, ks0 + buf * KBUF + j * 4 * kHD * 2);
       }
     }
 #pragma unroll
-    for (int j = 0; j < VI; ++j) dma16s(vt_head + kv0, v_voff[j], vs0 + buf * VBUF + j * 8 * kBKV * 2);
+    for (int j = 0; j < VI; ++j)
+      dma_s<EXTRA>(vt_head + kv0, vvo(j), vs0 + buf * VBUF + j * 8 * kBKV * 2);
   };
 
   f32x16 o[4];
@@ -229,7 +254,7 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
   // one key tile; CUR = its LDS buffer (compile time, so every LDS offset is immediate);
   // MASK: the tile reaches past its keys (the last tile of the sequence, and of the extra
   // keys), whose count in the tile is `lim`
-  auto tile = [&](int it, auto cur_c, auto mask_c) {
+  auto tile = [&](int it, auto cur_c, auto mask_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
     const int lim = (EXTRA && it >= nm) ? xn - (it - nm) * kBKV : seq - it * kBKV;
@@ -326,19 +351,27 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
   using Buf1 = std::integral_constant<int, 1>;
   using NoMask = std::false_type;
   using Mask = std::true_type;
-  if constexpr (EXTRA) {
-    // up to two partial tiles: the sequence's last and the extra keys' last
-    for (int it = t_begin; it < t_end; ++it) {
-      const bool mk = (it == nm - 1 && (seq % kBKV) != 0) ||
-                      (it == ntiles - 1 && (xn % kBKV) != 0);
-      if (it & 1) {
-        if (mk) tile(it, Buf1{}, Mask{});
-        else tile(it, Buf1{}, NoMask{});
-      } else {
-        if (mk) tile(it, Buf0{}, Mask{});
-        else tile(it, Buf0{}, NoMask{});
-      }
+  // tiles [t0, t1) of one key source whose tile t_last is partial when `partial`
+  auto run_tiles = [&](int t0, int t1, int t_last, bool partial) __attribute__((always_inline)) {
+    const int t_full = partial ? min(t1, t_last) : t1;
+    int it = t0;
+    if (it < t_full && (it & 1)) tile(it++, Buf1{}, NoMask{});
+    for (; it + 1 < t_full; it += 2) {
+      tile(it, Buf0{}, NoMask{});
+      tile(it + 1, Buf1{}, NoMask{});
     }
+    if (it < t_full) tile(it++, Buf0{}, NoMask{});
+    if (it < t1) {
+      if (it & 1)
+        tile(it, Buf1{}, Mask{});
+      else
+        tile(it, Buf0{}, Mask{});
+    }
+  };
+  if constexpr (EXTRA) {
+    // the sequence's own tiles, then the extra source's (each may end with a partial tile)
+    run_tiles(t_begin, min(t_end, nm), nm - 1, (seq % kBKV) != 0);
+    run_tiles(max(t_begin, nm), t_end, ntiles - 1, (xn % kBKV) != 0);
   } else {
     // tiles [t_begin, t_full) lie inside the sequence; a partial last tile is masked
     const int t_full = min(t_end, seq / kBKV);

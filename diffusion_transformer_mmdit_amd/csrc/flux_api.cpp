@@ -566,7 +566,7 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
   HIP_TRY(layernorm_modulate(in_dt, T, x, D, d.ln, D, rows, D, L, mod, mod + D, mbs, c->eps, s));
   const int64_t ldvt = vt_pitch(L);
   {
-    TimedSite ts(FLUX_SITE_SINGLE_QKV, s);
+    TimedSite ts(fill ? 0 : FLUX_SITE_SINGLE_QKV, s);
     CHECK(lin_qkv(c, rows, d.ln, w->linear1, qkb, vtb, ldvt, 0, L, s, d.split));
   }
   if (ldvt > L) HIP_TRY(zero_cols(T, vtb, ldvt, (int64_t)B * D, L, (int)ldvt, s));
@@ -583,7 +583,7 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
     return FLUX_OK;
   }
   {
-    TimedSite ts(FLUX_SITE_SINGLE_MLP_IN, s);
+    TimedSite ts(fill ? 0 : FLUX_SITE_SINGLE_MLP_IN, s);
     CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln, D, w_mlp, D,
               static_cast<char*>(d.cat) + (size_t)D * es, ldc, T, nullptr, 0, 0, nullptr, 0, 1,
               s, d.split));
@@ -601,13 +601,13 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
   HIP_TRY(qk_norm_rope(T, qv, kv, B, L, c->heads, w->q_norm, w->k_norm, w->q_norm, w->k_norm, cs,
                        c->eps, s));
   {
-    TimedSite ts(FLUX_SITE_SINGLE_ATTENTION, s);
+    TimedSite ts(fill ? 0 : FLUX_SITE_SINGLE_ATTENTION, s);
     KvExtra xk{};
     if (ref_use == REF_KEYS) xk = extra_keys(c, ref, B);
     HIP_TRY(attention(T, qv, kv, vtb, ldvt, ov, B, L, c->heads, d.split, s,
                       ref_use == REF_KEYS ? &xk : nullptr));
   }
-  TimedSite ts(FLUX_SITE_SINGLE_LINEAR2, s);
+  TimedSite ts(fill ? 0 : FLUX_SITE_SINGLE_LINEAR2, s);
   CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D + H, d.cat, ldc, w->linear2, D + H, out, D, out_dt,
             x, D, in_dt, mod + 2 * D, mbs, L, s, d.split));
   return FLUX_OK;

@@ -62,7 +62,7 @@ class Workload:
     n_single: int = 0            # single-stream blocks (step only)
     t_fixed: float | None = None # fixed timestep, else drawn U[0,1)
     seed: int = 1000
-    kind: str = "single"         # "single", "double", "pair", "step" or "generate"
+    kind: str = "single"         # "single", "double", "pair", "step", "generate" or "edit"
 
     @property
     def seq(self) -> int:
@@ -97,6 +97,11 @@ WORKLOADS: dict[str, Workload] = {
     "klein9b_generate_1024": Workload("klein9b_generate_1024", 4096, 32, 12288, 4096, 512,
                                       in_channels=128, context_dim=12288, n_double=8,
                                       n_single=24, seed=1006, kind="generate"),
+    # Klein-9B editing with reference images: the generation above conditioned on 1024^2
+    # reference latents (64 x 64 tokens each) through the reference K/V cache.
+    "klein9b_edit_1024": Workload("klein9b_edit_1024", 4096, 32, 12288, 4096, 512,
+                                  in_channels=128, context_dim=12288, n_double=8, n_single=24,
+                                  seed=1007, kind="edit"),
     # FLUX.2-dev-shaped long-sequence block pair at 2048^2 (one double + one single).
     "dev_pair_2048": Workload("dev_pair_2048", 6144, 48, 18432, 16384, 512,
                               seed=1005, kind="pair"),

@@ -136,7 +136,8 @@ const char* flux_version(void);
  * flux_timing_begin(site, max_launches) creates 2*max_launches HIP events and arms `site`:
  * from then on every launch of that site that this process enqueues (from any block or
  * step call) is bracketed by an event pair recorded on the launch's own stream, so the
- * timed calls create nothing.  flux_timing_end waits for the recorded events, returns the
+ * timed calls create nothing (the reference-only forward of flux_ref_cache_fill is not
+ * timed).  flux_timing_end waits for the recorded events, returns the
  * number of timed launches and their mean duration in microseconds, disarms the site and
  * destroys the events.  One site is armed at a time per process; begin while armed
  * discards the previous arming.  Errors: FLUX_EINVAL for an unknown site, a capacity

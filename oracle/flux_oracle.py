@@ -32,9 +32,12 @@ Readings of points the pages leave open (each also listed in the design doc):
     v taken at sigma; guidance v_u + g (v_c - v_u)
   * reference K/V cache: reference image j has ids (1 + j, r, c, 0); all reference tokens
     attend to all reference tokens (one segment); the fixed reference timestep is 0
+  * FP8 linear: OCP E4M3, per-row (activation) and per-output-channel (weight) scales
+    amax / 448, round to nearest even with saturation
 
 Parity pins for every function live in tests/test_oracle_pins.py and, for the sampling
-loop and the reference K/V cache, tests/test_oracle_sampler.py and tests/test_oracle_refkv.py (closed forms, invariants, brute force and an
+loop, the reference K/V cache and the FP8 linear, tests/test_oracle_sampler.py,
+tests/test_oracle_refkv.py and tests/test_oracle_fp8.py (closed forms, invariants, brute force and an
 independent library routine); none is "parity unpinned".
 """
 from __future__ import annotations
@@ -795,3 +798,78 @@ def denoise_with_refs(noise, refs, ctx, w: Mapping, sigmas, n_double: int, n_sin
         if on_step:
             on_step(i)
     return unpack_latents(x, H, W)
+
+
+# ----------------------------------------------------------------------------------
+# FP8 (E4M3) linear layer
+#
+# [KLEIN] Infra (量化): the pages report FP8 versions of the models and their speed-ups but
+# give no recipe.  Reading: OCP E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa
+# bits; largest finite 448, no infinities, S.1111.111 is NaN); values are scaled into
+# range per activation row and per weight row (output channel) by amax / 448, rounded to
+# nearest even with saturation at 448; the layer is y = s_a[m] s_w[n] sum_k qa[m, k] qw[n, k]
+# with fp32 accumulation of the exact fp8 products.
+# ----------------------------------------------------------------------------------
+FP8_MAX = 448.0
+
+
+def fp8_decode(code) -> np.ndarray:
+    """E4M3 byte -> float64 (NaN for the NaN codes)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * val)
+
+
+def fp8_encode(x) -> np.ndarray:
+    """float -> E4M3 byte, round to nearest (ties to even mantissa), magnitudes past 448
+    saturate to 448; NaN -> 0x7F.  Works on the exact value of x (x in float64)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.uint8)
+    flat_x, flat_o = x.ravel(), out.ravel()
+    for i, v in enumerate(flat_x):
+        if np.isnan(v):
+            flat_o[i] = 0x7F
+            continue
+        s = 0x80 if np.signbit(v) else 0
+        a = min(abs(v), FP8_MAX)
+        if a == 0.0:
+            flat_o[i] = s
+            continue
+        # exponent of the binade holding a (subnormals share the binade of 2^-6)
+        e = max(int(np.floor(np.log2(a))), -6)
+        while 2.0 ** e > a and e > -6:     # guard log2 rounding at binade edges
+            e -= 1
+        while 2.0 ** (e + 1) <= a:
+            e += 1
+        q = a / 2.0 ** e * 8.0              # mantissa in units of 2^(e-3), in [8, 16) (or [0, 8))
+        n = np.floor(q)
+        r = q - n
+        if r > 0.5 or (r == 0.5 and int(n) % 2 == 1):
+            n += 1
+        n = int(n)
+        if n == 16:                         # rounded up into the next binade
+            n, e = 8, e + 1
+        if e == -6 and n < 8:
+            code = n                        # subnormal
+        else:
+            code = ((e + 7) << 3) | (n - 8)
+        flat_o[i] = s | min(code, 0x7E)
+    return out
+
+
+def quantize_rows_fp8(x):
+    """Per-row E4M3 quantization: s = amax(|row|) / 448 in fp32 (1 for an all-zero row),
+    q = encode(fp32(x / s)) with the division done in fp32.  Returns (q uint8, s float32)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    s = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    q = fp8_encode((x32 / s[..., None]).astype(np.float32).astype(np.float64))
+    return q, s
+
+
+def linear_fp8(qa, sa, qw, sw) -> np.ndarray:
+    """y[m, n] = sa[m] sw[n] sum_k dec(qa[m, k]) dec(qw[n, k]), exactly (float64)."""
+    return (fp8_decode(qa) * f64(sa)[..., None]) @ (fp8_decode(qw) * f64(sw)[..., None]).T

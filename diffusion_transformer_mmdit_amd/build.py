@@ -21,7 +21,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflux.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "cond.hip", "sampler.hip", "flux_api.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "cond.hip", "sampler.hip", "fp8.hip",
+           "flux_api.cpp"]
 
 
 def hipcc() -> str:

@@ -1353,6 +1353,88 @@ extern "C" int flux_attention(const flux_cfg* c, int B, int seq, const void* q, 
   return FLUX_OK;
 }
 
+// ------------------------------------------------------------------------------------
+// FP8 (E4M3) linear layer ([KLEIN] Infra, 量化: FP8 releases; recipe = reading: per-row
+// amax / 448 scales, round to nearest even, saturating)
+// ------------------------------------------------------------------------------------
+extern "C" int flux_quantize_fp8_rows(int rows, int cols, const void* x, int x_dtype,
+                                      int64_t ldx, void* q, int64_t ldq, float* scales,
+                                      void* stream) {
+  if (rows <= 0 || cols <= 0) return fail(FLUX_EINVAL, "rows and cols must be > 0");
+  if (x_dtype != FLUX_BF16 && x_dtype != FLUX_F32) return fail(FLUX_EDTYPE, "bad x_dtype");
+  if (ldx < cols || ldq < cols) return fail(FLUX_ESHAPE, "ldx and ldq must be >= cols");
+  if (!x || !q || !scales) return fail(FLUX_EINVAL, "x, q and scales are required");
+  HIP_TRY(quantize_fp8_rows(x_dtype, x, ldx, rows, cols, static_cast<uint8_t*>(q), ldq, scales,
+                            static_cast<hipStream_t>(stream)));
+  return FLUX_OK;
+}
+
+extern "C" int flux_linear_fp8(const flux_cfg* c, int epi, int m, int n, int k, const void* qa,
+                               int64_t lda, const float* sa, const void* qw, int64_t ldw,
+                               const float* sw, void* y, int64_t ldy, int y_dtype,
+                               const void* resid, int64_t ldr, const float* gate, int rpb,
+                               void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(c));
+  if (m <= 0 || n <= 0 || k <= 0) return fail(FLUX_EINVAL, "m, n, k must be > 0");
+  if (k % 128) return fail(FLUX_ESHAPE, "k must be a multiple of 128 for the fp8 linear");
+  if (lda < k || ldw < k || lda % 16 || ldw % 16)
+    return fail(FLUX_EALIGN, "lda/ldw must be >= k and multiples of 16 bytes");
+  if ((int64_t)m * lda >= (int64_t{1} << 32) || (int64_t)n * ldw >= (int64_t{1} << 32))
+    return fail(FLUX_ESHAPE, "operands of 4 GiB or more");
+  CHECK(need(qa, "qa"));
+  CHECK(need(qw, "qw"));
+  if (!sa || !sw) return fail(FLUX_EINVAL, "sa and sw are required");
+  if (!y) return fail(FLUX_EINVAL, "y is NULL");
+  float* split = nullptr;
+  if (ws) {
+    if (reinterpret_cast<uintptr_t>(ws) & 255u)
+      return fail(FLUX_EWORKSPACE, "workspace is not 256-byte aligned");
+    if (ws_bytes < linear_splitk_bytes())
+      return fail(FLUX_EWORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes,
+                  linear_splitk_bytes());
+    split = static_cast<float*>(ws);
+  }
+  LinearArgs a{};
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  a.x = qa;
+  a.ldx = lda;
+  a.w = qw;
+  a.ldw = ldw;
+  a.y = y;
+  a.ldy = ldy;
+  a.y_dtype = y_dtype;
+  a.rows_per_batch = 1;
+  a.split_ws = split;
+  if (epi == FLUX_EPI_SWIGLU) {
+    if (n % 2) return fail(FLUX_ESHAPE, "SwiGLU needs an even n");
+    if (ldy < n / 2) return fail(FLUX_ESHAPE, "ldy < n/2");
+    a.epilogue = EPI_SWIGLU;
+  } else {
+    if (y_dtype != FLUX_BF16 && y_dtype != FLUX_F32) return fail(FLUX_EDTYPE, "bad y_dtype");
+    if (ldy < n) return fail(FLUX_ESHAPE, "ldy < n");
+    if (epi == FLUX_EPI_STORE) {
+      a.epilogue = EPI_STORE;
+    } else if (epi == FLUX_EPI_GATED_RESIDUAL) {
+      if (!resid || !gate) return fail(FLUX_EINVAL, "resid and gate are required");
+      if (rpb <= 0 || m % rpb) return fail(FLUX_ESHAPE, "m must be a multiple of rows_per_batch");
+      if (ldr < n) return fail(FLUX_ESHAPE, "ldr < n");
+      a.epilogue = EPI_GATED_RESIDUAL;
+      a.resid = resid;
+      a.ldr = ldr;
+      a.r_dtype = y_dtype;
+      a.gate = gate;
+      a.gate_bs = n;
+      a.rows_per_batch = rpb;
+    } else {
+      return fail(FLUX_EINVAL, "unknown epilogue %d", epi);
+    }
+  }
+  HIP_TRY(linear_fp8(a, sa, sw, static_cast<hipStream_t>(stream)));
+  return FLUX_OK;
+}
+
 extern "C" size_t flux_linear_workspace_size(void) { return linear_splitk_bytes(); }
 
 extern "C" int flux_linear(const flux_cfg* c, int epi, int m, int n, int k, const void* x,

@@ -402,42 +402,53 @@ FLUX_DEV void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   logical_coords(xcd_remap(bid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
-// LDS layout of one operand slice: rows of BK bf16 (BK/8 chunks of 16 bytes).  With
-// 64 banks x 4 bytes (256 bytes) per bank row, 256/(2 BK) consecutive rows share a bank
-// row; XOR-ing the chunk index with (row / rows_per_bank_row) spreads the 16 rows read by
-// 16 lanes of a ds_read_b128 over 16 distinct 16-byte bank groups.
-template <int BK>
+// LDS layout of one operand slice: rows of BK elements of ES bytes (CPR chunks of 16
+// bytes).  With 64 banks x 4 bytes (256 bytes) per bank row, 256 / (16 CPR) consecutive
+// rows share a bank row; XOR-ing the chunk index with (row / rows_per_bank_row) spreads the
+// 16 rows read by 16 lanes of a ds_read_b128 over 16 distinct 16-byte bank groups.
+template <int BK, int ES = 2>
 struct Swz {
-  static constexpr int CPR = BK / 8;
-  static constexpr int RSH = (BK == 64) ? 1 : 2;
+  static constexpr int CE = 16 / ES;  // elements per chunk
+  static constexpr int CPR = BK / CE;
+  static constexpr int RSH = (CPR == 8) ? 1 : 2;
   FLUX_DEV static int slot(int row, int c) { return c ^ ((row >> RSH) & (CPR - 1)); }
-  FLUX_DEV static int off(int row, int c) { return row * BK + (slot(row, c) << 3); }
+  FLUX_DEV static int off(int row, int c) { return row * BK + slot(row, c) * CE; }
 };
 
-template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
-__global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
-    const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw, int M,
-    int N, int K, int n_half, int tiles_m, int tiles_n, int full_tiles, int splits,
-    float* __restrict__ partial, Epi epi) {
-  static_assert(BK == 32 || BK == 64, "BK");
+typedef uint8_t fp8;  // OCP E4M3 byte
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// Body of the large-tile kernels.  TIn = bf16 (MFMA 32x32x16) or fp8 (E4M3 bytes, MFMA
+// 32x32x64 with unit block scales; the accumulators are multiplied by the per-row scale
+// sa[m] and the per-weight-row scale sw[n] before the epilogue).  Rows of a K slice are
+// 64 or 128 bytes either way, so the load plan, the LDS layout and the schedule are shared.
+template <class TIn, int BM, int BN, int BK, int ST, int NWM, int NWN, class Epi>
+FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* __restrict__ W,
+                            int64_t ldw, int M, int N, int K, int n_half, int tiles_m,
+                            int tiles_n, int full_tiles, int splits, float* __restrict__ partial,
+                            Epi epi, const float* __restrict__ sa, const float* __restrict__ sw) {
+  constexpr int ES = sizeof(TIn);
+  constexpr bool F8 = ES == 1;
+  static_assert(BK * ES == 64 || BK * ES == 128, "BK: 64- or 128-byte slice rows");
   static_assert(ST >= 2 && ST <= 4, "stages");
-  using S = Swz<BK>;
+  using S = Swz<BK, ES>;
   constexpr int NWV = NWM * NWN;        // waves per workgroup
-  constexpr int CPR = BK / 8;           // chunks per row
+  constexpr int CPR = S::CPR;           // chunks per row
   constexpr int RPI = 64 / CPR;         // rows per wave load instruction
   constexpr int AI = BM / (NWV * RPI);  // A load instructions per wave per slice
   constexpr int BI = BN / (NWV * RPI);
   constexpr int LOADS = AI + BI;
   constexpr int WTM = BM / NWM, WTN = BN / NWN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int KK = BK / 16;           // MFMA k-steps per slice
+  constexpr int KK = BK / (F8 ? 64 : 16);  // MFMA k-steps per slice
   constexpr int NF = TM + TN;           // fragments per k-step
-  constexpr uint32_t STAGE_B = (BM + BN) * BK * 2;
+  constexpr uint32_t STAGE_B = (BM + BN) * BK * ES;
   static_assert(AI >= 1 && BI >= 1, "tile too small for the load plan");
   static_assert(KK % 2 == 0, "fragment sets alternate with the k-step parity");
   static_assert(!Epi::kPaired || (TN % 2 == 0), "SwiGLU needs gate/up tile pairs");
 
-  extern __shared__ __align__(16) bf16 smem[];
+  extern __shared__ __align__(16) char lds_raw[];
+  TIn* smem = reinterpret_cast<TIn*>(lds_raw);
   // stage s: A rows at smem + s * (BM + BN) * BK, B rows right after
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -468,7 +479,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
   for (int j = 0; j < AI; ++j) {
     const int r = (wave * AI + j) * RPI + lane / CPR;
     const int gr = min(m0 + r, M - 1);
-    a_off[j] = (uint32_t)(((int64_t)gr * lda + S::slot(r, lane % CPR) * 8) * 2);
+    a_off[j] = (uint32_t)(((int64_t)gr * lda + S::slot(r, lane % CPR) * S::CE) * ES);
   }
 #pragma unroll
   for (int j = 0; j < BI; ++j) {
@@ -480,15 +491,15 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
     } else {
       gn = min(gn, N - 1);
     }
-    b_off[j] = (uint32_t)(((int64_t)gn * ldw + S::slot(r, lane % CPR) * 8) * 2);
+    b_off[j] = (uint32_t)(((int64_t)gn * ldw + S::slot(r, lane % CPR) * S::CE) * ES);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_u32(smem));
   auto dma = [&](int q, int stage, int k0) {  // q-th load instruction of this wave's share
     const uint32_t sb = lds0 + (uint32_t)stage * STAGE_B;
     if (q < AI)
-      dma16s(A + k0, a_off[q], sb + (uint32_t)((wave * AI + q) * RPI * BK * 2));
+      dma16s(A + k0, a_off[q], sb + (uint32_t)((wave * AI + q) * RPI * BK * ES));
     else
-      dma16s(W + k0, b_off[q - AI], sb + (uint32_t)(BM * BK * 2 + (wave * BI + q - AI) * RPI * BK * 2));
+      dma16s(W + k0, b_off[q - AI], sb + (uint32_t)(BM * BK * ES + (wave * BI + q - AI) * RPI * BK * ES));
   };
 
   f32x16 acc[TM][TN];
@@ -500,14 +511,21 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int lrow = lane & 31, lk = lane >> 5;
-  bf16x8 fr[2][NF];  // [set][A fragments | B fragments]
+  using Frag = typename std::conditional<F8, v8i, bf16x8>::type;
+  Frag fr[2][NF];  // [set][A fragments | B fragments]
   auto rd = [&](int set, int q, int stage, int kk) {
-    const bf16* base = smem + stage * (BM + BN) * BK;
-    if (q < TM)
-      fr[set][q] = *reinterpret_cast<const bf16x8*>(base + S::off(wm * WTM + q * 32 + lrow, kk * 2 + lk));
-    else
-      fr[set][q] = *reinterpret_cast<const bf16x8*>(base + BM * BK +
-                                                     S::off(wn * WTN + (q - TM) * 32 + lrow, kk * 2 + lk));
+    const TIn* base = smem + stage * (BM + BN) * BK;
+    const TIn* ob = q < TM ? base : base + BM * BK;
+    const int row = q < TM ? wm * WTM + q * 32 + lrow : wn * WTN + (q - TM) * 32 + lrow;
+    if constexpr (F8) {
+      // k-step kk covers chunks 4 kk .. 4 kk + 3 (64 k); lane group lk holds two of them
+      const uint4 lo = *reinterpret_cast<const uint4*>(ob + S::off(row, kk * 4 + 2 * lk));
+      const uint4 hi = *reinterpret_cast<const uint4*>(ob + S::off(row, kk * 4 + 2 * lk + 1));
+      fr[set][q] = Frag{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      fr[set][q] = *reinterpret_cast<const bf16x8*>(ob + S::off(row, kk * 2 + lk));
+    }
   };
 
   const int nk = k_end - k_begin;
@@ -569,7 +587,11 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
 #pragma unroll
       for (int q = 0; q < TM * TN; ++q) {
         const int i = q / TN, j = q % TN;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0);
+        if constexpr (F8)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0, 127, 0, 127);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (do_rd && q < NF) rd(nxt, q, rst, rkk);
         if (q0 + q < q1) dma(q0 + q, dst, dk);
@@ -599,6 +621,30 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
       slice(kt, Off{}, Off{}, Off{});
   }
 
+  if constexpr (F8) {
+    // dequantize: y = sa[m] sw[n] acc (W row of logical column n: the SwiGLU pairing)
+    float swv[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * WTN + j * 32 + lrow;
+      int pn;
+      if constexpr (Epi::kPaired) {
+        const int jj = min(((n >> 6) << 5) + (n & 31), n_half - 1);
+        pn = ((n >> 5) & 1) ? n_half + jj : jj;
+      } else {
+        pn = min(n, N - 1);
+      }
+      swv[j] = sw[pn];
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float av = sa[min(m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3), M - 1)];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j][r] *= av * swv[j];
+      }
+  }
   if (unit >= 0) {
     // split-K unit: raw fp32 partial tile [BM][BN] (local coordinates)
     float* pt = partial + (size_t)unit * BM * BN;
@@ -707,6 +753,27 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
   }
 }
 
+template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
+__global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
+    const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw, int M,
+    int N, int K, int n_half, int tiles_m, int tiles_n, int full_tiles, int splits,
+    float* __restrict__ partial, Epi epi) {
+  gemm_lds_body<bf16, BM, BN, BK, ST, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, n_half, tiles_m,
+                                                     tiles_n, full_tiles, splits, partial, epi,
+                                                     nullptr, nullptr);
+}
+
+template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
+__global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_fp8_lds_kernel(
+    const fp8* __restrict__ A, int64_t lda, const fp8* __restrict__ W, int64_t ldw, int M,
+    int N, int K, int n_half, int tiles_m, int tiles_n, int full_tiles, int splits,
+    float* __restrict__ partial, Epi epi, const float* __restrict__ sa,
+    const float* __restrict__ sw) {
+  gemm_lds_body<fp8, BM, BN, BK, ST, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, n_half, tiles_m,
+                                                    tiles_n, full_tiles, splits, partial, epi, sa,
+                                                    sw);
+}
+
 // Split-K tail: sum the `splits` partial tiles of each tail tile in a fixed order (so the
 // result is deterministic) and apply the fused epilogue.  grid = (tail tiles, chunks);
 // each thread owns 4 consecutive columns of one row (16-byte loads per partial).
@@ -801,8 +868,82 @@ static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t 
   return hipGetLastError();
 }
 
+// Same for the fp8 kernel (K slices of 128 bytes = 128 elements).
+template <int BM, int BN, int ST, int OCC, int NWM, int NWN, class Epi>
+static hipError_t launch_lds_fp8(const fp8* A, int64_t lda, const fp8* W, int64_t ldw, int M,
+                                 int N, int K, int n_half, const Epi& epi, int splits,
+                                 float* partial, const float* sa, const float* sw, hipStream_t s) {
+  constexpr int BK = 128;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int tiles = tiles_m * tiles_n;
+  const int slots = 256 * OCC;
+  const int tail = splits > 1 ? tiles % slots : 0;
+  const int full = tiles - tail;
+  if (tail == 0) splits = 1;
+  const size_t lds = (size_t)ST * (BM + BN) * BK;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_fp8_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemm_fp8_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
+                     dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, A, lda, W, ldw, M,
+                     N, K, n_half, tiles_m, tiles_n, full, splits, partial, epi, sa, sw);
+  if (tail > 0) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int chunks = Epi::kPaired ? BM * BN / 8 / 256 : BM * BN / 4 / 256;
+    hipLaunchKernelGGL((splitk_reduce_kernel<BM, BN, Epi>), dim3(tail, chunks), dim3(256), 0, s,
+                       partial, splits, full, tiles_m, tiles_n, M, N, n_half, epi);
+  }
+  return hipGetLastError();
+}
+
 // Bytes of split-K scratch the large-tile path may use (tail tiles x splits x tile).
 constexpr size_t kSplitkBytes = (size_t)256 * 256 * 256 * sizeof(float);
+
+// Choose the tile configuration (and split-K of the last partial round) with the smallest
+// estimated time.  A round of resident workgroups costs its MACs at about 1 PFLOP/s over
+// the chip (times `rate`: 2 for fp8), scaled by the configuration's relative efficiency; a
+// tail round split s ways along K costs 1/s of a round plus the fp32 partial tiles' round
+// trip through HBM and the reduce launch.  best: 0 = 256x256, 1 = 256x128, 2 = 128x128.
+static void pick_tile(int M, int N, int K, int bk, double rate, bool can_split, int& best,
+                      int& best_split) {
+  const int cus = 256;
+  constexpr double kFlopPerCu = 4.0e12, kHbm = 5.0e12, kReduceLaunch = 3e-6;
+  struct Cand { int bm, bn, occ; double eff; };
+  const Cand cands[3] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.8}, {128, 128, 2, 0.85}};
+  const int nk = K / bk;
+  best = 0;
+  best_split = 1;
+  double best_t = 1e300;
+  for (int c = 0; c < 3; ++c) {
+    const long tiles = (long)((M + cands[c].bm - 1) / cands[c].bm) *
+                       ((N + cands[c].bn - 1) / cands[c].bn);
+    const long slots = (long)cus * cands[c].occ;
+    const double round = 2.0 * cands[c].bm * cands[c].bn * cands[c].occ * (double)K /
+                         cands[c].eff / (kFlopPerCu * rate);
+    const long tail = tiles % slots;
+    const size_t tile_bytes = (size_t)cands[c].bm * cands[c].bn * sizeof(float);
+    double t = (double)((tiles + slots - 1) / slots) * round;
+    int split = 1;
+    // split the tail: s units per tail tile, at least 8 K-slices each
+    if (tail > 0 && can_split && 2 * tail <= slots) {
+      int sp = (int)(slots / tail);
+      sp = sp < nk / 8 ? sp : nk / 8;
+      while (sp > 1 && (size_t)tail * sp * tile_bytes > kSplitkBytes) --sp;
+      if (sp >= 2) {
+        const double ts = (double)(tiles / slots) * round + round / sp +
+                          2.0 * tail * sp * tile_bytes / kHbm + kReduceLaunch;
+        if (ts < t) { t = ts; split = sp; }
+      }
+    }
+    if (t < best_t * 0.999) { best_t = t; best = c; best_split = split; }
+  }
+}
 
 // ------------------------------------------------------------------------------------
 // fp32 path (tiny fp32 workloads): LDS-tiled FMA, 64 x 64 tile, 4 x 4 per thread with
@@ -883,41 +1024,8 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
     const bool off32 = (int64_t)M * lda * 2 < (int64_t{1} << 32) &&
                        (int64_t)N * ldw * 2 < (int64_t{1} << 32);
     if (K % kBK == 0 && off32) {
-      // choose the tile configuration (and split-K of the last partial round) with the
-      // smallest estimated time.  A round of resident workgroups costs its MACs at about
-      // 1 PFLOP/s over the chip, scaled by the configuration's relative efficiency; a tail
-      // round split s ways along K costs 1/s of a round plus the fp32 partial tiles'
-      // round trip through HBM and the reduce launch.
-      const int cus = 256;
-      constexpr double kFlopPerCu = 4.0e12, kHbm = 5.0e12, kReduceLaunch = 3e-6;
-      struct Cand { int bm, bn, occ; double eff; };
-      const Cand cands[3] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.8}, {128, 128, 2, 0.85}};
-      const int nk = K / kBK;
-      int best = 0, best_split = 1;
-      double best_t = 1e300;
-      for (int c = 0; c < 3; ++c) {
-        const long tiles = (long)((M + cands[c].bm - 1) / cands[c].bm) *
-                           ((N + cands[c].bn - 1) / cands[c].bn);
-        const long slots = (long)cus * cands[c].occ;
-        const double round = 2.0 * cands[c].bm * cands[c].bn * cands[c].occ * (double)K /
-                             cands[c].eff / kFlopPerCu;
-        const long tail = tiles % slots;
-        const size_t tile_bytes = (size_t)cands[c].bm * cands[c].bn * sizeof(float);
-        double t = (double)((tiles + slots - 1) / slots) * round;
-        int split = 1;
-        // split the tail: s units per tail tile, at least 8 K-slices each
-        if (tail > 0 && split_ws != nullptr && 2 * tail <= slots) {
-          int sp = (int)(slots / tail);
-          sp = sp < nk / 8 ? sp : nk / 8;
-          while (sp > 1 && (size_t)tail * sp * tile_bytes > kSplitkBytes) --sp;
-          if (sp >= 2) {
-            const double ts = (double)(tiles / slots) * round + round / sp +
-                              2.0 * tail * sp * tile_bytes / kHbm + kReduceLaunch;
-            if (ts < t) { t = ts; split = sp; }
-          }
-        }
-        if (t < best_t * 0.999) { best_t = t; best = c; best_split = split; }
-      }
+      int best, best_split;
+      pick_tile(M, N, K, kBK, 1.0, split_ws != nullptr, best, best_split);
       auto* a = static_cast<const bf16*>(A);
       auto* w = static_cast<const bf16*>(W);
       if (best == 0)
@@ -983,6 +1091,59 @@ static hipError_t linear_t(const LinearArgs& a, hipStream_t s) {
       epi.set_vec();
       return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws);
     }
+  }
+  return hipErrorInvalidValue;
+}
+
+// fp8 linear: operands E4M3 with per-row scales (checked by the caller: K % 128 == 0,
+// 32-bit byte offsets)
+template <class Epi>
+static hipError_t launch_fp8(const LinearArgs& a, const float* sa, const float* sw, int n_half,
+                             const Epi& epi, hipStream_t s) {
+  if (a.m <= 0 || a.n <= 0) return hipSuccess;
+  int best, split;
+  pick_tile(a.m, a.n, a.k, 128, 2.0, a.split_ws != nullptr, best, split);
+  auto* x = static_cast<const fp8*>(a.x);
+  auto* w = static_cast<const fp8*>(a.w);
+  if (best == 0)
+    return launch_lds_fp8<256, 256, 2, 1, 4, 2>(x, a.ldx, w, a.ldw, a.m, a.n, a.k, n_half, epi,
+                                                 split, a.split_ws, sa, sw, s);
+  if (best == 1)
+    return launch_lds_fp8<256, 128, 2, 1, 4, 2>(x, a.ldx, w, a.ldw, a.m, a.n, a.k, n_half, epi,
+                                                 split, a.split_ws, sa, sw, s);
+  return launch_lds_fp8<128, 128, 2, 2, 2, 2>(x, a.ldx, w, a.ldw, a.m, a.n, a.k, n_half, epi,
+                                               split, a.split_ws, sa, sw, s);
+}
+
+template <class TY, class TR>
+static hipError_t gated_fp8(const LinearArgs& a, const float* sa, const float* sw, hipStream_t s) {
+  EpiGatedResid<TY, TR> epi{static_cast<TY*>(a.y), a.ldy, static_cast<const TR*>(a.resid),
+                            a.ldr, a.gate, a.gate_bs, a.rows_per_batch};
+  epi.set_vec();
+  return launch_fp8(a, sa, sw, 0, epi, s);
+}
+
+hipError_t linear_fp8(const LinearArgs& a, const float* sa, const float* sw, hipStream_t s) {
+  switch (a.epilogue) {
+    case EPI_STORE:
+      if (a.y_dtype == DT_F32) {
+        EpiStore<float> epi{static_cast<float*>(a.y), a.ldy};
+        epi.set_vec();
+        return launch_fp8(a, sa, sw, 0, epi, s);
+      } else {
+        EpiStore<bf16> epi{static_cast<bf16*>(a.y), a.ldy};
+        epi.set_vec();
+        return launch_fp8(a, sa, sw, 0, epi, s);
+      }
+    case EPI_SWIGLU:
+      return launch_fp8(a, sa, sw, a.n / 2, EpiSwiGLU<bf16>{static_cast<bf16*>(a.y), a.ldy, a.n / 2},
+                        s);
+    case EPI_GATED_RESIDUAL:
+      if (a.y_dtype == DT_F32)
+        return a.r_dtype == DT_F32 ? gated_fp8<float, float>(a, sa, sw, s)
+                                   : gated_fp8<float, bf16>(a, sa, sw, s);
+      return a.r_dtype == DT_F32 ? gated_fp8<bf16, float>(a, sa, sw, s)
+                                 : gated_fp8<bf16, bf16>(a, sa, sw, s);
   }
   return hipErrorInvalidValue;
 }

@@ -42,6 +42,13 @@ size_t linear_splitk_bytes();
 
 // y = x W^T with epilogue; dtype = type of x and W (DT_BF16 -> MFMA path).
 hipError_t linear(int dtype, const LinearArgs& a, hipStream_t s);
+// fp8 (E4M3) linear: x [m, ldx] and W [n, ldw] bytes, y = sa[m] sw[n] (x W^T) with the
+// epilogue (EPI_STORE, EPI_SWIGLU, EPI_GATED_RESIDUAL); k % 128 == 0.
+hipError_t linear_fp8(const LinearArgs& a, const float* sa, const float* sw, hipStream_t s);
+// Per-row E4M3 quantization of x [rows, ldx] (x_dtype): s[r] = amax(|x[r, :cols]|) / 448
+// (1 for an all-zero row), q[r, c] = E4M3(x / s) rounded to nearest even, saturating.
+hipError_t quantize_fp8_rows(int x_dtype, const void* x, int64_t ldx, int rows, int cols,
+                             uint8_t* q, int64_t ldq, float* s_out, hipStream_t s);
 
 // e[b, :] = [cos(1000 t_b f) | sin(1000 t_b f)], f_k = 10000^(-k/half); e: [batch, 2*half]
 hipError_t timestep_sinusoid(const float* t, int batch, int half, float* e, hipStream_t s);

@@ -109,6 +109,9 @@ _PROTOS = {
     "flux_denoise_refs": (c_int, [P(flux_cfg), P(flux_model_weights), c_int, vp, c_int, c_int,
                                   c_int, c_int, vp, vp, c_int, c_int, c_int, vp, c_int, vp, vp,
                                   c_size, vp]),
+    "flux_quantize_fp8_rows": (c_int, [c_int, c_int, vp, c_int, c_i64, vp, c_i64, vp, vp]),
+    "flux_linear_fp8": (c_int, [P(flux_cfg), c_int, c_int, c_int, c_int, vp, c_i64, vp, vp, c_i64,
+                                vp, vp, c_i64, c_int, vp, c_i64, vp, c_int, vp, c_size, vp]),
     "flux_pack_latents": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp]),
     "flux_unpack_latents": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp]),
     "flux_generation_ids": (c_int, [c_int, c_int, c_int, vp, vp, vp]),
@@ -369,6 +372,20 @@ def flux_denoise_refs(cfg, w, n_steps, sigmas, batch, latent_h, latent_w, n_txt,
                                    n_refs, ref_h, ref_w, _ptr(refs), int(bool(use_cache)),
                                    _ptr(latents_out), _ptr(workspace), workspace_bytes,
                                    _stream(stream)))
+
+
+def flux_quantize_fp8_rows(rows, cols, x, x_dtype, ldx, q, ldq, scales, stream=None):
+    _check(lib().flux_quantize_fp8_rows(rows, cols, _ptr(x), x_dtype, ldx, _ptr(q), ldq,
+                                        _ptr(scales), _stream(stream)))
+
+
+def flux_linear_fp8(cfg, epilogue, m, n, k, qa, lda, sa, qw, ldw, sw, y, ldy, y_dtype, resid=None,
+                    ldr=0, gate=None, rows_per_batch=1, workspace=None, workspace_bytes=0,
+                    stream=None):
+    _check(lib().flux_linear_fp8(ctypes.byref(cfg), epilogue, m, n, k, _ptr(qa), lda, _ptr(sa),
+                                 _ptr(qw), ldw, _ptr(sw), _ptr(y), ldy, y_dtype, _ptr(resid), ldr,
+                                 _ptr(gate), rows_per_batch, _ptr(workspace), workspace_bytes,
+                                 _stream(stream)))
 
 
 def flux_pack_latents(batch, channels, h, w, z, tokens, stream=None):

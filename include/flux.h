@@ -358,6 +358,29 @@ typedef enum {
   FLUX_EPI_SWIGLU = 1,
   FLUX_EPI_GATED_RESIDUAL = 2
 } flux_epilogue;
+/* FP8 (E4M3) linear layer ([KLEIN] Infra, 量化: the pages report FP8 releases and speed-ups;
+ * the recipe is this library's reading).  Codes are OCP E4M3 bytes (bias 7, largest finite
+ * 448, no infinities).
+ *
+ * flux_quantize_fp8_rows: per-row quantization of x [rows, ldx] (x_dtype FLUX_BF16 or
+ *   FLUX_F32, device): scales[r] = amax(|x[r, :cols]|) / 448 (1 for an all-zero row; fp32,
+ *   correctly rounded), q[r, c] = E4M3(x[r, c] / scales[r]) rounded to nearest even with
+ *   saturation at 448 (device bytes [rows, ldq]).  Activation rows and weight rows (output
+ *   channels) are quantized the same way.  Errors: FLUX_EINVAL, FLUX_EDTYPE, FLUX_ESHAPE.
+ * flux_linear_fp8: y = sa[m] sw[n] sum_k dec(qa[m, k]) dec(qw[n, k]) (fp32 accumulation)
+ *   followed by the epilogue of flux_linear (STORE, SWIGLU with bf16 output, GATED_RESIDUAL
+ *   with gate_bs = n).  qa device [m, lda] bytes, qw device [n, ldw] bytes (lda, ldw >= k,
+ *   multiples of 16; operands under 4 GiB), sa device float [m], sw device float [n];
+ *   k % 128 == 0.  workspace as flux_linear.  Errors: FLUX_EINVAL, FLUX_ESHAPE, FLUX_EALIGN,
+ *   FLUX_EDTYPE, FLUX_EWORKSPACE. */
+int flux_quantize_fp8_rows(int rows, int cols, const void* x, int x_dtype, int64_t ldx, void* q,
+                           int64_t ldq, float* scales, void* stream);
+int flux_linear_fp8(const flux_cfg* cfg, int epilogue, int m, int n, int k, const void* qa,
+                    int64_t lda, const float* sa, const void* qw, int64_t ldw, const float* sw,
+                    void* y, int64_t ldy, int y_dtype, const void* resid, int64_t ldr,
+                    const float* gate, int rows_per_batch, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* workspace: NULL, or flux_linear_workspace_size() bytes (256-byte aligned) of scratch that
  * lets the large-tile path split the last partial round of output tiles along K (fp32
  * partials reduced in a fixed order, so results stay deterministic). */

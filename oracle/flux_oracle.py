@@ -825,39 +825,27 @@ def fp8_decode(code) -> np.ndarray:
 
 def fp8_encode(x) -> np.ndarray:
     """float -> E4M3 byte, round to nearest (ties to even mantissa), magnitudes past 448
-    saturate to 448; NaN -> 0x7F.  Works on the exact value of x (x in float64)."""
+    saturate to 448; NaN -> 0x7F.  Works on the exact value of x (x in float64): the
+    magnitude is written as n * 2^(e-3) in its binade e (e >= -6; below 2^-6 the subnormal
+    spacing 2^-9 is the binade -6 spacing), n rounded to nearest even."""
     x = np.asarray(x, dtype=np.float64)
-    out = np.zeros(x.shape, dtype=np.uint8)
-    flat_x, flat_o = x.ravel(), out.ravel()
-    for i, v in enumerate(flat_x):
-        if np.isnan(v):
-            flat_o[i] = 0x7F
-            continue
-        s = 0x80 if np.signbit(v) else 0
-        a = min(abs(v), FP8_MAX)
-        if a == 0.0:
-            flat_o[i] = s
-            continue
-        # exponent of the binade holding a (subnormals share the binade of 2^-6)
-        e = max(int(np.floor(np.log2(a))), -6)
-        while 2.0 ** e > a and e > -6:     # guard log2 rounding at binade edges
-            e -= 1
-        while 2.0 ** (e + 1) <= a:
-            e += 1
-        q = a / 2.0 ** e * 8.0              # mantissa in units of 2^(e-3), in [8, 16) (or [0, 8))
-        n = np.floor(q)
-        r = q - n
-        if r > 0.5 or (r == 0.5 and int(n) % 2 == 1):
-            n += 1
-        n = int(n)
-        if n == 16:                         # rounded up into the next binade
-            n, e = 8, e + 1
-        if e == -6 and n < 8:
-            code = n                        # subnormal
-        else:
-            code = ((e + 7) << 3) | (n - 8)
-        flat_o[i] = s | min(code, 0x7E)
-    return out
+    nan = np.isnan(x)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.int64)
+    a = np.minimum(np.abs(np.where(nan, 0.0, x)), FP8_MAX)
+    with np.errstate(divide="ignore"):
+        e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6.0)
+    # guard log2 rounding at binade edges
+    e = np.where((np.exp2(e) > a) & (e > -6) & (a > 0), e - 1, e)
+    e = np.where(np.exp2(e + 1) <= a, e + 1, e)
+    q = a / np.exp2(e) * 8.0                       # in [8, 16) for normals, [0, 8) below
+    n = np.floor(q)
+    r = q - n
+    n = n + ((r > 0.5) | ((r == 0.5) & (n % 2 == 1)))
+    e = np.where(n == 16, e + 1, e)
+    n = np.where(n == 16, 8, n)
+    code = np.where((e == -6) & (n < 8), n, (e + 7) * 8 + (n - 8)).astype(np.int64)
+    code = np.where(a == 0, 0, np.minimum(code, 0x7E))
+    return np.where(nan, 0x7F, sign | code).astype(np.uint8)
 
 
 def quantize_rows_fp8(x):

@@ -195,6 +195,23 @@ def test_sampler_validation_errors():
     assert L.flux_generation_ids(4, 4, 2, FAKE, None, None) == F.FLUX_EINVAL
 
 
+def test_fp8_validation_errors():
+    L = F.lib()
+    c = F.make_cfg(256, 2, 768)
+    args = lambda epi, m, n, k, lda, ldw, sa=FAKE, ydt=0: (
+        ctypes.byref(c), epi, m, n, k, FAKE, lda, sa, FAKE, ldw, FAKE, FAKE, n, ydt, None, 0,
+        None, 1, None, 0, None)
+    assert L.flux_linear_fp8(*args(0, 8, 8, 100, 128, 128)) == F.FLUX_ESHAPE     # k % 128
+    assert L.flux_linear_fp8(*args(0, 8, 8, 128, 136, 128)) == F.FLUX_EALIGN     # lda % 16
+    assert L.flux_linear_fp8(*args(0, 8, 8, 128, 128, 128, sa=None)) == F.FLUX_EINVAL
+    assert L.flux_linear_fp8(*args(7, 8, 8, 128, 128, 128)) == F.FLUX_EINVAL     # epilogue
+    assert L.flux_linear_fp8(*args(0, 8, 8, 128, 128, 128, ydt=9)) == F.FLUX_EDTYPE
+    assert L.flux_linear_fp8(*args(2, 8, 8, 128, 128, 128)) == F.FLUX_EINVAL     # no resid
+    assert L.flux_quantize_fp8_rows(0, 8, FAKE, 0, 8, FAKE, 8, FAKE, None) == F.FLUX_EINVAL
+    assert L.flux_quantize_fp8_rows(4, 8, FAKE, 5, 8, FAKE, 8, FAKE, None) == F.FLUX_EDTYPE
+    assert L.flux_quantize_fp8_rows(4, 8, FAKE, 0, 4, FAKE, 8, FAKE, None) == F.FLUX_ESHAPE
+
+
 def test_timing_hook_validation():
     L = F.lib()
     n, us = ctypes.c_int(7), ctypes.c_double(1.0)

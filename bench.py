@@ -234,7 +234,9 @@ def cpu_baseline(wl, flops_step: float):
 # per-workload block timings and bandwidth-kernel rates
 # ------------------------------------------------------------------------------------
 PER_CONFIG = ("tiny_single_f32", "klein4b_single_512", "klein9b_double_1024",
-              "klein9b_step_1024", "dev_pair_2048", "klein9b_generate_1024", "klein9b_edit_1024")
+              "klein9b_step_1024", "dev_pair_2048", "klein9b_generate_1024", "klein9b_edit_1024",
+              "klein9b_fp8_linear_1024")
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 # editing cells (reference images, output side in pixels) of the pages' K/V cache table
 EDIT_CELLS = ((1, 512), (1, 1024), (2, 1024), (4, 1024))
 
@@ -351,9 +353,65 @@ def edit_line(F, fs, wl) -> dict:
     return res
 
 
+def fp8_line(F, fs, wl) -> dict:
+    """The single block's linears in bf16 and in FP8 (E4M3, per-row x per-channel scales)
+    on the same shapes and epilogues, and the per-row quantization of the activations."""
+    import torch
+    D, H, L = wl.dim, wl.mlp_hidden, wl.seq
+    cfg = F.make_cfg(D, wl.heads, H)
+    s = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed)
+    lnb = F.flux_linear_workspace_size()
+    lws = torch.empty(lnb, dtype=torch.uint8, device="cuda")
+    res = {"workload": wl.name, "tokens": L, "peak_fp8_tflops": PEAK_FP8_TFLOPS,
+           "peak_bf16_tflops": PEAK_BF16_TFLOPS, "linears": []}
+    shapes = (("mlp_in_swiglu", F.FLUX_EPI_SWIGLU, 2 * H, D),
+              ("qkv_store", F.FLUX_EPI_STORE, 3 * D, D),
+              ("linear2_gated_residual", F.FLUX_EPI_GATED_RESIDUAL, D, D + H))
+    for name, epi, n, k in shapes:
+        m = L
+        x = torch.randn((m, k), generator=g, device="cuda").to(torch.bfloat16)
+        w = (0.02 * torch.randn((n, k), generator=g, device="cuda")).to(torch.bfloat16)
+        nout = n // 2 if epi == F.FLUX_EPI_SWIGLU else n
+        ydt = F.FLUX_F32 if epi == F.FLUX_EPI_GATED_RESIDUAL else F.FLUX_BF16
+        y = torch.empty((m, nout), device="cuda",
+                        dtype=torch.float32 if ydt == F.FLUX_F32 else torch.bfloat16)
+        r = torch.randn((m, nout), generator=g, device="cuda") if ydt == F.FLUX_F32 else None
+        gt = torch.randn((1, nout), generator=g, device="cuda") if r is not None else None
+        qa = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+        qw = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+        sa = torch.empty(m, device="cuda")
+        sw = torch.empty(n, device="cuda")
+        F.flux_quantize_fp8_rows(n, k, w, F.FLUX_BF16, k, qw, k, sw, s)
+        quant = lambda: F.flux_quantize_fp8_rows(m, k, x, F.FLUX_BF16, k, qa, k, sa, s)
+        quant()
+        kw = dict(resid=r, ldr=nout, gate=gt, rows_per_batch=m, workspace=lws,
+                  workspace_bytes=lnb, stream=s)
+        b16 = _time_ms(lambda: F.flux_linear(cfg, epi, m, n, k, x, k, w, k, y, nout, ydt, **kw), s)
+        f8 = _time_ms(lambda: F.flux_linear_fp8(cfg, epi, m, n, k, qa, k, sa, qw, k, sw, y, nout,
+                                                ydt, **kw), s)
+        qms = _time_ms(quant, s)
+        flops = 2.0 * m * n * k
+        qbytes = m * k * 3 + m * 4
+        res["linears"].append({
+            "name": name, "shape": [m, n, k],
+            "bf16_us": round(b16 * 1e3, 1), "bf16_tflops": round(flops / (b16 * 1e-3) / 1e12, 1),
+            "fp8_us": round(f8 * 1e3, 1), "fp8_tflops": round(flops / (f8 * 1e-3) / 1e12, 1),
+            "fp8_frac_of_peak": round(flops / (f8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "speedup": round(b16 / f8, 3),
+            "quantize_activations_us": round(qms * 1e3, 1),
+            "quantize_gbs": round(qbytes / (qms * 1e-3) / 1e9, 1),
+            "speedup_incl_quantize": round(b16 / (f8 + qms), 3)})
+        del x, w, y, r, qa, qw
+    return res
+
+
 def per_config_line(F, fs, name: str) -> dict:
     import torch
     wl = fs.workload(name)
+    if wl.kind == "fp8":
+        return fp8_line(F, fs, wl)
     if wl.kind == "generate":
         return generate_line(F, fs, wl)
     if wl.kind == "edit":

@@ -3,43 +3,33 @@
 // The FLUX.2 [klein] research note, Infra (量化), reports FP8 releases of the models and
 // their speed-ups but no recipe.  Reading used here: OCP E4M3 (1 sign, 4 exponent bits with
 // bias 7, 3 mantissa bits, largest finite 448, no infinities), scales per row (activation
-// rows, weight rows = output channels) s = amax / 448, codes = E4M3(x / s) rounded to
-// nearest even with saturation at 448.
+// rows, weight rows = output channels) s = amax / 448 for dequantization, codes =
+// E4M3(x * (448 / amax)) rounded to nearest even with saturation at 448.
 //
-// One wave per row: a first pass finds the row's absolute maximum with 16-byte loads, a
-// second pass (the row is cache resident) divides by the scale and packs 8 codes per
-// 8-byte store.  HBM traffic: the row once, the codes once, 4 bytes of scale.
+// One wave per row.  Rows of up to 4096 elements are held in registers (8 16-byte loads per
+// lane, all in flight together): amax, then the codes from the registers, 8 codes per
+// 8-byte store.  Longer rows take two passes (amax, then the codes; the row is cache
+// resident).  HBM traffic: the row once, the codes once, 4 bytes of scale.
 #include "common.h"
 #include "kernels.h"
 
 namespace flux {
 
-// E4M3 code of a float, round to nearest (ties to even), |v| >= 448 saturates to 448,
-// NaN -> 0x7F.  Normal range: keep 3 of the 23 fp32 mantissa bits with RNE on the rest;
-// below 2^-6 the spacing is 2^-9, so the code is rint(|v| * 2^9) (8 = smallest normal).
-FLUX_DEV uint32_t e4m3_rne(float v) {
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fu;
-  const float a = fminf(fabsf(v), 448.f);
-  const uint32_t ab = __float_as_uint(a);
-  const int e = (int)(ab >> 23) - 127;
-  uint32_t code;
-  if (e >= -6) {
-    const uint32_t m = ab & 0x7fffffu;
-    const uint32_t keep = m >> 20, rem = m & 0xfffffu;
-    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ? 1u : 0u;
-    uint32_t ee = (uint32_t)(e + 7), kk = keep + up;
-    if (kk == 8u) {
-      kk = 0u;
-      ee += 1u;
-    }
-    code = (ee << 3) | kk;
-    if (code > 0x7eu) code = 0x7eu;
-  } else {
-    code = (uint32_t)__builtin_rintf(a * 512.f);
-  }
-  return sign | code;
+// Four E4M3 codes (low byte first) of v[0..3], round to nearest even, saturating at 448,
+// NaN -> 0x7F.  v_cvt_pk_fp8_f32 rounds to nearest even; over every fp32 value with
+// |v| <= 448 its codes equal those of the definition (an exhaustive comparison with a
+// bit-level encoder), so inputs are clamped into that range first.
+FLUX_DEV uint32_t e4m3x4(const float (&v)[4]) {
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_fmed3f(v[i], -448.f, 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  uint32_t u = (uint32_t)w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (v[i] != v[i]) u = (u & ~(0xffu << (8 * i))) | (0x7fu << (8 * i));
+  return u;
 }
 
 template <class T>
@@ -75,6 +65,33 @@ __global__ __launch_bounds__(256) void quant_fp8_rows_kernel(const T* __restrict
   const T* xr = x + (int64_t)row * ldx;
   uint8_t* qr = q + (int64_t)row * ldq;
   float amax = 0.f;
+  constexpr int CH = 8;  // chunks of 8 elements per lane kept in registers
+  if (vec && cols <= 512 * CH) {
+    float v[CH][8];
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (lane * 8 + 512 * i < cols) load8<T>(xr + lane * 8 + 512 * i, v[i]);
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (lane * 8 + 512 * i < cols)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float sc = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+    const float rc = amax > 0.f ? __fdiv_rn(448.f, amax) : 1.f;
+    if (lane == 0) s_out[row] = sc;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c0 = lane * 8 + 512 * i;
+      if (c0 < cols) {
+        const float a[4] = {v[i][0] * rc, v[i][1] * rc, v[i][2] * rc, v[i][3] * rc};
+        const float b[4] = {v[i][4] * rc, v[i][5] * rc, v[i][6] * rc, v[i][7] * rc};
+        *reinterpret_cast<uint2*>(qr + c0) = make_uint2(e4m3x4(a), e4m3x4(b));
+      }
+    }
+    return;
+  }
   if (vec) {
     for (int c0 = lane * 8; c0 < cols; c0 += 512) {
       float v[8];
@@ -88,21 +105,21 @@ __global__ __launch_bounds__(256) void quant_fp8_rows_kernel(const T* __restrict
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   const float sc = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  const float rc = amax > 0.f ? __fdiv_rn(448.f, amax) : 1.f;
   if (lane == 0) s_out[row] = sc;
   if (vec) {
     for (int c0 = lane * 8; c0 < cols; c0 += 512) {
       float v[8];
       load8<T>(xr + c0, v);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo |= e4m3_rne(__fdiv_rn(v[i], sc)) << (8 * i);
-        hi |= e4m3_rne(__fdiv_rn(v[4 + i], sc)) << (8 * i);
-      }
-      *reinterpret_cast<uint2*>(qr + c0) = make_uint2(lo, hi);
+      const float a[4] = {v[0] * rc, v[1] * rc, v[2] * rc, v[3] * rc};
+      const float b[4] = {v[4] * rc, v[5] * rc, v[6] * rc, v[7] * rc};
+      *reinterpret_cast<uint2*>(qr + c0) = make_uint2(e4m3x4(a), e4m3x4(b));
     }
   } else {
-    for (int c = lane; c < cols; c += 64) qr[c] = (uint8_t)e4m3_rne(__fdiv_rn(to_f32(xr[c]), sc));
+    for (int c = lane; c < cols; c += 64) {
+      const float a[4] = {to_f32(xr[c]) * rc, 0.f, 0.f, 0.f};
+      qr[c] = (uint8_t)(e4m3x4(a) & 0xffu);
+    }
   }
 }
 

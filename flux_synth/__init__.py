@@ -62,7 +62,7 @@ class Workload:
     n_single: int = 0            # single-stream blocks (step only)
     t_fixed: float | None = None # fixed timestep, else drawn U[0,1)
     seed: int = 1000
-    kind: str = "single"         # "single", "double", "pair", "step", "generate" or "edit"
+    kind: str = "single"  # "single", "double", "pair", "step", "generate", "edit" or "fp8"
 
     @property
     def seq(self) -> int:
@@ -102,6 +102,10 @@ WORKLOADS: dict[str, Workload] = {
     "klein9b_edit_1024": Workload("klein9b_edit_1024", 4096, 32, 12288, 4096, 512,
                                   in_channels=128, context_dim=12288, n_double=8, n_single=24,
                                   seed=1007, kind="edit"),
+    # The Klein-9B single block's linear layers at 1024^2 (4608 tokens) in FP8 (E4M3) against
+    # bf16: MLP-in + SwiGLU, the q|k|v projection shape, linear2 + gated residual.
+    "klein9b_fp8_linear_1024": Workload("klein9b_fp8_linear_1024", 4096, 32, 12288, 4096, 512,
+                                        seed=1008, kind="fp8"),
     # FLUX.2-dev-shaped long-sequence block pair at 2048^2 (one double + one single).
     "dev_pair_2048": Workload("dev_pair_2048", 6144, 48, 18432, 16384, 512,
                               seed=1005, kind="pair"),

@@ -33,7 +33,7 @@ Readings of points the pages leave open (each also listed in the design doc):
   * reference K/V cache: reference image j has ids (1 + j, r, c, 0); all reference tokens
     attend to all reference tokens (one segment); the fixed reference timestep is 0
   * FP8 linear: OCP E4M3, per-row (activation) and per-output-channel (weight) scales
-    amax / 448, round to nearest even with saturation
+    amax / 448 (values multiplied by 448 / amax), round to nearest even with saturation
 
 Parity pins for every function live in tests/test_oracle_pins.py and, for the sampling
 loop, the reference K/V cache and the FP8 linear, tests/test_oracle_sampler.py,
@@ -849,12 +849,16 @@ def fp8_encode(x) -> np.ndarray:
 
 
 def quantize_rows_fp8(x):
-    """Per-row E4M3 quantization: s = amax(|row|) / 448 in fp32 (1 for an all-zero row),
-    q = encode(fp32(x / s)) with the division done in fp32.  Returns (q uint8, s float32)."""
+    """Per-row E4M3 quantization: dequantization scale s = amax(|row|) / 448 and
+    quantization multiplier r = 448 / amax (both fp32, correctly rounded; s = r = 1 for an
+    all-zero row), q = encode(fp32(x * r)).  Returns (q uint8, s float32)."""
     x32 = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(x32), axis=-1)
-    s = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
-    q = fp8_encode((x32 / s[..., None]).astype(np.float32).astype(np.float64))
+    pos = amax > 0
+    safe = np.where(pos, amax, np.float32(1.0)).astype(np.float32)
+    s = np.where(pos, safe / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    r = np.where(pos, np.float32(FP8_MAX) / safe, np.float32(1.0)).astype(np.float32)
+    q = fp8_encode((x32 * r[..., None]).astype(np.float32).astype(np.float64))
     return q, s
 
 

@@ -16,6 +16,9 @@
 //   * softmax in the exp2 domain (log2(e)/sqrt(d) folded into one FMA per score) with a
 //     lazy running maximum: O and the row sum are rescaled only when a row's maximum
 //     grows by more than 2^8, which keeps p <= 256 and skips almost all rescales;
+//   * the key loop is software pipelined: while a wave takes the exponentials of one tile
+//     it already computes the next tile's scores, so its own MFMAs run beside its softmax
+//     (K is loaded two tiles ahead, V one tile ahead, one barrier per tile);
 //   * two workgroups per CU (<= 256 registers per wave) so one workgroup's softmax
 //     overlaps the other's MFMAs;
 //   * work units are (query block, head, batch).  Units that fill whole rounds of resident
@@ -149,23 +152,10 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     const int c = (lane & 7) ^ ((d >> 1) & 7);
     return (uint32_t)(((int64_t)d * ld_v + c * 8) * 2);
   };
-  // the plain kernel keeps them in registers; the extra-key variant, short of registers,
-  // recomputes them per tile
-  uint32_t k_voff[EXTRA ? 1 : KI], v_voff[EXTRA ? 1 : VI];
-  if constexpr (!EXTRA) {
-#pragma unroll
-    for (int j = 0; j < KI; ++j) k_voff[j] = k_lane_off(j, kv.ld);
-#pragma unroll
-    for (int j = 0; j < VI; ++j) v_voff[j] = v_lane_off(j, ld_vt);
-  }
-  auto kvo = [&](int j) __attribute__((always_inline)) {
-    if constexpr (EXTRA) return k_lane_off(j, kv.ld);
-    else return k_voff[j];
-  };
-  auto vvo = [&](int j) __attribute__((always_inline)) {
-    if constexpr (EXTRA) return v_lane_off(j, ld_vt);
-    else return v_voff[j];
-  };
+  // recomputed per tile (a few VALU operations) rather than held in registers: the
+  // pipelined key loop keeps two tiles' scores live
+  auto kvo = [&](int j) __attribute__((always_inline)) { return k_lane_off(j, kv.ld); };
+  auto vvo = [&](int j) __attribute__((always_inline)) { return v_lane_off(j, ld_vt); };
   const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ks0 = __builtin_amdgcn_readfirstlane(lds_u32(&Ks[0][0])) + wv * KI * 4 * kHD * 2;
   const uint32_t vs0 = __builtin_amdgcn_readfirstlane(lds_u32(&Vs[0][0])) + wv * VI * 8 * kBKV * 2;
@@ -186,29 +176,29 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     xldv = xkv.ld_vt;
     xn = xkv.n;
   }
-  auto issue_extra = [&](int buf, int x0) __attribute__((always_inline)) {
-    if (x0 + kBKV <= xn) {
-      const bf16* kb = xk + (int64_t)x0 * xld;
+  // K rows of key tile `it` into K buffer `buf`.  A tile inside one segment of its key
+  // source takes the scalar base + per-lane offsets; others (the last one, one straddling
+  // the txt/img boundary) per-lane addresses with the key clamped to the source's last.
+  auto issue_k = [&](int buf, int it) __attribute__((always_inline)) {
+    const uint32_t dst = ks0 + buf * KBUF;
+    if constexpr (EXTRA) {
+      if (it >= nm) {
+        const int x0 = (it - nm) * kBKV;
+        if (x0 + kBKV <= xn) {
+          const bf16* kb = xk + (int64_t)x0 * xld;
 #pragma unroll
-      for (int j = 0; j < KI; ++j)
-        dma_s<true>(kb, k_lane_off(j, xld), ks0 + buf * KBUF + j * 4 * kHD * 2);
-    } else {
+          for (int j = 0; j < KI; ++j) dma_s<true>(kb, k_lane_off(j, xld), dst + j * 4 * kHD * 2);
+        } else {
 #pragma unroll
-      for (int j = 0; j < KI; ++j) {
-        const int row = (wave * KI + j) * 4 + (lane >> 4);
-        const int key = min(x0 + row, xn - 1);
-        const int c = (lane & 15) ^ (row & 15);
-        dma_v<true>(xk + (int64_t)key * xld + hoff + c * 8, ks0 + buf * KBUF + j * 4 * kHD * 2);
+          for (int j = 0; j < KI; ++j) {
+            const int row = (wave * KI + j) * 4 + (lane >> 4);
+            const int key = min(x0 + row, xn - 1);
+            const int c = (lane & 15) ^ (row & 15);
+            dma_v<true>(xk + (int64_t)key * xld + hoff + c * 8, dst + j * 4 * kHD * 2);
+          }
+        }
+        return;
       }
-    }
-#pragma unroll
-    for (int j = 0; j < VI; ++j)
-      dma_s<true>(xvt + x0, v_lane_off(j, xldv), vs0 + buf * VBUF + j * 8 * kBKV * 2);
-  };
-  auto issue = [&](int buf, int it) __attribute__((always_inline)) {
-    if (EXTRA && it >= nm) {
-      issue_extra(buf, (it - nm) * kBKV);
-      return;
     }
     const int kv0 = it * kBKV;
     const bool in0 = kv0 + kBKV <= kv.n0, in1 = kv0 >= kv.n0;
@@ -217,19 +207,31 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
                            : static_cast<const bf16*>(kv.base1) + b * kv.bs1 +
                                  (int64_t)(kv0 - kv.n0) * kv.ld;
 #pragma unroll
-      for (int j = 0; j < KI; ++j) dma_s<EXTRA>(kb, kvo(j), ks0 + buf * KBUF + j * 4 * kHD * 2);
+      for (int j = 0; j < KI; ++j) dma_s<EXTRA>(kb, kvo(j), dst + j * 4 * kHD * 2);
     } else {
 #pragma unroll
       for (int j = 0; j < KI; ++j) {
         const int row = (wave * KI + j) * 4 + (lane >> 4);
         const int key = min(kv0 + row, seq - 1);  // past the end: a valid row, masked later
         const int c = (lane & 15) ^ (row & 15);
-        dma_v<EXTRA>(seq_cptr<bf16>(kv, b, key) + hoff + c * 8, ks0 + buf * KBUF + j * 4 * kHD * 2);
+        dma_v<EXTRA>(seq_cptr<bf16>(kv, b, key) + hoff + c * 8, dst + j * 4 * kHD * 2);
+      }
+    }
+  };
+  // V^T columns of key tile `it` into V buffer `buf` (the V^T rows are padded to whole
+  // tiles, so a partial tile reads padding, never past the rows)
+  auto issue_v = [&](int buf, int it) __attribute__((always_inline)) {
+    const uint32_t dst = vs0 + buf * VBUF;
+    if constexpr (EXTRA) {
+      if (it >= nm) {
+        const int x0 = (it - nm) * kBKV;
+#pragma unroll
+        for (int j = 0; j < VI; ++j) dma_s<true>(xvt + x0, v_lane_off(j, xldv), dst + j * 8 * kBKV * 2);
+        return;
       }
     }
 #pragma unroll
-    for (int j = 0; j < VI; ++j)
-      dma_s<EXTRA>(vt_head + kv0, vvo(j), vs0 + buf * VBUF + j * 8 * kBKV * 2);
+    for (int j = 0; j < VI; ++j) dma_s<EXTRA>(vt_head + it * kBKV, vvo(j), dst + j * 8 * kBKV * 2);
   };
 
   f32x16 o[4];
@@ -251,55 +253,53 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
 #pragma unroll
   for (int c = 0; c < 4; ++c) voff[c] = v_off(l32, 2 * c + g);
 
-  // one key tile; CUR = its LDS buffer (compile time, so every LDS offset is immediate);
-  // MASK: the tile reaches past its keys (the last tile of the sequence, and of the extra
-  // keys), whose count in the tile is `lim`
-  auto tile = [&](int it, auto cur_c, auto mask_c) __attribute__((always_inline)) {
-    constexpr int cur = decltype(cur_c)::value;
-    constexpr bool MASK = decltype(mask_c)::value;
-    const int lim = (EXTRA && it >= nm) ? xn - (it - nm) * kBKV : seq - it * kBKV;
-    if (it + 1 < t_end) issue(cur ^ 1, it + 1);
-
-    // S^T = K Q^T: s[h] covers MFMA rows of key block h (keys 32 h + key_perm(row))
-    f32x16 s[2];
+  // S^T = K Q^T of the key tile in K buffer BUF: s[h] covers MFMA rows of key block h
+  // (keys 32 h + key_perm(row)); register r of block h holds key 32 h + 16 (r >> 3) +
+  // 8 g + (r & 7)
+  auto scores = [&](f32x16 (&s)[2], auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[h][r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[cur][koff[kk]]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[cur][koff[kk] + 32 * kHD]);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][koff[kk]]);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[buf][koff[kk] + 32 * kHD]);
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[kk], s[1], 0, 0, 0);
     }
-    // register r of block h holds key 32 h + 16 (r >> 3) + 8 g + (r & 7)
-    if (MASK) {
+  };
+
+  // One key tile, software pipelined with the next one so that a wave's softmax (VALU)
+  // runs beside MFMAs of its own instead of alternating with them.  Tile t of the range
+  // lives in LDS buffers (t - t_begin) & 1 = CUR.  On entry the tile's scores are in sc,
+  // its V^T in V buffer CUR and the next tile's K in K buffer CUR ^ 1.  The step refills
+  // K buffer CUR with tile it + 2 and V buffer CUR ^ 1 with tile it + 1, computes the next
+  // tile's scores into sn (NEXT) between this tile's exponentials, and adds V^T P^T to O.
+  auto step = [&](int it, auto cur_c, auto next_c, f32x16 (&sc)[2], f32x16 (&sn)[2])
+                  __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value;
+    // a tile reaching past its source's keys (`lim` of them in the tile) is masked
+    const int lim = (EXTRA && it >= nm) ? xn - (it - nm) * kBKV : seq - it * kBKV;
+    if (lim < kBKV) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * h + 16 * (r >> 3) + 8 * g + (r & 7) >= lim) s[h][r] = -INFINITY;
+          if (32 * h + 16 * (r >> 3) + 8 * g + (r & 7) >= lim) sc[h][r] = -INFINITY;
     }
-
-    // online softmax in the log2 domain with a lazily updated maximum: the exponentials
-    // are taken against the running maximum while the tile maximum is found; only when
-    // some row's maximum grows by more than 2^8 are O and the sum rescaled and the
-    // exponentials redone (every row on the first tile, rarely afterwards)
-    float p[2][16];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        // raw v_exp_f32: arguments are <= 8, results below 2^-126 may flush to zero
-        p[h][r] = __builtin_amdgcn_exp2f(fmaf(s[h][r], scale_log2, -m_run));
+    // online softmax in the log2 domain with a lazily updated maximum: O and the sum are
+    // rescaled only when some row's maximum grows by more than 2^8 (every row on the first
+    // tile, rarely afterwards), so p <= 256
     float mx4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx4[i] = fmaxf(s[0][i], s[1][i]);
+    for (int i = 0; i < 4; ++i) mx4[i] = fmaxf(sc[0][i], sc[1][i]);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 4 * (1 - h); r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[h][r]);
+      for (int r = 4 * (1 - h); r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], sc[h][r]);
     float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
     const bool grow = mx > m_run + 8.f;
@@ -312,12 +312,17 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
       m_run = m_new;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[h][r] = __builtin_amdgcn_exp2f(fmaf(s[h][r], scale_log2, -m_run));
     }
+    if (it + 2 < t_end) issue_k(cur, it + 2);
+    if (NEXT) issue_v(cur ^ 1, it + 1);
 
+    if constexpr (NEXT) scores(sn, std::integral_constant<int, cur ^ 1>{});
+    // raw v_exp_f32: arguments are <= 8, results below 2^-126 may flush to zero
+    float p[2][16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[h][r] = __builtin_amdgcn_exp2f(fmaf(sc[h][r], scale_log2, -m_run));
     // P in bf16 (the PV product's operand); the row sum is taken over the same rounded
     // values with bf16 dot products against (1, 1)
     uint32_t pw[16];
@@ -340,53 +345,35 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
       }
     }
 
+    // this wave's refills landed; after the barrier every wave's have, and every wave is
+    // done reading the buffers the next step refills
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
-  issue(t_begin & 1, t_begin);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   using Buf0 = std::integral_constant<int, 0>;
   using Buf1 = std::integral_constant<int, 1>;
-  using NoMask = std::false_type;
-  using Mask = std::true_type;
-  // tiles [t0, t1) of one key source whose tile t_last is partial when `partial`
-  auto run_tiles = [&](int t0, int t1, int t_last, bool partial) __attribute__((always_inline)) {
-    const int t_full = partial ? min(t1, t_last) : t1;
-    int it = t0;
-    if (it < t_full && (it & 1)) tile(it++, Buf1{}, NoMask{});
-    for (; it + 1 < t_full; it += 2) {
-      tile(it, Buf0{}, NoMask{});
-      tile(it + 1, Buf1{}, NoMask{});
-    }
-    if (it < t_full) tile(it++, Buf0{}, NoMask{});
-    if (it < t1) {
-      if (it & 1)
-        tile(it, Buf1{}, Mask{});
-      else
-        tile(it, Buf0{}, Mask{});
-    }
-  };
-  if constexpr (EXTRA) {
-    // the sequence's own tiles, then the extra source's (each may end with a partial tile)
-    run_tiles(t_begin, min(t_end, nm), nm - 1, (seq % kBKV) != 0);
-    run_tiles(max(t_begin, nm), t_end, ntiles - 1, (xn % kBKV) != 0);
-  } else {
-    // tiles [t_begin, t_full) lie inside the sequence; a partial last tile is masked
-    const int t_full = min(t_end, seq / kBKV);
+  using On = std::true_type;
+  using Off = std::false_type;
+  if (t_begin < t_end) {
+    issue_k(0, t_begin);
+    issue_v(0, t_begin);
+    if (t_begin + 1 < t_end) issue_k(1, t_begin + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    scores(sa, Buf0{});
+    __syncthreads();  // K buffer 0 is refilled by the first step
     int it = t_begin;
-    if (it < t_full && (it & 1)) tile(it++, Buf1{}, NoMask{});
-    for (; it + 1 < t_full; it += 2) {
-      tile(it, Buf0{}, NoMask{});
-      tile(it + 1, Buf1{}, NoMask{});
+    for (; it + 2 < t_end; it += 2) {
+      step(it, Buf0{}, On{}, sa, sb);
+      step(it + 1, Buf1{}, On{}, sb, sa);
     }
-    if (it < t_full) tile(it++, Buf0{}, NoMask{});
-    if (it < t_end) {
-      if (it & 1)
-        tile(it, Buf1{}, Mask{});
-      else
-        tile(it, Buf0{}, Mask{});
+    if (it + 1 < t_end) {
+      step(it, Buf0{}, On{}, sa, sb);
+      step(it + 1, Buf1{}, Off{}, sb, sa);
+    } else {
+      step(it, Buf0{}, Off{}, sa, sb);
     }
   }
 

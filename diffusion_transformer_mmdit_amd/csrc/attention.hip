@@ -241,8 +241,6 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const int krow0 = key_perm(l32), krow1 = 32 + key_perm(l32);
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
   // per-lane LDS element offsets of the fragments: K rows krow0 (krow1 = krow0 + 32 has
   // the same swizzle, so its fragments sit 32 rows further) for each of the 8 k-steps;
@@ -323,16 +321,18 @@ __global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[h][r] = __builtin_amdgcn_exp2f(fmaf(sc[h][r], scale_log2, -m_run));
-    // P in bf16 (the PV product's operand); the row sum is taken over the same rounded
-    // values with bf16 dot products against (1, 1)
+    // the row sum in fp32 over the unrounded probabilities (plain adds run beside the
+    // MFMAs; bf16 dot products against (1, 1) would take the matrix pipe's turn), P in
+    // bf16 as the PV product's operand
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ls[r & 3] += p[h][r];
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     uint32_t pw[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) pw[i] = pack2(p[i >> 3][2 * (i & 7)], p[i >> 3][2 * (i & 7) + 1]);
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      ls[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[i]), ones, ls[i & 3], false);
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
     // O^T += V^T P^T over 4 chunks of 16 keys; lane group g owns keys 16 c + 8 g .. + 8
 #pragma unroll

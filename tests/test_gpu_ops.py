@@ -257,7 +257,12 @@ def test_linear_gated_residual(m, n, k, dtype, use_ws):
     (1, 1, 1, "bf16", None), (1536, 24, 1, "bf16", 96), (4608, 32, 1, "bf16", 48),
     # query blocks of a partial last round split along the keys and merged: 2-wave blocks
     # with 2 key ranges, 4-wave blocks with 4 ranges and a ragged last tile, batch 2
-    (600, 3, 1, "bf16", None), (1100, 64, 1, "bf16", 64), (700, 6, 2, "bf16", None)])
+    (600, 3, 1, "bf16", None), (1100, 64, 1, "bf16", 64), (700, 6, 2, "bf16", None),
+    # key ranges of 1, 2 and 3 tiles, whole or with a ragged last tile (the pipelined key
+    # loop's last steps), and 256 4-wave units: the smallest grid that takes 4-wave blocks,
+    # its partial round split in 2
+    (64, 2, 1, "bf16", None), (128, 1, 1, "bf16", None), (150, 2, 1, "bf16", None),
+    (192, 1, 1, "bf16", None), (1024, 32, 1, "bf16", 48)])
 def test_attention(seq, heads, batch, dtype, n_q):
     t = G.torch()
     seed = seq + heads

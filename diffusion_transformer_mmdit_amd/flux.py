@@ -198,7 +198,9 @@ def flux_timing_end() -> tuple[int, float]:
 
 
 # ------------------------------------------------------------------------------------
-# Structure builders (marshalling dicts of device tensors into the C structures)
+# Structure builders (marshalling dicts of device tensors into the C structures).  The C
+# structures hold raw device pointers, so every structure built here keeps the mapping it
+# was built from (and with it the tensors) alive for as long as the structure exists.
 # ------------------------------------------------------------------------------------
 def make_cfg(dim: int, heads: int, mlp_hidden: int, dtype: int = FLUX_BF16, head_dim: int = 128,
              axes_dim=(32, 32, 32, 32), rope_theta: float = 2000.0, eps: float = 1e-6,
@@ -229,6 +231,7 @@ def double_weights(w: Mapping, prefix: str = "", with_mod: bool = True) -> flux_
         d.mod_img, d.mod_txt = _ptr(w["mod_img"]), _ptr(w["mod_txt"])
     d.img = stream_weights(w, prefix + "img.")
     d.txt = stream_weights(w, prefix + "txt.")
+    d._tensors = w
     return d
 
 
@@ -239,6 +242,7 @@ def single_weights(w: Mapping, prefix: str = "", with_mod: bool = True) -> flux_
         s.mod = _ptr(w["mod"])
     s.linear1, s.linear2 = _ptr(w[prefix + "linear1"]), _ptr(w[prefix + "linear2"])
     s.q_norm, s.k_norm = _ptr(w[prefix + "q_norm"]), _ptr(w[prefix + "k_norm"])
+    s._tensors = w
     return s
 
 
@@ -246,6 +250,7 @@ class ModelWeights:
     """flux_model_weights plus the host arrays of per-block structures it points to."""
 
     def __init__(self, w: Mapping, n_double: int, n_single: int):
+        self._tensors = w  # the device pointers below stay valid while this object lives
         self.doubles = (flux_double_weights * max(n_double, 1))()
         for i in range(n_double):
             self.doubles[i] = double_weights(w, prefix=f"double.{i}.", with_mod=False)

@@ -16,6 +16,11 @@
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default
  *     stream).  Nothing is synchronised.  Overlapping calls on different streams must
  *     use different workspaces.
+ *   - Only kernels (and, for guided sampling, device-to-device copies) are enqueued, so
+ *     the calls can be captured into a HIP graph on `stream`; make one call of each kind
+ *     outside the capture first (the first launch of a kernel configuration sets its
+ *     LDS limit).  Pointers are baked into the graph: keep the buffers alive and at the
+ *     same addresses while it is replayed.
  *   - Arguments are validated before anything is enqueued: a non-OK status means no
  *     work was enqueued, and flux_last_error() returns a message (thread-local).
  *   - A HIP launch/runtime error reported while enqueuing returns FLUX_EHIP.  Faults

@@ -231,3 +231,39 @@ def test_binding_raises_when_library_missing(tmp_path, monkeypatch):
     with pytest.raises(F.FluxError):
         F.lib(str(tmp_path / "nope.so"))
     monkeypatch.setattr(F, "_lib", None)
+
+
+def test_weight_structures_keep_their_tensors_alive():
+    """The C structures hold raw pointers: the binding's builders keep the tensors they point
+    to alive for as long as the structure exists (a temporary dict must not leave them
+    dangling)."""
+    import gc
+    import weakref
+    import numpy as np
+    import torch
+    import flux_synth as fs
+    wl = fs.workload("tiny_single_f32", kind="step", in_channels=32, context_dim=48, n_double=1,
+                     n_single=1, n_img=16, n_txt=5)
+    inp = fs.step_inputs(wl)
+
+    def fresh():
+        return {k: torch.from_numpy(v.astype(np.float32)) for k, v in inp["weights"].items()}
+
+    w = fresh()
+    probe = weakref.ref(w["proj_out"])
+    mw = F.ModelWeights(w, wl.n_double, wl.n_single)
+    del w
+    gc.collect()
+    assert probe() is not None, "ModelWeights let its tensors be freed"
+    del mw
+    gc.collect()
+    assert probe() is None
+    for kind, build in (("double", F.double_weights), ("single", F.single_weights)):
+        bw = fs.block_inputs(fs.workload("tiny_single_f32", kind=kind), kind=kind)["weights"]
+        w = {k: torch.from_numpy(v.astype(np.float32)) for k, v in bw.items()}
+        probe = weakref.ref(next(iter(w.values())))
+        s = build(w)
+        del w
+        gc.collect()
+        assert probe() is not None, f"{kind}_weights let its tensors be freed"
+        del s

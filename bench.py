@@ -2,7 +2,7 @@
 MI355X through the C ABI.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-    python bench.py --probe dominant|copy      # a few bare launches, for counter runs
+    python bench.py --probe dominant|attention|copy   # a few bare launches, for counter runs
     python bench.py --per-config               # one JSON line per traced workload: ms per
                                                # block, LN+modulate and RMSNorm+RoPE GB/s
 
@@ -180,6 +180,23 @@ def dominant_roofline(wl, launches: int, mean_us: float) -> dict:
         "timed": "inside the timed steps: HIP event pair around each launch on the step's stream",
         "algorithmic_flops_per_launch": flops,
     }
+
+
+def attention_probe(F, wl):
+    """The joint attention at the step's shape (L x heads, bf16) through flux_attention,
+    launched 3 times: the MFMA / VALU counter runs of the attention kernel use it."""
+    import torch
+    D, L = wl.dim, wl.seq
+    qkv = torch.randn((wl.batch, L, 3 * D), device="cuda").to(torch.bfloat16)
+    o = torch.empty((wl.batch, L, D), device="cuda", dtype=torch.bfloat16)
+    cfg = F.make_cfg(D, wl.heads, wl.mlp_hidden)
+    s = torch.cuda.current_stream()
+    nb = F.flux_attention_workspace_size(cfg, wl.batch, L)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        F.flux_attention(cfg, wl.batch, L, qkv, qkv[..., D:], qkv[..., 2 * D:], 3 * D, o, D, ws,
+                         nb, s)
+    torch.cuda.synchronize()
 
 
 def copy_probe(mib: int = 1024):
@@ -489,7 +506,7 @@ def main(argv=None) -> int:
                     help="time the blocks and bandwidth kernels of every traced workload")
     ap.add_argument("--only", default=None, choices=PER_CONFIG,
                     help="with --per-config: just this workload")
-    ap.add_argument("--probe", choices=("dominant", "copy"), default=None,
+    ap.add_argument("--probe", choices=("dominant", "attention", "copy"), default=None,
                     help="only launch the dominant kernel (or a 1 GiB copy) 3 times and exit")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -515,6 +532,10 @@ def main(argv=None) -> int:
     if args.probe == "dominant":
         dominant_probe(F, wl)
         print("[bench] probe: dominant kernel launched 3 times", file=sys.stderr, flush=True)
+        return 0
+    if args.probe == "attention":
+        attention_probe(F, wl)
+        print("[bench] probe: attention launched 3 times", file=sys.stderr, flush=True)
         return 0
     if args.probe == "copy":
         copy_probe()

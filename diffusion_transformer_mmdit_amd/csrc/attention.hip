@@ -15,7 +15,8 @@
 //     makes the V^T fragment of O^T = V^T P^T a single 16-byte LDS read;
 //   * softmax in the exp2 domain (log2(e)/sqrt(d) folded into one FMA per score) with a
 //     lazy running maximum: O and the row sum are rescaled only when a row's maximum
-//     grows by more than 2^8, which keeps p <= 256 and skips almost all rescales;
+//     grows by more than 2^8, which keeps p <= 256 and skips almost all rescales; row
+//     sums are fp32 adds of the unrounded probabilities, P enters the PV product in bf16;
 //   * the key loop is software pipelined: while a wave takes the exponentials of one tile
 //     it already computes the next tile's scores, so its own MFMAs run beside its softmax
 //     (K is loaded two tiles ahead, V one tile ahead, one barrier per tile);

@@ -133,21 +133,36 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const TX* __restrict__
 }
 
 // fp32 rows of exactly 256 J values (the residual stream): lane l holds the float4s
-// 4 (l + 64 j), j < J, so every load instruction reads 1 KB contiguously.
+// 4 (l + 64 j), j < J, so every load instruction reads 1 KB contiguously. The workgroups
+// are laid out per batch item (rows_per_batch / 4 of them, rounded up, for each item), so
+// the 4 rows of one workgroup share one shift / scale pair, which is staged in LDS while
+// the rows' loads are in flight. Reading the modulation from LDS instead of holding it in
+// registers leaves room for 5 waves per SIMD at J = 16 (4 with the vectors in registers).
 template <class TY, int J>
 __global__ __launch_bounds__(256) void ln_modulate_f32_kernel(const float* __restrict__ x,
                                                               int64_t ldx, TY* __restrict__ y,
                                                               int64_t ldy, int rows, int rpb,
+                                                              int wg_per_item,
                                                               const float* __restrict__ shift,
                                                               const float* __restrict__ scale,
                                                               int64_t mod_bs, float eps) {
   constexpr int D = 256 * J;
+  __shared__ float4 mod_shift[D / 4], mod_scale[D / 4];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)min(row, rows - 1) * ldx);
+  const int item = blockIdx.x / wg_per_item;
+  const int r = (blockIdx.x % wg_per_item) * 4 + (threadIdx.x >> 6);  // row within the item
+  const int row = item * rpb + r;
+  const bool live = r < rpb && row < rows;  // wave-uniform; a dead wave reads the item's first row
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)(live ? row : item * rpb) * ldx);
   float4 v[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) v[j] = xr[lane + 64 * j];
+  const float4* sh = reinterpret_cast<const float4*>(shift + item * mod_bs);
+  const float4* sc = reinterpret_cast<const float4*>(scale + item * mod_bs);
+  for (int c = threadIdx.x; c < D / 4; c += 256) {
+    mod_shift[c] = sh[c];
+    mod_scale[c] = sc[c];
+  }
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < J; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
@@ -162,21 +177,16 @@ __global__ __launch_bounds__(256) void ln_modulate_f32_kernel(const float* __res
     q += (v[j].x * v[j].x + v[j].y * v[j].y) + (v[j].z * v[j].z + v[j].w * v[j].w);
   }
   const float rstd = rsqrtf(wave_sum(q) * (1.f / D) + eps);
-  if (row >= rows) return;
-  const int b = row / rpb;
-  const float4* sh = reinterpret_cast<const float4*>(shift + b * mod_bs);
-  const float4* sc = reinterpret_cast<const float4*>(scale + b * mod_bs);
+  __syncthreads();
+  if (!live) return;
   TY* yr = y + (int64_t)row * ldy;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int c = lane + 64 * j;
-    const float4 a = sh[c], m = sc[c];
+    const float4 a = mod_shift[c], m = mod_scale[c];
     float o[4] = {(1.f + m.x) * (v[j].x * rstd) + a.x, (1.f + m.y) * (v[j].y * rstd) + a.y,
                   (1.f + m.z) * (v[j].z * rstd) + a.z, (1.f + m.w) * (v[j].w * rstd) + a.w};
     store_cw<TY, 4>(yr + 4 * c, o);
-    // the modulation vectors' loads are issued 4 chunks at a time, not all hoisted ahead
-    // of the loop (that doubles the registers and halves the waves in flight)
-    if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -190,11 +200,15 @@ static hipError_t ln_dispatch(const void* x, int64_t ldx, void* y, int64_t ldy, 
   auto* xp = static_cast<const TX*>(x);
   auto* yp = static_cast<TY*>(y);
   if constexpr (sizeof(TX) == 4) {
-#define FLUX_LN32(J)                                                                          \
-  if (dim == 256 * J) {                                                                      \
-    hipLaunchKernelGGL((ln_modulate_f32_kernel<TY, J>), grid, block, 0, s, xp, ldx, yp, ldy, \
-                       rows, rpb, shift, scale, mod_bs, eps);                               \
-    return hipGetLastError();                                                               \
+    // rows of one batch item: a row count past the last item's end only shortens that item
+    const int per_item = rpb < rows ? rpb : rows;
+    const int items = (rows + per_item - 1) / per_item, wg_per_item = (per_item + 3) / 4;
+#define FLUX_LN32(J)                                                                         \
+  if (dim == 256 * J) {                                                                     \
+    hipLaunchKernelGGL((ln_modulate_f32_kernel<TY, J>), dim3(items * wg_per_item), block, 0, \
+                       s, xp, ldx, yp, ldy, rows, per_item, wg_per_item, shift, scale,      \
+                       mod_bs, eps);                                                        \
+    return hipGetLastError();                                                              \
   }
     FLUX_LN32(12) FLUX_LN32(16) FLUX_LN32(24) FLUX_LN32(32)
 #undef FLUX_LN32

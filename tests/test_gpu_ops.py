@@ -88,11 +88,16 @@ def test_modulation(D, dtype, batch, n_chunks):
 # ------------------------------------------------------------------------------------
 @pytest.mark.parametrize("D,rows,rpb,x_dtype,y_dtype", [
     (256, 80, 80, "f32", "f32"), (256, 77, 7, "bf16", "bf16"), (3072, 1536, 1536, "bf16", "bf16"),
-    (4096, 4608, 4608, "f32", "bf16"), (6144, 333, 111, "bf16", "bf16")])
+    (4096, 4608, 4608, "f32", "bf16"), (6144, 333, 111, "bf16", "bf16"),
+    # fp32 residual rows at every width of the per-item kernel: items of a row count that is
+    # not a multiple of 4, a last item cut short (rows not a multiple of rows_per_batch) and
+    # rows_per_batch beyond rows
+    (3072, 150, 75, "f32", "bf16"), (4096, 70, 30, "f32", "bf16"), (4096, 9, 100, "f32", "f32"),
+    (6144, 222, 37, "f32", "bf16"), (8192, 37, 37, "f32", "f32")])
 def test_layernorm_modulate(D, rows, rpb, x_dtype, y_dtype):
     t = G.torch()
     seed = 11 + rows
-    B = rows // rpb
+    B = -(-rows // rpb)
     # scale / shift before rounding, so both sides read the same representable values
     x = fs.normal(seed, "x", (rows, D), std=2.0, mean=0.5, dtype=x_dtype)
     shift = fs.normal(seed, "shift", (B, D), std=0.3, dtype="f32")
@@ -103,8 +108,12 @@ def test_layernorm_modulate(D, rows, rpb, x_dtype, y_dtype):
                               f.FLUX_BF16 if x_dtype == "bf16" else f.FLUX_F32, G.dev(shift),
                               G.dev(scale), y, G.stream())
     t.cuda.synchronize()
-    ref = O.layernorm_modulate(x.reshape(B, rpb, D).astype(np.float64), shift.astype(np.float64),
-                               scale.astype(np.float64)).reshape(rows, D)
+    # row r takes item r // rpb: pad the last item to whole rows for the oracle, then drop the pad
+    xp = np.zeros((B * rpb, D), np.float64)
+    xp[:rows] = x.astype(np.float64)
+    xp[rows:] = 1.0 + np.arange(D) / D  # any row with non-zero variance
+    ref = O.layernorm_modulate(xp.reshape(B, rpb, D), shift.astype(np.float64),
+                               scale.astype(np.float64)).reshape(B * rpb, D)[:rows]
     if y_dtype == "bf16":
         G.assert_op_close(G.host(y), ref, f"LN+mod D={D} rows={rows}")
     else:

@@ -399,10 +399,13 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(SeqView q, SeqView k,
   store8(p, o);
 }
 
-// One workgroup per token: thread t owns chunks c = t + 256 i of the token's [q | k] (8
-// values each); c % 16 == t % 16, so the thread's (cos, sin) slice of the token and its
-// position in every head are fixed, and the angle table row is read once per token.
-template <class T>
+// One workgroup per token: thread t owns chunks c = t + 256 i, i < NI, of the token's
+// [q | k] (8 values each); c % 16 == t % 16, so the thread's (cos, sin) slice of the token
+// and its position in every head are fixed, and the angle table row is read once per
+// token. All NI chunks are loaded before the first is normalised, so NI loads per thread
+// are in flight at once. Unless the chunks fill all NI rounds (EXACT: heads % 8 == 0), those
+// past the token's 2 * heads * 16 (whole 32-lane groups) are computed on zeros, not stored.
+template <class T, int NI, bool EXACT>
 __global__ __launch_bounds__(256) void qk_norm_rope_token_kernel(
     SeqView q, SeqView k, int batch, int seq, int heads, const float* __restrict__ qg0,
     const float* __restrict__ kg0, const float* __restrict__ qg1, const float* __restrict__ kg1,
@@ -415,29 +418,42 @@ __global__ __launch_bounds__(256) void qk_norm_rope_token_kernel(
   const float4 c01 = c4[0], c23 = c4[1];
   const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
   const float sn[4] = {c01.y, c01.w, c23.y, c23.w};
-  for (int c = threadIdx.x; c < nch; c += 256) {
+  float x[NI][8];
+  T* ptr[NI];
+  const float* gam[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = threadIdx.x + 256 * i;
     const int which = c >= qchunks;
     const int head = (c - which * qchunks) >> 4;
     const SeqView& v = which ? k : q;
     const bool seg1 = j >= v.n0;
-    const float* g = which ? (seg1 ? kg1 : kg0) : (seg1 ? qg1 : qg0);
-    T* p = seq_ptr<T>(v, b, j) + head * 128 + l16 * 8;
-    float x[8], gm[8];
-    load8(p, x);
+    gam[i] = which ? (seg1 ? kg1 : kg0) : (seg1 ? qg1 : qg0);
+    ptr[i] = seq_ptr<T>(v, b, j) + head * 128 + l16 * 8;
+    if (EXACT || c < nch) {
+      load8(ptr[i], x[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    for (int e = 0; e < 8; ++e) ss += x[i][e] * x[i][e];
     const float r = rsqrtf(group_sum16(ss) * (1.f / 128.f) + eps);
-    load8(g + l16 * 8, gm);
+    float gm[8];
+    load8(gam[i] + l16 * 8, gm);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = x[e] * r * gm[e];
+    for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] * r * gm[e];
     float o[8];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      o[2 * t] = x[2 * t] * cc[t] - x[2 * t + 1] * sn[t];
-      o[2 * t + 1] = x[2 * t] * sn[t] + x[2 * t + 1] * cc[t];
+      o[2 * t] = x[i][2 * t] * cc[t] - x[i][2 * t + 1] * sn[t];
+      o[2 * t + 1] = x[i][2 * t] * sn[t] + x[i][2 * t + 1] * cc[t];
     }
-    store8(p, o);
+    if (EXACT || threadIdx.x + 256 * i < nch) store8(ptr[i], o);
   }
 }
 
@@ -447,16 +463,24 @@ hipError_t qk_norm_rope(int dtype, SeqView q, SeqView k, int batch, int seq, int
   const int64_t units = (int64_t)batch * seq * heads * 2;
   if (units <= 0) return hipSuccess;
   // measured on MI355X: the per-token kernel is faster up to 32 heads (4 chunks per
-  // thread), the per-(token, head) one above
+  // thread), the per-(token, head) one above (at 48 heads and 16896 tokens by 8%)
   if (heads <= 32) {
     dim3 grid((unsigned)((int64_t)batch * seq)), block(256);
-    if (dtype == DT_BF16)
-      hipLaunchKernelGGL(qk_norm_rope_token_kernel<bf16>, grid, block, 0, s, q, k, batch, seq,
-                         heads, qg0, kg0, qg1, kg1, cs, eps);
-    else
-      hipLaunchKernelGGL(qk_norm_rope_token_kernel<float>, grid, block, 0, s, q, k, batch, seq,
-                         heads, qg0, kg0, qg1, kg1, cs, eps);
-    return hipGetLastError();
+    const int ni = (heads + 7) / 8;  // chunks per thread: 2 * heads * 16 over 256 threads
+    const bool exact = heads % 8 == 0;
+#define FLUX_QKT(NI, EX)                                                                      \
+  if (ni == NI && exact == EX) {                                                             \
+    if (dtype == DT_BF16)                                                                    \
+      hipLaunchKernelGGL((qk_norm_rope_token_kernel<bf16, NI, EX>), grid, block, 0, s, q, k,  \
+                         batch, seq, heads, qg0, kg0, qg1, kg1, cs, eps);                   \
+    else                                                                                     \
+      hipLaunchKernelGGL((qk_norm_rope_token_kernel<float, NI, EX>), grid, block, 0, s, q, k, \
+                         batch, seq, heads, qg0, kg0, qg1, kg1, cs, eps);                   \
+    return hipGetLastError();                                                               \
+  }
+    FLUX_QKT(1, true) FLUX_QKT(2, true) FLUX_QKT(3, true) FLUX_QKT(4, true)
+    FLUX_QKT(1, false) FLUX_QKT(2, false) FLUX_QKT(3, false) FLUX_QKT(4, false)
+#undef FLUX_QKT
   }
   dim3 grid((units + 15) / 16), block(256);
   if (dtype == DT_BF16)

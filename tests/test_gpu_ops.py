@@ -125,7 +125,10 @@ def test_layernorm_modulate(D, rows, rpb, x_dtype, y_dtype):
 # ------------------------------------------------------------------------------------
 @pytest.mark.parametrize("D,n_txt,n_img,batch,dtype", [
     (256, 16, 64, 1, "f32"), (256, 5, 36, 2, "bf16"), (3072, 512, 1024, 1, "bf16"),
-    (4096, 512, 4096, 1, "bf16")])
+    (4096, 512, 4096, 1, "bf16"),
+    # head counts whose last chunk per thread is partial (12, 20 heads), and 48 heads
+    # (the per-(token, head) kernel)
+    (1536, 7, 36, 2, "bf16"), (2560, 3, 49, 1, "f32"), (6144, 7, 25, 1, "bf16")])
 def test_qk_norm_rope(D, n_txt, n_img, batch, dtype):
     t = G.torch()
     seed = 5 + D + n_img

@@ -132,56 +132,67 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const TX* __restrict__
   }
 }
 
-// fp32 rows of exactly 256 J values (the residual stream): lane l holds the float4s
-// 4 (l + 64 j), j < J, so every load instruction reads 1 KB contiguously. This form reads
-// the modulation from global memory chunk by chunk and is used for the wide rows (J >= 24):
-// there the LDS-staged kernel below wins only while its grid fits in one round of
-// resident workgroups and loses 4-9% on larger grids, where its per-workgroup barrier
-// costs more than its extra wave per SIMD brings.
+// fp32 rows of exactly 256 J values (the residual stream), wide rows (J >= 24): two waves
+// per row, each holding half of it (lane l of half h holds the float4s
+// 4 (h 32 J + l + 64 j), j < J / 2, so every load instruction reads 1 KB contiguously).
+// The halves' sums meet in LDS and are added in a fixed order (half 0 + half 1), so both
+// waves compute the same mean and rstd. A whole row per wave needs 208 VGPRs at J = 24
+// (2 waves per SIMD); half a row needs 114 (4 waves per SIMD).
 template <class TY, int J>
-__global__ __launch_bounds__(256) void ln_modulate_f32_regs_kernel(
+__global__ __launch_bounds__(256) void ln_modulate_f32_split_kernel(
     const float* __restrict__ x, int64_t ldx, TY* __restrict__ y, int64_t ldy, int rows, int rpb,
     const float* __restrict__ shift, const float* __restrict__ scale, int64_t mod_bs, float eps) {
-  constexpr int D = 256 * J;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)min(row, rows - 1) * ldx);
-  float4 v[J];
+  constexpr int D = 256 * J, JH = J / 2;
+  __shared__ float part[2][4];  // [sum | centred sum of squares][wave]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = w & 1;
+  const int row = blockIdx.x * 2 + (w >> 1);
+  // a wave past the last row reads that row and stores nothing (it still meets the barriers)
+  const float4* xr =
+      reinterpret_cast<const float4*>(x + (int64_t)min(row, rows - 1) * ldx) + half * 64 * JH;
+  float4 v[JH];
 #pragma unroll
-  for (int j = 0; j < J; ++j) v[j] = xr[lane + 64 * j];
+  for (int j = 0; j < JH; ++j) v[j] = xr[lane + 64 * j];
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < J; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
-  const float mean = wave_sum(s) * (1.f / D);
+  for (int j = 0; j < JH; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+  s = wave_sum(s);
+  if (lane == 0) part[0][w] = s;
+  __syncthreads();
+  const float mean = (part[0][w & 2] + part[0][w | 1]) * (1.f / D);
   float q = 0.f;
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
+  for (int j = 0; j < JH; ++j) {
     v[j].x -= mean;
     v[j].y -= mean;
     v[j].z -= mean;
     v[j].w -= mean;
     q += (v[j].x * v[j].x + v[j].y * v[j].y) + (v[j].z * v[j].z + v[j].w * v[j].w);
   }
-  const float rstd = rsqrtf(wave_sum(q) * (1.f / D) + eps);
+  q = wave_sum(q);
+  if (lane == 0) part[1][w] = q;
+  __syncthreads();
+  const float rstd = rsqrtf((part[1][w & 2] + part[1][w | 1]) * (1.f / D) + eps);
   if (row >= rows) return;
   const int b = row / rpb;
-  const float4* sh = reinterpret_cast<const float4*>(shift + b * mod_bs);
-  const float4* sc = reinterpret_cast<const float4*>(scale + b * mod_bs);
-  TY* yr = y + (int64_t)row * ldy;
+  const float4* sh = reinterpret_cast<const float4*>(shift + b * mod_bs) + half * 64 * JH;
+  const float4* sc = reinterpret_cast<const float4*>(scale + b * mod_bs) + half * 64 * JH;
+  TY* yr = y + (int64_t)row * ldy + half * 256 * JH;
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
+  for (int j = 0; j < JH; ++j) {
     const int c = lane + 64 * j;
     const float4 a = sh[c], m = sc[c];
     float o[4] = {(1.f + m.x) * (v[j].x * rstd) + a.x, (1.f + m.y) * (v[j].y * rstd) + a.y,
                   (1.f + m.z) * (v[j].z * rstd) + a.z, (1.f + m.w) * (v[j].w * rstd) + a.w};
     store_cw<TY, 4>(yr + 4 * c, o);
     // the modulation vectors' loads are issued 4 chunks at a time, not all hoisted ahead
-    // of the loop (that doubles the registers and halves the waves in flight)
+    // of the loop (that would cost the registers the split saves)
     if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// The same rows for J <= 16, the widths of the Klein models. The workgroups
+// The same rows for J <= 16 (the Klein widths), one wave per row: lane l holds the
+// float4s 4 (l + 64 j), j < J. Here the row fits one wave at 5-6 waves per SIMD, and this
+// form beats the two-wave split at the step's 4608 rows. The workgroups
 // are laid out per batch item (rows_per_batch / 4 of them, rounded up, for each item), so
 // the 4 rows of one workgroup share one shift / scale pair, which is staged in LDS while
 // the rows' loads are in flight. Reading the modulation from LDS instead of holding it in
@@ -258,14 +269,14 @@ static hipError_t ln_dispatch(const void* x, int64_t ldx, void* y, int64_t ldy, 
                        mod_bs, eps);                                                        \
     return hipGetLastError();                                                              \
   }
-#define FLUX_LN32R(J)                                                                       \
+#define FLUX_LN32S(J)                                                                       \
   if (dim == 256 * J) {                                                                     \
-    hipLaunchKernelGGL((ln_modulate_f32_regs_kernel<TY, J>), grid, block, 0, s, xp, ldx, yp, \
-                       ldy, rows, rpb, shift, scale, mod_bs, eps);                          \
+    hipLaunchKernelGGL((ln_modulate_f32_split_kernel<TY, J>), dim3((rows + 1) / 2), block, 0, \
+                       s, xp, ldx, yp, ldy, rows, rpb, shift, scale, mod_bs, eps);          \
     return hipGetLastError();                                                              \
   }
-    FLUX_LN32(12) FLUX_LN32(16) FLUX_LN32R(24) FLUX_LN32R(32)
-#undef FLUX_LN32R
+    FLUX_LN32(12) FLUX_LN32(16) FLUX_LN32S(24) FLUX_LN32S(32)
+#undef FLUX_LN32S
 #undef FLUX_LN32
   }
   // rows that fill whole sets of 64 chunks (every traced width) take the unguarded kernel

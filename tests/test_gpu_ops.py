@@ -93,7 +93,7 @@ def test_modulation(D, dtype, batch, n_chunks):
     # not a multiple of 4, a last item cut short (rows not a multiple of rows_per_batch) and
     # rows_per_batch beyond rows
     (3072, 150, 75, "f32", "bf16"), (4096, 70, 30, "f32", "bf16"), (4096, 9, 100, "f32", "f32"),
-    (6144, 222, 37, "f32", "bf16"), (8192, 37, 37, "f32", "f32")])
+    (6144, 222, 37, "f32", "bf16"), (6144, 75, 25, "f32", "f32"), (8192, 37, 37, "f32", "f32")])
 def test_layernorm_modulate(D, rows, rpb, x_dtype, y_dtype):
     t = G.torch()
     seed = 11 + rows

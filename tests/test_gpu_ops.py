@@ -90,9 +90,10 @@ def test_modulation(D, dtype, batch, n_chunks):
     (256, 80, 80, "f32", "f32"), (256, 77, 7, "bf16", "bf16"), (3072, 1536, 1536, "bf16", "bf16"),
     (4096, 4608, 4608, "f32", "bf16"), (6144, 333, 111, "bf16", "bf16"),
     # fp32 residual rows at every width of the per-item kernel: items of a row count that is
-    # not a multiple of 4, a last item cut short (rows not a multiple of rows_per_batch) and
-    # rows_per_batch beyond rows
+    # not a multiple of 4, a last item cut short (rows not a multiple of rows_per_batch),
+    # rows_per_batch beyond rows, and items of fewer rows than a workgroup's 4 waves
     (3072, 150, 75, "f32", "bf16"), (4096, 70, 30, "f32", "bf16"), (4096, 9, 100, "f32", "f32"),
+    (4096, 9, 1, "f32", "bf16"), (3072, 10, 3, "f32", "bf16"),
     (6144, 222, 37, "f32", "bf16"), (6144, 75, 25, "f32", "f32"), (8192, 37, 37, "f32", "f32")])
 def test_layernorm_modulate(D, rows, rpb, x_dtype, y_dtype):
     t = G.torch()

@@ -3,9 +3,10 @@
 //
 // LayerNorm + modulate ("双流块" AdaLN pre-norm of the Diffusers walk-through, eps 1e-6):
 //   y = (1 + scale) * (x - mean) / sqrt(var + eps) + shift   (biased variance, no affine)
-// One wave per row: the row is held in registers (each lane moves 16 bytes of the input
-// per chunk, so a wave instruction reads 1 KB contiguously), mean and variance are two
-// exact passes over the registers with wave64 shuffle reductions.
+// One wave per row (two for fp32 rows of 6144 or more values): the row is held in
+// registers (each lane moves 16 bytes of the input per chunk, so a wave instruction reads
+// 1 KB contiguously), mean and variance are two exact passes over the registers with
+// wave64 shuffle reductions.
 //
 // QK RMSNorm + RoPE ("双流块" norm_q / norm_k; "位置 id 的维度" per-axis rotary embedding,
 // theta 2000, axes 32/32/32/32): 16 lanes own one (token, head) vector of 128 values;

@@ -74,7 +74,10 @@ FLUX_DEV uint32_t lds_u32(const void* p) {
 // 16-byte global->LDS loads issued through inline asm (M0 = wave-uniform LDS byte address;
 // lane i writes LDS bytes [16 i, 16 i + 16)).  The compiler does not track these loads, so
 // it adds no conservative vmcnt(0) before later LDS reads or barriers; callers wait
-// explicitly (s_waitcnt vmcnt) before they read the data.
+// explicitly (s_waitcnt vmcnt) before they read the data.  M0 is listed as clobbered, a
+// reserved register clang warns it may not preserve: that is safe because no instruction
+// the compiler generates for these kernels uses M0 (tests/test_asm_m0.py checks the
+// gfx950 assembly of every source that includes these helpers).
 //   dma16s: global address = scalar base + per-lane 32-bit byte offset
 //   dma16v: per-lane 64-bit global address
 FLUX_DEV void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {

@@ -90,8 +90,10 @@ FLUX_DEV int attn_xcd_remap(int bid, int total) {
 }
 
 // EXTRA: key tiles past the sequence's own come from the extra source `xkv` (see KvExtra).
+// The 64 KB of LDS per workgroup allow 2 workgroups per CU: 2 waves per SIMD with 4-wave
+// workgroups (so at most 256 registers each), 1 with 2-wave ones (which may use AGPRs).
 template <int NW, bool EXTRA>
-__global__ __launch_bounds__(64 * NW, 2) void flash_attn_bf16_kernel(
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void flash_attn_bf16_kernel(
     SeqView qv, SeqView kv, const bf16* __restrict__ vt, int64_t ld_vt, int dim, SeqView ov,
     int seq, float scale_log2, int nqb, int heads, int full_units, int splits,
     float* __restrict__ partial, KvExtra xkv) {

@@ -1,0 +1,50 @@
+"""Host logic of bench.py (no GPU): the one-GPU refusal, the roofline arithmetic of the
+dominant kernel, and the HBM traffic figure being withdrawn once the GEMM sources no longer
+match the hash its counter summary records."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import flux_synth as fs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""  # no JSON line
+
+
+def test_dominant_roofline_arithmetic():
+    wl = fs.workload("klein9b_step_1024")
+    m, n, k = bench.dominant_shape(wl)
+    assert (m, n, k) == (4608, 24576, 4096)  # single-block linear1, MLP part (gate | up)
+    line = bench.dominant_roofline(wl, launches=240, mean_us=742.0)
+    flops = 2.0 * 4608 * 24576 * 4096
+    assert line["algorithmic_flops_per_launch"] == flops
+    assert line["achieved"] == pytest.approx(flops / 742e-6 / 1e12, abs=0.05)
+    assert line["peak"] == 2500.0 and line["unit"] == "TFLOP/s" and line["bound"] == "mfma"
+    assert line["frac"] == pytest.approx(line["achieved"] / 2500.0, abs=1e-4)
+    # A and W read once, the SwiGLU output (half the columns) written once, all bf16
+    assert line["algorithmic_bytes_per_launch"] == 2 * (4608 * 4096 + 24576 * 4096 + 4608 * 12288)
+    assert line["launches_timed"] == 240 and line["avg_launch_us"] == 742.0
+
+
+def test_traffic_figure_follows_the_kernel_sources(monkeypatch, tmp_path):
+    got = bench.measured_traffic()
+    assert isinstance(got, int) and got > bench.dominant_roofline(
+        fs.workload("klein9b_step_1024"), 1, 1.0)["algorithmic_bytes_per_launch"]
+    # another source set hashes differently: the committed figure no longer applies
+    other = tmp_path / "gemm.hip"
+    other.write_text("// a changed kernel\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", (str(other),))
+    assert bench.measured_traffic() is None
+    # a summary without the figure
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "missing.md"))
+    assert bench.measured_traffic() is None

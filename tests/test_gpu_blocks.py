@@ -88,6 +88,17 @@ def test_klein9b_double_block_1024():
     check_block("double", wl, inp, "Klein-9B double 1024^2")
 
 
+def test_klein9b_single_block_1024():
+    """The Klein-9B single-stream block at its real shape (D 4096, 32 heads, MLP 12288,
+    512 + 4096 tokens): the whole output element by element against the oracle.  The step's
+    24 single blocks take about three quarters of its time; this runs the dominant GEMM
+    (linear1's MLP part, 4608 x 24576 x 4096, 1728 tiles over 256 CUs: a partial last
+    round) with its real operands."""
+    wl = fs.workload("klein9b_double_1024", kind="single", seed=1009)
+    inp = fs.block_inputs(wl, kind="single")
+    check_block("single", wl, inp, "Klein-9B single 1024^2")
+
+
 def _sample(n, k, seed):
     if n == 0:
         return np.array([], dtype=np.int64)

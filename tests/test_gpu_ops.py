@@ -178,8 +178,13 @@ LIN_CASES = [  # m, n, k, dtype
 
 
 def _sample_rows(m, k=64, seed=0):
+    """First and last rows, k random rows, and two rows of every 256-row band (so every
+    output tile of the large-tile kernels is checked at some row)."""
     rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, size=k)]))
+    bands = np.arange(0, m, 256)
+    per_band = np.concatenate([np.minimum(bands + rng.integers(0, 256, size=len(bands)), m - 1)
+                               for _ in range(2)])
+    return np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, size=k), per_band]))
 
 
 def _lin_ws(use_ws):
@@ -214,7 +219,7 @@ def test_linear_store(m, n, k, dtype, use_ws):
 
 
 @pytest.mark.parametrize("use_ws", [False, True])
-@pytest.mark.parametrize("m,n,k,dtype", LIN_CASES)
+@pytest.mark.parametrize("m,n,k,dtype", LIN_CASES + [(4608, 12288, 4096, "bf16")])
 def test_linear_swiglu(m, n, k, dtype, use_ws):
     t = G.torch()
     seed = 3 * m + n + k

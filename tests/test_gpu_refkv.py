@@ -96,16 +96,16 @@ def check_against_oracle(wl, R, gh, gw, what):
         if wl.dtype == "bf16":
             # Element-wise bound.  K is stored twice in bf16 (after the projection and after
             # RMSNorm + RoPE: 2^-8 of |k|), V once.  Both also carry the bf16 LayerNorm
-            # output's rounding through the projection: a sum over the row, so its size is
-            # relative to the row's RMS, not to the element (about 2^-9/sqrt(3) = 1.1e-3 of
-            # the RMS per element, one standard deviation), plus the reference rows' own
-            # pipeline error from earlier blocks.  The maximum over a slot of ~16k values is
-            # several standard deviations: the oracle's bf16 storage mode reaches 8.8e-3 of
-            # the RMS beyond 2^-8 |ref| on these inputs, hence 1e-2 of the RMS.
+            # output's rounding through the projection (a sum over the row, so its size is
+            # relative to the row's RMS, not to the element: 2^-9/sqrt(3) = 1.1e-3 of the RMS
+            # per element) and the reference rows' own pipeline error from earlier blocks.
+            # Together that is a standard deviation of about 3e-3 of the RMS (the oracle's
+            # bf16 storage mode: nL2 2.9e-3 on these inputs), and the largest of a slot's
+            # up to ~70k values lies about 4.5 deviations out: hence 5 x 3e-3 of the RMS.
             G.assert_op_close(G.host(k), rk, f"{what}: block {l} cached K", rtol=2.0 ** -8,
-                              atol_rms=1e-2)
+                              atol_rms=1.5e-2)
             G.assert_op_close(G.host(vt), rv, f"{what}: block {l} cached V", rtol=2.0 ** -8,
-                              atol_rms=1e-2)
+                              atol_rms=1.5e-2)
         else:
             G.assert_close(G.host(k), rk, "f32", f"{what}: block {l} cached K")
             G.assert_close(G.host(vt), rv, "f32", f"{what}: block {l} cached V")

@@ -1437,29 +1437,12 @@ extern "C" int flux_linear_fp8(const flux_cfg* c, int epi, int m, int n, int k, 
 
 extern "C" size_t flux_linear_workspace_size(void) { return linear_splitk_bytes(); }
 
-extern "C" int flux_linear(const flux_cfg* c, int epi, int m, int n, int k, const void* x,
-                           int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
-                           int y_dtype, const void* resid, int64_t ldr, const float* gate,
-                           int rpb, void* ws, size_t ws_bytes, void* stream) {
-  CHECK(check_cfg(c));
-  if (m <= 0 || n <= 0 || k <= 0) return fail(FLUX_EINVAL, "m, n, k must be > 0");
-  if (k % 8) return fail(FLUX_ESHAPE, "k must be a multiple of 8");
-  const int es = esize(c->dtype);
-  if (ldx < k || ldw < k || (ldx * es) % 16 || (ldw * es) % 16)
-    return fail(FLUX_EALIGN, "ldx/ldw must be >= k and 16-byte multiples");
-  CHECK(need(x, "x"));
-  CHECK(need(w, "w"));
-  if (!y) return fail(FLUX_EINVAL, "y is NULL");
-  float* split = nullptr;
-  if (ws) {
-    if (reinterpret_cast<uintptr_t>(ws) & 255u)
-      return fail(FLUX_EWORKSPACE, "workspace is not 256-byte aligned");
-    if (ws_bytes < linear_splitk_bytes())
-      return fail(FLUX_EWORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes,
-                  linear_splitk_bytes());
-    split = static_cast<float*>(ws);
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// flux_linear / flux_linear_noalloc after the workspace is settled (split: split-K
+// scratch of linear_splitk_bytes() bytes, or NULL)
+static int linear_entry(const flux_cfg* c, int epi, int m, int n, int k, const void* x,
+                        int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
+                        int y_dtype, const void* resid, int64_t ldr, const float* gate, int rpb,
+                        float* split, hipStream_t s) {
   if (epi == FLUX_EPI_SWIGLU) {
     if (n % 2) return fail(FLUX_ESHAPE, "SwiGLU needs an even n");
     if (ldy < n / 2) return fail(FLUX_ESHAPE, "ldy < n/2");
@@ -1479,4 +1462,57 @@ extern "C" int flux_linear(const flux_cfg* c, int epi, int m, int n, int k, cons
                y_dtype, gate, n, rpb, s, split);
   }
   return fail(FLUX_EINVAL, "unknown epilogue %d", epi);
+}
+
+static int check_linear_args(const flux_cfg* c, int epi, int m, int n, int k, const void* x,
+                             int64_t ldx, const void* w, int64_t ldw, const void* y) {
+  CHECK(check_cfg(c));
+  if (m <= 0 || n <= 0 || k <= 0) return fail(FLUX_EINVAL, "m, n, k must be > 0");
+  if (k % 8) return fail(FLUX_ESHAPE, "k must be a multiple of 8");
+  const int es = esize(c->dtype);
+  if (ldx < k || ldw < k || (ldx * es) % 16 || (ldw * es) % 16)
+    return fail(FLUX_EALIGN, "ldx/ldw must be >= k and 16-byte multiples");
+  CHECK(need(x, "x"));
+  CHECK(need(w, "w"));
+  if (!y) return fail(FLUX_EINVAL, "y is NULL");
+  if (epi != FLUX_EPI_STORE && epi != FLUX_EPI_SWIGLU && epi != FLUX_EPI_GATED_RESIDUAL)
+    return fail(FLUX_EINVAL, "unknown epilogue %d", epi);
+  return FLUX_OK;
+}
+
+extern "C" int flux_linear(const flux_cfg* c, int epi, int m, int n, int k, const void* x,
+                           int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
+                           int y_dtype, const void* resid, int64_t ldr, const float* gate,
+                           int rpb, void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_linear_args(c, epi, m, n, k, x, ldx, w, ldw, y));
+  float* split = nullptr;
+  if (ws) {
+    if (reinterpret_cast<uintptr_t>(ws) & 255u)
+      return fail(FLUX_EWORKSPACE, "workspace is not 256-byte aligned");
+    if (ws_bytes < linear_splitk_bytes())
+      return fail(FLUX_EWORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes,
+                  linear_splitk_bytes());
+    split = static_cast<float*>(ws);
+  }
+  return linear_entry(c, epi, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid, ldr, gate, rpb,
+                      split, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int flux_linear_noalloc(const flux_cfg* c, int epi, int m, int n, int k, const void* x,
+                                   int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
+                                   int y_dtype, const void* resid, int64_t ldr, const float* gate,
+                                   int rpb, void* stream) {
+  CHECK(check_linear_args(c, epi, m, n, k, x, ldx, w, ldw, y));
+  float* split = nullptr;
+  size_t bytes = 0;
+  const hipError_t e = linear_static_scratch(&split, &bytes);
+  if (e != hipSuccess)
+    return fail(FLUX_EHIP, "flux_linear_noalloc: device scratch not available: %s",
+                hipGetErrorString(e));
+  // the tile planner never plans more split-K scratch than linear_splitk_bytes()
+  if (bytes < linear_splitk_bytes())
+    return fail(FLUX_EWORKSPACE, "static scratch has %zu bytes, the planner may use %zu", bytes,
+                linear_splitk_bytes());
+  return linear_entry(c, epi, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid, ldr, gate, rpb,
+                      split, static_cast<hipStream_t>(stream));
 }

@@ -837,6 +837,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// Bytes of split-K scratch the large-tile path may use (tail tiles x splits x tile).
+constexpr size_t kSplitkBytes = (size_t)256 * 256 * 256 * sizeof(float);
+
 // Raise a kernel's dynamic-LDS limit once per device.  `done` (one per kernel instance)
 // holds a bit per device whose limit is set; the first launches on a device may race from
 // several threads, so setting is serialised and the bit is published after it.
@@ -870,6 +873,7 @@ static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t 
   const int tail = splits > 1 ? tiles % slots : 0;
   const int full = tiles - tail;
   if (tail == 0) splits = 1;
+  if ((size_t)tail * splits * BM * BN * sizeof(float) > kSplitkBytes) return hipErrorInvalidValue;
   const size_t lds = (size_t)ST * (BM + BN) * BK * sizeof(bf16);
   static LdsLimit limit;
   hipError_t le = ensure_lds_limit(
@@ -902,6 +906,7 @@ static hipError_t launch_lds_fp8(const fp8* A, int64_t lda, const fp8* W, int64_
   const int tail = splits > 1 ? tiles % slots : 0;
   const int full = tiles - tail;
   if (tail == 0) splits = 1;
+  if ((size_t)tail * splits * BM * BN * sizeof(float) > kSplitkBytes) return hipErrorInvalidValue;
   const size_t lds = (size_t)ST * (BM + BN) * BK;
   static LdsLimit limit;
   hipError_t le = ensure_lds_limit(
@@ -922,8 +927,6 @@ static hipError_t launch_lds_fp8(const fp8* A, int64_t lda, const fp8* W, int64_
   return hipGetLastError();
 }
 
-// Bytes of split-K scratch the large-tile path may use (tail tiles x splits x tile).
-constexpr size_t kSplitkBytes = (size_t)256 * 256 * 256 * sizeof(float);
 
 // Choose the tile configuration (and split-K of the last partial round) with the smallest
 // estimated time.  A round of resident workgroups costs its MACs at about 1 PFLOP/s over
@@ -1169,6 +1172,38 @@ hipError_t linear_fp8(const LinearArgs& a, const float* sa, const float* sw, hip
 }
 
 size_t linear_splitk_bytes() { return kSplitkBytes; }
+
+// Split-K scratch of flux_linear_noalloc: a fixed device array (each device that loads the
+// library holds its own copy until the process ends), for callers that cannot allocate.
+// Its size is the most the tile planner ever uses (kSplitkBytes), so every shape flux_linear
+// accepts fits.  In host code `scratch` names a host-side stand-in, not the device
+// array: the device address is resolved once per device with hipGetSymbolAddress (with
+// that device current) and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[kSplitkBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+}  // namespace
+
+hipError_t linear_static_scratch(float** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = static_cast<float*>(g_scratch_dev[dev]);
+  *bytes = kSplitkBytes;
+  return hipSuccess;
+}
 
 hipError_t linear(int dtype, const LinearArgs& a, hipStream_t s) {
   return dtype == DT_BF16 ? linear_t<bf16>(a, s) : linear_t<float>(a, s);

@@ -39,6 +39,9 @@ struct LinearArgs {
 
 // scratch size that enables every split-K choice of linear()
 size_t linear_splitk_bytes();
+// Device address (for the current device) and size of the library's fixed split-K scratch
+// array, the one flux_linear_noalloc uses; resolved once per device.
+hipError_t linear_static_scratch(float** ptr, size_t* bytes);
 
 // y = x W^T with epilogue; dtype = type of x and W (DT_BF16 -> MFMA path).
 hipError_t linear(int dtype, const LinearArgs& a, hipStream_t s);

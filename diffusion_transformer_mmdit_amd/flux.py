@@ -129,6 +129,8 @@ _PROTOS = {
     "flux_linear_workspace_size": (c_size, []),
     "flux_linear": (c_int, [P(flux_cfg), c_int, c_int, c_int, c_int, vp, c_i64, vp, c_i64, vp,
                             c_i64, c_int, vp, c_i64, vp, c_int, vp, c_size, vp]),
+    "flux_linear_noalloc": (c_int, [P(flux_cfg), c_int, c_int, c_int, c_int, vp, c_i64, vp,
+                                    c_i64, vp, c_i64, c_int, vp, c_i64, vp, c_int, vp]),
 }
 
 EXPORTED = tuple(_PROTOS)
@@ -461,3 +463,10 @@ def flux_linear(cfg, epilogue, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid=N
     _check(lib().flux_linear(ctypes.byref(cfg), epilogue, m, n, k, _ptr(x), ldx, _ptr(w), ldw,
                              _ptr(y), ldy, y_dtype, _ptr(resid), ldr, _ptr(gate), rows_per_batch,
                              _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def flux_linear_noalloc(cfg, epilogue, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid=None,
+                        ldr=0, gate=None, rows_per_batch=1, stream=None):
+    _check(lib().flux_linear_noalloc(ctypes.byref(cfg), epilogue, m, n, k, _ptr(x), ldx, _ptr(w),
+                                     ldw, _ptr(y), ldy, y_dtype, _ptr(resid), ldr, _ptr(gate),
+                                     rows_per_batch, _stream(stream)))

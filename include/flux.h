@@ -399,6 +399,22 @@ int flux_linear(const flux_cfg* cfg, int epilogue, int m, int n, int k, const vo
                 const void* resid, int64_t ldr, const float* gate, int rows_per_batch,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* flux_linear for callers that cannot allocate memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation with the split-K
+ * scratch taken from a fixed device array inside the library instead of a workspace.  The
+ * array holds flux_linear_workspace_size() bytes (64 MiB), the most the tile planner ever
+ * uses, so every shape flux_linear accepts fits and results equal flux_linear's with a
+ * workspace bit for bit; each device holds its own copy from its first call until the
+ * process ends.  The call allocates nothing (no hipMalloc / hipFree, no allocating library
+ * routine).  Every call on a device shares that device's array: calls that may overlap on
+ * one device (different streams, or host threads) race and must be serialised by the
+ * caller.  Errors: those of flux_linear, and FLUX_EHIP if the array's device address cannot
+ * be resolved. */
+int flux_linear_noalloc(const flux_cfg* cfg, int epilogue, int m, int n, int k, const void* x,
+                        int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
+                        int y_dtype, const void* resid, int64_t ldr, const float* gate,
+                        int rows_per_batch, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

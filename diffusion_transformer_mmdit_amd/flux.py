@@ -15,12 +15,13 @@ from typing import Mapping
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libflux.so")
 
-FLUX_OK, FLUX_EINVAL, FLUX_ESHAPE, FLUX_EDTYPE, FLUX_EALIGN, FLUX_EWORKSPACE, FLUX_EHIP = range(7)
+FLUX_OK, FLUX_EINVAL, FLUX_ESHAPE, FLUX_EDTYPE, FLUX_EALIGN, FLUX_EWORKSPACE, FLUX_EHIP = (
+    0, -1, -2, -3, -4, -5, -6)
 FLUX_BF16, FLUX_F32 = 0, 1
 FLUX_EPI_STORE, FLUX_EPI_SWIGLU, FLUX_EPI_GATED_RESIDUAL = 0, 1, 2
 
-STATUS_NAMES = {0: "FLUX_OK", 1: "FLUX_EINVAL", 2: "FLUX_ESHAPE", 3: "FLUX_EDTYPE",
-                4: "FLUX_EALIGN", 5: "FLUX_EWORKSPACE", 6: "FLUX_EHIP"}
+STATUS_NAMES = {0: "FLUX_OK", -1: "FLUX_EINVAL", -2: "FLUX_ESHAPE", -3: "FLUX_EDTYPE",
+                -4: "FLUX_EALIGN", -5: "FLUX_EWORKSPACE", -6: "FLUX_EHIP"}
 
 
 class FluxError(RuntimeError):

@@ -41,14 +41,15 @@
 extern "C" {
 #endif
 
+/* Status of every int-returning entry point: 0 on success, a negative code on error. */
 typedef enum {
   FLUX_OK = 0,
-  FLUX_EINVAL = 1,     /* NULL pointer, non-positive size, unsupported value        */
-  FLUX_ESHAPE = 2,     /* inconsistent dimensions (dim != heads*head_dim, ...)      */
-  FLUX_EDTYPE = 3,     /* unknown dtype                                             */
-  FLUX_EALIGN = 4,     /* pointer or leading dimension not 16-byte aligned          */
-  FLUX_EWORKSPACE = 5, /* workspace NULL / too small / not 256-byte aligned         */
-  FLUX_EHIP = 6        /* HIP runtime error while enqueuing                         */
+  FLUX_EINVAL = -1,     /* NULL pointer, non-positive size, unsupported value        */
+  FLUX_ESHAPE = -2,     /* inconsistent dimensions (dim != heads*head_dim, ...)      */
+  FLUX_EDTYPE = -3,     /* unknown dtype                                             */
+  FLUX_EALIGN = -4,     /* pointer or leading dimension not 16-byte aligned          */
+  FLUX_EWORKSPACE = -5, /* workspace NULL / too small / not 256-byte aligned         */
+  FLUX_EHIP = -6        /* HIP runtime error while enqueuing                         */
 } flux_status;
 
 typedef enum { FLUX_BF16 = 0, FLUX_F32 = 1 } flux_dtype;

@@ -267,3 +267,16 @@ def test_weight_structures_keep_their_tensors_alive():
         gc.collect()
         assert probe() is not None, f"{kind}_weights let its tensors be freed"
         del s
+
+
+def test_status_codes_match_the_header():
+    """The binding's status constants are the header's flux_status values (0 = OK, errors
+    negative)."""
+    src = open(HEADER).read()
+    vals = dict((n, int(v)) for n, v in re.findall(r"(FLUX_E?[A-Z]+)\s*=\s*(-?\d+)\s*,?\s*/\*", src)
+                if n.startswith(("FLUX_E", "FLUX_OK")))
+    vals["FLUX_OK"] = int(re.search(r"FLUX_OK\s*=\s*(-?\d+)", src).group(1))
+    for name in ("FLUX_OK", "FLUX_EINVAL", "FLUX_ESHAPE", "FLUX_EDTYPE", "FLUX_EALIGN",
+                 "FLUX_EWORKSPACE", "FLUX_EHIP"):
+        assert getattr(F, name) == vals[name], name
+        assert name == "FLUX_OK" or vals[name] < 0

@@ -167,8 +167,19 @@ static int check_cfg(const flux_cfg* c) {
   if (!(c->rope_theta > 0.f)) return fail(FLUX_EINVAL, "rope_theta must be > 0");
   if (!(c->eps > 0.f)) return fail(FLUX_EINVAL, "eps must be > 0");
   if (c->dim > 8192) return fail(FLUX_ESHAPE, "dim > 8192 is not supported");
+  if (c->precision != FLUX_PRECISION_BF16 && c->precision != FLUX_PRECISION_SPLIT)
+    return fail(FLUX_EINVAL, "unknown precision %d", c->precision);
+  if (c->precision == FLUX_PRECISION_SPLIT) {
+    if (c->dtype != FLUX_BF16) return fail(FLUX_EDTYPE, "FLUX_PRECISION_SPLIT needs FLUX_BF16");
+    if (c->mlp_hidden % 64)
+      return fail(FLUX_ESHAPE, "FLUX_PRECISION_SPLIT needs mlp_hidden % 64 == 0 (got %d)",
+                  c->mlp_hidden);
+  }
   return FLUX_OK;
 }
+
+// hi / lo operands (FLUX_PRECISION_SPLIT): 2 planes, else 1
+static int planes(const flux_cfg* c) { return c->precision == FLUX_PRECISION_SPLIT ? 2 : 1; }
 
 static int check_sizes(int batch, int n_img, int n_txt) {
   if (batch <= 0) return fail(FLUX_EINVAL, "batch must be > 0 (got %d)", batch);
@@ -262,8 +273,10 @@ static int lin(const flux_cfg* c, int epi, int m, int n, int k, const void* x, i
                const void* w, int64_t ldw, void* y, int64_t ldy, int y_dtype,
                const void* resid = nullptr, int64_t ldr = 0, int r_dtype = FLUX_F32,
                const float* gate = nullptr, int64_t gate_bs = 0, int rpb = 1, hipStream_t s = 0,
-               float* split_ws = nullptr) {
+               float* split_ws = nullptr, int kdup = 0, bool swiglu_lo = false) {
   LinearArgs a{};
+  a.kdup = kdup;
+  a.swiglu_lo = swiglu_lo;
   a.epilogue = epi;
   a.m = m;
   a.n = n;
@@ -286,16 +299,19 @@ static int lin(const flux_cfg* c, int epi, int m, int n, int k, const void* x, i
   return FLUX_OK;
 }
 
-// q | k row-major into qk [m, 2D]; v transposed into vt [B*D, ldvt] at token offset vt_off
+// q | k row-major into qk [m, 2D]; v transposed into vt [B*D, ldvt] at token offset vt_off.
+// x: [m, D] or, with hi / lo operands, [m, 2D] (hi | lo planes).
 static int lin_qkv(const flux_cfg* c, int m, const void* x, const void* w, void* qk, void* vt,
                    int64_t ldvt, int vt_off, int rpb, hipStream_t s, float* split_ws) {
   LinearArgs a{};
+  const int P = planes(c);
   a.epilogue = EPI_QKV;
   a.m = m;
   a.n = 3 * c->dim;
-  a.k = c->dim;
+  a.k = P * c->dim;
+  a.kdup = (P - 1) * c->dim;
   a.x = x;
-  a.ldx = c->dim;
+  a.ldx = P * c->dim;
   a.w = w;
   a.ldw = c->dim;
   a.y = qk;
@@ -336,6 +352,7 @@ struct RefSlot {
 // them as extra keys.
 enum RefUse { REF_NONE = 0, REF_FILL = 1, REF_KEYS = 2 };
 
+// With hi / lo operands (FLUX_PRECISION_SPLIT) ln and mlp hold two planes per row.
 struct DoubleScratch {
   void* ln[2];    // [B*N_s, D] compute dtype       (0 = txt, 1 = img)
   void* qk[2];    // [B*N_s, 2D] q | k
@@ -348,16 +365,16 @@ struct DoubleScratch {
 
 static DoubleScratch carve_double(Carver& cv, const flux_cfg* c, int B, int Ni, int Nt) {
   DoubleScratch d;
-  const int es = esize(c->dtype);
+  const int es = esize(c->dtype), P = planes(c);
   const int D = c->dim, H = c->mlp_hidden;
   const int n[2] = {Nt, Ni};
   for (int i = 0; i < 2; ++i) {
     const size_t rows = (size_t)B * n[i];
-    d.ln[i] = cv.take<char>(rows * D * es);
+    d.ln[i] = cv.take<char>(rows * P * D * es);
     d.qk[i] = cv.take<char>(rows * 2 * D * es);
     d.o[i] = cv.take<char>(rows * D * es);
     d.mid[i] = cv.take<float>(rows * D);
-    d.mlp[i] = cv.take<char>(rows * H * es);
+    d.mlp[i] = cv.take<char>(rows * P * H * es);
   }
   d.vt = cv.take<char>((size_t)B * D * vt_pitch(Ni + Nt) * es);
   d.split = cv.take<float>(split_scratch_bytes() / sizeof(float));
@@ -411,11 +428,18 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
   const bool fill = ref_use == REF_FILL;
   void* qk[2] = {d.qk[0], fill ? ref->qk : d.qk[1]};
   void* vtb = fill ? ref->vt : d.vt;
+  const int P = planes(c);
+  // LayerNorm + modulate into ln (two planes: hi | lo with FLUX_PRECISION_SPLIT)
+  auto ln_mod = [&](int dt, const void* x, void* y, int rows, int rpb, const float* sh,
+                    const float* sc) -> hipError_t {
+    if (P == 2)
+      return layernorm_modulate_hilo(dt, x, D, y, 2 * D, rows, D, rpb, sh, sc, mbs, c->eps, s);
+    return layernorm_modulate(dt, T, x, D, y, D, rows, D, rpb, sh, sc, mbs, c->eps, s);
+  };
   for (int i = 0; i < 2; ++i) {
     if (n[i] == 0) continue;
     const int rows = B * n[i];
-    HIP_TRY(layernorm_modulate(in_dt, T, in[i], D, d.ln[i], D, rows, D, n[i], mods[i],
-                               mods[i] + D, mbs, c->eps, s));
+    HIP_TRY(ln_mod(in_dt, in[i], d.ln[i], rows, n[i], mods[i], mods[i] + D));
     CHECK(lin_qkv(c, rows, d.ln[i], sw[i]->qkv, qk[i], vtb, ldvt, i == 0 ? 0 : Nt, n[i], s,
                   d.split));
   }
@@ -446,13 +470,13 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
     // x + gate1 * (O W_o^T)  -> mid (f32)
     CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D, d.o[i], D, sw[i]->out, D, d.mid[i], D, FLUX_F32,
               in[i], D, in_dt, mods[i] + 2 * D, mbs, n[i], s, d.split));
-    HIP_TRY(layernorm_modulate(FLUX_F32, T, d.mid[i], D, d.ln[i], D, rows, D, n[i],
-                               mods[i] + 3 * D, mods[i] + 4 * D, mbs, c->eps, s));
-    CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln[i], D, sw[i]->mlp_in, D, d.mlp[i], H, T,
-              nullptr, 0, 0, nullptr, 0, 1, s, d.split));
+    HIP_TRY(ln_mod(FLUX_F32, d.mid[i], d.ln[i], rows, n[i], mods[i] + 3 * D, mods[i] + 4 * D));
+    CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, P * D, d.ln[i], P * D, sw[i]->mlp_in, D, d.mlp[i],
+              P * H, T, nullptr, 0, 0, nullptr, 0, 1, s, d.split, (P - 1) * D, P == 2));
     // mid + gate2 * (M W_out^T) -> out
-    CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, H, d.mlp[i], H, sw[i]->mlp_out, H, out[i], D,
-              out_dt, d.mid[i], D, FLUX_F32, mods[i] + 5 * D, mbs, n[i], s, d.split));
+    CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, P * H, d.mlp[i], P * H, sw[i]->mlp_out, H, out[i],
+              D, out_dt, d.mid[i], D, FLUX_F32, mods[i] + 5 * D, mbs, n[i], s, d.split,
+              (P - 1) * H));
   }
   return FLUX_OK;
 }
@@ -518,21 +542,22 @@ extern "C" int flux_double_block_fwd(const flux_cfg* c, const flux_double_weight
 // single-stream block (on the merged [txt ; img] sequence)
 // ------------------------------------------------------------------------------------
 struct SingleScratch {
-  void* ln;   // [B*L, D]
+  void* ln;   // [B*L, D]  (hi | lo planes: [B*L, 2D])
   void* qk;   // [B*L, 2D] q | k
   void* vt;   // [B*D, vt_pitch(L)] V^T
   void* cat;  // [B*L, D + H]  = [attention output | SwiGLU output]
+              // (hi / lo: [B*L, D + 2H] = [attention output | SwiGLU hi | SwiGLU lo])
   float* split;  // split-K scratch of the linear layers
 };
 
 static SingleScratch carve_single(Carver& cv, const flux_cfg* c, int B, int L) {
   SingleScratch d;
-  const int es = esize(c->dtype);
+  const int es = esize(c->dtype), P = planes(c);
   const size_t rows = (size_t)B * L;
-  d.ln = cv.take<char>(rows * c->dim * es);
+  d.ln = cv.take<char>(rows * P * c->dim * es);
   d.qk = cv.take<char>(rows * 2 * c->dim * es);
   d.vt = cv.take<char>((size_t)B * c->dim * vt_pitch(L) * es);
-  d.cat = cv.take<char>(rows * (c->dim + c->mlp_hidden) * es);
+  d.cat = cv.take<char>(rows * (c->dim + P * c->mlp_hidden) * es);
   d.split = cv.take<float>(split_scratch_bytes() / sizeof(float));
   return d;
 }
@@ -557,13 +582,17 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
                       int in_dt, void* out, int out_dt, const float* mod, const float2* cs,
                       const SingleScratch& d, hipStream_t s, const RefSlot* ref = nullptr,
                       int ref_use = REF_NONE, bool kv_only = false) {
-  const int D = c->dim, H = c->mlp_hidden, T = c->dtype, es = esize(T);
+  const int D = c->dim, H = c->mlp_hidden, T = c->dtype, es = esize(T), P = planes(c);
   const int rows = B * L;
-  const int64_t mbs = 3 * (int64_t)D, ldc = D + H;
+  const int64_t mbs = 3 * (int64_t)D, ldc = D + P * H;
   const bool fill = ref_use == REF_FILL;
   void* qkb = fill ? ref->qk : d.qk;
   void* vtb = fill ? ref->vt : d.vt;
-  HIP_TRY(layernorm_modulate(in_dt, T, x, D, d.ln, D, rows, D, L, mod, mod + D, mbs, c->eps, s));
+  if (P == 2)
+    HIP_TRY(layernorm_modulate_hilo(in_dt, x, D, d.ln, 2 * D, rows, D, L, mod, mod + D, mbs,
+                                    c->eps, s));
+  else
+    HIP_TRY(layernorm_modulate(in_dt, T, x, D, d.ln, D, rows, D, L, mod, mod + D, mbs, c->eps, s));
   const int64_t ldvt = vt_pitch(L);
   {
     TimedSite ts(fill ? 0 : FLUX_SITE_SINGLE_QKV, s);
@@ -584,9 +613,9 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
   }
   {
     TimedSite ts(fill ? 0 : FLUX_SITE_SINGLE_MLP_IN, s);
-    CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, D, d.ln, D, w_mlp, D,
+    CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, P * D, d.ln, P * D, w_mlp, D,
               static_cast<char*>(d.cat) + (size_t)D * es, ldc, T, nullptr, 0, 0, nullptr, 0, 1,
-              s, d.split));
+              s, d.split, (P - 1) * D, P == 2));
   }
   auto view = [&](void* base, int col, int64_t ld) {
     SeqView v;
@@ -608,8 +637,9 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
                       ref_use == REF_KEYS ? &xk : nullptr));
   }
   TimedSite ts(fill ? 0 : FLUX_SITE_SINGLE_LINEAR2, s);
-  CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D + H, d.cat, ldc, w->linear2, D + H, out, D, out_dt,
-            x, D, in_dt, mod + 2 * D, mbs, L, s, d.split));
+  // [O | M] W2^T, or with hi / lo [O | M_hi | M_lo] whose M_lo columns repeat W2's M columns
+  CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, (int)ldc, d.cat, ldc, w->linear2, D + H, out, D,
+            out_dt, x, D, in_dt, mod + 2 * D, mbs, L, s, d.split, (P - 1) * H));
   return FLUX_OK;
 }
 
@@ -699,7 +729,7 @@ struct StepBufs {
   float* res;      // merged residual [B, L, D] f32
   float* res_txt;  // double-phase stream residuals (alias into res when B == 1)
   float* res_img;
-  void* ln_head;   // [B*Ni, D] compute dtype
+  void* ln_head;   // [B*Ni, D] compute dtype; bf16: [B*Ni, 2D] hi | lo planes
   DoubleScratch d;
   SingleScratch sg;
 };
@@ -721,7 +751,8 @@ static StepBufs carve_step(Carver& cv, const flux_cfg* c, int B, int Ni, int Nt)
     sb.res_txt = cv.take<float>((size_t)B * Nt * D);
     sb.res_img = cv.take<float>((size_t)B * Ni * D);
   }
-  sb.ln_head = cv.take<char>((size_t)B * Ni * D * esize(c->dtype));
+  const bool hilo = c->dtype == FLUX_BF16;
+  sb.ln_head = cv.take<char>((size_t)B * Ni * D * esize(c->dtype) * (hilo ? 2 : 1));
   // block scratch: the double and single phases never overlap, so they share memory
   Carver dc(cv.base ? cv.base + ((cv.off + 255) & ~size_t(255)) : nullptr);
   sb.d = carve_double(dc, c, B, Ni, Nt);
@@ -817,6 +848,21 @@ static int run_step(const flux_cfg* c, const flux_model_weights* w, const float*
                      sb.mod_single, sb.rb.cs, sb.sg, s, &slot, use));
   }
   // head: keep image tokens, final LayerNorm + modulate, proj_out
+  if (T == FLUX_BF16) {
+    // The projection's input is the one bf16 operand whose rounding reaches the output
+    // without passing another block: it is carried as bf16 hi + lo planes, and one GEMM
+    // over K = 2D reads proj_out for both (fp32 accumulation).
+    for (int b = 0; b < B; ++b) {
+      const float* rows = sb.res + ((size_t)b * L + Nt) * D;
+      void* lnb = static_cast<char*>(sb.ln_head) + (size_t)b * Ni * 2 * D * 2;
+      HIP_TRY(layernorm_modulate_hilo(FLUX_F32, rows, D, lnb, 2 * D, Ni, D, Ni,
+                                      sb.mod_final + (size_t)b * 2 * D,
+                                      sb.mod_final + (size_t)b * 2 * D + D, 2 * D, c->eps, s));
+    }
+    CHECK(lin(c, EPI_STORE, B * Ni, c->in_channels, 2 * D, sb.ln_head, 2 * D, w->proj_out, D,
+              out, c->in_channels, FLUX_F32, nullptr, 0, 0, nullptr, 0, 1, s, sb.sg.split, D));
+    return FLUX_OK;
+  }
   for (int b = 0; b < B; ++b) {
     const float* rows = sb.res + ((size_t)b * L + Nt) * D;
     void* lnb = static_cast<char*>(sb.ln_head) + (size_t)b * Ni * D * esize(T);

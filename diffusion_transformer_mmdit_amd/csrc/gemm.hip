@@ -80,6 +80,7 @@ struct EpiSwiGLU {
   TY* y;
   int64_t ldy;
   int n_half;  // H
+  bool lo = false;  // also store lo = v - hi at column H + j (bf16 hi / lo pair)
   static constexpr bool kPaired = true;
   static constexpr bool kQuad = false;
   static constexpr bool kRow4 = false;
@@ -89,7 +90,10 @@ struct EpiSwiGLU {
     return ((n >> 5) & 1) ? H + j : j;
   }
   FLUX_DEV void pair(int m, int j, float g, float u) const {
-    y[m * ldy + j] = from_f32<TY>(silu_f(g) * u);
+    const float v = silu_f(g) * u;
+    const TY h = from_f32<TY>(v);
+    y[m * ldy + j] = h;
+    if (lo) y[m * ldy + n_half + j] = from_f32<TY>(v - to_f32(h));
   }
 };
 
@@ -204,7 +208,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
                                                              int64_t lda,
                                                              const bf16* __restrict__ W,
                                                              int64_t ldw, int M, int N, int K,
-                                                             int n_half, int tiles_n, Epi epi) {
+                                                             int kw, int kdup, int n_half,
+                                                             int tiles_n, Epi epi) {
   constexpr int WGM = 2, WGN = 2;                // 2 x 2 waves
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA tiles per wave
@@ -271,12 +276,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
   uint4 ra[LA], rb[LB];
   auto load_slice = [&](int k0) {
     const bool kin = (k0 + c8 * 8) < K;
+    const int kb = (k0 + c8 * 8 >= kw) ? k0 - kdup : k0;  // W column of the hi / lo repeat
 #pragma unroll
     for (int i = 0; i < LA; ++i)
       ra[i] = (a_ok[i] && kin) ? ld16(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < LB; ++i)
-      rb[i] = (b_ok[i] && kin) ? ld16(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
+      rb[i] = (b_ok[i] && kin) ? ld16(b_src[i] + kb) : make_uint4(0, 0, 0, 0);
   };
   auto store_slice = [&](int buf) {
     bf16* as = As + buf * BM * kBK;
@@ -426,7 +432,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 // 64 or 128 bytes either way, so the load plan, the LDS layout and the schedule are shared.
 template <class TIn, int BM, int BN, int BK, int ST, int NWM, int NWN, class Epi>
 FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* __restrict__ W,
-                            int64_t ldw, int M, int N, int K, int n_half, int tiles_m,
+                            int64_t ldw, int M, int N, int K, int kw, int kdup, int n_half,
+                            int tiles_m,
                             int tiles_n, int full_tiles, int splits, float* __restrict__ partial,
                             Epi epi, const float* __restrict__ sa, const float* __restrict__ sw) {
   constexpr int ES = sizeof(TIn);
@@ -498,10 +505,13 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_u32(smem));
   auto dma = [&](int q, int stage, int k0) {  // q-th load instruction of this wave's share
     const uint32_t sb = lds0 + (uint32_t)stage * STAGE_B;
-    if (q < AI)
+    if (q < AI) {
       dma16s(A + k0, a_off[q], sb + (uint32_t)((wave * AI + q) * RPI * BK * ES));
-    else
-      dma16s(W + k0, b_off[q - AI], sb + (uint32_t)(BM * BK * ES + (wave * BI + q - AI) * RPI * BK * ES));
+    } else {
+      // slices past kw repeat W columns (the lo plane of a hi / lo operand)
+      const int kb = k0 >= kw ? k0 - kdup : k0;
+      dma16s(W + kb, b_off[q - AI], sb + (uint32_t)(BM * BK * ES + (wave * BI + q - AI) * RPI * BK * ES));
+    }
   };
 
   f32x16 acc[TM][TN];
@@ -758,11 +768,11 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
 template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
 __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw, int M,
-    int N, int K, int n_half, int tiles_m, int tiles_n, int full_tiles, int splits,
-    float* __restrict__ partial, Epi epi) {
-  gemm_lds_body<bf16, BM, BN, BK, ST, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, n_half, tiles_m,
-                                                     tiles_n, full_tiles, splits, partial, epi,
-                                                     nullptr, nullptr);
+    int N, int K, int kw, int kdup, int n_half, int tiles_m, int tiles_n, int full_tiles,
+    int splits, float* __restrict__ partial, Epi epi) {
+  gemm_lds_body<bf16, BM, BN, BK, ST, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, kw, kdup, n_half,
+                                                     tiles_m, tiles_n, full_tiles, splits,
+                                                     partial, epi, nullptr, nullptr);
 }
 
 template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
@@ -771,9 +781,9 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_fp8_lds_kernel(
     int N, int K, int n_half, int tiles_m, int tiles_n, int full_tiles, int splits,
     float* __restrict__ partial, Epi epi, const float* __restrict__ sa,
     const float* __restrict__ sw) {
-  gemm_lds_body<fp8, BM, BN, BK, ST, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, n_half, tiles_m,
-                                                    tiles_n, full_tiles, splits, partial, epi, sa,
-                                                    sw);
+  gemm_lds_body<fp8, BM, BN, BK, ST, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, K, 0, n_half,
+                                                    tiles_m, tiles_n, full_tiles, splits, partial,
+                                                    epi, sa, sw);
 }
 
 // Split-K tail: sum the `splits` partial tiles of each tail tile in a fixed order (so the
@@ -865,8 +875,8 @@ static hipError_t ensure_lds_limit(LdsLimit& st, const void* fn, size_t bytes) {
 // Launch one large-tile configuration (sets the dynamic LDS limit once per instance).
 template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
 static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N,
-                             int K, int n_half, const Epi& epi, int splits, float* partial,
-                             hipStream_t s) {
+                             int K, int kw, int kdup, int n_half, const Epi& epi, int splits,
+                             float* partial, hipStream_t s) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int tiles = tiles_m * tiles_n;
   const int slots = 256 * OCC;
@@ -883,7 +893,7 @@ static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t 
   if (le != hipSuccess) return le;
   hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
                      dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, A, lda, W, ldw, M, N,
-                     K, n_half, tiles_m, tiles_n, full, splits, partial, epi);
+                     K, kw, kdup, n_half, tiles_m, tiles_n, full, splits, partial, epi);
   if (tail > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1040,8 +1050,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 template <class T, class Epi>
 static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw, int M, int N,
                          int K, int n_half, const Epi& epi, hipStream_t s,
-                         float* split_ws = nullptr) {
+                         float* split_ws = nullptr, int kdup = 0) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  const int kw = K - kdup;  // W columns; A columns past kw repeat W columns [kw - kdup, kw)
   if constexpr (sizeof(T) == 2) {
     // the large-tile kernel addresses operands with 32-bit byte offsets from their base
     const bool off32 = (int64_t)M * lda * 2 < (int64_t{1} << 32) &&
@@ -1052,21 +1063,22 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
       auto* a = static_cast<const bf16*>(A);
       auto* w = static_cast<const bf16*>(W);
       if (best == 0)
-        return launch_lds<256, 256, 64, 2, 1, 4, 2>(a, lda, w, ldw, M, N, K, n_half, epi,
-                                                     best_split, split_ws, s);
+        return launch_lds<256, 256, 64, 2, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
+                                                     epi, best_split, split_ws, s);
       if (best == 1)
-        return launch_lds<256, 128, 64, 2, 1, 4, 2>(a, lda, w, ldw, M, N, K, n_half, epi,
-                                                     best_split, split_ws, s);
-      return launch_lds<128, 128, 64, 2, 2, 2, 2>(a, lda, w, ldw, M, N, K, n_half, epi, best_split,
-                                                   split_ws, s);
+        return launch_lds<256, 128, 64, 2, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
+                                                     epi, best_split, split_ws, s);
+      return launch_lds<128, 128, 64, 2, 2, 2, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half, epi,
+                                                   best_split, split_ws, s);
     }
     constexpr int BM = 128, BN = 128;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const size_t lds = 2 * (BM + BN) * kBK * sizeof(bf16);
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi>), dim3(tiles_m * tiles_n), dim3(kThreads),
                        lds, s, static_cast<const bf16*>(A), lda, static_cast<const bf16*>(W), ldw,
-                       M, N, K, n_half, tiles_n, epi);
+                       M, N, K, kw, kdup, n_half, tiles_n, epi);
   } else {
+    if (kdup) return hipErrorInvalidValue;  // hi / lo operands are a bf16-path feature
     dim3 grid((N + 63) / 64, (M + 63) / 64);
     hipLaunchKernelGGL((gemm_f32_kernel<Epi>), grid, dim3(256), 0, s,
                        static_cast<const float*>(A), lda, static_cast<const float*>(W), ldw, M,
@@ -1080,7 +1092,7 @@ static hipError_t gated2(const LinearArgs& a, hipStream_t s) {
   EpiGatedResid<TY, TR> epi{static_cast<TY*>(a.y), a.ldy, static_cast<const TR*>(a.resid),
                             a.ldr, a.gate, a.gate_bs, a.rows_per_batch};
   epi.set_vec();
-  return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws);
+  return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws, a.kdup);
 }
 
 template <class T>
@@ -1097,22 +1109,24 @@ static hipError_t linear_t(const LinearArgs& a, hipStream_t s) {
       if (a.y_dtype == DT_F32) {
         EpiStore<float> epi{static_cast<float*>(a.y), a.ldy};
         epi.set_vec();
-        return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws);
+        return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws, a.kdup);
       } else {
         EpiStore<bf16> epi{static_cast<bf16*>(a.y), a.ldy};
         epi.set_vec();
-        return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws);
+        return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws, a.kdup);
       }
-    case EPI_SWIGLU:
-      return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, a.n / 2,
-                       EpiSwiGLU<T>{static_cast<T*>(a.y), a.ldy, a.n / 2}, s, a.split_ws);
+    case EPI_SWIGLU: {
+      EpiSwiGLU<T> epi{static_cast<T*>(a.y), a.ldy, a.n / 2, a.swiglu_lo};
+      return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, a.n / 2, epi, s, a.split_ws,
+                       a.kdup);
+    }
     case EPI_GATED_RESIDUAL:
       return gated<T>(a, s);
     case EPI_QKV: {
       EpiQKV<T> epi{static_cast<T*>(a.y), a.ldy, static_cast<T*>(a.vt), a.ldvt,
                     2 * a.dim, a.dim, a.rows_per_batch, a.vt_off};
       epi.set_vec();
-      return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws);
+      return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws, a.kdup);
     }
   }
   return hipErrorInvalidValue;

@@ -35,6 +35,13 @@ struct LinearArgs {
   // optional scratch of linear_splitk_bytes() bytes: lets the large-tile path split the
   // last partial round of tiles along K (nullptr: never split)
   float* split_ws;
+  // hi / lo operands: x has k = kw + kdup columns whose last kdup repeat the W columns
+  // [kw - kdup, kw) (x column c >= kw reads W column c - kdup), so one product sums
+  // x_hi W^T + x_lo W^T.  kdup = 0: plain (W has k columns).  kw and kdup are multiples of 64.
+  int kdup;
+  // EPI_SWIGLU: with swiglu_lo, the output is a bf16 hi / lo pair, hi at column j and
+  // lo = bf16(v - hi) at column n / 2 + j of the same row
+  bool swiglu_lo;
 };
 
 // scratch size that enables every split-K choice of linear()
@@ -67,6 +74,11 @@ hipError_t layernorm_modulate(int x_dtype, int y_dtype, const void* x, int64_t l
                               int64_t ldy, int rows, int dim, int rows_per_batch,
                               const float* shift, const float* scale, int64_t mod_bs, float eps,
                               hipStream_t s);
+// The same with the output as bf16 hi / lo planes in one row of y (bf16): hi = bf16(out)
+// at columns [0, dim), lo = bf16(out - hi) at [dim, 2 dim); ldy >= 2 dim.
+hipError_t layernorm_modulate_hilo(int x_dtype, const void* x, int64_t ldx, void* y, int64_t ldy,
+                                   int rows, int dim, int rpb, const float* shift,
+                                   const float* scale, int64_t mod_bs, float eps, hipStream_t s);
 
 // RoPE tables for the joint sequence [txt ; img]: pos [L, P] int32 and cs [L, P] (cos, sin)
 // with P = head_dim / 2 pairs; axes_dim gives the per-axis widths (4 axes).

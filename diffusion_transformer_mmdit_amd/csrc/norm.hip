@@ -77,7 +77,10 @@ FLUX_DEV void load_mod(const float* p, float* f, int n) {
   }
 }
 
-template <class TX, class TY, int MAXI, bool EXACT>
+// HILO: the output is carried at twice bf16's precision as a pair of bf16 planes in one
+// row, hi = bf16(y) at columns [0, dim) and lo = bf16(y - hi) at [dim, 2 dim), so that a
+// bf16 product over K = 2 dim against [W | W] gives y W^T to fp32 accumulation (TY = bf16).
+template <class TX, class TY, int MAXI, bool EXACT, bool HILO = false>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(const TX* __restrict__ x, int64_t ldx,
                                                           TY* __restrict__ y, int64_t ldy,
                                                           int rows, int dim, int rpb,
@@ -128,7 +131,21 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const TX* __restrict__
       load_mod(sc + c * CW, m, CW);
 #pragma unroll
       for (int e = 0; e < CW; ++e) o[e] = (1.f + m[e]) * (v[i][e] * rstd) + a[e];
-      store_cw<TY, CW>(yr + c * CW, o);
+      if constexpr (HILO) {
+        static_assert(sizeof(TY) == 2, "hi/lo planes are bf16");
+        // hi is exactly representable, so its store does not round again; o - hi is exact
+        // in fp32 and lo rounds it to bf16
+        float hi[CW], lo[CW];
+#pragma unroll
+        for (int e = 0; e < CW; ++e) {
+          hi[e] = to_f32(from_f32<bf16>(o[e]));
+          lo[e] = o[e] - hi[e];
+        }
+        store_cw<TY, CW>(yr + c * CW, hi);
+        store_cw<TY, CW>(yr + dim + c * CW, lo);
+      } else {
+        store_cw<TY, CW>(yr + c * CW, o);
+      }
     }
   }
 }
@@ -315,6 +332,46 @@ hipError_t layernorm_modulate(int x_dtype, int y_dtype, const void* x, int64_t l
   return y_dtype == DT_BF16
              ? ln_dispatch<float, bf16>(x, ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps, s)
              : ln_dispatch<float, float>(x, ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps, s);
+}
+
+template <class TX>
+static hipError_t ln_hilo_dispatch(const TX* x, int64_t ldx, bf16* y, int64_t ldy, int rows,
+                                   int dim, int rpb, const float* shift, const float* scale,
+                                   int64_t mod_bs, float eps, hipStream_t s) {
+  constexpr int CW = 16 / sizeof(TX);
+  const int per_lane = (dim / CW + 63) / 64;
+  const bool exact = (dim / CW) % 64 == 0;
+  dim3 grid((rows + 3) / 4), block(256);
+#define FLUX_LNH(N)                                                                            \
+  do {                                                                                        \
+    if (exact && (dim / CW) == 64 * N)                                                        \
+      hipLaunchKernelGGL((ln_modulate_kernel<TX, bf16, N, true, true>), grid, block, 0, s, x, \
+                         ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps);             \
+    else                                                                                      \
+      hipLaunchKernelGGL((ln_modulate_kernel<TX, bf16, N, false, true>), grid, block, 0, s,   \
+                         x, ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps);          \
+  } while (0)
+  if (per_lane <= 2) FLUX_LNH(2);
+  else if (per_lane <= 4) FLUX_LNH(4);
+  else if (per_lane <= 8) FLUX_LNH(8);
+  else if (per_lane <= 16) FLUX_LNH(16);
+  else if (per_lane <= 24) FLUX_LNH(24);
+  else if (per_lane <= 32) FLUX_LNH(32);
+  else return hipErrorInvalidValue;
+#undef FLUX_LNH
+  return hipGetLastError();
+}
+
+hipError_t layernorm_modulate_hilo(int x_dtype, const void* x, int64_t ldx, void* y, int64_t ldy,
+                                   int rows, int dim, int rpb, const float* shift,
+                                   const float* scale, int64_t mod_bs, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  bf16* yp = static_cast<bf16*>(y);
+  if (x_dtype == DT_BF16)
+    return ln_hilo_dispatch(static_cast<const bf16*>(x), ldx, yp, ldy, rows, dim, rpb, shift,
+                            scale, mod_bs, eps, s);
+  return ln_hilo_dispatch(static_cast<const float*>(x), ldx, yp, ldy, rows, dim, rpb, shift,
+                          scale, mod_bs, eps, s);
 }
 
 // ------------------------------------------------------------------------------------

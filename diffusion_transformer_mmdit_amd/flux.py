@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libflux.so")
 FLUX_OK, FLUX_EINVAL, FLUX_ESHAPE, FLUX_EDTYPE, FLUX_EALIGN, FLUX_EWORKSPACE, FLUX_EHIP = (
     0, -1, -2, -3, -4, -5, -6)
 FLUX_BF16, FLUX_F32 = 0, 1
+FLUX_PRECISION_BF16, FLUX_PRECISION_SPLIT = 0, 1
 FLUX_EPI_STORE, FLUX_EPI_SWIGLU, FLUX_EPI_GATED_RESIDUAL = 0, 1, 2
 
 STATUS_NAMES = {0: "FLUX_OK", -1: "FLUX_EINVAL", -2: "FLUX_ESHAPE", -3: "FLUX_EDTYPE",
@@ -42,7 +43,7 @@ class flux_cfg(ctypes.Structure):
                 ("rope_theta", ctypes.c_float), ("eps", ctypes.c_float),
                 ("in_channels", ctypes.c_int32), ("context_dim", ctypes.c_int32),
                 ("n_double", ctypes.c_int32), ("n_single", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("precision", ctypes.c_int32)]
 
 
 class flux_temb_weights(ctypes.Structure):
@@ -208,13 +209,14 @@ def flux_timing_end() -> tuple[int, float]:
 def make_cfg(dim: int, heads: int, mlp_hidden: int, dtype: int = FLUX_BF16, head_dim: int = 128,
              axes_dim=(32, 32, 32, 32), rope_theta: float = 2000.0, eps: float = 1e-6,
              in_channels: int = 128, context_dim: int = 0, n_double: int = 0,
-             n_single: int = 0) -> flux_cfg:
+             n_single: int = 0, precision: int = FLUX_PRECISION_BF16) -> flux_cfg:
     c = flux_cfg()
     c.dim, c.heads, c.head_dim, c.mlp_hidden = dim, heads, head_dim, mlp_hidden
     c.axes_dim = (ctypes.c_int32 * 4)(*axes_dim)
     c.rope_theta, c.eps = rope_theta, eps
     c.in_channels, c.context_dim = in_channels, context_dim
     c.n_double, c.n_single, c.dtype = n_double, n_single, dtype
+    c.precision = precision
     return c
 
 

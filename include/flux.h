@@ -54,10 +54,26 @@ typedef enum {
 
 typedef enum { FLUX_BF16 = 0, FLUX_F32 = 1 } flux_dtype;
 
+/* Operand precision of the bf16 path (flux_cfg.precision).
+ *   FLUX_PRECISION_BF16  every MFMA operand is stored in bf16 (fp32 accumulation).
+ *   FLUX_PRECISION_SPLIT the LayerNorm + modulate outputs (the inputs of the QKV, MLP-in and
+ *                        fused linear1 projections) and the SwiGLU outputs (the inputs of
+ *                        MLP-out and of linear2's MLP part) are carried as bf16 hi + lo
+ *                        pairs (hi = bf16(v), lo = bf16(v - hi)) and multiplied against the
+ *                        same weights twice: those products are exact to fp32 accumulation
+ *                        and take twice the MFMA work.  Through the 32 blocks of the
+ *                        Klein-9B step (D 4096) the bf16 rounding of these two operands is
+ *                        amplified more than any other; carrying them removes most of the
+ *                        step's error against the exact forward.
+ * Both modes project the step's final LayerNorm output as a hi + lo pair.  FLUX_F32
+ * workloads take FLUX_PRECISION_BF16 only (their operands are fp32 already). */
+typedef enum { FLUX_PRECISION_BF16 = 0, FLUX_PRECISION_SPLIT = 1 } flux_precision;
+
 /* Model hyper-parameters ([DIFF] 模型配置参数全解; [KLEIN] config table).
  * head_dim must be 128; dim = heads * head_dim; axes_dim are the per-axis RoPE widths
  * (even, summing to head_dim; the pages use 32,32,32,32); rope_theta 2000; eps 1e-6.
- * in_channels / context_dim / n_double / n_single are used by the step only. */
+ * in_channels / context_dim / n_double / n_single are used by the step only.
+ * FLUX_PRECISION_SPLIT needs dtype FLUX_BF16 and mlp_hidden a multiple of 64. */
 typedef struct {
   int32_t dim;
   int32_t heads;
@@ -70,7 +86,8 @@ typedef struct {
   int32_t context_dim;
   int32_t n_double;
   int32_t n_single;
-  int32_t dtype; /* flux_dtype */
+  int32_t dtype;     /* flux_dtype */
+  int32_t precision; /* flux_precision (0 = FLUX_PRECISION_BF16) */
 } flux_cfg;
 
 /* Timestep MLPEmbedder: temb = w2 silu(w1 sinusoid(1000 t)); w1 [D,256], w2 [D,D]. */

@@ -52,12 +52,12 @@ def workspace(nbytes: int):
     return t.empty(max(int(nbytes), 256), dtype=t.uint8, device="cuda")
 
 
-def cfg_for(wl: fs.Workload):
+def cfg_for(wl: fs.Workload, precision: int = 0):
     from diffusion_transformer_mmdit_amd import flux as F
     return F.make_cfg(wl.dim, wl.heads, wl.mlp_hidden,
                       dtype=F.FLUX_BF16 if wl.dtype == "bf16" else F.FLUX_F32,
                       in_channels=wl.in_channels, context_dim=wl.context_dim,
-                      n_double=wl.n_double, n_single=wl.n_single)
+                      n_double=wl.n_double, n_single=wl.n_single, precision=precision)
 
 
 def errors(got, ref) -> tuple[float, float]:
@@ -113,10 +113,10 @@ def stream():
 # ------------------------------------------------------------------------------------
 # Block runners through the C ABI
 # ------------------------------------------------------------------------------------
-def run_double_block(wl: fs.Workload, inp: dict, w_dev: dict | None = None):
+def run_double_block(wl: fs.Workload, inp: dict, w_dev: dict | None = None, precision: int = 0):
     from diffusion_transformer_mmdit_amd import flux as F
     t = torch()
-    cfg = cfg_for(wl)
+    cfg = cfg_for(wl, precision)
     w_dev = w_dev or upload_weights(inp["weights"], wl.dtype)
     img, txt = dev(inp["img"], wl.dtype), dev(inp["txt"], wl.dtype)
     img_out, txt_out = t.empty_like(img), t.empty_like(txt)
@@ -129,10 +129,10 @@ def run_double_block(wl: fs.Workload, inp: dict, w_dev: dict | None = None):
     return img_out, txt_out
 
 
-def run_single_block(wl: fs.Workload, inp: dict, w_dev: dict | None = None):
+def run_single_block(wl: fs.Workload, inp: dict, w_dev: dict | None = None, precision: int = 0):
     from diffusion_transformer_mmdit_amd import flux as F
     t = torch()
-    cfg = cfg_for(wl)
+    cfg = cfg_for(wl, precision)
     w_dev = w_dev or upload_weights(inp["weights"], wl.dtype)
     img, txt = dev(inp["img"], wl.dtype), dev(inp["txt"], wl.dtype)
     img_out, txt_out = t.empty_like(img), t.empty_like(txt)
@@ -145,10 +145,10 @@ def run_single_block(wl: fs.Workload, inp: dict, w_dev: dict | None = None):
     return img_out, txt_out
 
 
-def run_step(wl: fs.Workload, inp: dict, w_dev: dict | None = None):
+def run_step(wl: fs.Workload, inp: dict, w_dev: dict | None = None, precision: int = 0):
     from diffusion_transformer_mmdit_amd import flux as F
     t = torch()
-    cfg = cfg_for(wl)
+    cfg = cfg_for(wl, precision)
     w_dev = w_dev or upload_weights(inp["weights"], wl.dtype)
     mw = F.ModelWeights(w_dev, wl.n_double, wl.n_single)
     out = t.empty((wl.batch, wl.n_img, wl.in_channels), dtype=t.float32, device="cuda")

@@ -1,15 +1,15 @@
-"""Write the sampled fp64 oracle output of one full Klein-9B 1024² denoiser step.
+"""Write the fp64 oracle output of one full Klein-9B 1024² denoiser step.
 
-    python tests/golden/make_step_golden.py [--workload klein9b_step_1024] [--rows 16]
-                                            [--storage bf16]
+    python tests/golden/make_step_golden.py [--workload klein9b_step_1024] [--storage bf16]
 
 Calls only oracle/ (the fp64 definition) and the seeded input generator: the weights are
-generated block by block (flux_synth.LazyWeights), the step runs in fp64 on the host (a
-few minutes), and the output rows of a seeded sample of image tokens (always the first and
-the last) are written to tests/golden/<workload>.txt, all 128 channels each, for the GPU
-test that runs the same step through flux_denoiser_step.  With --storage bf16 the step is
-the oracle's bf16 storage mode (the definition with values rounded to bf16 where a bf16
-pipeline stores them) and the file is tests/golden/<workload>_bf16_storage.txt.
+generated block by block (flux_synth.LazyWeights), the step runs in fp64 on the host (about
+ten minutes), and the whole output [n_img, in_channels] is written to
+tests/golden/<workload>.npy (float64, no pickle) with its provenance in
+tests/golden/<workload>.meta.txt, for the GPU test that runs the same step through
+flux_denoiser_step.  With --storage bf16 the step is the oracle's bf16 storage mode (the
+definition with values rounded to bf16 where a bf16 pipeline stores them) and the files are
+tests/golden/<workload>_bf16_storage.*.
 """
 from __future__ import annotations
 
@@ -28,16 +28,9 @@ import flux_synth as fs  # noqa: E402
 from oracle import flux_oracle as O  # noqa: E402
 
 
-def sample_rows(n_img: int, k: int, seed: int) -> np.ndarray:
-    rng = np.random.default_rng([seed, 7])
-    mid = rng.choice(np.arange(1, n_img - 1), size=k - 2, replace=False)
-    return np.sort(np.concatenate([[0, n_img - 1], mid])).astype(np.int64)
-
-
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="klein9b_step_1024")
-    ap.add_argument("--rows", type=int, default=16)
     ap.add_argument("--storage", choices=("fp64", "bf16"), default="fp64")
     args = ap.parse_args(argv)
     wl = fs.workload(args.workload)
@@ -52,19 +45,18 @@ def main(argv=None) -> int:
     storage = O.bf16_storage if args.storage == "bf16" else None
     out = O.denoiser_step(inp["x"], inp["ctx"], inp["t"], w, inp["img_ids"], inp["txt_ids"],
                           wl.n_double, wl.n_single, on_block=progress, storage=storage)
-    rows = sample_rows(wl.n_img, args.rows, wl.seed)
     suffix = "_bf16_storage" if storage else ""
     what = "fp64 oracle, bf16 storage mode," if storage else "fp64 oracle"
-    path = os.path.join(HERE, f"{wl.name}{suffix}.txt")
-    with open(path, "w") as f:
-        f.write(f"# {what} output of one {wl.name} denoiser step (flux_synth seed {wl.seed},"
+    base = os.path.join(HERE, f"{wl.name}{suffix}")
+    np.save(base + ".npy", np.ascontiguousarray(out[0], dtype=np.float64), allow_pickle=False)
+    with open(base + ".meta.txt", "w") as f:
+        f.write(f"{what} output of one {wl.name} denoiser step (flux_synth seed {wl.seed},"
                 f" t = {float(inp['t'][0]):.9g})\n")
-        f.write("# written by tests/golden/make_step_golden.py (oracle/ + flux_synth only)\n")
-        f.write(f"# output rms over all rows: {np.sqrt(np.mean(out[0] ** 2)):.17g}\n")
-        f.write("# each line: image token index, then its 128 output channels\n")
-        for r in rows:
-            f.write(" ".join([str(int(r))] + [f"{v:.17g}" for v in out[0, r]]) + "\n")
-    print(f"[golden] wrote {path} ({len(rows)} rows) in {time.time() - t0:.0f} s", flush=True)
+        f.write(f"array: {os.path.basename(base)}.npy, float64 [{wl.n_img}, {wl.in_channels}]"
+                f" (image tokens x output channels, batch item 0)\n")
+        f.write("written by tests/golden/make_step_golden.py (oracle/ + flux_synth only)\n")
+        f.write(f"output rms: {np.sqrt(np.mean(out[0] ** 2)):.17g}\n")
+    print(f"[golden] wrote {base}.npy in {time.time() - t0:.0f} s", flush=True)
     return 0
 
 

@@ -24,12 +24,13 @@ def oracle_block(kind, inp):
     return fn(inp["img"], inp["txt"], inp["t"], inp["weights"], inp["img_ids"], inp["txt_ids"])
 
 
-def run(kind, wl, inp):
-    return (G.run_double_block if kind == "double" else G.run_single_block)(wl, inp)
+def run(kind, wl, inp, precision=0):
+    return (G.run_double_block if kind == "double" else G.run_single_block)(wl, inp,
+                                                                              precision=precision)
 
 
-def check_block(kind, wl, inp, what):
-    img, txt = run(kind, wl, inp)
+def check_block(kind, wl, inp, what, precision=0):
+    img, txt = run(kind, wl, inp, precision)
     ref_img, ref_txt = oracle_block(kind, inp)
     G.assert_close(G.host(img), ref_img, wl.dtype, f"{what} img")
     if wl.n_txt:
@@ -58,13 +59,15 @@ def test_tiny_fp32_block(kind):
     check_block(kind, wl, inp, f"tiny fp32 {kind}")
 
 
+@pytest.mark.parametrize("precision", [0, 1])
 @pytest.mark.parametrize("kind", ["single", "double"])
 @pytest.mark.parametrize("n_txt,n_img,batch", [(16, 64, 1), (5, 36, 2), (0, 49, 1), (130, 196, 1)])
-def test_small_bf16_block(kind, n_txt, n_img, batch):
+def test_small_bf16_block(kind, n_txt, n_img, batch, precision):
     wl = fs.workload("tiny_single_f32", dtype="bf16", n_txt=n_txt, n_img=n_img, batch=batch,
                      t_fixed=None, seed=2000 + n_img)
     inp = fs.block_inputs(wl, kind=kind)
-    check_block(kind, wl, inp, f"bf16 {kind} Nt={n_txt} Ni={n_img} B={batch}")
+    check_block(kind, wl, inp, f"bf16 {kind} Nt={n_txt} Ni={n_img} B={batch} p{precision}",
+                precision)
 
 
 def test_tiny_fp32_single_batch_and_text_free():
@@ -86,6 +89,17 @@ def test_klein9b_double_block_1024():
     wl = fs.workload("klein9b_double_1024")
     inp = fs.block_inputs(wl)
     check_block("double", wl, inp, "Klein-9B double 1024^2")
+
+
+@pytest.mark.parametrize("kind,name", [("single", "klein4b_single_512"),
+                                       ("double", "klein9b_double_1024")])
+def test_split_precision_block_full_shape(kind, name):
+    """FLUX_PRECISION_SPLIT (LayerNorm and SwiGLU outputs as bf16 hi + lo pairs) at the
+    Klein-4B single / Klein-9B double block shapes: the hi / lo products take other K extents
+    (2D, 2H, D + 2H) and the SwiGLU epilogue writes two planes."""
+    wl = fs.workload(name)
+    inp = fs.block_inputs(wl, kind=kind)
+    check_block(kind, wl, inp, f"{name} {kind} (split precision)", precision=1)
 
 
 def test_klein9b_single_block_1024():

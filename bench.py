@@ -52,6 +52,17 @@ def step_flops(wl) -> float:
     return f
 
 
+def split_mfma_flops(wl) -> float:
+    """MFMA work of a step with FLUX_PRECISION_SPLIT: the products that read the LayerNorm
+    outputs (QKV, MLP-in, linear1) or the SwiGLU outputs (MLP-out, linear2's MLP columns) run
+    twice (hi and lo planes)."""
+    D, H, B, L = wl.dim, wl.mlp_hidden, wl.batch, wl.seq
+    extra_double = 2.0 * L * B * (3 * D * D + 2 * H * D + H * D)
+    extra_single = 2.0 * L * B * ((3 * D + 2 * H) * D + H * D)
+    extra_head = 2.0 * B * wl.n_img * D * wl.in_channels  # in both precisions
+    return step_flops(wl) + wl.n_double * extra_double + wl.n_single * extra_single + extra_head
+
+
 # ------------------------------------------------------------------------------------
 # device-resident synthetic weights (seeded, generated on the GPU for speed)
 # ------------------------------------------------------------------------------------
@@ -182,6 +193,53 @@ def dominant_roofline(wl, launches: int, mean_us: float) -> dict:
     }
 
 
+# Every timing-hook site of the step: (site name, what it launches, its shape and
+# algorithmic FLOP per launch at the workload).  The double-block sites time the image
+# stream's launches (the text stream's are 1/8 of their size) and the joint attention.
+def site_table(F, wl):
+    D, H, L, Ni = wl.dim, wl.mlp_hidden, wl.seq, wl.n_img
+    lin = lambda m, n, k: (2.0 * m * n * k, [m, n, k])
+    att = (4.0 * L * L * D * wl.batch, [wl.batch, wl.heads, L, L])
+    return [
+        ("single_qkv", F.FLUX_SITE_SINGLE_QKV, "linear1 q|k|v, V^T epilogue", wl.n_single,
+         *lin(L, 3 * D, D)),
+        ("single_mlp_in", F.FLUX_SITE_SINGLE_MLP_IN, "linear1 gate|up, SwiGLU epilogue",
+         wl.n_single, *lin(L, 2 * H, D)),
+        ("single_attention", F.FLUX_SITE_SINGLE_ATTENTION, "flash joint attention (+ merge)",
+         wl.n_single, *att),
+        ("single_linear2", F.FLUX_SITE_SINGLE_LINEAR2, "linear2, gated-residual epilogue",
+         wl.n_single, *lin(L, D, D + H)),
+        ("double_qkv_img", F.FLUX_SITE_DOUBLE_QKV, "image QKV, V^T epilogue", wl.n_double,
+         *lin(Ni, 3 * D, D)),
+        ("double_attention", F.FLUX_SITE_DOUBLE_ATTENTION, "flash joint attention (+ merge)",
+         wl.n_double, *att),
+        ("double_out_img", F.FLUX_SITE_DOUBLE_OUT, "image out-proj, gated-residual epilogue",
+         wl.n_double, *lin(Ni, D, D)),
+        ("double_mlp_in_img", F.FLUX_SITE_DOUBLE_MLP_IN, "image MLP-in, SwiGLU epilogue",
+         wl.n_double, *lin(Ni, 2 * H, D)),
+        ("double_mlp_out_img", F.FLUX_SITE_DOUBLE_MLP_OUT, "image MLP-out, gated-residual "
+         "epilogue", wl.n_double, *lin(Ni, D, H)),
+    ]
+
+
+def site_rooflines(F, wl, step, steps: int) -> list:
+    """One timed pass of `steps` steps per site, the site's launches bracketed by HIP events
+    on the step's stream (libflux's timing hook); TFLOP/s from the algorithmic FLOPs."""
+    import torch
+    out = []
+    for name, site, what, per_step, flops, shape in site_table(F, wl):
+        F.flux_timing_begin(site, per_step * steps)
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        n, us = F.flux_timing_end()
+        tf = flops / (us * 1e-6) / 1e12
+        out.append({"site": name, "launch": what, "shape": shape, "launches_timed": n,
+                    "avg_launch_us": round(us, 1), "algorithmic_flops_per_launch": flops,
+                    "achieved_tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+    return out
+
+
 def attention_probe(F, wl):
     """The joint attention at the step's shape (L x heads, bf16) through flux_attention,
     launched 3 times: the MFMA / VALU counter runs of the attention kernel use it."""
@@ -268,6 +326,28 @@ def _time_ms(fn, s, warmup=3, reps=10):
     for _ in range(reps):
         fn()
     return ev.stop_ms() / reps
+
+
+def _time_rotating_ms(fns, s, rounds=3):
+    """Mean duration of one call when consecutive calls use different buffer sets: `fns` are
+    the same kernel call on len(fns) disjoint sets of operands, together larger than the
+    256 MB MALL, so a set's last use lies several hundred MB of other traffic back and every
+    call streams its operands from HBM.  Timed back to back between two events on `s`."""
+    for fn in fns:
+        fn()
+    ev = Events(s)
+    import torch
+    torch.cuda.synchronize()
+    ev.start()
+    for _ in range(rounds):
+        for fn in fns:
+            fn()
+    return ev.stop_ms() / (rounds * len(fns))
+
+
+def _sets_for(nbytes: int, floor_mb: int = 768) -> int:
+    """Buffer sets so that the others' traffic between two uses of one set is > floor_mb."""
+    return max(2, -(-floor_mb * (1 << 20) // nbytes) + 1)
 
 
 def generate_line(F, fs, wl) -> dict:
@@ -472,27 +552,67 @@ def per_config_line(F, fs, name: str) -> dict:
         res[f"{kind}_block_tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
         del w, ws, bw
     # LN + modulate over the joint sequence: fp32 residual in, model dtype out (as the step)
-    x32 = torch.randn((B * L, D), generator=g, device="cuda")
-    y = torch.empty((B * L, D), device="cuda", dtype=dtype)
     sh = torch.randn((B, D), generator=g, device="cuda")
     sc = torch.randn((B, D), generator=g, device="cuda")
-    ms = _time_ms(lambda: F.flux_layernorm_modulate(cfg, B * L, L, x32, F.FLUX_F32, sh, sc, y, s), s)
-    nbytes = B * L * D * (4 + y.element_size())
-    res["ln_modulate_us"] = round(ms * 1e3, 2)
-    res["ln_modulate_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
-    res["ln_modulate_pct_hbm"] = round(100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+    esz = 2 if dtype == torch.bfloat16 else 4
+    nbytes = B * L * D * (4 + esz)
+    fns = []
+    for _ in range(_sets_for(nbytes)):
+        x32 = torch.randn((B * L, D), generator=g, device="cuda")
+        y = torch.empty((B * L, D), device="cuda", dtype=dtype)
+        fns.append(lambda x32=x32, y=y: F.flux_layernorm_modulate(cfg, B * L, L, x32, F.FLUX_F32,
+                                                                  sh, sc, y, s))
+    bandwidth_entry(res, "ln_modulate", nbytes, len(fns), _time_rotating_ms(fns, s),
+                    _time_ms(fns[0], s))
+    del fns, x32, y
     # RMSNorm + RoPE on q and k in place, inside a [B, L, 3D] QKV buffer
-    qkv = torch.randn((B, L, 3 * D), generator=g, device="cuda").to(dtype)
     gam = torch.ones(128, device="cuda")
     nb = F.flux_qk_norm_rope_workspace_size(cfg, Nt, Ni)
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
-    ms = _time_ms(lambda: F.flux_qk_norm_rope(cfg, B, Nt, Ni, qkv, qkv[..., D:], 3 * D, gam, gam,
-                                              gam, gam, txt_ids, img_ids, ws, nb, s), s)
-    nbytes = 2 * 2 * B * L * D * qkv.element_size()
-    res["qk_norm_rope_us"] = round(ms * 1e3, 2)
-    res["qk_norm_rope_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
-    res["qk_norm_rope_pct_hbm"] = round(100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+    nbytes = 2 * 2 * B * L * D * esz
+    fns = []
+    for _ in range(_sets_for(nbytes)):
+        qkv = torch.randn((B, L, 3 * D), generator=g, device="cuda").to(dtype)
+        fns.append(lambda qkv=qkv: F.flux_qk_norm_rope(cfg, B, Nt, Ni, qkv, qkv[..., D:], 3 * D,
+                                                       gam, gam, gam, gam, txt_ids, img_ids, ws,
+                                                       nb, s))
+    bandwidth_entry(res, "qk_norm_rope", nbytes, len(fns), _time_rotating_ms(fns, s),
+                    _time_ms(fns[0], s))
+    del fns, qkv
+    # modulation: timestep MLP + one modulation GEMV (the double block's image set, 6D x D);
+    # weight reads dominate: (256 D + D^2 + 6 D^2) bf16
+    if wl.dtype == "bf16":
+        mout = torch.empty((B, 6 * D), device="cuda")
+        mnb = F.flux_modulation_workspace_size(cfg, B)
+        mws = torch.empty(max(mnb, 256), dtype=torch.uint8, device="cuda")
+        nbytes = 2 * (256 * D + D * D + 6 * D * D)
+        fns, keep = [], []
+        for _ in range(_sets_for(nbytes)):
+            tw = device_weights(fs.temb_weight_specs(D), wl.seed, dtype)
+            wmod = (0.02 * torch.randn((6 * D, D), generator=g, device="cuda")).to(dtype)
+            tws = F.temb_weights(tw)
+            keep.append((tw, wmod, tws))
+            fns.append(lambda tws=tws, wmod=wmod: F.flux_modulation(cfg, tws, wmod, 6 * D, t, B,
+                                                                    mout, mws, mnb, s))
+        bandwidth_entry(res, "modulation_gemv", nbytes, len(fns), _time_rotating_ms(fns, s),
+                        _time_ms(fns[0], s))
+        del fns, keep
     return res
+
+
+def bandwidth_entry(res: dict, name: str, nbytes: int, sets: int, ms_cold: float,
+                    ms_warm: float):
+    """GB/s of an HBM-bound kernel from its algorithmic bytes: over rotating buffer sets
+    larger than the MALL together (operands come from HBM: the HBM figure), and back to back
+    on one set (operands may stay in the 256 MB MALL)."""
+    gbs = nbytes / (ms_cold * 1e-3) / 1e9
+    res[f"{name}_bytes"] = int(nbytes)
+    res[f"{name}_buffer_sets"] = int(sets)
+    res[f"{name}_us"] = round(ms_cold * 1e3, 2)
+    res[f"{name}_gbs"] = round(gbs, 1)
+    res[f"{name}_pct_hbm"] = round(100.0 * gbs / PEAK_HBM_GBS, 1)
+    res[f"{name}_us_back_to_back"] = round(ms_warm * 1e3, 2)
+    res[f"{name}_gbs_back_to_back"] = round(nbytes / (ms_warm * 1e-3) / 1e9, 1)
 
 
 def main(argv=None) -> int:
@@ -589,7 +709,41 @@ def main(argv=None) -> int:
     roof = dominant_roofline(wl, launches, mean_us)
     print(f"[bench] dominant kernel {roof['achieved']} TFLOP/s ({launches} launches, "
           f"{mean_us:.1f} us each)", file=sys.stderr, flush=True)
-    del w, mw, ws
+    # every GEMM epilogue and the attention, each timed the same way in passes of its own
+    sites = site_rooflines(F, wl, step, args.steps)
+    for r in sites:
+        print(f"[bench]   {r['site']}: {r['avg_launch_us']} us, {r['achieved_tflops']} TFLOP/s "
+              f"({100 * r['frac']:.1f}%)", file=sys.stderr, flush=True)
+    del ws
+    torch.cuda.empty_cache()
+    # the same step with the LayerNorm and SwiGLU outputs carried as bf16 hi + lo pairs
+    # (FLUX_PRECISION_SPLIT: the mode that meets the fp64 parity bars at this workload)
+    cfg_s = F.make_cfg(wl.dim, wl.heads, wl.mlp_hidden, in_channels=wl.in_channels,
+                       context_dim=wl.context_dim, n_double=wl.n_double, n_single=wl.n_single,
+                       precision=F.FLUX_PRECISION_SPLIT)
+    nb_s = F.flux_denoiser_step_workspace_size(cfg_s, wl.batch, wl.n_img, wl.n_txt)
+    ws_s = torch.empty(nb_s, dtype=torch.uint8, device="cuda")
+
+    def step_split():
+        F.flux_denoiser_step(cfg_s, mw, t, None, wl.batch, wl.n_img, wl.n_txt, x, ctx, img_ids,
+                             txt_ids, out, ws_s, nb_s, s)
+
+    split_steps = max(1, args.steps // 2)
+    step_split()
+    torch.cuda.synchronize()
+    ev.start()
+    for _ in range(split_steps):
+        step_split()
+    ms_split = ev.stop_ms() / split_steps
+    torch.cuda.synchronize()
+    split = {"precision": "FLUX_PRECISION_SPLIT", "steps": split_steps,
+             "ms_per_step": round(ms_split, 3),
+             "algorithmic_tflops": round(flops / (ms_split * 1e-3) / 1e12, 2),
+             "mfma_tflop_per_step": round(split_mfma_flops(wl) / 1e12, 3),
+             "time_vs_bf16": round(ms_split / ms, 3)}
+    print(f"[bench] split precision: {ms_split:.2f} ms/step ({ms_split / ms:.2f}x)",
+          file=sys.stderr, flush=True)
+    del w, mw, ws_s
     torch.cuda.empty_cache()
 
     cpu = None
@@ -619,6 +773,8 @@ def main(argv=None) -> int:
                    "seq_len": wl.seq, "algorithmic_tflop_per_step": round(flops / 1e12, 3),
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
+        "kernels": sites,
+        "precision_split": split,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

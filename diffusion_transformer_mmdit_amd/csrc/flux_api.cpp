@@ -93,7 +93,7 @@ class TimedSite {
 }  // namespace
 
 extern "C" int flux_timing_begin(int site, int max_launches) {
-  if (site < FLUX_SITE_SINGLE_QKV || site > FLUX_SITE_SINGLE_LINEAR2)
+  if (site < FLUX_SITE_SINGLE_QKV || site > FLUX_SITE_DOUBLE_MLP_OUT)
     return fail(FLUX_EINVAL, "unknown timing site %d", site);
   if (max_launches <= 0 || max_launches > (1 << 16))
     return fail(FLUX_EINVAL, "max_launches must be in [1, 65536] (got %d)", max_launches);
@@ -436,10 +436,14 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
       return layernorm_modulate_hilo(dt, x, D, y, 2 * D, rows, D, rpb, sh, sc, mbs, c->eps, s);
     return layernorm_modulate(dt, T, x, D, y, D, rows, D, rpb, sh, sc, mbs, c->eps, s);
   };
+  // timing-hook sites: the image stream's launches (i == 1) of a block that is not filling
+  // the reference cache
+  auto site = [&](int i, int id) { return (i == 1 && !fill) ? id : 0; };
   for (int i = 0; i < 2; ++i) {
     if (n[i] == 0) continue;
     const int rows = B * n[i];
     HIP_TRY(ln_mod(in_dt, in[i], d.ln[i], rows, n[i], mods[i], mods[i] + D));
+    TimedSite ts(site(i, FLUX_SITE_DOUBLE_QKV), s);
     CHECK(lin_qkv(c, rows, d.ln[i], sw[i]->qkv, qk[i], vtb, ldvt, i == 0 ? 0 : Nt, n[i], s,
                   d.split));
   }
@@ -462,18 +466,28 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
                        sw[1]->k_norm, cs, c->eps, s));
   KvExtra xk{};
   if (ref_use == REF_KEYS) xk = extra_keys(c, ref, B);
-  HIP_TRY(attention(T, qv, kv, vtb, ldvt, ov, B, L, c->heads, d.split, s,
-                    ref_use == REF_KEYS ? &xk : nullptr));
+  {
+    TimedSite ts(site(1, FLUX_SITE_DOUBLE_ATTENTION), s);
+    HIP_TRY(attention(T, qv, kv, vtb, ldvt, ov, B, L, c->heads, d.split, s,
+                      ref_use == REF_KEYS ? &xk : nullptr));
+  }
   for (int i = 0; i < 2; ++i) {
     if (n[i] == 0) continue;
     const int rows = B * n[i];
     // x + gate1 * (O W_o^T)  -> mid (f32)
-    CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D, d.o[i], D, sw[i]->out, D, d.mid[i], D, FLUX_F32,
-              in[i], D, in_dt, mods[i] + 2 * D, mbs, n[i], s, d.split));
+    {
+      TimedSite ts(site(i, FLUX_SITE_DOUBLE_OUT), s);
+      CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D, d.o[i], D, sw[i]->out, D, d.mid[i], D,
+                FLUX_F32, in[i], D, in_dt, mods[i] + 2 * D, mbs, n[i], s, d.split));
+    }
     HIP_TRY(ln_mod(FLUX_F32, d.mid[i], d.ln[i], rows, n[i], mods[i] + 3 * D, mods[i] + 4 * D));
-    CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, P * D, d.ln[i], P * D, sw[i]->mlp_in, D, d.mlp[i],
-              P * H, T, nullptr, 0, 0, nullptr, 0, 1, s, d.split, (P - 1) * D, P == 2));
+    {
+      TimedSite ts(site(i, FLUX_SITE_DOUBLE_MLP_IN), s);
+      CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, P * D, d.ln[i], P * D, sw[i]->mlp_in, D, d.mlp[i],
+                P * H, T, nullptr, 0, 0, nullptr, 0, 1, s, d.split, (P - 1) * D, P == 2));
+    }
     // mid + gate2 * (M W_out^T) -> out
+    TimedSite ts(site(i, FLUX_SITE_DOUBLE_MLP_OUT), s);
     CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, P * H, d.mlp[i], P * H, sw[i]->mlp_out, H, out[i],
               D, out_dt, d.mid[i], D, FLUX_F32, mods[i] + 5 * D, mbs, n[i], s, d.split,
               (P - 1) * H));

@@ -187,6 +187,8 @@ def flux_version() -> str:
 
 FLUX_SITE_SINGLE_QKV, FLUX_SITE_SINGLE_MLP_IN = 1, 2
 FLUX_SITE_SINGLE_ATTENTION, FLUX_SITE_SINGLE_LINEAR2 = 3, 4
+FLUX_SITE_DOUBLE_QKV, FLUX_SITE_DOUBLE_ATTENTION, FLUX_SITE_DOUBLE_OUT = 5, 6, 7
+FLUX_SITE_DOUBLE_MLP_IN, FLUX_SITE_DOUBLE_MLP_OUT = 8, 9
 
 
 def flux_timing_begin(site: int, max_launches: int) -> None:

@@ -217,7 +217,7 @@ def test_timing_hook_validation():
     n, us = ctypes.c_int(7), ctypes.c_double(1.0)
     # unknown site, capacity out of range, NULL outputs: rejected before any HIP call
     assert L.flux_timing_begin(0, 4) == F.FLUX_EINVAL
-    assert L.flux_timing_begin(5, 4) == F.FLUX_EINVAL
+    assert L.flux_timing_begin(10, 4) == F.FLUX_EINVAL
     assert L.flux_timing_begin(F.FLUX_SITE_SINGLE_MLP_IN, 0) == F.FLUX_EINVAL
     assert L.flux_timing_begin(F.FLUX_SITE_SINGLE_MLP_IN, (1 << 16) + 1) == F.FLUX_EINVAL
     assert L.flux_timing_end(None, None) == F.FLUX_EINVAL

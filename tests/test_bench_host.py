@@ -57,3 +57,19 @@ def test_committed_traffic_summary_is_well_formed():
     with open(bench.TRAFFIC_SUMMARY) as f:
         text = f.read()
     assert "traffic_bytes_per_launch:" in text and "kernel_source_sha256:" in text
+
+
+def test_site_table_and_split_flops():
+    from diffusion_transformer_mmdit_amd import flux as F
+    wl = fs.workload("klein9b_step_1024")
+    rows = {r[0]: r for r in bench.site_table(F, wl)}
+    assert len(rows) == 9
+    # (name, site, what, launches per step, flops, shape)
+    assert rows["single_mlp_in"][4] == 2.0 * 4608 * 24576 * 4096 and rows["single_mlp_in"][3] == 24
+    assert rows["single_linear2"][5] == [4608, 4096, 16384]
+    assert rows["double_mlp_out_img"][5] == [4096, 4096, 12288] and rows["double_qkv_img"][3] == 8
+    assert rows["single_attention"][4] == 4.0 * 4608 * 4608 * 4096
+    # split precision: the LN-fed and SwiGLU-fed products twice, the head's projection twice
+    extra = 8 * 2.0 * 4608 * (3 * 4096 ** 2 + 2 * 12288 * 4096 + 12288 * 4096) + \
+        24 * 2.0 * 4608 * ((3 * 4096 + 2 * 12288) * 4096 + 12288 * 4096) + 2.0 * 4096 * 4096 * 128
+    assert bench.split_mfma_flops(wl) == pytest.approx(bench.step_flops(wl) + extra)

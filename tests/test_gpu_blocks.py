@@ -180,8 +180,8 @@ def test_block_is_deterministic(kind):
 
 
 def test_timing_hook_times_only_the_armed_site():
-    """The measurement hook brackets exactly the armed site's launches (one per single block,
-    none from a double block) and refuses more launches than it was armed for."""
+    """The measurement hook brackets exactly the armed site's launches (one per block of its
+    kind, none from the other kind) and refuses more launches than it was armed for."""
     from diffusion_transformer_mmdit_amd import flux as F
     wl = fs.workload("tiny_single_f32", dtype="bf16", n_txt=64, n_img=256, t_fixed=None,
                      dim=512, heads=4, mlp_hidden=1536)
@@ -197,6 +197,17 @@ def test_timing_hook_times_only_the_armed_site():
         G.run_single_block(wl, single, ws_single)
         n, us = F.flux_timing_end()
         assert n == 2 and 0.0 < us < 1e5, (site, n, us)
+    # double-block sites: the image stream's launches (and the joint attention), one each per
+    # double block, none from a single block
+    for site in (F.FLUX_SITE_DOUBLE_QKV, F.FLUX_SITE_DOUBLE_ATTENTION, F.FLUX_SITE_DOUBLE_OUT,
+                 F.FLUX_SITE_DOUBLE_MLP_IN, F.FLUX_SITE_DOUBLE_MLP_OUT):
+        F.flux_timing_begin(site, 4)
+        G.run_double_block(wl, double, ws_double)
+        G.run_single_block(wl, single, ws_single)
+        G.run_double_block(wl, double, ws_double)
+        G.run_double_block(wl, double, ws_double)
+        n, us = F.flux_timing_end()
+        assert n == 3 and 0.0 < us < 1e5, (site, n, us)
     # capacity exceeded: an error, and the hook is disarmed afterwards
     F.flux_timing_begin(F.FLUX_SITE_SINGLE_MLP_IN, 1)
     G.run_single_block(wl, single, ws_single)

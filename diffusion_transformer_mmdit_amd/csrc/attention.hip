@@ -263,12 +263,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void flash_attn_bf16_kern
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[h][r] = 0.f;
+    // K fragments read one k-step ahead of their MFMAs
+    bf16x8 ka[2], kb[2];
+    ka[0] = *reinterpret_cast<const bf16x8*>(&Ks[buf][koff[0]]);
+    kb[0] = *reinterpret_cast<const bf16x8*>(&Ks[buf][koff[0] + 32 * kHD]);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][koff[kk]]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[buf][koff[kk] + 32 * kHD]);
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[kk], s[1], 0, 0, 0);
+      if (kk + 1 < 8) {
+        ka[(kk + 1) & 1] = *reinterpret_cast<const bf16x8*>(&Ks[buf][koff[kk + 1]]);
+        kb[(kk + 1) & 1] = *reinterpret_cast<const bf16x8*>(&Ks[buf][koff[kk + 1] + 32 * kHD]);
+      }
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk & 1], qf[kk], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[kk & 1], qf[kk], s[1], 0, 0, 0);
     }
   };
 
@@ -302,7 +308,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void flash_attn_bf16_kern
 #pragma unroll
       for (int r = 4 * (1 - h); r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], sc[h][r]);
     float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    {
+      // lane l and lane l ^ 32 hold the two halves of one query's keys: exchange the
+      // halves in registers (v_permlane32_swap) instead of through LDS
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    }
     const bool grow = mx > m_run + 8.f;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_run;

@@ -114,9 +114,10 @@ def test_klein9b_step_1024_split_precision_vs_fp64(klein9b_step):
 
 @pytest.mark.xfail(strict=True, reason=(
     "with every GEMM operand stored in bf16, the roundings of the LayerNorm and SwiGLU "
-    "outputs are amplified through the 32 blocks at D 4096 beyond the bars: the oracle's own "
-    "bf16 storage mode measures nL2 1.18e-2 / max-abs 7.3e-2 on these inputs (everything "
-    "rounded but the final projection's input); FLUX_PRECISION_SPLIT meets them"))
+    "outputs are amplified through the 32 blocks at D 4096 beyond the bars (measured on the "
+    "GPU: max-abs 8.1e-2, nL2 1.17e-2 over the whole output; the oracle's bf16 storage mode "
+    "with the same rounding points: 7.3e-2 / 1.18e-2 at 128 + 1024 tokens); "
+    "FLUX_PRECISION_SPLIT meets them (7.1e-3 / 1.0e-3)"))
 def test_klein9b_step_1024_bf16_precision_vs_fp64(klein9b_step):
     from diffusion_transformer_mmdit_amd import flux as F
     got = klein9b_step(F.FLUX_PRECISION_BF16)

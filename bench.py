@@ -565,6 +565,7 @@ def per_config_line(F, fs, name: str) -> dict:
     bandwidth_entry(res, "ln_modulate", nbytes, len(fns), _time_rotating_ms(fns, s),
                     _time_ms(fns[0], s))
     del fns, x32, y
+    copy_reference(res, "ln_modulate", nbytes, s)
     # RMSNorm + RoPE on q and k in place, inside a [B, L, 3D] QKV buffer
     gam = torch.ones(128, device="cuda")
     nb = F.flux_qk_norm_rope_workspace_size(cfg, Nt, Ni)
@@ -579,6 +580,7 @@ def per_config_line(F, fs, name: str) -> dict:
     bandwidth_entry(res, "qk_norm_rope", nbytes, len(fns), _time_rotating_ms(fns, s),
                     _time_ms(fns[0], s))
     del fns, qkv
+    copy_reference(res, "qk_norm_rope", nbytes, s)
     # modulation: timestep MLP + one modulation GEMV (the double block's image set, 6D x D);
     # weight reads dominate: (256 D + D^2 + 6 D^2) bf16
     if wl.dtype == "bf16":
@@ -598,6 +600,21 @@ def per_config_line(F, fs, name: str) -> dict:
                         _time_ms(fns[0], s))
         del fns, keep
     return res
+
+
+def copy_reference(res: dict, name: str, nbytes: int, s):
+    """A plain device copy with the same total traffic (nbytes / 2 read, nbytes / 2 written),
+    timed the same way over rotating buffer sets: the rate HBM gives a read + write stream."""
+    import torch
+    half = (nbytes // 2 + 15) // 16 * 16
+    fns = []
+    for _ in range(_sets_for(nbytes)):
+        a = torch.empty(half, dtype=torch.uint8, device="cuda")
+        b = torch.empty(half, dtype=torch.uint8, device="cuda")
+        fns.append(lambda a=a, b=b: b.copy_(a))
+    ms = _time_rotating_ms(fns, s)
+    res[f"{name}_copy_reference_gbs"] = round(2 * half / (ms * 1e-3) / 1e9, 1)
+    res[f"{name}_pct_of_copy"] = round(100.0 * res[f"{name}_gbs"] / res[f"{name}_copy_reference_gbs"], 1)
 
 
 def bandwidth_entry(res: dict, name: str, nbytes: int, sets: int, ms_cold: float,

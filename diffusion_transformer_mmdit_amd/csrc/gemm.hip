@@ -383,6 +383,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
 // of a slice are read under the MFMAs of the previous one.  The K loop is peeled so the
 // steady state carries no branches.  Rows past M / N are clamped to valid rows (their
 // results are never stored).
+//
+// 256x256 tiles run an asymmetric variant in the full 160 KB of LDS: two A stages and three
+// W stages.  W slices are loaded two slices ahead, in the first k-step of a slice, and get
+// seven k-steps to land; A slices are loaded in the last k-step, after the barrier, and get
+// four.  Weights are streamed from HBM once per step, so their latency is the one to hide.
 // ------------------------------------------------------------------------------------
 template <int N>
 FLUX_DEV void wait_vmcnt() {
@@ -430,7 +435,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 // 32x32x64 with unit block scales; the accumulators are multiplied by the per-row scale
 // sa[m] and the per-weight-row scale sw[n] before the epilogue).  Rows of a K slice are
 // 64 or 128 bytes either way, so the load plan, the LDS layout and the schedule are shared.
-template <class TIn, int BM, int BN, int BK, int ST, int NWM, int NWN, class Epi>
+template <class TIn, int BM, int BN, int BK, int ST, int STW, int NWM, int NWN, class Epi>
 FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* __restrict__ W,
                             int64_t ldw, int M, int N, int K, int kw, int kdup, int n_half,
                             int tiles_m,
@@ -440,6 +445,10 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
   constexpr bool F8 = ES == 1;
   static_assert(BK * ES == 64 || BK * ES == 128, "BK: 64- or 128-byte slice rows");
   static_assert(ST >= 2 && ST <= 4, "stages");
+  // STW == ST: A and W slices share the schedule; STW == 3 with ST == 2: W runs one slice
+  // further ahead (the asymmetric schedule below)
+  static_assert(STW == ST || (ST == 2 && STW == 3), "W stages");
+  constexpr bool ASYM = STW != ST;
   using S = Swz<BK, ES>;
   constexpr int NWV = NWM * NWN;        // waves per workgroup
   constexpr int CPR = S::CPR;           // chunks per row
@@ -451,14 +460,14 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int KK = BK / (F8 ? 64 : 16);  // MFMA k-steps per slice
   constexpr int NF = TM + TN;           // fragments per k-step
-  constexpr uint32_t STAGE_B = (BM + BN) * BK * ES;
+  constexpr uint32_t A_STAGE_B = BM * BK * ES, W_STAGE_B = BN * BK * ES;
   static_assert(AI >= 1 && BI >= 1, "tile too small for the load plan");
   static_assert(KK % 2 == 0, "fragment sets alternate with the k-step parity");
   static_assert(!Epi::kPaired || (TN % 2 == 0), "SwiGLU needs gate/up tile pairs");
 
   extern __shared__ __align__(16) char lds_raw[];
   TIn* smem = reinterpret_cast<TIn*>(lds_raw);
-  // stage s: A rows at smem + s * (BM + BN) * BK, B rows right after
+  // A stage s at smem + s * BM * BK; W stage s at smem + ST * BM * BK + s * BN * BK
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -503,14 +512,19 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
     b_off[j] = (uint32_t)(((int64_t)gn * ldw + S::slot(r, lane % CPR) * S::CE) * ES);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_u32(smem));
-  auto dma = [&](int q, int stage, int k0) {  // q-th load instruction of this wave's share
-    const uint32_t sb = lds0 + (uint32_t)stage * STAGE_B;
+  const int nk = k_end - k_begin;
+  const int kb = k_begin * BK;
+  // q-th load instruction of this wave's share of slice sl (q < AI: A rows, else W rows)
+  auto dma = [&](int q, int sl) {
+    const int k0 = kb + sl * BK;
     if (q < AI) {
+      const uint32_t sb = lds0 + (uint32_t)(sl % ST) * A_STAGE_B;
       dma16s(A + k0, a_off[q], sb + (uint32_t)((wave * AI + q) * RPI * BK * ES));
     } else {
       // slices past kw repeat W columns (the lo plane of a hi / lo operand)
-      const int kb = k0 >= kw ? k0 - kdup : k0;
-      dma16s(W + kb, b_off[q - AI], sb + (uint32_t)(BM * BK * ES + (wave * BI + q - AI) * RPI * BK * ES));
+      const int kw0 = k0 >= kw ? k0 - kdup : k0;
+      const uint32_t sb = lds0 + ST * A_STAGE_B + (uint32_t)(sl % STW) * W_STAGE_B;
+      dma16s(W + kw0, b_off[q - AI], sb + (uint32_t)((wave * BI + q - AI) * RPI * BK * ES));
     }
   };
 
@@ -525,9 +539,9 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
   const int lrow = lane & 31, lk = lane >> 5;
   using Frag = typename std::conditional<F8, v8i, bf16x8>::type;
   Frag fr[2][NF];  // [set][A fragments | B fragments]
-  auto rd = [&](int set, int q, int stage, int kk) {
-    const TIn* base = smem + stage * (BM + BN) * BK;
-    const TIn* ob = q < TM ? base : base + BM * BK;
+  auto rd = [&](int set, int q, int sl, int kk) {  // fragment q of k-step kk of slice sl
+    const TIn* ob = q < TM ? smem + (sl % ST) * BM * BK
+                           : smem + ST * BM * BK + (sl % STW) * BN * BK;
     const int row = q < TM ? wm * WTM + q * 32 + lrow : wn * WTN + (q - TM) * 32 + lrow;
     if constexpr (F8) {
       // k-step kk covers chunks 4 kk .. 4 kk + 3 (64 k); lane group lk holds two of them
@@ -540,16 +554,17 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
     }
   };
 
-  const int nk = k_end - k_begin;
-  const int kb = k_begin * BK;
-  // prologue: fill every stage, wait for slice 0, read its first fragments
+  // prologue: fill the stages, wait for slice 0, read its first fragments.  Symmetric: ST
+  // whole slices.  Asymmetric: A and W of slices 0 and 1 (W of slice 2 goes with the first
+  // k-step of slice 0).
+  constexpr int PRE = ASYM ? 2 : ST;  // slices loaded by the prologue
 #pragma unroll
-  for (int p = 0; p < ST; ++p)
+  for (int p = 0; p < PRE; ++p)
     if (p < nk)
 #pragma unroll
-      for (int q = 0; q < LOADS; ++q) dma(q, p, kb + p * BK);
-  if (nk >= ST)
-    wait_vmcnt<(ST - 1) * LOADS>();
+      for (int q = 0; q < LOADS; ++q) dma(q, p);
+  if (nk >= PRE)
+    wait_vmcnt<(PRE - 1) * LOADS>();
   else
     wait_vmcnt<0>();
   __syncthreads();
@@ -557,23 +572,23 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
 #pragma unroll
     for (int q = 0; q < NF; ++q) rd(0, q, 0, 0);
 
-  // One slice.  The loads of slice kt+ST go into stage kt%ST, which the barrier of the last
-  // k-step of slice kt frees; they are split over that k-step and the first k-step of
-  // slice kt+1 (fewer loads in flight at once), and land before the barrier of slice kt+1.
+  // One slice, symmetric stages.  The loads of slice kt+ST go into stage kt%ST, which the
+  // barrier of the last k-step of slice kt frees; they are split over that k-step and the
+  // first k-step of slice kt+1 (fewer loads in flight at once), and land before the barrier
+  // of slice kt+1.
   // DMA_ON: start loading slice kt+ST; CONT: finish the loads begun in slice kt-1;
   // RD_ON: read the next slice's first fragments.
   constexpr int PER = (LOADS + 1) / 2;  // loads per k-step
   auto slice = [&](int kt, auto dma_on, auto rd_on, auto cont_on) {
     constexpr bool DMA_ON = decltype(dma_on)::value, RD_ON = decltype(rd_on)::value;
     constexpr bool CONT = decltype(cont_on)::value;
-    const int st = kt % ST;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1, nxt = cur ^ 1;
       const bool last = kk == KK - 1;
       if (last) {
         // slice kt+1 landed (later slices may still be in flight) and, after the barrier,
-        // every wave is done reading stage st
+        // every wave is done reading slice kt's stage
         if (DMA_ON)
           wait_vmcnt<(ST - 2) * LOADS>();
         else
@@ -581,20 +596,17 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
         __syncthreads();
       }
       const bool do_rd = !last || RD_ON;
-      const int rst = last ? (kt + 1) % ST : st, rkk = last ? 0 : kk + 1;
-      // loads [q0, q1) of slice `ds` into stage `dst` in this k-step
-      int q0 = 0, q1 = 0, dst = 0, ds = 0;
+      const int rsl = last ? kt + 1 : kt, rkk = last ? 0 : kk + 1;
+      // loads [q0, q1) of slice ds in this k-step
+      int q0 = 0, q1 = 0, ds = 0;
       if (last && DMA_ON) {
         q1 = PER;
-        dst = st;
         ds = kt + ST;
       } else if (kk == 0 && CONT) {
         q0 = PER;
         q1 = LOADS;
-        dst = (kt + ST - 1) % ST;
         ds = kt + ST - 1;
       }
-      const int dk = kb + ds * BK;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < TM * TN; ++q) {
@@ -605,32 +617,86 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
         else
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (do_rd && q < NF) rd(nxt, q, rst, rkk);
-        if (q0 + q < q1) dma(q0 + q, dst, dk);
+        if (do_rd && q < NF) rd(nxt, q, rsl, rkk);
+        if (q0 + q < q1) dma(q0 + q, ds);
         __builtin_amdgcn_sched_barrier(0);
       }
       // leftovers when a k-step has fewer MFMAs than reads or loads
 #pragma unroll
       for (int q = TM * TN; q < PER; ++q)
-        if (q0 + q < q1) dma(q0 + q, dst, dk);
+        if (q0 + q < q1) dma(q0 + q, ds);
       if (do_rd)
 #pragma unroll
-        for (int q = TM * TN; q < NF; ++q) rd(nxt, q, rst, rkk);
+        for (int q = TM * TN; q < NF; ++q) rd(nxt, q, rsl, rkk);
     }
   };
+
+  // One slice, asymmetric stages (A: 2, W: 3).  The first k-step of slice kt loads W of
+  // slice kt+2 (its stage, that of slice kt-1, was freed by slice kt-1's last barrier); the
+  // last k-step, after its barrier, loads A of slice kt+2 into the A stage of slice kt.  At
+  // that barrier the only loads allowed in flight are the W loads of slice kt+2, issued
+  // last: W gets seven k-steps to land, A four.  ON: slice kt+2 exists (both loads);
+  // RD_ON: read the next slice's first fragments.
+  auto slice_aw = [&](int kt, auto on, auto rd_on) {
+    constexpr bool ON = decltype(on)::value, RD_ON = decltype(rd_on)::value;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      const bool last = kk == KK - 1;
+      if (last) {
+        if (ON)
+          wait_vmcnt<BI>();
+        else
+          wait_vmcnt<0>();
+        __syncthreads();
+      }
+      const bool do_rd = !last || RD_ON;
+      const int rsl = last ? kt + 1 : kt, rkk = last ? 0 : kk + 1;
+      // loads [q0, q1) of slice kt+2 in this k-step: W rows first, A rows last
+      const int q0 = (ON && kk == 0) ? AI : 0;
+      const int q1 = !ON ? 0 : kk == 0 ? LOADS : last ? AI : 0;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < TM * TN; ++q) {
+        const int i = q / TN, j = q % TN;
+        if constexpr (F8)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0, 127, 0, 127);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (do_rd && q < NF) rd(nxt, q, rsl, rkk);
+        if (q0 + q < q1) dma(q0 + q, kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int q = TM * TN; q < LOADS; ++q)
+        if (q0 + q < q1) dma(q0 + q, kt + 2);
+      if (do_rd)
+#pragma unroll
+        for (int q = TM * TN; q < NF; ++q) rd(nxt, q, rsl, rkk);
+    }
+  };
+
   using On = std::true_type;
   using Off = std::false_type;
   int kt = 0;
-  if (kt + ST < nk) slice(kt++, On{}, On{}, Off{});
-  for (; kt + ST < nk; ++kt) slice(kt, On{}, On{}, On{});
-  // kt >= 1 here only if slice kt-1 started loading slice kt+ST-1 (< nk)
-  if (kt >= 1 && kt + 1 < nk) slice(kt++, Off{}, On{}, On{});
-  for (; kt + 1 < nk; ++kt) slice(kt, Off{}, On{}, Off{});
-  if (kt < nk) {
-    if (kt >= 1 && kt - 1 + ST < nk)
-      slice(kt, Off{}, Off{}, On{});
-    else
-      slice(kt, Off{}, Off{}, Off{});
+  if constexpr (ASYM) {
+    for (; kt + 2 < nk; ++kt) slice_aw(kt, On{}, On{});
+    if (kt + 1 < nk) slice_aw(kt++, Off{}, On{});
+    if (kt < nk) slice_aw(kt, Off{}, Off{});
+  } else {
+    if (kt + ST < nk) slice(kt++, On{}, On{}, Off{});
+    for (; kt + ST < nk; ++kt) slice(kt, On{}, On{}, On{});
+    // kt >= 1 here only if slice kt-1 started loading slice kt+ST-1 (< nk)
+    if (kt >= 1 && kt + 1 < nk) slice(kt++, Off{}, On{}, On{});
+    for (; kt + 1 < nk; ++kt) slice(kt, Off{}, On{}, Off{});
+    if (kt < nk) {
+      if (kt >= 1 && kt - 1 + ST < nk)
+        slice(kt, Off{}, Off{}, On{});
+      else
+        slice(kt, Off{}, Off{}, Off{});
+    }
   }
 
   if constexpr (F8) {
@@ -681,7 +747,7 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
     constexpr int PR = 16 * NWM, NT = 64 * NWV, CPO = BN / 4;
     constexpr int PER_T = PR * CPO / NT;
     static_assert(PR * CPO % NT == 0 && BN % 64 == 0, "staged epilogue shape");
-    static_assert(2 * PR * BN * 4 <= ST * STAGE_B, "staging buffers fit in the LDS stages");
+    static_assert(2 * PR * BN * 4 <= ST * A_STAGE_B + STW * W_STAGE_B, "staging buffers fit in the LDS stages");
     float* stg = reinterpret_cast<float*>(smem);
     __syncthreads();  // every wave is done reading the last slice
 #pragma unroll
@@ -765,12 +831,12 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
   }
 }
 
-template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
+template <int BM, int BN, int BK, int ST, int STW, int OCC, int NWM, int NWN, class Epi>
 __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw, int M,
     int N, int K, int kw, int kdup, int n_half, int tiles_m, int tiles_n, int full_tiles,
     int splits, float* __restrict__ partial, Epi epi) {
-  gemm_lds_body<bf16, BM, BN, BK, ST, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, kw, kdup, n_half,
+  gemm_lds_body<bf16, BM, BN, BK, ST, STW, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, kw, kdup, n_half,
                                                      tiles_m, tiles_n, full_tiles, splits,
                                                      partial, epi, nullptr, nullptr);
 }
@@ -781,7 +847,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_fp8_lds_kernel(
     int N, int K, int n_half, int tiles_m, int tiles_n, int full_tiles, int splits,
     float* __restrict__ partial, Epi epi, const float* __restrict__ sa,
     const float* __restrict__ sw) {
-  gemm_lds_body<fp8, BM, BN, BK, ST, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, K, 0, n_half,
+  gemm_lds_body<fp8, BM, BN, BK, ST, ST, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, K, 0, n_half,
                                                     tiles_m, tiles_n, full_tiles, splits, partial,
                                                     epi, sa, sw);
 }
@@ -873,7 +939,7 @@ static hipError_t ensure_lds_limit(LdsLimit& st, const void* fn, size_t bytes) {
 }
 
 // Launch one large-tile configuration (sets the dynamic LDS limit once per instance).
-template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
+template <int BM, int BN, int BK, int ST, int STW, int OCC, int NWM, int NWN, class Epi>
 static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N,
                              int K, int kw, int kdup, int n_half, const Epi& epi, int splits,
                              float* partial, hipStream_t s) {
@@ -884,14 +950,14 @@ static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t 
   const int full = tiles - tail;
   if (tail == 0) splits = 1;
   if ((size_t)tail * splits * BM * BN * sizeof(float) > kSplitkBytes) return hipErrorInvalidValue;
-  const size_t lds = (size_t)ST * (BM + BN) * BK * sizeof(bf16);
+  const size_t lds = (size_t)(ST * BM + STW * BN) * BK * sizeof(bf16);
   static LdsLimit limit;
   hipError_t le = ensure_lds_limit(
       limit,
-      reinterpret_cast<const void*>(&gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
+      reinterpret_cast<const void*>(&gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, OCC, NWM, NWN, Epi>),
       lds);
   if (le != hipSuccess) return le;
-  hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
+  hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, OCC, NWM, NWN, Epi>),
                      dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, A, lda, W, ldw, M, N,
                      K, kw, kdup, n_half, tiles_m, tiles_n, full, splits, partial, epi);
   if (tail > 0) {
@@ -1063,12 +1129,12 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
       auto* a = static_cast<const bf16*>(A);
       auto* w = static_cast<const bf16*>(W);
       if (best == 0)
-        return launch_lds<256, 256, 64, 2, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
+        return launch_lds<256, 256, 64, 2, 3, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
                                                      epi, best_split, split_ws, s);
       if (best == 1)
-        return launch_lds<256, 128, 64, 2, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
+        return launch_lds<256, 128, 64, 2, 2, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
                                                      epi, best_split, split_ws, s);
-      return launch_lds<128, 128, 64, 2, 2, 2, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half, epi,
+      return launch_lds<128, 128, 64, 2, 2, 2, 2, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half, epi,
                                                    best_split, split_ws, s);
     }
     constexpr int BM = 128, BN = 128;

@@ -13,10 +13,15 @@
 //     the tile's 64 keys; the K rows are fed to the MFMA in a permuted order chosen so
 //     that every lane's 8 probabilities of a 16-key chunk are 8 CONSECUTIVE keys, which
 //     makes the V^T fragment of O^T = V^T P^T a single 16-byte LDS read;
-//   * softmax in the exp2 domain (log2(e)/sqrt(d) folded into one FMA per score) with a
-//     lazy running maximum: O and the row sum are rescaled only when a row's maximum
-//     grows by more than 2^8, which keeps p <= 256 and skips almost all rescales; row
-//     sums are fp32 adds of the unrounded probabilities, P enters the PV product in bf16;
+//   * softmax in the exp2 domain (log2(e)/sqrt(d) folded into one FMA per score).  Each
+//     row takes the maximum of its first key tile and keeps it: later tiles take no
+//     maximum at all.  Any later score up to ~2^7 above it leaves p and the fp32 row sum
+//     finite, and nothing below it is lost (the first tile's best key alone gives a row
+//     sum >= 1), so the result is the same softmax.  If some row's sum or output is not
+//     finite after the loop, the workgroup recomputes its key range with a lazy running
+//     maximum (O and the sum rescaled only when a row's maximum grows by more than 2^8).
+//     Row sums are fp32 adds of the unrounded probabilities, P enters the PV product in
+//     bf16;
 //   * the key loop is software pipelined: while a wave takes the exponentials of one tile
 //     it already computes the next tile's scores, so its own MFMAs run beside its softmax
 //     (K is loaded two tiles ahead, V one tile ahead, one barrier per tile);
@@ -284,10 +289,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void flash_attn_bf16_kern
   // its V^T in V buffer CUR and the next tile's K in K buffer CUR ^ 1.  The step refills
   // K buffer CUR with tile it + 2 and V buffer CUR ^ 1 with tile it + 1, computes the next
   // tile's scores into sn (NEXT) between this tile's exponentials, and adds V^T P^T to O.
-  auto step = [&](int it, auto cur_c, auto next_c, f32x16 (&sc)[2], f32x16 (&sn)[2])
-                  __attribute__((always_inline)) {
+  // FIXED: the row maximum of an earlier tile stands (no maximum is taken).
+  auto step = [&](int it, auto cur_c, auto next_c, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                  auto fixed_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
     constexpr bool NEXT = decltype(next_c)::value;
+    constexpr bool FIXED = decltype(fixed_c)::value;
     // a tile reaching past its source's keys (`lim` of them in the tile) is masked
     const int lim = (EXTRA && it >= nm) ? xn - (it - nm) * kBKV : seq - it * kBKV;
     if (lim < kBKV) {
@@ -297,40 +304,44 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void flash_attn_bf16_kern
         for (int r = 0; r < 16; ++r)
           if (32 * h + 16 * (r >> 3) + 8 * g + (r & 7) >= lim) sc[h][r] = -INFINITY;
     }
-    // online softmax in the log2 domain with a lazily updated maximum: O and the sum are
-    // rescaled only when some row's maximum grows by more than 2^8 (every row on the first
-    // tile, rarely afterwards), so p <= 256
-    float mx4[4];
+    if constexpr (!FIXED) {
+      // online softmax in the log2 domain with a lazily updated maximum: O and the sum are
+      // rescaled only when some row's maximum grows by more than 2^8 (every row on the first
+      // tile, rarely afterwards), so p <= 256
+      float mx4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx4[i] = fmaxf(sc[0][i], sc[1][i]);
+      for (int i = 0; i < 4; ++i) mx4[i] = fmaxf(sc[0][i], sc[1][i]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 4 * (1 - h); r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], sc[h][r]);
-    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    {
-      // lane l and lane l ^ 32 hold the two halves of one query's keys: exchange the
-      // halves in registers (v_permlane32_swap) instead of through LDS
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-    }
-    const bool grow = mx > m_run + 8.f;
-    if (__any(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+        for (int r = 4 * (1 - h); r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], sc[h][r]);
+      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+      {
+        // lane l and lane l ^ 32 hold the two halves of one query's keys: exchange the
+        // halves in registers (v_permlane32_swap) instead of through LDS
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+      }
+      const bool grow = mx > m_run + 8.f;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      m_run = m_new;
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        m_run = m_new;
+      }
     }
     if (it + 2 < t_end) issue_k(cur, it + 2);
     if (NEXT) issue_v(cur ^ 1, it + 1);
 
     if constexpr (NEXT) scores(sn, std::integral_constant<int, cur ^ 1>{});
-    // raw v_exp_f32: arguments are <= 8, results below 2^-126 may flush to zero
+    // raw v_exp_f32: arguments are <= 8 with the lazy maximum (with a kept one they stay
+    // finite unless the overflow check after the loop fires); results below 2^-126 may
+    // flush to zero
     float p[2][16];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -370,7 +381,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void flash_attn_bf16_kern
   using Buf1 = std::integral_constant<int, 1>;
   using On = std::true_type;
   using Off = std::false_type;
-  if (t_begin < t_end) {
+  // The key loop.  The first tile always takes the row maximum (m_run starts at -inf, so
+  // every row adopts its first tile's maximum).  FIXED_REST: the later tiles keep that
+  // maximum and take none of their own; the result stands unless some score exceeded it by
+  // enough to overflow the fp32 sum, which the caller checks afterwards.
+  auto key_loop = [&](auto fixed_rest) __attribute__((always_inline)) {
+    using Rest = decltype(fixed_rest);
     issue_k(0, t_begin);
     issue_v(0, t_begin);
     if (t_begin + 1 < t_end) issue_k(1, t_begin + 1);
@@ -380,15 +396,41 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void flash_attn_bf16_kern
     scores(sa, Buf0{});
     __syncthreads();  // K buffer 0 is refilled by the first step
     int it = t_begin;
-    for (; it + 2 < t_end; it += 2) {
-      step(it, Buf0{}, On{}, sa, sb);
-      step(it + 1, Buf1{}, On{}, sb, sa);
-    }
     if (it + 1 < t_end) {
-      step(it, Buf0{}, On{}, sa, sb);
-      step(it + 1, Buf1{}, Off{}, sb, sa);
+      step(it++, Buf0{}, On{}, sa, sb, Off{});
+      for (; it + 2 < t_end; it += 2) {
+        step(it, Buf1{}, On{}, sb, sa, Rest{});
+        step(it + 1, Buf0{}, On{}, sa, sb, Rest{});
+      }
+      if (it + 1 < t_end) {
+        step(it, Buf1{}, On{}, sb, sa, Rest{});
+        step(it + 1, Buf0{}, Off{}, sa, sb, Rest{});
+      } else {
+        step(it, Buf1{}, Off{}, sb, sa, Rest{});
+      }
     } else {
-      step(it, Buf0{}, Off{}, sa, sb);
+      step(it, Buf0{}, Off{}, sa, sb, Off{});
+    }
+  };
+  if (t_begin < t_end) {
+    key_loop(On{});
+    // With the first tile's maximum m kept, p = 2^(s - m) stays finite unless a later score
+    // exceeds m by ~2^7; then the row sum or O is no longer finite.  (Below m nothing is
+    // lost: the first tile's best key alone gives a row sum >= 1.)  If any row of the
+    // workgroup overflowed, the whole range is recomputed with the lazily updated maximum.
+    float osum = l_run;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) osum += o[dt][r];
+    if (__syncthreads_or(!__builtin_isfinite(osum))) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+      m_run = -INFINITY;
+      l_run = 0.f;
+      key_loop(Off{});
     }
   }
 

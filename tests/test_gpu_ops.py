@@ -325,3 +325,38 @@ def test_attention_equal_scores_give_mean():
     t.cuda.synchronize()
     ref = np.broadcast_to(v.astype(np.float64).mean(axis=1, keepdims=True), (1, seq, D))
     G.assert_close(G.host(o), ref, "bf16", "attention equal scores", max_abs=1e-2, nl2=1e-2)
+
+
+@pytest.mark.parametrize("seq,heads,beta", [(640, 2, 2.0), (640, 2, 4.0), (1100, 64, 4.0),
+                                            (4608, 32, 4.0)])
+def test_attention_scores_far_above_first_tile(seq, heads, beta):
+    # Every query meets a few keys late in the sequence whose scores exceed those of its
+    # first key tile by ~2^6 (beta 2: the kept first-tile maximum still serves, p ~ 2^60) or
+    # by ~2^7 and more (beta 4: the fp32 row sum overflows with the first tile's maximum and
+    # the range is recomputed with a running one).  1100 x 64 heads takes the key-split
+    # path; 4608 x 32 is the Klein-9B shape.
+    t = G.torch()
+    D = heads * 128
+    seed = 31 + seq
+    q = fs.normal(seed, "q", (1, seq, D), std=0.1, mean=beta)  # bf16-exact values
+    k = fs.normal(seed, "k", (1, seq, D))
+    k[:, [seq // 2, seq - 5]] = beta
+    v = fs.normal(seed, "v", (1, seq, D))
+    o = t.empty((1, seq, D), dtype=t.bfloat16, device="cuda")
+    nb = F().flux_attention_workspace_size(cfg(D), 1, seq)
+    ws = G.workspace(nb)
+    F().flux_attention(cfg(D), 1, seq, G.dev(q, "bf16"), G.dev(k, "bf16"), G.dev(v, "bf16"), D,
+                       o, D, ws, nb, G.stream())
+    t.cuda.synchronize()
+    got = G.host(o)
+    rows = _sample_rows(seq, 48, seed)
+    qh = q.astype(np.float64).reshape(1, seq, heads, 128)
+    kh = k.astype(np.float64).reshape(1, seq, heads, 128)
+    vh = v.astype(np.float64).reshape(1, seq, heads, 128)
+    ref = np.empty((1, len(rows), heads, 128))
+    for h in range(heads):
+        p = O.attention_weights(qh[0, rows, h], kh[0, :, h])
+        ref[0, :, h] = p @ vh[0, :, h]
+    assert np.isfinite(got).all()
+    G.assert_close(got[:, rows], ref.reshape(1, len(rows), D), "bf16",
+                   f"attention L={seq} h={heads} late scores beta={beta}")

@@ -174,7 +174,10 @@ LIN_CASES = [  # m, n, k, dtype
     (1536, 3072, 3072, "bf16"), (4096, 12288, 4096, "bf16"), (512, 4096, 12288, "bf16"),
     # 1, 2, 3 and 5 K slices of 64: every branch of the peeled K loop, ragged M and N tails
     (300, 520, 64, "bf16"), (600, 1100, 128, "bf16"), (513, 700, 192, "bf16"),
-    (1030, 2050, 320, "bf16")]
+    (1030, 2050, 320, "bf16"),
+    # the same short K loops on 256 x 256 tiles (two A and three W stages), which the tile
+    # choice takes only for products of several rounds
+    (8192, 8192, 64, "bf16"), (8192, 8192, 128, "bf16"), (8192, 8192, 192, "bf16")]
 
 
 def _sample_rows(m, k=64, seed=0):

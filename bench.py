@@ -145,7 +145,7 @@ def measured_traffic():
 # bracketed by HIP events on the step's stream (libflux's timing hook); the probe mode
 # launches it alone, exactly as the step does, for the counter runs.
 # ------------------------------------------------------------------------------------
-DOMINANT_KERNEL = "gemm_bf16_lds_kernel<256,256,64,2,3,1,4,2,EpiSwiGLU<bf16>> (single-block linear1 MLP part)"
+DOMINANT_KERNEL = "gemm_bf16_lds_kernel<256,256,64,2,3,16,1,4,2,EpiSwiGLU<bf16>> (single-block linear1 MLP part)"
 
 
 def dominant_shape(wl):

@@ -1,10 +1,10 @@
 // Linear layers y = x W^T (W stored [N, K] row-major) with fused epilogues.
 //
-// bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation.  Each workgroup
-// (4 waves) computes a BM x BN tile; operands are staged through LDS in 64-wide K
-// slices, double buffered, with an XOR swizzle of the 16-byte chunks so the MFMA
-// fragment reads are bank-conflict free.  Global loads of the next slice are issued
-// before the MFMAs of the current one.
+// bf16 path: gfx950 MFMA (v_mfma_f32_16x16x32_bf16 in the large-tile kernels,
+// v_mfma_f32_32x32x16_bf16 in the generic one), fp32 accumulation.  A workgroup computes a
+// BM x BN tile; operands are staged through LDS in 64-wide K slices with an XOR swizzle of
+// the 16-byte chunks so the MFMA fragment reads are bank-conflict free, and the loads of
+// later slices are in flight during the MFMAs of the current one.
 //
 // Epilogues (the blocks' fused ops, "双流块 / 单流块 / 激活函数与 FFN" of the Diffusers
 // walk-through):
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
 // ------------------------------------------------------------------------------------
 // bf16 MFMA kernel, large tiles, direct global->LDS loads (K % BK == 0)
 //
-// NWM x NWN waves; each owns a (BM/NWM) x (BN/NWN) tile of 32x32 MFMA blocks.  256x256
+// NWM x NWN waves; each owns a (BM/NWM) x (BN/NWN) tile of MI x MI MFMA blocks.  256x256
 // tiles use 8 waves (two per SIMD, so one wave's waits overlap the other's MFMAs).  ST LDS
 // stages of BK-wide K slices are filled by global_load_lds_dwordx4: one wave instruction
 // writes 1 KB of LDS contiguously (lane i at byte 16 i), so each lane fetches the global
@@ -431,11 +431,14 @@ struct Swz {
 typedef uint8_t fp8;  // OCP E4M3 byte
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-// Body of the large-tile kernels.  TIn = bf16 (MFMA 32x32x16) or fp8 (E4M3 bytes, MFMA
-// 32x32x64 with unit block scales; the accumulators are multiplied by the per-row scale
-// sa[m] and the per-weight-row scale sw[n] before the epilogue).  Rows of a K slice are
-// 64 or 128 bytes either way, so the load plan, the LDS layout and the schedule are shared.
-template <class TIn, int BM, int BN, int BK, int ST, int STW, int NWM, int NWN, class Epi>
+// Body of the large-tile kernels.  TIn = bf16 (MFMA 32x32x16 or 16x16x32, MI = 32 / 16) or
+// fp8 (E4M3 bytes, MFMA 32x32x64 with unit block scales; the accumulators are multiplied by
+// the per-row scale sa[m] and the per-weight-row scale sw[n] before the epilogue).  Rows of
+// a K slice are 64 or 128 bytes either way, so the load plan, the LDS layout and the
+// schedule are shared.  The 16x16x32 form does the same work with a quarter of the
+// accumulator registers per MFMA and measured ~10% more sustained throughput with real
+// (full-entropy) operands, where the chip is power-bound.
+template <class TIn, int BM, int BN, int BK, int ST, int STW, int MI, int NWM, int NWN, class Epi>
 FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* __restrict__ W,
                             int64_t ldw, int M, int N, int K, int kw, int kdup, int n_half,
                             int tiles_m,
@@ -457,13 +460,19 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
   constexpr int BI = BN / (NWV * RPI);
   constexpr int LOADS = AI + BI;
   constexpr int WTM = BM / NWM, WTN = BN / NWN;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int KK = BK / (F8 ? 64 : 16);  // MFMA k-steps per slice
+  static_assert(MI == 32 || (MI == 16 && !F8), "MFMA shape");
+  constexpr int TM = WTM / MI, TN = WTN / MI;
+  constexpr int KK = BK / (F8 ? 64 : 512 / MI);  // MFMA k-steps per slice
   constexpr int NF = TM + TN;           // fragments per k-step
+  constexpr int AR = MI == 32 ? 16 : 4;  // accumulator registers per lane and MFMA block
+  // fragment reads of the next k-step: one after every RSTEP-th MFMA
+  constexpr int RSTEP = TM * TN >= 2 * NF ? 2 : 1;
   constexpr uint32_t A_STAGE_B = BM * BK * ES, W_STAGE_B = BN * BK * ES;
   static_assert(AI >= 1 && BI >= 1, "tile too small for the load plan");
   static_assert(KK % 2 == 0, "fragment sets alternate with the k-step parity");
-  static_assert(!Epi::kPaired || (TN % 2 == 0), "SwiGLU needs gate/up tile pairs");
+  // SwiGLU: gate and up rows interleave per 32 W rows, so a gate block's partner is the
+  // next 32x32 block or the 16x16 block two further
+  static_assert(!Epi::kPaired || (TN % (64 / MI) == 0), "SwiGLU needs gate/up tile pairs");
 
   extern __shared__ __align__(16) char lds_raw[];
   TIn* smem = reinterpret_cast<TIn*>(lds_raw);
@@ -528,21 +537,30 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
     }
   };
 
-  f32x16 acc[TM][TN];
+  using Acc = typename std::conditional<MI == 32, f32x16, f32x4>::type;
+  Acc acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < AR; ++r) acc[i][j][r] = 0.f;
 
-  const int lrow = lane & 31, lk = lane >> 5;
+  // MFMA lane layout.  32x32: lane holds column lane & 31 and rows 8 (r/4) + 4 (lane/32) +
+  // r%4; its A / B fragment is row lane & 31, k 8 (lane/32) .. + 8 of a 16-deep k-step.
+  // 16x16: lane holds column lane & 15 and rows 4 (lane/16) + r; its fragment is row
+  // lane & 15, k 8 (lane/16) .. + 8 of a 32-deep k-step.
+  const int lrow = lane & (MI - 1), lk = lane / MI;
+  auto acc_row = [&](int i, int r) {  // row of register r of block i within the wave tile
+    return MI == 32 ? i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3) : i * 16 + 4 * lk + r;
+  };
+  auto acc_col = [&](int j) { return j * MI + lrow; };
   using Frag = typename std::conditional<F8, v8i, bf16x8>::type;
   Frag fr[2][NF];  // [set][A fragments | B fragments]
   auto rd = [&](int set, int q, int sl, int kk) {  // fragment q of k-step kk of slice sl
     const TIn* ob = q < TM ? smem + (sl % ST) * BM * BK
                            : smem + ST * BM * BK + (sl % STW) * BN * BK;
-    const int row = q < TM ? wm * WTM + q * 32 + lrow : wn * WTN + (q - TM) * 32 + lrow;
+    const int row = q < TM ? wm * WTM + q * MI + lrow : wn * WTN + (q - TM) * MI + lrow;
     if constexpr (F8) {
       // k-step kk covers chunks 4 kk .. 4 kk + 3 (64 k); lane group lk holds two of them
       const uint4 lo = *reinterpret_cast<const uint4*>(ob + S::off(row, kk * 4 + 2 * lk));
@@ -550,8 +568,18 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
       fr[set][q] = Frag{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     } else {
-      fr[set][q] = *reinterpret_cast<const bf16x8*>(ob + S::off(row, kk * 2 + lk));
+      fr[set][q] = *reinterpret_cast<const bf16x8*>(ob + S::off(row, kk * (64 / MI) + lk));
     }
+  };
+
+  auto mfma = [&](int set, int i, int j) {
+    if constexpr (F8)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          fr[set][i], fr[set][TM + j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    else if constexpr (MI == 32)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[set][i], fr[set][TM + j], acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[set][i], fr[set][TM + j], acc[i][j], 0, 0, 0);
   };
 
   // prologue: fill the stages, wait for slice 0, read its first fragments.  Symmetric: ST
@@ -611,13 +639,9 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
 #pragma unroll
       for (int q = 0; q < TM * TN; ++q) {
         const int i = q / TN, j = q % TN;
-        if constexpr (F8)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0, 127, 0, 127);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0);
+        mfma(cur, i, j);
         __builtin_amdgcn_sched_barrier(0);
-        if (do_rd && q < NF) rd(nxt, q, rsl, rkk);
+        if (do_rd && q % RSTEP == 0 && q / RSTEP < NF) rd(nxt, q / RSTEP, rsl, rkk);
         if (q0 + q < q1) dma(q0 + q, ds);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -627,7 +651,7 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
         if (q0 + q < q1) dma(q0 + q, ds);
       if (do_rd)
 #pragma unroll
-        for (int q = TM * TN; q < NF; ++q) rd(nxt, q, rsl, rkk);
+        for (int q = (TM * TN + RSTEP - 1) / RSTEP; q < NF; ++q) rd(nxt, q, rsl, rkk);
     }
   };
 
@@ -659,13 +683,9 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
 #pragma unroll
       for (int q = 0; q < TM * TN; ++q) {
         const int i = q / TN, j = q % TN;
-        if constexpr (F8)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0, 127, 0, 127);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[cur][i], fr[cur][TM + j], acc[i][j], 0, 0, 0);
+        mfma(cur, i, j);
         __builtin_amdgcn_sched_barrier(0);
-        if (do_rd && q < NF) rd(nxt, q, rsl, rkk);
+        if (do_rd && q % RSTEP == 0 && q / RSTEP < NF) rd(nxt, q / RSTEP, rsl, rkk);
         if (q0 + q < q1) dma(q0 + q, kt + 2);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -674,7 +694,7 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
         if (q0 + q < q1) dma(q0 + q, kt + 2);
       if (do_rd)
 #pragma unroll
-        for (int q = TM * TN; q < NF; ++q) rd(nxt, q, rsl, rkk);
+        for (int q = (TM * TN + RSTEP - 1) / RSTEP; q < NF; ++q) rd(nxt, q, rsl, rkk);
     }
   };
 
@@ -704,7 +724,7 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
     float swv[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * WTN + j * 32 + lrow;
+      const int n = n0 + wn * WTN + acc_col(j);
       int pn;
       if constexpr (Epi::kPaired) {
         const int jj = min(((n >> 6) << 5) + (n & 31), n_half - 1);
@@ -717,8 +737,8 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float av = sa[min(m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3), M - 1)];
+      for (int r = 0; r < AR; ++r) {
+        const float av = sa[min(m0 + wm * WTM + acc_row(i, r), M - 1)];
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j][r] *= av * swv[j];
       }
@@ -729,37 +749,39 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ml = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+      for (int r = 0; r < AR; ++r) {
+        const int ml = wm * WTM + acc_row(i, r);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) pt[ml * BN + wn * WTN + j * 32 + lrow] = acc[i][j][r];
+        for (int j = 0; j < TN; ++j) pt[ml * BN + wn * WTN + acc_col(j)] = acc[i][j][r];
       }
     return;
   }
   if constexpr (Epi::kRow4) {
-    // Row-vector epilogue through the (now idle) LDS stages.  Pass p = (i, h) stages the 16
-    // rows i*32 + 16h + [0, 16) of every wave's tile: PR = 16*NWM rows of BN fp32 (two
-    // buffers, alternating), then each wave moves whole staged rows with 16-byte LDS reads
-    // and row-contiguous global accesses (the residual / gate loads of a pass are all in
-    // flight together).  Staged row sr holds tile row (sr/16)*WTM + i*32 + 16h + sr%16;
-    // its 32-column halves of each 64 are swapped when bit 2 of sr is set, so the two
-    // half-waves of a ds_write (rows 4 apart) hit different banks.
+    // Row-vector epilogue through the (now idle) LDS stages.  Pass p stages the 16 rows
+    // 16p .. 16p + 15 of every wave's tile (registers RPP p' .. of block p / (MI / 16)):
+    // PR = 16*NWM rows of BN fp32 (two buffers, alternating), then each wave moves whole
+    // staged rows with 16-byte LDS reads and row-contiguous global accesses (the residual /
+    // gate loads of a pass are all in flight together).  Staged row sr holds tile row
+    // (sr/16)*WTM + 16p + sr%16.  Its columns are XOR-ed with swz(sr) so the lane groups of
+    // a ds_write (rows 4 apart) hit different banks.
     constexpr int PR = 16 * NWM, NT = 64 * NWV, CPO = BN / 4;
     constexpr int PER_T = PR * CPO / NT;
+    constexpr int RPP = MI == 32 ? 8 : 4;  // accumulator registers per pass
     static_assert(PR * CPO % NT == 0 && BN % 64 == 0, "staged epilogue shape");
     static_assert(2 * PR * BN * 4 <= ST * A_STAGE_B + STW * W_STAGE_B, "staging buffers fit in the LDS stages");
+    auto swz = [](int sr) { return MI == 32 ? ((sr >> 2) & 1) << 5 : ((sr >> 2) & 3) << 4; };
     float* stg = reinterpret_cast<float*>(smem);
     __syncthreads();  // every wave is done reading the last slice
 #pragma unroll
-    for (int p = 0; p < 2 * TM; ++p) {
-      const int i = p >> 1, h = p & 1;
+    for (int p = 0; p < WTM / 16; ++p) {
+      const int i = p / (MI / 16), r0 = (p % (MI / 16)) * RPP;
       float* buf = stg + (p & 1) * PR * BN;
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int sr = wm * 16 + 8 * (rr >> 2) + 4 * lk + (rr & 3);
+      for (int rr = 0; rr < RPP; ++rr) {
+        const int sr = wm * 16 + (acc_row(i, r0 + rr) & 15);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          buf[sr * BN + ((wn * WTN + j * 32 + lrow) ^ (lk << 5))] = acc[i][j][8 * h + rr];
+          buf[sr * BN + ((wn * WTN + acc_col(j)) ^ swz(sr))] = acc[i][j][r0 + rr];
       }
       __syncthreads();
       if (n0 < epi.col_major_from()) {
@@ -767,22 +789,21 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
         for (int u = 0; u < PER_T; ++u) {
           const int e = tid + u * NT;
           const int sr = e / CPO, c = e % CPO;
-          const int m = m0 + (sr >> 4) * WTM + i * 32 + 16 * h + (sr & 15);
+          const int m = m0 + (sr >> 4) * WTM + 16 * p + (sr & 15);
           const int n = n0 + 4 * c;
-          const float4 v = *reinterpret_cast<const float4*>(buf + sr * BN +
-                                                            ((4 * c) ^ (((sr >> 2) & 1) << 5)));
+          const float4 v = *reinterpret_cast<const float4*>(buf + sr * BN + ((4 * c) ^ swz(sr)));
           if (m < M && n < N) epi.vec4(m, n, v, N);
         }
       } else if constexpr (Epi::kQuad) {
         // column-major output: item = 4 consecutive rows (staged rows 4q .. 4q+3 of a wave
-        // block, same bit 2) of one column; 4 lanes in a row cover 16 contiguous rows
+        // block, one swizzle) of one column; 4 lanes in a row cover 16 contiguous rows
 #pragma unroll 2
         for (int u = 0; u < PER_T; ++u) {
           const int e = tid + u * NT;
           const int q = e & 3, col = (e >> 2) % BN, wb = (e >> 2) / BN;
           const int sr = wb * 16 + 4 * q;
-          const float* src = buf + sr * BN + (col ^ ((q & 1) << 5));
-          const int m = m0 + wb * WTM + i * 32 + 16 * h + 4 * q;
+          const float* src = buf + sr * BN + (col ^ swz(sr));
+          const int m = m0 + wb * WTM + 16 * p + 4 * q;
           const int n = n0 + col;
           if (m < M && n < N) epi.quad(m, n, src[0], src[BN], src[2 * BN], src[3 * BN], M);
         }
@@ -794,12 +815,12 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int m = m0 + wm * WTM + i * 32 + 8 * r4 + 4 * lk;
+      for (int r4 = 0; r4 < AR / 4; ++r4) {
+        const int m = m0 + wm * WTM + acc_row(i, 4 * r4);
         if (m >= M) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int n = n0 + wn * WTN + j * 32 + lrow;
+          const int n = n0 + wn * WTN + acc_col(j);
           if (n < N)
             epi.quad(m, n, acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
                      acc[i][j][4 * r4 + 3], M);
@@ -810,20 +831,22 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+    for (int r = 0; r < AR; ++r) {
+      const int m = m0 + wm * WTM + acc_row(i, r);
       if (m >= M) continue;
       if constexpr (Epi::kPaired) {
+        constexpr int PO = 32 / MI;  // up block of gate block j: j + PO
 #pragma unroll
-        for (int j = 0; j < TN; j += 2) {
-          const int nl = n0 + wn * WTN + j * 32 + lrow;
+        for (int j = 0; j < TN; ++j) {
+          if (j & PO) continue;
+          const int nl = n0 + wn * WTN + acc_col(j);
           const int jj = ((nl >> 6) << 5) + (nl & 31);
-          if (jj < n_half) epi.pair(m, jj, acc[i][j][r], acc[i][j + 1][r]);
+          if (jj < n_half) epi.pair(m, jj, acc[i][j][r], acc[i][j + PO][r]);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int n = n0 + wn * WTN + j * 32 + lrow;
+          const int n = n0 + wn * WTN + acc_col(j);
           if (n < N) epi(m, n, acc[i][j][r]);
         }
       }
@@ -831,12 +854,12 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
   }
 }
 
-template <int BM, int BN, int BK, int ST, int STW, int OCC, int NWM, int NWN, class Epi>
+template <int BM, int BN, int BK, int ST, int STW, int MI, int OCC, int NWM, int NWN, class Epi>
 __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw, int M,
     int N, int K, int kw, int kdup, int n_half, int tiles_m, int tiles_n, int full_tiles,
     int splits, float* __restrict__ partial, Epi epi) {
-  gemm_lds_body<bf16, BM, BN, BK, ST, STW, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, kw, kdup, n_half,
+  gemm_lds_body<bf16, BM, BN, BK, ST, STW, MI, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, kw, kdup, n_half,
                                                      tiles_m, tiles_n, full_tiles, splits,
                                                      partial, epi, nullptr, nullptr);
 }
@@ -847,7 +870,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_fp8_lds_kernel(
     int N, int K, int n_half, int tiles_m, int tiles_n, int full_tiles, int splits,
     float* __restrict__ partial, Epi epi, const float* __restrict__ sa,
     const float* __restrict__ sw) {
-  gemm_lds_body<fp8, BM, BN, BK, ST, ST, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, K, 0, n_half,
+  gemm_lds_body<fp8, BM, BN, BK, ST, ST, 32, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, K, 0, n_half,
                                                     tiles_m, tiles_n, full_tiles, splits, partial,
                                                     epi, sa, sw);
 }
@@ -939,7 +962,7 @@ static hipError_t ensure_lds_limit(LdsLimit& st, const void* fn, size_t bytes) {
 }
 
 // Launch one large-tile configuration (sets the dynamic LDS limit once per instance).
-template <int BM, int BN, int BK, int ST, int STW, int OCC, int NWM, int NWN, class Epi>
+template <int BM, int BN, int BK, int ST, int STW, int MI, int OCC, int NWM, int NWN, class Epi>
 static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N,
                              int K, int kw, int kdup, int n_half, const Epi& epi, int splits,
                              float* partial, hipStream_t s) {
@@ -954,10 +977,10 @@ static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t 
   static LdsLimit limit;
   hipError_t le = ensure_lds_limit(
       limit,
-      reinterpret_cast<const void*>(&gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, OCC, NWM, NWN, Epi>),
+      reinterpret_cast<const void*>(&gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, MI, OCC, NWM, NWN, Epi>),
       lds);
   if (le != hipSuccess) return le;
-  hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, OCC, NWM, NWN, Epi>),
+  hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, MI, OCC, NWM, NWN, Epi>),
                      dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, A, lda, W, ldw, M, N,
                      K, kw, kdup, n_half, tiles_m, tiles_n, full, splits, partial, epi);
   if (tail > 0) {
@@ -1129,12 +1152,12 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
       auto* a = static_cast<const bf16*>(A);
       auto* w = static_cast<const bf16*>(W);
       if (best == 0)
-        return launch_lds<256, 256, 64, 2, 3, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
+        return launch_lds<256, 256, 64, 2, 3, 16, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
                                                      epi, best_split, split_ws, s);
       if (best == 1)
-        return launch_lds<256, 128, 64, 2, 2, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
+        return launch_lds<256, 128, 64, 2, 2, 16, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
                                                      epi, best_split, split_ws, s);
-      return launch_lds<128, 128, 64, 2, 2, 2, 2, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half, epi,
+      return launch_lds<128, 128, 64, 2, 2, 16, 2, 2, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half, epi,
                                                    best_split, split_ws, s);
     }
     constexpr int BM = 128, BN = 128;

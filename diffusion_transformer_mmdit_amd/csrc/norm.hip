@@ -51,6 +51,26 @@ FLUX_DEV float4 ld_stream4(const float4* p) {
   return make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// Streaming load of 8 bf16 / fp32 values that a kernel reads once (q and k rows before the
+// in-place RMSNorm + RoPE).  Measured from HBM at 4608 tokens x 32 heads: 36.7 -> 34.1 us;
+// at 48 heads (the per-(token, head) kernel) it was 3% slower, so that kernel keeps plain
+// loads.
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+template <class T>
+FLUX_DEV void load8_stream(const T* p, float* f);
+template <>
+FLUX_DEV void load8_stream<bf16>(const bf16* p, float* f) {
+  const u32x4s v = __builtin_nontemporal_load(reinterpret_cast<const u32x4s*>(p));
+  unpack8(make_uint4(v[0], v[1], v[2], v[3]), f);
+}
+template <>
+FLUX_DEV void load8_stream<float>(const float* p, float* f) {
+  const float4 a = ld_stream4(reinterpret_cast<const float4*>(p));
+  const float4 b = ld_stream4(reinterpret_cast<const float4*>(p + 4));
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
 // ------------------------------------------------------------------------------------
 // LayerNorm + modulate
 // ------------------------------------------------------------------------------------
@@ -508,22 +528,23 @@ __global__ __launch_bounds__(256) void qk_norm_rope_token_kernel(
     gam[i] = which ? (seg1 ? kg1 : kg0) : (seg1 ? qg1 : qg0);
     ptr[i] = seq_ptr<T>(v, b, j) + head * 128 + l16 * 8;
     if (EXACT || c < nch) {
-      load8(ptr[i], x[i]);
+      load8_stream(ptr[i], x[i]);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
     }
   }
+  float gm[NI][8];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) load8(gam[i] + l16 * 8, gm[i]);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += x[i][e] * x[i][e];
     const float r = rsqrtf(group_sum16(ss) * (1.f / 128.f) + eps);
-    float gm[8];
-    load8(gam[i] + l16 * 8, gm);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] * r * gm[e];
+    for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] * r * gm[i][e];
     float o[8];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {

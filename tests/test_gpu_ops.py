@@ -59,8 +59,12 @@ def test_rope_positions_random_ids_bit_exact():
 # ------------------------------------------------------------------------------------
 # a1/a2: timestep embedding + modulation
 # ------------------------------------------------------------------------------------
+# x of batch x D floats is staged in LDS up to 64 KB (the last three cases: 48 KB with fp32
+# weights, 48 KB with bf16, 80 KB through the kernel that reads x from the caches)
 @pytest.mark.parametrize("D,dtype,batch,n_chunks", [(256, "f32", 1, 3), (256, "bf16", 3, 6),
-                                                    (3072, "bf16", 1, 3), (4096, "bf16", 2, 6)])
+                                                    (3072, "bf16", 1, 3), (4096, "bf16", 2, 6),
+                                                    (3072, "f32", 4, 2), (6144, "bf16", 2, 2),
+                                                    (4096, "bf16", 5, 3)])
 def test_modulation(D, dtype, batch, n_chunks):
     t = G.torch()
     seed = 77 + D

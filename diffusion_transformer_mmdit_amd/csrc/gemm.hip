@@ -889,6 +889,34 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int m0 = tm * BM, n0 = tn * BN;
   const float* p = partial + (size_t)t * splits * BM * BN;
   const size_t stride = (size_t)BM * BN;
+  if constexpr (Epi::kQuad) {
+    if (n0 >= epi.col_major_from()) {
+      // column-major output (V^T): the workgroup sums a 64-row x 16-column block with
+      // row-contiguous 16-byte reads, transposes it through LDS, and stores 4 consecutive
+      // rows of one column per thread (16 lanes cover 64 contiguous rows of a column)
+      static_assert(BM % 64 == 0 && BN % 16 == 0, "transposed reduce blocks");
+      __shared__ float sT[16][65];
+      const int mb = blockIdx.y / (BN / 16), nb = blockIdx.y % (BN / 16);
+      const int r = threadIdx.x >> 2, c4 = (threadIdx.x & 3) * 4;
+      const float* pp = p + (size_t)(mb * 64 + r) * BN + nb * 16 + c4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+      for (int sp = 0; sp < splits; ++sp) {
+        const float4 a = *reinterpret_cast<const float4*>(pp + sp * stride);
+        v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+      }
+      sT[c4][r] = v.x;
+      sT[c4 + 1][r] = v.y;
+      sT[c4 + 2][r] = v.z;
+      sT[c4 + 3][r] = v.w;
+      __syncthreads();
+      const int cl = threadIdx.x >> 4, q = threadIdx.x & 15;
+      const int m = m0 + mb * 64 + 4 * q, n = n0 + nb * 16 + cl;
+      if (m < M && n < N)
+        epi.quad(m, n, sT[cl][4 * q], sT[cl][4 * q + 1], sT[cl][4 * q + 2], sT[cl][4 * q + 3], M);
+      return;
+    }
+  }
   const int e = blockIdx.y * 256 + threadIdx.x;
   if constexpr (Epi::kPaired) {
     // logical columns come in 64-groups: 32 gate columns, then their 32 up columns

@@ -194,10 +194,10 @@ def dominant_roofline(wl, launches: int, mean_us: float) -> dict:
 
 
 # Every timing-hook site of the step: (site name, what it launches, its shape and
-# algorithmic FLOP per launch at the workload).  The double-block sites time the image
-# stream's launches (the text stream's are 1/8 of their size) and the joint attention.
+# algorithmic FLOP per launch at the workload).  The double block runs each linear of its
+# two streams as one launch (image rows, then text rows), so those sites time both streams.
 def site_table(F, wl):
-    D, H, L, Ni = wl.dim, wl.mlp_hidden, wl.seq, wl.n_img
+    D, H, L = wl.dim, wl.mlp_hidden, wl.seq
     lin = lambda m, n, k: (2.0 * m * n * k, [m, n, k])
     att = (4.0 * L * L * D * wl.batch, [wl.batch, wl.heads, L, L])
     return [
@@ -209,16 +209,16 @@ def site_table(F, wl):
          wl.n_single, *att),
         ("single_linear2", F.FLUX_SITE_SINGLE_LINEAR2, "linear2, gated-residual epilogue",
          wl.n_single, *lin(L, D, D + H)),
-        ("double_qkv_img", F.FLUX_SITE_DOUBLE_QKV, "image QKV, V^T epilogue", wl.n_double,
-         *lin(Ni, 3 * D, D)),
+        ("double_qkv", F.FLUX_SITE_DOUBLE_QKV, "image + text QKV (one launch), V^T epilogue",
+         wl.n_double, *lin(L, 3 * D, D)),
         ("double_attention", F.FLUX_SITE_DOUBLE_ATTENTION, "flash joint attention (+ merge)",
          wl.n_double, *att),
-        ("double_out_img", F.FLUX_SITE_DOUBLE_OUT, "image out-proj, gated-residual epilogue",
-         wl.n_double, *lin(Ni, D, D)),
-        ("double_mlp_in_img", F.FLUX_SITE_DOUBLE_MLP_IN, "image MLP-in, SwiGLU epilogue",
-         wl.n_double, *lin(Ni, 2 * H, D)),
-        ("double_mlp_out_img", F.FLUX_SITE_DOUBLE_MLP_OUT, "image MLP-out, gated-residual "
-         "epilogue", wl.n_double, *lin(Ni, D, H)),
+        ("double_out", F.FLUX_SITE_DOUBLE_OUT, "image + text out-proj (one launch), "
+         "gated-residual epilogue", wl.n_double, *lin(L, D, D)),
+        ("double_mlp_in", F.FLUX_SITE_DOUBLE_MLP_IN, "image + text MLP-in (one launch), SwiGLU "
+         "epilogue", wl.n_double, *lin(L, 2 * H, D)),
+        ("double_mlp_out", F.FLUX_SITE_DOUBLE_MLP_OUT, "image + text MLP-out (one launch), "
+         "gated-residual epilogue", wl.n_double, *lin(L, D, H)),
     ]
 
 

@@ -269,11 +269,12 @@ static RopeBufs carve_rope(Carver& cv, int L) {
 // ------------------------------------------------------------------------------------
 // linear helper
 // ------------------------------------------------------------------------------------
-static int lin(const flux_cfg* c, int epi, int m, int n, int k, const void* x, int64_t ldx,
-               const void* w, int64_t ldw, void* y, int64_t ldy, int y_dtype,
-               const void* resid = nullptr, int64_t ldr = 0, int r_dtype = FLUX_F32,
-               const float* gate = nullptr, int64_t gate_bs = 0, int rpb = 1, hipStream_t s = 0,
-               float* split_ws = nullptr, int kdup = 0, bool swiglu_lo = false) {
+static LinearArgs lin_args(int epi, int m, int n, int k, const void* x, int64_t ldx,
+                           const void* w, int64_t ldw, void* y, int64_t ldy, int y_dtype,
+                           const void* resid = nullptr, int64_t ldr = 0,
+                           int r_dtype = FLUX_F32, const float* gate = nullptr,
+                           int64_t gate_bs = 0, int rpb = 1, float* split_ws = nullptr,
+                           int kdup = 0, bool swiglu_lo = false) {
   LinearArgs a{};
   a.kdup = kdup;
   a.swiglu_lo = swiglu_lo;
@@ -295,14 +296,24 @@ static int lin(const flux_cfg* c, int epi, int m, int n, int k, const void* x, i
   a.gate_bs = gate_bs;
   a.rows_per_batch = rpb;
   a.split_ws = split_ws;
-  HIP_TRY(linear(c->dtype, a, s));
+  return a;
+}
+
+static int lin(const flux_cfg* c, int epi, int m, int n, int k, const void* x, int64_t ldx,
+               const void* w, int64_t ldw, void* y, int64_t ldy, int y_dtype,
+               const void* resid = nullptr, int64_t ldr = 0, int r_dtype = FLUX_F32,
+               const float* gate = nullptr, int64_t gate_bs = 0, int rpb = 1, hipStream_t s = 0,
+               float* split_ws = nullptr, int kdup = 0, bool swiglu_lo = false) {
+  HIP_TRY(linear(c->dtype, lin_args(epi, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid, ldr,
+                                    r_dtype, gate, gate_bs, rpb, split_ws, kdup, swiglu_lo),
+                 s));
   return FLUX_OK;
 }
 
 // q | k row-major into qk [m, 2D]; v transposed into vt [B*D, ldvt] at token offset vt_off.
 // x: [m, D] or, with hi / lo operands, [m, 2D] (hi | lo planes).
-static int lin_qkv(const flux_cfg* c, int m, const void* x, const void* w, void* qk, void* vt,
-                   int64_t ldvt, int vt_off, int rpb, hipStream_t s, float* split_ws) {
+static LinearArgs qkv_args(const flux_cfg* c, int m, const void* x, const void* w, void* qk,
+                           void* vt, int64_t ldvt, int vt_off, int rpb, float* split_ws) {
   LinearArgs a{};
   const int P = planes(c);
   a.epilogue = EPI_QKV;
@@ -323,7 +334,12 @@ static int lin_qkv(const flux_cfg* c, int m, const void* x, const void* w, void*
   a.vt_off = vt_off;
   a.dim = c->dim;
   a.split_ws = split_ws;
-  HIP_TRY(linear(c->dtype, a, s));
+  return a;
+}
+
+static int lin_qkv(const flux_cfg* c, int m, const void* x, const void* w, void* qk, void* vt,
+                   int64_t ldvt, int vt_off, int rpb, hipStream_t s, float* split_ws) {
+  HIP_TRY(linear(c->dtype, qkv_args(c, m, x, w, qk, vt, ldvt, vt_off, rpb, split_ws), s));
   return FLUX_OK;
 }
 
@@ -436,16 +452,20 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
       return layernorm_modulate_hilo(dt, x, D, y, 2 * D, rows, D, rpb, sh, sc, mbs, c->eps, s);
     return layernorm_modulate(dt, T, x, D, y, D, rows, D, rpb, sh, sc, mbs, c->eps, s);
   };
-  // timing-hook sites: the image stream's launches (i == 1) of a block that is not filling
-  // the reference cache
-  auto site = [&](int i, int id) { return (i == 1 && !fill) ? id : 0; };
-  for (int i = 0; i < 2; ++i) {
-    if (n[i] == 0) continue;
-    const int rows = B * n[i];
-    HIP_TRY(ln_mod(in_dt, in[i], d.ln[i], rows, n[i], mods[i], mods[i] + D));
-    TimedSite ts(site(i, FLUX_SITE_DOUBLE_QKV), s);
-    CHECK(lin_qkv(c, rows, d.ln[i], sw[i]->qkv, qk[i], vtb, ldvt, i == 0 ? 0 : Nt, n[i], s,
-                  d.split));
+  // timing-hook sites: the block's launches (both streams' products in one launch), unless
+  // the block is filling the reference cache
+  auto site = [&](int id) { return fill ? 0 : id; };
+  // The two streams' products share N and K: each linear runs as one launch, the image
+  // stream's tiles first (whole rounds at the common sizes) and the text stream's after them.
+  for (int i = 0; i < 2; ++i)
+    if (n[i] > 0) HIP_TRY(ln_mod(in_dt, in[i], d.ln[i], B * n[i], n[i], mods[i], mods[i] + D));
+  {
+    TimedSite ts(site(FLUX_SITE_DOUBLE_QKV), s);
+    HIP_TRY(linear_pair(T, qkv_args(c, B * Ni, d.ln[1], sw[1]->qkv, qk[1], vtb, ldvt, Nt, Ni,
+                                    d.split),
+                        qkv_args(c, B * Nt, d.ln[0], sw[0]->qkv, qk[0], vtb, ldvt, 0, Nt,
+                                 d.split),
+                        s));
   }
   if (ldvt > L) HIP_TRY(zero_cols(T, vtb, ldvt, (int64_t)B * D, L, (int)ldvt, s));
   // joint views: segment 0 = text rows, segment 1 = image rows
@@ -467,31 +487,40 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
   KvExtra xk{};
   if (ref_use == REF_KEYS) xk = extra_keys(c, ref, B);
   {
-    TimedSite ts(site(1, FLUX_SITE_DOUBLE_ATTENTION), s);
+    TimedSite ts(site(FLUX_SITE_DOUBLE_ATTENTION), s);
     HIP_TRY(attention(T, qv, kv, vtb, ldvt, ov, B, L, c->heads, d.split, s,
                       ref_use == REF_KEYS ? &xk : nullptr));
   }
-  for (int i = 0; i < 2; ++i) {
-    if (n[i] == 0) continue;
-    const int rows = B * n[i];
-    // x + gate1 * (O W_o^T)  -> mid (f32)
-    {
-      TimedSite ts(site(i, FLUX_SITE_DOUBLE_OUT), s);
-      CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, D, d.o[i], D, sw[i]->out, D, d.mid[i], D,
-                FLUX_F32, in[i], D, in_dt, mods[i] + 2 * D, mbs, n[i], s, d.split));
-    }
-    HIP_TRY(ln_mod(FLUX_F32, d.mid[i], d.ln[i], rows, n[i], mods[i] + 3 * D, mods[i] + 4 * D));
-    {
-      TimedSite ts(site(i, FLUX_SITE_DOUBLE_MLP_IN), s);
-      CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, P * D, d.ln[i], P * D, sw[i]->mlp_in, D, d.mlp[i],
-                P * H, T, nullptr, 0, 0, nullptr, 0, 1, s, d.split, (P - 1) * D, P == 2));
-    }
-    // mid + gate2 * (M W_out^T) -> out
-    TimedSite ts(site(i, FLUX_SITE_DOUBLE_MLP_OUT), s);
-    CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, P * H, d.mlp[i], P * H, sw[i]->mlp_out, H, out[i],
-              D, out_dt, d.mid[i], D, FLUX_F32, mods[i] + 5 * D, mbs, n[i], s, d.split,
-              (P - 1) * H));
+  // x + gate1 * (O W_o^T)  -> mid (f32)
+  auto out_args = [&](int i) {
+    return lin_args(EPI_GATED_RESIDUAL, B * n[i], D, D, d.o[i], D, sw[i]->out, D, d.mid[i], D,
+                    FLUX_F32, in[i], D, in_dt, mods[i] + 2 * D, mbs, n[i], d.split);
+  };
+  {
+    TimedSite ts(site(FLUX_SITE_DOUBLE_OUT), s);
+    HIP_TRY(linear_pair(T, out_args(1), out_args(0), s));
   }
+  for (int i = 0; i < 2; ++i)
+    if (n[i] > 0)
+      HIP_TRY(ln_mod(FLUX_F32, d.mid[i], d.ln[i], B * n[i], n[i], mods[i] + 3 * D,
+                     mods[i] + 4 * D));
+  auto mlp_in_args = [&](int i) {
+    return lin_args(EPI_SWIGLU, B * n[i], 2 * H, P * D, d.ln[i], P * D, sw[i]->mlp_in, D,
+                    d.mlp[i], P * H, T, nullptr, 0, 0, nullptr, 0, 1, d.split, (P - 1) * D,
+                    P == 2);
+  };
+  {
+    TimedSite ts(site(FLUX_SITE_DOUBLE_MLP_IN), s);
+    HIP_TRY(linear_pair(T, mlp_in_args(1), mlp_in_args(0), s));
+  }
+  // mid + gate2 * (M W_out^T) -> out
+  auto mlp_out_args = [&](int i) {
+    return lin_args(EPI_GATED_RESIDUAL, B * n[i], D, P * H, d.mlp[i], P * H, sw[i]->mlp_out, H,
+                    out[i], D, out_dt, d.mid[i], D, FLUX_F32, mods[i] + 5 * D, mbs, n[i],
+                    d.split, (P - 1) * H);
+  };
+  TimedSite ts(site(FLUX_SITE_DOUBLE_MLP_OUT), s);
+  HIP_TRY(linear_pair(T, mlp_out_args(1), mlp_out_args(0), s));
   return FLUX_OK;
 }
 

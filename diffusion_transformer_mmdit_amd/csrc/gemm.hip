@@ -16,6 +16,7 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <mutex>
@@ -438,12 +439,24 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 // schedule are shared.  The 16x16x32 form does the same work with a quarter of the
 // accumulator registers per MFMA and measured ~10% more sustained throughput with real
 // (full-entropy) operands, where the chip is power-bound.
+// One product of a launch: operands, rows (and their tile count) and epilogue.  A launch
+// runs one product, or two with the same N and K and operand strides (the double block's
+// image and text streams); segment 1's tiles follow segment 0's in the logical tile order,
+// so a partial last round of tiles (and its split-K) falls on segment 1.
+template <class TIn, class Epi>
+struct GemmSeg {
+  const TIn* A;
+  const TIn* W;
+  int M;
+  int tiles_m;
+  Epi epi;
+};
+
 template <class TIn, int BM, int BN, int BK, int ST, int STW, int MI, int NWM, int NWN, class Epi>
-FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* __restrict__ W,
-                            int64_t ldw, int M, int N, int K, int kw, int kdup, int n_half,
-                            int tiles_m,
+FLUX_DEV void gemm_lds_body(const GemmSeg<TIn, Epi>& s0, const GemmSeg<TIn, Epi>& s1, int tiles0,
+                            int64_t lda, int64_t ldw, int N, int K, int kw, int kdup, int n_half,
                             int tiles_n, int full_tiles, int splits, float* __restrict__ partial,
-                            Epi epi, const float* __restrict__ sa, const float* __restrict__ sw) {
+                            const float* __restrict__ sa, const float* __restrict__ sw) {
   constexpr int ES = sizeof(TIn);
   constexpr bool F8 = ES == 1;
   static_assert(BK * ES == 64 || BK * ES == 128, "BK: 64- or 128-byte slice rows");
@@ -494,8 +507,15 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
     k_begin = split * nk_all / splits;
     k_end = (split + 1) * nk_all / splits;
   }
+  // the tile's product (segment); the selection is uniform across the workgroup
+  const bool seg1 = logical >= tiles0;
+  const GemmSeg<TIn, Epi>& G = seg1 ? s1 : s0;
+  const TIn* __restrict__ A = G.A;
+  const TIn* __restrict__ W = G.W;
+  const int M = G.M;
+  const Epi epi = G.epi;
   int tm, tn;
-  logical_coords(logical, tiles_m, tiles_n, tm, tn);
+  logical_coords(seg1 ? logical - tiles0 : logical, G.tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // load plan: instruction j of wave w covers rows (w*AI + j)*RPI + [0, RPI); lane ->
@@ -856,36 +876,41 @@ FLUX_DEV void gemm_lds_body(const TIn* __restrict__ A, int64_t lda, const TIn* _
 
 template <int BM, int BN, int BK, int ST, int STW, int MI, int OCC, int NWM, int NWN, class Epi>
 __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
-    const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw, int M,
-    int N, int K, int kw, int kdup, int n_half, int tiles_m, int tiles_n, int full_tiles,
-    int splits, float* __restrict__ partial, Epi epi) {
-  gemm_lds_body<bf16, BM, BN, BK, ST, STW, MI, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, kw, kdup, n_half,
-                                                     tiles_m, tiles_n, full_tiles, splits,
-                                                     partial, epi, nullptr, nullptr);
+    GemmSeg<bf16, Epi> s0, GemmSeg<bf16, Epi> s1, int tiles0, int64_t lda, int64_t ldw, int N,
+    int K, int kw, int kdup, int n_half, int tiles_n, int full_tiles, int splits,
+    float* __restrict__ partial) {
+  gemm_lds_body<bf16, BM, BN, BK, ST, STW, MI, NWM, NWN, Epi>(s0, s1, tiles0, lda, ldw, N, K, kw,
+                                                              kdup, n_half, tiles_n, full_tiles,
+                                                              splits, partial, nullptr, nullptr);
 }
 
 template <int BM, int BN, int BK, int ST, int OCC, int NWM, int NWN, class Epi>
 __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_fp8_lds_kernel(
-    const fp8* __restrict__ A, int64_t lda, const fp8* __restrict__ W, int64_t ldw, int M,
-    int N, int K, int n_half, int tiles_m, int tiles_n, int full_tiles, int splits,
-    float* __restrict__ partial, Epi epi, const float* __restrict__ sa,
+    GemmSeg<fp8, Epi> s0, int64_t lda, int64_t ldw, int N, int K, int n_half, int tiles_n,
+    int full_tiles, int splits, float* __restrict__ partial, const float* __restrict__ sa,
     const float* __restrict__ sw) {
-  gemm_lds_body<fp8, BM, BN, BK, ST, ST, 32, NWM, NWN, Epi>(A, lda, W, ldw, M, N, K, K, 0, n_half,
-                                                    tiles_m, tiles_n, full_tiles, splits, partial,
-                                                    epi, sa, sw);
+  gemm_lds_body<fp8, BM, BN, BK, ST, ST, 32, NWM, NWN, Epi>(s0, s0, INT_MAX, lda, ldw, N, K, K, 0,
+                                                            n_half, tiles_n, full_tiles, splits,
+                                                            partial, sa, sw);
 }
 
 // Split-K tail: sum the `splits` partial tiles of each tail tile in a fixed order (so the
 // result is deterministic) and apply the fused epilogue.  grid = (tail tiles, chunks);
 // each thread owns 4 consecutive columns of one row (16-byte loads per partial).
-template <int BM, int BN, class Epi>
+template <int BM, int BN, class Epi, class TIn>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
-                                                            int splits, int full_tiles, int tiles_m,
-                                                            int tiles_n, int M, int N, int n_half,
-                                                            Epi epi) {
+                                                            int splits, int full_tiles,
+                                                            GemmSeg<TIn, Epi> s0,
+                                                            GemmSeg<TIn, Epi> s1, int tiles0,
+                                                            int tiles_n, int N, int n_half) {
   const int t = blockIdx.x;
+  const int logical = full_tiles + t;
+  const bool seg1 = logical >= tiles0;
+  const GemmSeg<TIn, Epi>& G = seg1 ? s1 : s0;
+  const int M = G.M;
+  const Epi epi = G.epi;
   int tm, tn;
-  logical_coords(full_tiles + t, tiles_m, tiles_n, tm, tn);
+  logical_coords(seg1 ? logical - tiles0 : logical, G.tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const float* p = partial + (size_t)t * splits * BM * BN;
   const size_t stride = (size_t)BM * BN;
@@ -989,13 +1014,18 @@ static hipError_t ensure_lds_limit(LdsLimit& st, const void* fn, size_t bytes) {
   return e;
 }
 
-// Launch one large-tile configuration (sets the dynamic LDS limit once per instance).
+// Launch one large-tile configuration (sets the dynamic LDS limit once per instance) over
+// the products seg[0 .. nseg) (nseg 1 or 2; segment 1 may have no rows).
 template <int BM, int BN, int BK, int ST, int STW, int MI, int OCC, int NWM, int NWN, class Epi>
-static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N,
-                             int K, int kw, int kdup, int n_half, const Epi& epi, int splits,
+static hipError_t launch_lds(const GemmSeg<bf16, Epi>* seg, int nseg, int64_t lda, int64_t ldw,
+                             int N, int K, int kw, int kdup, int n_half, int splits,
                              float* partial, hipStream_t s) {
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int tiles = tiles_m * tiles_n;
+  GemmSeg<bf16, Epi> g0 = seg[0], g1 = nseg > 1 ? seg[1] : seg[0];
+  const int tiles_n = (N + BN - 1) / BN;
+  g0.tiles_m = (g0.M + BM - 1) / BM;
+  g1.tiles_m = (g1.M + BM - 1) / BM;
+  const int tiles0 = g0.tiles_m * tiles_n;
+  const int tiles = tiles0 + (nseg > 1 ? g1.tiles_m * tiles_n : 0);
   const int slots = 256 * OCC;
   const int tail = splits > 1 ? tiles % slots : 0;
   const int full = tiles - tail;
@@ -1009,19 +1039,19 @@ static hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t 
       lds);
   if (le != hipSuccess) return le;
   hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, MI, OCC, NWM, NWN, Epi>),
-                     dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, A, lda, W, ldw, M, N,
-                     K, kw, kdup, n_half, tiles_m, tiles_n, full, splits, partial, epi);
+                     dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, g0, g1, tiles0, lda,
+                     ldw, N, K, kw, kdup, n_half, tiles_n, full, splits, partial);
   if (tail > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int chunks = Epi::kPaired ? BM * BN / 8 / 256 : BM * BN / 4 / 256;
-    hipLaunchKernelGGL((splitk_reduce_kernel<BM, BN, Epi>), dim3(tail, chunks), dim3(256), 0, s,
-                       partial, splits, full, tiles_m, tiles_n, M, N, n_half, epi);
+    hipLaunchKernelGGL((splitk_reduce_kernel<BM, BN, Epi, bf16>), dim3(tail, chunks), dim3(256),
+                       0, s, partial, splits, full, g0, g1, tiles0, tiles_n, N, n_half);
   }
   return hipGetLastError();
 }
 
-// Same for the fp8 kernel (K slices of 128 bytes = 128 elements).
+// Same for the fp8 kernel (K slices of 128 bytes = 128 elements; one product).
 template <int BM, int BN, int ST, int OCC, int NWM, int NWN, class Epi>
 static hipError_t launch_lds_fp8(const fp8* A, int64_t lda, const fp8* W, int64_t ldw, int M,
                                  int N, int K, int n_half, const Epi& epi, int splits,
@@ -1034,6 +1064,7 @@ static hipError_t launch_lds_fp8(const fp8* A, int64_t lda, const fp8* W, int64_
   const int full = tiles - tail;
   if (tail == 0) splits = 1;
   if ((size_t)tail * splits * BM * BN * sizeof(float) > kSplitkBytes) return hipErrorInvalidValue;
+  const GemmSeg<fp8, Epi> g{A, W, M, tiles_m, epi};
   const size_t lds = (size_t)ST * (BM + BN) * BK;
   static LdsLimit limit;
   hipError_t le = ensure_lds_limit(
@@ -1042,26 +1073,27 @@ static hipError_t launch_lds_fp8(const fp8* A, int64_t lda, const fp8* W, int64_
       lds);
   if (le != hipSuccess) return le;
   hipLaunchKernelGGL((gemm_fp8_lds_kernel<BM, BN, BK, ST, OCC, NWM, NWN, Epi>),
-                     dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, A, lda, W, ldw, M,
-                     N, K, n_half, tiles_m, tiles_n, full, splits, partial, epi, sa, sw);
+                     dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, g, lda, ldw, N, K,
+                     n_half, tiles_n, full, splits, partial, sa, sw);
   if (tail > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int chunks = Epi::kPaired ? BM * BN / 8 / 256 : BM * BN / 4 / 256;
-    hipLaunchKernelGGL((splitk_reduce_kernel<BM, BN, Epi>), dim3(tail, chunks), dim3(256), 0, s,
-                       partial, splits, full, tiles_m, tiles_n, M, N, n_half, epi);
+    hipLaunchKernelGGL((splitk_reduce_kernel<BM, BN, Epi, fp8>), dim3(tail, chunks), dim3(256), 0,
+                       s, partial, splits, full, g, g, INT_MAX, tiles_n, N, n_half);
   }
   return hipGetLastError();
 }
 
 
 // Choose the tile configuration (and split-K of the last partial round) with the smallest
-// estimated time.  A round of resident workgroups costs its MACs at about 1 PFLOP/s over
+// estimated time (over the tiles of one product, or of two with the same N and K).  A
+// round of resident workgroups costs its MACs at about 1 PFLOP/s over
 // the chip (times `rate`: 2 for fp8), scaled by the configuration's relative efficiency; a
 // tail round split s ways along K costs 1/s of a round plus the fp32 partial tiles' round
 // trip through HBM and the reduce launch.  best: 0 = 256x256, 1 = 256x128, 2 = 128x128.
 static void pick_tile(int M, int N, int K, int bk, double rate, bool can_split, int& best,
-                      int& best_split) {
+                      int& best_split, int M1 = 0) {
   const int cus = 256;
   constexpr double kFlopPerCu = 4.0e12, kHbm = 5.0e12, kReduceLaunch = 3e-6;
   struct Cand { int bm, bn, occ; double eff; };
@@ -1071,7 +1103,9 @@ static void pick_tile(int M, int N, int K, int bk, double rate, bool can_split, 
   best_split = 1;
   double best_t = 1e300;
   for (int c = 0; c < 3; ++c) {
-    const long tiles = (long)((M + cands[c].bm - 1) / cands[c].bm) *
+    // M1: rows of a second product in the same launch (tiles of both)
+    const long tiles = (long)((M + cands[c].bm - 1) / cands[c].bm +
+                              (M1 + cands[c].bm - 1) / cands[c].bm) *
                        ((N + cands[c].bn - 1) / cands[c].bn);
     const long slots = (long)cus * cands[c].occ;
     const double round = 2.0 * cands[c].bm * cands[c].bn * cands[c].occ * (double)K /
@@ -1164,30 +1198,45 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // ------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------
+// Products y = A W^T (+ epilogue): one, or two with the same N, K and operand strides
+// (A1, W1, M1, epi1) in one launch when the large-tile kernel takes them both, else one
+// launch each.
 template <class T, class Epi>
 static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw, int M, int N,
                          int K, int n_half, const Epi& epi, hipStream_t s,
-                         float* split_ws = nullptr, int kdup = 0) {
+                         float* split_ws = nullptr, int kdup = 0, const void* A1 = nullptr,
+                         const void* W1 = nullptr, int M1 = 0, const Epi* epi1 = nullptr) {
+  if (M1 > 0 && M <= 0) return launch<T>(A1, lda, W1, ldw, M1, N, K, n_half, *epi1, s, split_ws, kdup);
   if (M <= 0 || N <= 0) return hipSuccess;
   const int kw = K - kdup;  // W columns; A columns past kw repeat W columns [kw - kdup, kw)
   if constexpr (sizeof(T) == 2) {
     // the large-tile kernel addresses operands with 32-bit byte offsets from their base
-    const bool off32 = (int64_t)M * lda * 2 < (int64_t{1} << 32) &&
+    const bool off32 = (int64_t)std::max(M, M1) * lda * 2 < (int64_t{1} << 32) &&
                        (int64_t)N * ldw * 2 < (int64_t{1} << 32);
     if (K % kBK == 0 && off32) {
       int best, best_split;
-      pick_tile(M, N, K, kBK, 1.0, split_ws != nullptr, best, best_split);
-      auto* a = static_cast<const bf16*>(A);
-      auto* w = static_cast<const bf16*>(W);
+      pick_tile(M, N, K, kBK, 1.0, split_ws != nullptr, best, best_split, M1 > 0 ? M1 : 0);
+      const GemmSeg<bf16, Epi> seg[2] = {
+          {static_cast<const bf16*>(A), static_cast<const bf16*>(W), M, 0, epi},
+          {static_cast<const bf16*>(M1 > 0 ? A1 : A), static_cast<const bf16*>(M1 > 0 ? W1 : W),
+           M1 > 0 ? M1 : M, 0, M1 > 0 ? *epi1 : epi}};
+      const int nseg = M1 > 0 ? 2 : 1;
       if (best == 0)
-        return launch_lds<256, 256, 64, 2, 3, 16, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
-                                                     epi, best_split, split_ws, s);
+        return launch_lds<256, 256, 64, 2, 3, 16, 1, 4, 2>(seg, nseg, lda, ldw, N, K, kw, kdup,
+                                                          n_half, best_split, split_ws, s);
       if (best == 1)
-        return launch_lds<256, 128, 64, 2, 2, 16, 1, 4, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half,
-                                                     epi, best_split, split_ws, s);
-      return launch_lds<128, 128, 64, 2, 2, 16, 2, 2, 2>(a, lda, w, ldw, M, N, K, kw, kdup, n_half, epi,
-                                                   best_split, split_ws, s);
+        return launch_lds<256, 128, 64, 2, 2, 16, 1, 4, 2>(seg, nseg, lda, ldw, N, K, kw, kdup,
+                                                          n_half, best_split, split_ws, s);
+      return launch_lds<128, 128, 64, 2, 2, 16, 2, 2, 2>(seg, nseg, lda, ldw, N, K, kw, kdup,
+                                                        n_half, best_split, split_ws, s);
     }
+  }
+  if (M1 > 0) {
+    hipError_t e = launch<T>(A, lda, W, ldw, M, N, K, n_half, epi, s, split_ws, kdup);
+    if (e != hipSuccess) return e;
+    return launch<T>(A1, lda, W1, ldw, M1, N, K, n_half, *epi1, s, split_ws, kdup);
+  }
+  if constexpr (sizeof(T) == 2) {
     constexpr int BM = 128, BN = 128;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const size_t lds = 2 * (BM + BN) * kBK * sizeof(bf16);
@@ -1204,47 +1253,64 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
   return hipGetLastError();
 }
 
+// Launch a's product (and b's, when given, in the same launch) with the epilogue that
+// make(args) builds for each.
+template <class T, class Make>
+static hipError_t launch_args(const LinearArgs& a, const LinearArgs* b, int n_half, Make make,
+                              hipStream_t s) {
+  const auto e0 = make(a);
+  if (!b)
+    return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, n_half, e0, s, a.split_ws, a.kdup);
+  const auto e1 = make(*b);
+  return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, n_half, e0, s, a.split_ws, a.kdup, b->x,
+                   b->w, b->m, &e1);
+}
+
 template <class T, class TY, class TR>
-static hipError_t gated2(const LinearArgs& a, hipStream_t s) {
-  EpiGatedResid<TY, TR> epi{static_cast<TY*>(a.y), a.ldy, static_cast<const TR*>(a.resid),
-                            a.ldr, a.gate, a.gate_bs, a.rows_per_batch};
-  epi.set_vec();
-  return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws, a.kdup);
+static hipError_t gated2(const LinearArgs& a, const LinearArgs* b, hipStream_t s) {
+  return launch_args<T>(a, b, 0, [](const LinearArgs& q) {
+    EpiGatedResid<TY, TR> epi{static_cast<TY*>(q.y), q.ldy, static_cast<const TR*>(q.resid),
+                              q.ldr, q.gate, q.gate_bs, q.rows_per_batch};
+    epi.set_vec();
+    return epi;
+  }, s);
 }
 
 template <class T>
-static hipError_t gated(const LinearArgs& a, hipStream_t s) {
+static hipError_t gated(const LinearArgs& a, const LinearArgs* b, hipStream_t s) {
   if (a.y_dtype == DT_F32)
-    return a.r_dtype == DT_F32 ? gated2<T, float, float>(a, s) : gated2<T, float, bf16>(a, s);
-  return a.r_dtype == DT_F32 ? gated2<T, bf16, float>(a, s) : gated2<T, bf16, bf16>(a, s);
+    return a.r_dtype == DT_F32 ? gated2<T, float, float>(a, b, s) : gated2<T, float, bf16>(a, b, s);
+  return a.r_dtype == DT_F32 ? gated2<T, bf16, float>(a, b, s) : gated2<T, bf16, bf16>(a, b, s);
 }
 
 template <class T>
-static hipError_t linear_t(const LinearArgs& a, hipStream_t s) {
+static hipError_t linear_t(const LinearArgs& a, const LinearArgs* b, hipStream_t s) {
   switch (a.epilogue) {
     case EPI_STORE:
-      if (a.y_dtype == DT_F32) {
-        EpiStore<float> epi{static_cast<float*>(a.y), a.ldy};
+      if (a.y_dtype == DT_F32)
+        return launch_args<T>(a, b, 0, [](const LinearArgs& q) {
+          EpiStore<float> epi{static_cast<float*>(q.y), q.ldy};
+          epi.set_vec();
+          return epi;
+        }, s);
+      return launch_args<T>(a, b, 0, [](const LinearArgs& q) {
+        EpiStore<bf16> epi{static_cast<bf16*>(q.y), q.ldy};
         epi.set_vec();
-        return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws, a.kdup);
-      } else {
-        EpiStore<bf16> epi{static_cast<bf16*>(a.y), a.ldy};
-        epi.set_vec();
-        return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws, a.kdup);
-      }
-    case EPI_SWIGLU: {
-      EpiSwiGLU<T> epi{static_cast<T*>(a.y), a.ldy, a.n / 2, a.swiglu_lo};
-      return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, a.n / 2, epi, s, a.split_ws,
-                       a.kdup);
-    }
+        return epi;
+      }, s);
+    case EPI_SWIGLU:
+      return launch_args<T>(a, b, a.n / 2, [](const LinearArgs& q) {
+        return EpiSwiGLU<T>{static_cast<T*>(q.y), q.ldy, q.n / 2, q.swiglu_lo};
+      }, s);
     case EPI_GATED_RESIDUAL:
-      return gated<T>(a, s);
-    case EPI_QKV: {
-      EpiQKV<T> epi{static_cast<T*>(a.y), a.ldy, static_cast<T*>(a.vt), a.ldvt,
-                    2 * a.dim, a.dim, a.rows_per_batch, a.vt_off};
-      epi.set_vec();
-      return launch<T>(a.x, a.ldx, a.w, a.ldw, a.m, a.n, a.k, 0, epi, s, a.split_ws, a.kdup);
-    }
+      return gated<T>(a, b, s);
+    case EPI_QKV:
+      return launch_args<T>(a, b, 0, [](const LinearArgs& q) {
+        EpiQKV<T> epi{static_cast<T*>(q.y), q.ldy, static_cast<T*>(q.vt), q.ldvt,
+                      2 * q.dim, q.dim, q.rows_per_batch, q.vt_off};
+        epi.set_vec();
+        return epi;
+      }, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1337,7 +1403,20 @@ hipError_t linear_static_scratch(float** ptr, size_t* bytes) {
 }
 
 hipError_t linear(int dtype, const LinearArgs& a, hipStream_t s) {
-  return dtype == DT_BF16 ? linear_t<bf16>(a, s) : linear_t<float>(a, s);
+  return dtype == DT_BF16 ? linear_t<bf16>(a, nullptr, s) : linear_t<float>(a, nullptr, s);
+}
+
+hipError_t linear_pair(int dtype, const LinearArgs& a, const LinearArgs& b, hipStream_t s) {
+  // one launch needs the same output width, depth, operand strides and epilogue kind
+  const bool same = a.epilogue == b.epilogue && a.n == b.n && a.k == b.k && a.ldx == b.ldx &&
+                    a.ldw == b.ldw && a.kdup == b.kdup && a.y_dtype == b.y_dtype &&
+                    a.r_dtype == b.r_dtype && a.swiglu_lo == b.swiglu_lo && a.dim == b.dim;
+  if (!same || a.m <= 0 || b.m <= 0) {
+    hipError_t e = linear(dtype, a, s);
+    if (e != hipSuccess) return e;
+    return linear(dtype, b, s);
+  }
+  return dtype == DT_BF16 ? linear_t<bf16>(a, &b, s) : linear_t<float>(a, &b, s);
 }
 
 }  // namespace flux

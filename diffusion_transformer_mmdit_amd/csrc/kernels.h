@@ -52,6 +52,11 @@ hipError_t linear_static_scratch(float** ptr, size_t* bytes);
 
 // y = x W^T with epilogue; dtype = type of x and W (DT_BF16 -> MFMA path).
 hipError_t linear(int dtype, const LinearArgs& a, hipStream_t s);
+// Two independent products with the same epilogue kind, n, k, operand strides and dtypes
+// (the double block's image and text streams) in one launch: b's tiles follow a's, so a
+// partial last round of tiles falls on b.  Otherwise (or when either has no rows) one launch
+// each.  The split-K scratch is a's.
+hipError_t linear_pair(int dtype, const LinearArgs& a, const LinearArgs& b, hipStream_t s);
 // fp8 (E4M3) linear: x [m, ldx] and W [n, ldw] bytes, y = sa[m] sw[n] (x W^T) with the
 // epilogue (EPI_STORE, EPI_SWIGLU, EPI_GATED_RESIDUAL); k % 128 == 0.
 hipError_t linear_fp8(const LinearArgs& a, const float* sa, const float* sw, hipStream_t s);

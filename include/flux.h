@@ -173,11 +173,11 @@ typedef enum {
   FLUX_SITE_SINGLE_ATTENTION = 3, /* single block: joint attention (with its key-split merge) */
   FLUX_SITE_SINGLE_LINEAR2 = 4,   /* single block: linear2 + gated residual (with its split-K
                                      reduce) */
-  FLUX_SITE_DOUBLE_QKV = 5,       /* double block, image stream: QKV projection */
+  FLUX_SITE_DOUBLE_QKV = 5,       /* double block: QKV projection (both streams, one launch) */
   FLUX_SITE_DOUBLE_ATTENTION = 6, /* double block: joint attention (with its merge) */
-  FLUX_SITE_DOUBLE_OUT = 7,       /* double block, image stream: out-proj + gated residual */
-  FLUX_SITE_DOUBLE_MLP_IN = 8,    /* double block, image stream: MLP-in + SwiGLU */
-  FLUX_SITE_DOUBLE_MLP_OUT = 9    /* double block, image stream: MLP-out + gated residual */
+  FLUX_SITE_DOUBLE_OUT = 7,       /* double block: out-proj + gated residual (both streams) */
+  FLUX_SITE_DOUBLE_MLP_IN = 8,    /* double block: MLP-in + SwiGLU (both streams) */
+  FLUX_SITE_DOUBLE_MLP_OUT = 9    /* double block: MLP-out + gated residual (both streams) */
 } flux_timing_site;
 int flux_timing_begin(int site, int max_launches);
 int flux_timing_end(int* launches, double* mean_us);

@@ -67,7 +67,8 @@ def test_site_table_and_split_flops():
     # (name, site, what, launches per step, flops, shape)
     assert rows["single_mlp_in"][4] == 2.0 * 4608 * 24576 * 4096 and rows["single_mlp_in"][3] == 24
     assert rows["single_linear2"][5] == [4608, 4096, 16384]
-    assert rows["double_mlp_out_img"][5] == [4096, 4096, 12288] and rows["double_qkv_img"][3] == 8
+    # the double block's sites time one launch over both streams' rows
+    assert rows["double_mlp_out"][5] == [4608, 4096, 12288] and rows["double_qkv"][3] == 8
     assert rows["single_attention"][4] == 4.0 * 4608 * 4608 * 4096
     # split precision: the LN-fed and SwiGLU-fed products twice, the head's projection twice
     extra = 8 * 2.0 * 4608 * (3 * 4096 ** 2 + 2 * 12288 * 4096 + 12288 * 4096) + \

@@ -197,8 +197,8 @@ def test_timing_hook_times_only_the_armed_site():
         G.run_single_block(wl, single, ws_single)
         n, us = F.flux_timing_end()
         assert n == 2 and 0.0 < us < 1e5, (site, n, us)
-    # double-block sites: the image stream's launches (and the joint attention), one each per
-    # double block, none from a single block
+    # double-block sites: each linear (both streams in one launch) and the joint attention, one
+    # each per double block, none from a single block
     for site in (F.FLUX_SITE_DOUBLE_QKV, F.FLUX_SITE_DOUBLE_ATTENTION, F.FLUX_SITE_DOUBLE_OUT,
                  F.FLUX_SITE_DOUBLE_MLP_IN, F.FLUX_SITE_DOUBLE_MLP_OUT):
         F.flux_timing_begin(site, 4)

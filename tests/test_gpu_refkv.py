@@ -44,9 +44,9 @@ def cache_views(wl, cache, B, Nr):
     return out
 
 
-def run_fill_and_cached(wl, inp, ref, rid, w_dev=None):
+def run_fill_and_cached(wl, inp, ref, rid, w_dev=None, precision=0):
     F, t = F_(), G.torch()
-    cfg = G.cfg_for(wl)
+    cfg = G.cfg_for(wl, precision)
     w_dev = w_dev or G.upload_weights(inp["weights"], wl.dtype)
     mw = F.ModelWeights(w_dev, wl.n_double, wl.n_single)
     B, Nr = wl.batch, ref.shape[1]
@@ -78,13 +78,13 @@ def small_bf16(batch=1):
                        n_img=64, n_txt=24, t_fixed=None, batch=batch, seed=1012)
 
 
-def check_against_oracle(wl, R, gh, gw, what):
+def check_against_oracle(wl, R, gh, gw, what, precision=0):
     inp = fs.step_inputs(wl)
     Nr = R * gh * gw
     ref = fs.normal(wl.seed, "ref_tokens", (wl.batch, Nr, wl.in_channels), dtype=wl.dtype)
     rid = O.reference_ids(R, gh, gw)
     print(f"[refkv] {what}: batch {wl.batch}, {Nr} reference tokens", flush=True)
-    out, cache = run_fill_and_cached(wl, inp, ref, rid)
+    out, cache = run_fill_and_cached(wl, inp, ref, rid, precision=precision)
     ref_out, ref_cache = O.step_extract(inp["x"], ref, inp["ctx"], inp["t"], inp["weights"],
                                         inp["img_ids"], rid, inp["txt_ids"], wl.n_double,
                                         wl.n_single)
@@ -120,6 +120,17 @@ def test_tiny_fp32_cache_and_cached_step(batch):
 def test_small_bf16_cache_and_cached_step(batch):
     # two 5 x 7 references: 70 reference tokens, a partial second extra key tile
     check_against_oracle(small_bf16(batch), 2, 5, 7, "small bf16")
+
+
+def test_klein9b_width_cache_and_cached_step_split_precision():
+    """The reference cache and the cached step at the Klein-9B width (D 4096, 32 heads,
+    MLP 12288; 2 + 2 blocks): one 6 x 8 reference (48 tokens, a partial extra key tile).  In
+    FLUX_PRECISION_SPLIT: with bf16 LayerNorm outputs the reference rows' own pipeline error
+    grows with the width (the linears' gain 0.02 sqrt(D) > 1), and at D 4096 the cached K of
+    the third block exceeded the element-wise bound above by 2e-3 while the cached step met
+    3e-2 / 1e-2 (2.1e-2 / 4.1e-3)."""
+    from tests.test_gpu_sampler import klein9b_width
+    check_against_oracle(klein9b_width(seed=1014), 1, 6, 8, "Klein-9B width (split)", precision=1)
 
 
 def run_denoise_refs(wl, inp, refs, n_steps, use_cache, sigmas=None, w_dev=None, lat=None):

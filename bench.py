@@ -2,7 +2,7 @@
 MI355X through the C ABI.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-    python bench.py --probe dominant|attention|copy   # a few bare launches, for counter runs
+    python bench.py --probe dominant|attention|copy|bandwidth   # bare launches, for counter runs
     python bench.py --per-config               # one JSON line per traced workload: ms per
                                                # block, LN+modulate and RMSNorm+RoPE GB/s
 
@@ -551,6 +551,22 @@ def per_config_line(F, fs, name: str) -> dict:
         res[f"{kind}_block_ms"] = round(ms, 4)
         res[f"{kind}_block_tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
         del w, ws, bw
+    for kname, nbytes, fns in bandwidth_kernels(F, fs, wl, cfg, t, txt_ids, img_ids, g, dtype, s):
+        bandwidth_entry(res, kname, nbytes, len(fns), _time_rotating_ms(fns, s),
+                        _time_ms(fns[0], s))
+        del fns
+        if kname != "modulation_gemv":
+            copy_reference(res, kname, nbytes, s)
+    return res
+
+
+def bandwidth_kernels(F, fs, wl, cfg, t, txt_ids, img_ids, g, dtype, s):
+    """The HBM-bound kernels at the workload's shape, each as calls over several disjoint
+    buffer sets that together exceed the MALL: [(name, algorithmic bytes per call, calls)].
+    Yields one kernel at a time so only its sets are resident."""
+    import torch
+    D, B = wl.dim, wl.batch
+    Nt, Ni, L = wl.n_txt, wl.n_img, wl.seq
     # LN + modulate over the joint sequence: fp32 residual in, model dtype out (as the step)
     sh = torch.randn((B, D), generator=g, device="cuda")
     sc = torch.randn((B, D), generator=g, device="cuda")
@@ -562,10 +578,8 @@ def per_config_line(F, fs, name: str) -> dict:
         y = torch.empty((B * L, D), device="cuda", dtype=dtype)
         fns.append(lambda x32=x32, y=y: F.flux_layernorm_modulate(cfg, B * L, L, x32, F.FLUX_F32,
                                                                   sh, sc, y, s))
-    bandwidth_entry(res, "ln_modulate", nbytes, len(fns), _time_rotating_ms(fns, s),
-                    _time_ms(fns[0], s))
+    yield "ln_modulate", nbytes, fns
     del fns, x32, y
-    copy_reference(res, "ln_modulate", nbytes, s)
     # RMSNorm + RoPE on q and k in place, inside a [B, L, 3D] QKV buffer
     gam = torch.ones(128, device="cuda")
     nb = F.flux_qk_norm_rope_workspace_size(cfg, Nt, Ni)
@@ -577,10 +591,8 @@ def per_config_line(F, fs, name: str) -> dict:
         fns.append(lambda qkv=qkv: F.flux_qk_norm_rope(cfg, B, Nt, Ni, qkv, qkv[..., D:], 3 * D,
                                                        gam, gam, gam, gam, txt_ids, img_ids, ws,
                                                        nb, s))
-    bandwidth_entry(res, "qk_norm_rope", nbytes, len(fns), _time_rotating_ms(fns, s),
-                    _time_ms(fns[0], s))
+    yield "qk_norm_rope", nbytes, fns
     del fns, qkv
-    copy_reference(res, "qk_norm_rope", nbytes, s)
     # modulation: timestep MLP + one modulation GEMV (the double block's image set, 6D x D);
     # weight reads dominate: (256 D + D^2 + 6 D^2) bf16
     if wl.dtype == "bf16":
@@ -596,10 +608,32 @@ def per_config_line(F, fs, name: str) -> dict:
             keep.append((tw, wmod, tws))
             fns.append(lambda tws=tws, wmod=wmod: F.flux_modulation(cfg, tws, wmod, 6 * D, t, B,
                                                                     mout, mws, mnb, s))
-        bandwidth_entry(res, "modulation_gemv", nbytes, len(fns), _time_rotating_ms(fns, s),
-                        _time_ms(fns[0], s))
+        yield "modulation_gemv", nbytes, fns
         del fns, keep
-    return res
+
+
+def bandwidth_probe(F, fs, name: str = "klein9b_step_1024"):
+    """Each HBM-bound kernel of bandwidth_kernels, called twice over its buffer sets (every
+    call after the first pass finds its operands evicted from the MALL): the HBM byte counter
+    runs use it."""
+    import torch
+    wl = fs.workload(name)
+    dtype = torch.bfloat16
+    cfg = F.make_cfg(wl.dim, wl.heads, wl.mlp_hidden)
+    s = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed)
+    t = torch.rand((wl.batch,), generator=g, device="cuda")
+    img_ids = torch.from_numpy(fs.image_ids(wl.n_img)).cuda()
+    txt_ids = torch.from_numpy(fs.text_ids(wl.n_txt)).cuda()
+    for kname, nbytes, fns in bandwidth_kernels(F, fs, wl, cfg, t, txt_ids, img_ids, g, dtype, s):
+        for _ in range(2):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        print(f"[bench] probe: {kname} ({nbytes} algorithmic bytes per call), 2 x {len(fns)} "
+              "calls", file=sys.stderr, flush=True)
+        del fns
 
 
 def copy_reference(res: dict, name: str, nbytes: int, s):
@@ -643,8 +677,10 @@ def main(argv=None) -> int:
                     help="time the blocks and bandwidth kernels of every traced workload")
     ap.add_argument("--only", default=None, choices=PER_CONFIG,
                     help="with --per-config: just this workload")
-    ap.add_argument("--probe", choices=("dominant", "attention", "copy"), default=None,
-                    help="only launch the dominant kernel (or a 1 GiB copy) 3 times and exit")
+    ap.add_argument("--probe", choices=("dominant", "attention", "copy", "bandwidth"),
+                    default=None,
+                    help="only launch the dominant kernel, the attention or a 1 GiB copy 3 "
+                         "times (bandwidth: the HBM-bound kernels over rotating sets) and exit")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -673,6 +709,9 @@ def main(argv=None) -> int:
     if args.probe == "attention":
         attention_probe(F, wl)
         print("[bench] probe: attention launched 3 times", file=sys.stderr, flush=True)
+        return 0
+    if args.probe == "bandwidth":
+        bandwidth_probe(F, fs)
         return 0
     if args.probe == "copy":
         copy_probe()

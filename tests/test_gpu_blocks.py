@@ -61,7 +61,10 @@ def test_tiny_fp32_block(kind):
 
 @pytest.mark.parametrize("precision", [0, 1])
 @pytest.mark.parametrize("kind", ["single", "double"])
-@pytest.mark.parametrize("n_txt,n_img,batch", [(16, 64, 1), (5, 36, 2), (0, 49, 1), (130, 196, 1)])
+# (1, 64): a one-token text stream; (300, 289): both streams' products in one launch with
+# several tiles each and ragged last tiles in both
+@pytest.mark.parametrize("n_txt,n_img,batch", [(16, 64, 1), (5, 36, 2), (0, 49, 1), (130, 196, 1),
+                                               (1, 64, 1), (300, 289, 1)])
 def test_small_bf16_block(kind, n_txt, n_img, batch, precision):
     wl = fs.workload("tiny_single_f32", dtype="bf16", n_txt=n_txt, n_img=n_img, batch=batch,
                      t_fixed=None, seed=2000 + n_img)

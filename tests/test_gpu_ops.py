@@ -287,7 +287,9 @@ def test_linear_gated_residual(m, n, k, dtype, use_ws):
     # loop's last steps), and 256 4-wave units: the smallest grid that takes 4-wave blocks,
     # its partial round split in 2
     (64, 2, 1, "bf16", None), (128, 1, 1, "bf16", None), (150, 2, 1, "bf16", None),
-    (192, 1, 1, "bf16", None), (1024, 32, 1, "bf16", 48)])
+    (192, 1, 1, "bf16", None), (1024, 32, 1, "bf16", 48),
+    # 264 4-wave units (more than CUs, fewer than slots): 256 whole, 8 split 5 ways
+    (1300, 24, 1, "bf16", 64)])
 def test_attention(seq, heads, batch, dtype, n_q):
     t = G.torch()
     seed = seq + heads

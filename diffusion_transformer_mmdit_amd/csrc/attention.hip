@@ -101,7 +101,7 @@ template <int NW, bool EXTRA>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void flash_attn_bf16_kernel(
     SeqView qv, SeqView kv, const bf16* __restrict__ vt, int64_t ld_vt, int dim, SeqView ov,
     int seq, float scale_log2, int nqb, int heads, int full_units, int splits,
-    float* __restrict__ partial, KvExtra xkv) {
+    float* __restrict__ partial, KvExtra xkv, int o_f16) {
   constexpr int NT = 64 * NW;
   __shared__ __align__(16) bf16 Ks[2][kBKV * kHD];
   __shared__ __align__(16) bf16 Vs[2][kHD * kBKV];
@@ -456,19 +456,25 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void flash_attn_bf16_kern
     }
     return;
   }
-  // normalise and write O[query][d]
+  // normalise and write O[query][d] (bf16, or binary16 with o_f16)
   const float inv = 1.f / l_tot;
   if (qi < seq) {
     bf16* op = seq_mptr<bf16>(ov, b, qi) + hoff;
+    auto put = [&](auto pk2) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = 32 * dt + 8 * r4 + 4 * g;
-        uint2 pk = make_uint2(pack2(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv),
-                              pack2(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv));
-        *reinterpret_cast<uint2*>(op + d) = pk;
-      }
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = 32 * dt + 8 * r4 + 4 * g;
+          *reinterpret_cast<uint2*>(op + d) =
+              make_uint2(pk2(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv),
+                         pk2(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv));
+        }
+    };
+    if (o_f16)
+      put([](float x, float y) { return pack2h(x, y); });
+    else
+      put([](float x, float y) { return pack2(x, y); });
   }
 }
 
@@ -479,7 +485,8 @@ template <int QPU>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ partial,
                                                          int64_t ml_offset, int splits,
                                                          int n_units, int full_units, int nqb,
-                                                         int heads, int seq, SeqView ov) {
+                                                         int heads, int seq, SeqView ov,
+                                                         int o_f16) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int d4 = (int)(idx & 31);
   const int64_t uq = idx >> 5;  // split unit * QPU + query
@@ -507,7 +514,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   }
   const float inv = 1.f / lsum;
   bf16* op = seq_mptr<bf16>(ov, b, qi) + head * kHD + 4 * d4;
-  *reinterpret_cast<uint2*>(op) = make_uint2(pack2(acc.x * inv, acc.y * inv), pack2(acc.z * inv, acc.w * inv));
+  *reinterpret_cast<uint2*>(op) =
+      o_f16 ? make_uint2(pack2h(acc.x * inv, acc.y * inv), pack2h(acc.z * inv, acc.w * inv))
+            : make_uint2(pack2(acc.x * inv, acc.y * inv), pack2(acc.z * inv, acc.w * inv));
 }
 
 // fp32 path (tiny fp32 workloads): one wave per (query, head); each lane owns 2 dims.
@@ -572,7 +581,7 @@ size_t attention_split_bytes() { return (size_t)kAttnSlots * 128 * (kHD + 2) * s
 template <int NW, bool EXTRA>
 static hipError_t launch_flash(SeqView q, SeqView k, const bf16* vt, int64_t ld_vt, int dim,
                                SeqView o, int batch, int seq, int heads, float* split_ws,
-                               const KvExtra& x, hipStream_t s) {
+                               const KvExtra& x, int o_f16, hipStream_t s) {
   constexpr int QPU = 32 * NW;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHD);
   const int nqb = (seq + QPU - 1) / QPU;
@@ -598,35 +607,40 @@ static hipError_t launch_flash(SeqView q, SeqView k, const bf16* vt, int64_t ld_
   const int full = units - tail;
   const int grid = full + tail * splits;
   hipLaunchKernelGGL((flash_attn_bf16_kernel<NW, EXTRA>), dim3(grid), dim3(64 * NW), 0, s, q, k, vt,
-                     ld_vt, dim, o, seq, scale_log2, nqb, heads, full, splits, split_ws, x);
+                     ld_vt, dim, o, seq, scale_log2, nqb, heads, full, splits, split_ws, x,
+                     o_f16);
   if (tail > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t ml_offset = (int64_t)tail * splits * QPU * kHD;  // after the split units' O rows
     const int64_t threads = (int64_t)tail * QPU * 32;
     hipLaunchKernelGGL(attn_merge_kernel<QPU>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       s, split_ws, ml_offset, splits, tail, full, nqb, heads, seq, o);
+                       s, split_ws, ml_offset, splits, tail, full, nqb, heads, seq, o, o_f16);
   }
   return hipGetLastError();
 }
 
 hipError_t attention(int dtype, SeqView q, SeqView k, const void* vt, int64_t ld_vt, SeqView o,
                      int batch, int seq, int heads, float* split_ws, hipStream_t s,
-                     const KvExtra* extra) {
+                     const KvExtra* extra, int o_dtype) {
   if (seq <= 0 || batch <= 0) return hipSuccess;
   const int dim = heads * kHD;
   KvExtra x{};
   x.nb = 1;
   if (extra != nullptr && extra->n > 0) x = *extra;
   if (dtype == DT_BF16) {
+    if (o_dtype < 0) o_dtype = DT_BF16;
+    if (o_dtype != DT_BF16 && o_dtype != DT_F16) return hipErrorInvalidValue;
+    const int of16 = o_dtype == DT_F16;
     const bf16* v = static_cast<const bf16*>(vt);
     // extra keys: 4-wave workgroups only (the 2-wave variant of the extra-source path does
     // not fit the register budget)
     if (x.n > 0)
-      return launch_flash<4, true>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, x, s);
+      return launch_flash<4, true>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, x, of16, s);
     if (attn_waves(seq, heads, batch) == 4)
-      return launch_flash<4, false>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, x, s);
-    return launch_flash<2, false>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, x, s);
+      return launch_flash<4, false>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, x, of16,
+                                    s);
+    return launch_flash<2, false>(q, k, v, ld_vt, dim, o, batch, seq, heads, split_ws, x, of16, s);
   } else {
     dim3 grid(seq, heads, batch);
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(64), 0, s, q, k, static_cast<const float*>(vt),

@@ -9,12 +9,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;  // IEEE binary16
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define FLUX_DEV __device__ __forceinline__
 
 // ---- scalar conversions -------------------------------------------------------------
 FLUX_DEV float to_f32(float x) { return x; }
 FLUX_DEV float to_f32(bf16 x) { return static_cast<float>(x); }
+FLUX_DEV float to_f32(f16 x) { return static_cast<float>(x); }
 
 template <class T>
 FLUX_DEV T from_f32(float x);
@@ -22,6 +26,8 @@ template <>
 FLUX_DEV float from_f32<float>(float x) { return x; }
 template <>
 FLUX_DEV bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }  // RNE
+template <>
+FLUX_DEV f16 from_f32<f16>(float x) { return static_cast<f16>(x); }  // RNE
 
 // ---- 16-byte vector loads / stores of 8 bf16 or 4 fp32 ------------------------------
 FLUX_DEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -48,6 +54,25 @@ FLUX_DEV uint32_t pack2(float a, float b) {
 
 FLUX_DEV uint4 pack8(const float* f) {
   return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+}
+
+// two floats -> packed binary16 pair (round to nearest even)
+FLUX_DEV uint32_t pack2h(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// the pair packing of a 2-byte storage type
+template <class T>
+FLUX_DEV uint32_t pack2_as(float a, float b);
+template <>
+FLUX_DEV uint32_t pack2_as<bf16>(float a, float b) { return pack2(a, b); }
+template <>
+FLUX_DEV uint32_t pack2_as<f16>(float a, float b) { return pack2h(a, b); }
+template <class T>
+FLUX_DEV uint4 pack8_as(const float* f) {
+  return make_uint4(pack2_as<T>(f[0], f[1]), pack2_as<T>(f[2], f[3]), pack2_as<T>(f[4], f[5]),
+                    pack2_as<T>(f[6], f[7]));
 }
 
 // ---- wave64 reductions ---------------------------------------------------------------
@@ -93,4 +118,4 @@ FLUX_DEV void dma16v(const void* g, uint32_t lds_addr) {
 }
 
 // ---- dtype tags shared with the host -------------------------------------------------
-enum { DT_BF16 = 0, DT_F32 = 1 };
+enum { DT_BF16 = 0, DT_F32 = 1, DT_F16 = 2 };

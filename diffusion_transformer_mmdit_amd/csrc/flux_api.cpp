@@ -167,8 +167,11 @@ static int check_cfg(const flux_cfg* c) {
   if (!(c->rope_theta > 0.f)) return fail(FLUX_EINVAL, "rope_theta must be > 0");
   if (!(c->eps > 0.f)) return fail(FLUX_EINVAL, "eps must be > 0");
   if (c->dim > 8192) return fail(FLUX_ESHAPE, "dim > 8192 is not supported");
-  if (c->precision != FLUX_PRECISION_BF16 && c->precision != FLUX_PRECISION_SPLIT)
+  if (c->precision != FLUX_PRECISION_BF16 && c->precision != FLUX_PRECISION_SPLIT &&
+      c->precision != FLUX_PRECISION_F16)
     return fail(FLUX_EINVAL, "unknown precision %d", c->precision);
+  if (c->precision == FLUX_PRECISION_F16 && c->dtype != FLUX_BF16)
+    return fail(FLUX_EDTYPE, "FLUX_PRECISION_F16 needs FLUX_BF16");
   if (c->precision == FLUX_PRECISION_SPLIT) {
     if (c->dtype != FLUX_BF16) return fail(FLUX_EDTYPE, "FLUX_PRECISION_SPLIT needs FLUX_BF16");
     if (c->mlp_hidden % 64)
@@ -180,6 +183,12 @@ static int check_cfg(const flux_cfg* c) {
 
 // hi / lo operands (FLUX_PRECISION_SPLIT): 2 planes, else 1
 static int planes(const flux_cfg* c) { return c->precision == FLUX_PRECISION_SPLIT ? 2 : 1; }
+
+// Storage type of the block linears' operands (their weights, the LayerNorm + modulate and
+// SwiGLU outputs, the attention output): binary16 with FLUX_PRECISION_F16, else cfg->dtype
+static int blk_dtype(const flux_cfg* c) {
+  return c->precision == FLUX_PRECISION_F16 ? FLUX_F16 : c->dtype;
+}
 
 static int check_sizes(int batch, int n_img, int n_txt) {
   if (batch <= 0) return fail(FLUX_EINVAL, "batch must be > 0 (got %d)", batch);
@@ -310,6 +319,20 @@ static int lin(const flux_cfg* c, int epi, int m, int n, int k, const void* x, i
   return FLUX_OK;
 }
 
+// lin for the block linears: operands of blk_dtype(c)
+static int lin_b(const flux_cfg* c, int epi, int m, int n, int k, const void* x, int64_t ldx,
+                 const void* w, int64_t ldw, void* y, int64_t ldy, int y_dtype,
+                 const void* resid = nullptr, int64_t ldr = 0, int r_dtype = FLUX_F32,
+                 const float* gate = nullptr, int64_t gate_bs = 0, int rpb = 1,
+                 hipStream_t s = 0, float* split_ws = nullptr, int kdup = 0,
+                 bool swiglu_lo = false) {
+  HIP_TRY(linear(blk_dtype(c), lin_args(epi, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid,
+                                        ldr, r_dtype, gate, gate_bs, rpb, split_ws, kdup,
+                                        swiglu_lo),
+                 s));
+  return FLUX_OK;
+}
+
 // q | k row-major into qk [m, 2D]; v transposed into vt [B*D, ldvt] at token offset vt_off.
 // x: [m, D] or, with hi / lo operands, [m, 2D] (hi | lo planes).
 static LinearArgs qkv_args(const flux_cfg* c, int m, const void* x, const void* w, void* qk,
@@ -339,7 +362,7 @@ static LinearArgs qkv_args(const flux_cfg* c, int m, const void* x, const void* 
 
 static int lin_qkv(const flux_cfg* c, int m, const void* x, const void* w, void* qk, void* vt,
                    int64_t ldvt, int vt_off, int rpb, hipStream_t s, float* split_ws) {
-  HIP_TRY(linear(c->dtype, qkv_args(c, m, x, w, qk, vt, ldvt, vt_off, rpb, split_ws), s));
+  HIP_TRY(linear(blk_dtype(c), qkv_args(c, m, x, w, qk, vt, ldvt, vt_off, rpb, split_ws), s));
   return FLUX_OK;
 }
 
@@ -436,7 +459,7 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
                       const void* in[2], int in_dt, void* out[2], int out_dt,
                       const float* mods[2], const float2* cs, const DoubleScratch& d,
                       hipStream_t s, const RefSlot* ref = nullptr, int ref_use = REF_NONE) {
-  const int D = c->dim, H = c->mlp_hidden, T = c->dtype;
+  const int D = c->dim, H = c->mlp_hidden, T = c->dtype, TB = blk_dtype(c);
   const int n[2] = {Nt, Ni};
   const int64_t mbs = 6 * (int64_t)D;
   const int L = Nt + Ni;
@@ -450,7 +473,7 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
                     const float* sc) -> hipError_t {
     if (P == 2)
       return layernorm_modulate_hilo(dt, x, D, y, 2 * D, rows, D, rpb, sh, sc, mbs, c->eps, s);
-    return layernorm_modulate(dt, T, x, D, y, D, rows, D, rpb, sh, sc, mbs, c->eps, s);
+    return layernorm_modulate(dt, TB, x, D, y, D, rows, D, rpb, sh, sc, mbs, c->eps, s);
   };
   // timing-hook sites: the block's launches (both streams' products in one launch), unless
   // the block is filling the reference cache
@@ -461,7 +484,7 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
     if (n[i] > 0) HIP_TRY(ln_mod(in_dt, in[i], d.ln[i], B * n[i], n[i], mods[i], mods[i] + D));
   {
     TimedSite ts(site(FLUX_SITE_DOUBLE_QKV), s);
-    HIP_TRY(linear_pair(T, qkv_args(c, B * Ni, d.ln[1], sw[1]->qkv, qk[1], vtb, ldvt, Nt, Ni,
+    HIP_TRY(linear_pair(TB, qkv_args(c, B * Ni, d.ln[1], sw[1]->qkv, qk[1], vtb, ldvt, Nt, Ni,
                                     d.split),
                         qkv_args(c, B * Nt, d.ln[0], sw[0]->qkv, qk[0], vtb, ldvt, 0, Nt,
                                  d.split),
@@ -489,7 +512,7 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
   {
     TimedSite ts(site(FLUX_SITE_DOUBLE_ATTENTION), s);
     HIP_TRY(attention(T, qv, kv, vtb, ldvt, ov, B, L, c->heads, d.split, s,
-                      ref_use == REF_KEYS ? &xk : nullptr));
+                      ref_use == REF_KEYS ? &xk : nullptr, TB));
   }
   // x + gate1 * (O W_o^T)  -> mid (f32)
   auto out_args = [&](int i) {
@@ -498,7 +521,7 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
   };
   {
     TimedSite ts(site(FLUX_SITE_DOUBLE_OUT), s);
-    HIP_TRY(linear_pair(T, out_args(1), out_args(0), s));
+    HIP_TRY(linear_pair(TB, out_args(1), out_args(0), s));
   }
   for (int i = 0; i < 2; ++i)
     if (n[i] > 0)
@@ -506,12 +529,12 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
                      mods[i] + 4 * D));
   auto mlp_in_args = [&](int i) {
     return lin_args(EPI_SWIGLU, B * n[i], 2 * H, P * D, d.ln[i], P * D, sw[i]->mlp_in, D,
-                    d.mlp[i], P * H, T, nullptr, 0, 0, nullptr, 0, 1, d.split, (P - 1) * D,
+                    d.mlp[i], P * H, TB, nullptr, 0, 0, nullptr, 0, 1, d.split, (P - 1) * D,
                     P == 2);
   };
   {
     TimedSite ts(site(FLUX_SITE_DOUBLE_MLP_IN), s);
-    HIP_TRY(linear_pair(T, mlp_in_args(1), mlp_in_args(0), s));
+    HIP_TRY(linear_pair(TB, mlp_in_args(1), mlp_in_args(0), s));
   }
   // mid + gate2 * (M W_out^T) -> out
   auto mlp_out_args = [&](int i) {
@@ -520,7 +543,7 @@ static int run_double(const flux_cfg* c, const flux_stream_weights* sw[2], int B
                     d.split, (P - 1) * H);
   };
   TimedSite ts(site(FLUX_SITE_DOUBLE_MLP_OUT), s);
-  HIP_TRY(linear_pair(T, mlp_out_args(1), mlp_out_args(0), s));
+  HIP_TRY(linear_pair(TB, mlp_out_args(1), mlp_out_args(0), s));
   return FLUX_OK;
 }
 
@@ -626,6 +649,7 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
                       const SingleScratch& d, hipStream_t s, const RefSlot* ref = nullptr,
                       int ref_use = REF_NONE, bool kv_only = false) {
   const int D = c->dim, H = c->mlp_hidden, T = c->dtype, es = esize(T), P = planes(c);
+  const int TB = blk_dtype(c);  // es is also its size: 2 bytes for bf16 and binary16
   const int rows = B * L;
   const int64_t mbs = 3 * (int64_t)D, ldc = D + P * H;
   const bool fill = ref_use == REF_FILL;
@@ -635,7 +659,7 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
     HIP_TRY(layernorm_modulate_hilo(in_dt, x, D, d.ln, 2 * D, rows, D, L, mod, mod + D, mbs,
                                     c->eps, s));
   else
-    HIP_TRY(layernorm_modulate(in_dt, T, x, D, d.ln, D, rows, D, L, mod, mod + D, mbs, c->eps, s));
+    HIP_TRY(layernorm_modulate(in_dt, TB, x, D, d.ln, D, rows, D, L, mod, mod + D, mbs, c->eps, s));
   const int64_t ldvt = vt_pitch(L);
   {
     TimedSite ts(fill ? 0 : FLUX_SITE_SINGLE_QKV, s);
@@ -656,8 +680,8 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
   }
   {
     TimedSite ts(fill ? 0 : FLUX_SITE_SINGLE_MLP_IN, s);
-    CHECK(lin(c, EPI_SWIGLU, rows, 2 * H, P * D, d.ln, P * D, w_mlp, D,
-              static_cast<char*>(d.cat) + (size_t)D * es, ldc, T, nullptr, 0, 0, nullptr, 0, 1,
+    CHECK(lin_b(c, EPI_SWIGLU, rows, 2 * H, P * D, d.ln, P * D, w_mlp, D,
+              static_cast<char*>(d.cat) + (size_t)D * es, ldc, TB, nullptr, 0, 0, nullptr, 0, 1,
               s, d.split, (P - 1) * D, P == 2));
   }
   auto view = [&](void* base, int col, int64_t ld) {
@@ -677,11 +701,11 @@ static int run_single(const flux_cfg* c, const flux_single_weights* w, int B, in
     KvExtra xk{};
     if (ref_use == REF_KEYS) xk = extra_keys(c, ref, B);
     HIP_TRY(attention(T, qv, kv, vtb, ldvt, ov, B, L, c->heads, d.split, s,
-                      ref_use == REF_KEYS ? &xk : nullptr));
+                      ref_use == REF_KEYS ? &xk : nullptr, TB));
   }
   TimedSite ts(fill ? 0 : FLUX_SITE_SINGLE_LINEAR2, s);
   // [O | M] W2^T, or with hi / lo [O | M_hi | M_lo] whose M_lo columns repeat W2's M columns
-  CHECK(lin(c, EPI_GATED_RESIDUAL, rows, D, (int)ldc, d.cat, ldc, w->linear2, D + H, out, D,
+  CHECK(lin_b(c, EPI_GATED_RESIDUAL, rows, D, (int)ldc, d.cat, ldc, w->linear2, D + H, out, D,
             out_dt, x, D, in_dt, mod + 2 * D, mbs, L, s, d.split, (P - 1) * H));
   return FLUX_OK;
 }
@@ -1344,7 +1368,7 @@ extern "C" int flux_layernorm_modulate(const flux_cfg* c, int rows, int rpb, con
   CHECK(need(y, "y"));
   CHECK(need(shift, "shift"));
   CHECK(need(scale, "scale"));
-  HIP_TRY(layernorm_modulate(x_dtype, c->dtype, x, c->dim, y, c->dim, rows, c->dim, rpb, shift,
+  HIP_TRY(layernorm_modulate(x_dtype, blk_dtype(c), x, c->dim, y, c->dim, rows, c->dim, rpb, shift,
                              scale, c->dim, c->eps, static_cast<hipStream_t>(stream)));
   return FLUX_OK;
 }
@@ -1438,7 +1462,7 @@ extern "C" int flux_attention(const flux_cfg* c, int B, int seq, const void* q, 
   HIP_TRY(transpose_v(c->dtype, mk(v, ld_in), a.vt, ldvt, c->dim, B, seq, s));
   if (ldvt > seq) HIP_TRY(zero_cols(c->dtype, a.vt, ldvt, (int64_t)B * c->dim, seq, (int)ldvt, s));
   HIP_TRY(attention(c->dtype, mk(q, ld_in), mk(k, ld_in), a.vt, ldvt, mk(o, ld_out), B, seq,
-                    c->heads, a.split, s));
+                    c->heads, a.split, s, nullptr, blk_dtype(c)));
   return FLUX_OK;
 }
 
@@ -1535,20 +1559,20 @@ static int linear_entry(const flux_cfg* c, int epi, int m, int n, int k, const v
   if (epi == FLUX_EPI_SWIGLU) {
     if (n % 2) return fail(FLUX_ESHAPE, "SwiGLU needs an even n");
     if (ldy < n / 2) return fail(FLUX_ESHAPE, "ldy < n/2");
-    return lin(c, EPI_SWIGLU, m, n, k, x, ldx, w, ldw, y, ldy, c->dtype, nullptr, 0, 0, nullptr,
+    return lin_b(c, EPI_SWIGLU, m, n, k, x, ldx, w, ldw, y, ldy, blk_dtype(c), nullptr, 0, 0, nullptr,
                0, 1, s, split);
   }
   if (y_dtype != FLUX_BF16 && y_dtype != FLUX_F32) return fail(FLUX_EDTYPE, "bad y_dtype");
   if (ldy < n) return fail(FLUX_ESHAPE, "ldy < n");
   if (epi == FLUX_EPI_STORE)
-    return lin(c, EPI_STORE, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, nullptr, 0, 0, nullptr, 0,
-               1, s, split);
+    return lin_b(c, EPI_STORE, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, nullptr, 0, 0, nullptr,
+                 0, 1, s, split);
   if (epi == FLUX_EPI_GATED_RESIDUAL) {
     if (!resid || !gate) return fail(FLUX_EINVAL, "resid and gate are required");
     if (rpb <= 0 || m % rpb) return fail(FLUX_ESHAPE, "m must be a multiple of rows_per_batch");
     if (ldr < n) return fail(FLUX_ESHAPE, "ldr < n");
-    return lin(c, EPI_GATED_RESIDUAL, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid, ldr,
-               y_dtype, gate, n, rpb, s, split);
+    return lin_b(c, EPI_GATED_RESIDUAL, m, n, k, x, ldx, w, ldw, y, ldy, y_dtype, resid, ldr,
+                 y_dtype, gate, n, rpb, s, split);
   }
   return fail(FLUX_EINVAL, "unknown epilogue %d", epi);
 }

@@ -1,7 +1,9 @@
 // Linear layers y = x W^T (W stored [N, K] row-major) with fused epilogues.
 //
-// bf16 path: gfx950 MFMA (v_mfma_f32_16x16x32_bf16 in the large-tile kernels,
-// v_mfma_f32_32x32x16_bf16 in the generic one), fp32 accumulation.  A workgroup computes a
+// 2-byte operands (bf16, or IEEE binary16 for the block linears under the binary16
+// precision mode): gfx950 MFMA (v_mfma_f32_16x16x32_{bf16,f16} in the large-tile kernels,
+// v_mfma_f32_32x32x16_{bf16,f16} in the generic one; the kernels keep their bf16 names),
+// fp32 accumulation.  A workgroup computes a
 // BM x BN tile; operands are staged through LDS in 64-wide K slices with an XOR swizzle of
 // the 16-byte chunks so the MFMA fragment reads are bank-conflict free, and the loads of
 // later slices are in flight during the MFMAs of the current one.
@@ -204,13 +206,38 @@ constexpr int kThreads = 256;
 FLUX_DEV int swz_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
 FLUX_DEV int swz(int row, int c) { return row * kBK + (swz_slot(row, c) << 3); }
 
-template <int BM, int BN, class Epi>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restrict__ A,
+// 8-element MFMA fragments and products of the 2-byte operand types (bf16, binary16)
+template <class T>
+struct Frag8;
+template <>
+struct Frag8<bf16> {
+  using type = bf16x8;
+};
+template <>
+struct Frag8<f16> {
+  using type = f16x8;
+};
+FLUX_DEV f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+FLUX_DEV f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+FLUX_DEV f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+FLUX_DEV f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int BM, int BN, class Epi, class TIn>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const TIn* __restrict__ A,
                                                              int64_t lda,
-                                                             const bf16* __restrict__ W,
+                                                             const TIn* __restrict__ W,
                                                              int64_t ldw, int M, int N, int K,
                                                              int kw, int kdup, int n_half,
                                                              int tiles_n, Epi epi) {
+  using Frag = typename Frag8<TIn>::type;
   constexpr int WGM = 2, WGN = 2;                // 2 x 2 waves
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA tiles per wave
@@ -219,9 +246,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
   static_assert(LA >= 1 && LB >= 1, "tile too small");
   static_assert(!Epi::kPaired || (TN % 2 == 0), "SwiGLU needs gate/up tile pairs");
 
-  extern __shared__ __align__(16) bf16 smem[];
-  bf16* As = smem;                   // [2][BM][64]
-  bf16* Bs = smem + 2 * BM * kBK;    // [2][BN][64]
+  extern __shared__ __align__(16) char gen_lds[];
+  TIn* smem = reinterpret_cast<TIn*>(gen_lds);
+  TIn* As = smem;                   // [2][BM][64]
+  TIn* Bs = smem + 2 * BM * kBK;    // [2][BN][64]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -242,10 +270,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
   const int m0 = tm * BM, n0 = tn * BN;
 
   // per-thread global source pointers (row fixed over the K loop)
-  const bf16* a_src[LA];
+  const TIn* a_src[LA];
   bool a_ok[LA];
   int a_lds[LA];
-  const bf16* b_src[LB];
+  const TIn* b_src[LB];
   bool b_ok[LB];
   int b_lds[LB];
   const int c8 = tid & 7;
@@ -286,8 +314,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
       rb[i] = (b_ok[i] && kin) ? ld16(b_src[i] + kb) : make_uint4(0, 0, 0, 0);
   };
   auto store_slice = [&](int buf) {
-    bf16* as = As + buf * BM * kBK;
-    bf16* bs = Bs + buf * BN * kBK;
+    TIn* as = As + buf * BM * kBK;
+    TIn* bs = Bs + buf * BN * kBK;
 #pragma unroll
     for (int i = 0; i < LA; ++i) st16(as + a_lds[i], ra[i]);
 #pragma unroll
@@ -312,26 +340,26 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16* __restr
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load_slice((kt + 1) * kBK);
-    const bf16* as = As + cur * BM * kBK;
-    const bf16* bs = Bs + cur * BN * kBK;
+    const TIn* as = As + cur * BM * kBK;
+    const TIn* bs = Bs + cur * BN * kBK;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 af[TM], bfr[TN];
+      Frag af[TM], bfr[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * WTM + i * 32 + lrow;
-        af[i] = *reinterpret_cast<const bf16x8*>(as + swz(r, kk * 2 + lk));
+        af[i] = *reinterpret_cast<const Frag*>(as + swz(r, kk * 2 + lk));
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int r = wn * WTN + j * 32 + lrow;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + swz(r, kk * 2 + lk));
+        bfr[j] = *reinterpret_cast<const Frag*>(bs + swz(r, kk * 2 + lk));
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
     }
     if (kt + 1 < nk) store_slice(cur ^ 1);
     __syncthreads();
@@ -432,7 +460,8 @@ struct Swz {
 typedef uint8_t fp8;  // OCP E4M3 byte
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-// Body of the large-tile kernels.  TIn = bf16 (MFMA 32x32x16 or 16x16x32, MI = 32 / 16) or
+// Body of the large-tile kernels.  TIn = bf16 / binary16 (MFMA 32x32x16 or 16x16x32,
+// MI = 32 / 16) or
 // fp8 (E4M3 bytes, MFMA 32x32x64 with unit block scales; the accumulators are multiplied by
 // the per-row scale sa[m] and the per-weight-row scale sw[n] before the epilogue).  Rows of
 // a K slice are 64 or 128 bytes either way, so the load plan, the LDS layout and the
@@ -575,7 +604,8 @@ FLUX_DEV void gemm_lds_body(const GemmSeg<TIn, Epi>& s0, const GemmSeg<TIn, Epi>
     return MI == 32 ? i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3) : i * 16 + 4 * lk + r;
   };
   auto acc_col = [&](int j) { return j * MI + lrow; };
-  using Frag = typename std::conditional<F8, v8i, bf16x8>::type;
+  using Frag = typename std::conditional<F8, v8i, typename Frag8<
+      typename std::conditional<F8, bf16, TIn>::type>::type>::type;
   Frag fr[2][NF];  // [set][A fragments | B fragments]
   auto rd = [&](int set, int q, int sl, int kk) {  // fragment q of k-step kk of slice sl
     const TIn* ob = q < TM ? smem + (sl % ST) * BM * BK
@@ -588,7 +618,7 @@ FLUX_DEV void gemm_lds_body(const GemmSeg<TIn, Epi>& s0, const GemmSeg<TIn, Epi>
       fr[set][q] = Frag{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     } else {
-      fr[set][q] = *reinterpret_cast<const bf16x8*>(ob + S::off(row, kk * (64 / MI) + lk));
+      fr[set][q] = *reinterpret_cast<const Frag*>(ob + S::off(row, kk * (64 / MI) + lk));
     }
   };
 
@@ -597,9 +627,9 @@ FLUX_DEV void gemm_lds_body(const GemmSeg<TIn, Epi>& s0, const GemmSeg<TIn, Epi>
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           fr[set][i], fr[set][TM + j], acc[i][j], 0, 0, 0, 127, 0, 127);
     else if constexpr (MI == 32)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[set][i], fr[set][TM + j], acc[i][j], 0, 0, 0);
+      acc[i][j] = mfma32x32x16(fr[set][i], fr[set][TM + j], acc[i][j]);
     else
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[set][i], fr[set][TM + j], acc[i][j], 0, 0, 0);
+      acc[i][j] = mfma16x16x32(fr[set][i], fr[set][TM + j], acc[i][j]);
   };
 
   // prologue: fill the stages, wait for slice 0, read its first fragments.  Symmetric: ST
@@ -874,12 +904,13 @@ FLUX_DEV void gemm_lds_body(const GemmSeg<TIn, Epi>& s0, const GemmSeg<TIn, Epi>
   }
 }
 
-template <int BM, int BN, int BK, int ST, int STW, int MI, int OCC, int NWM, int NWN, class Epi>
+template <int BM, int BN, int BK, int ST, int STW, int MI, int OCC, int NWM, int NWN, class Epi,
+          class TIn>
 __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_bf16_lds_kernel(
-    GemmSeg<bf16, Epi> s0, GemmSeg<bf16, Epi> s1, int tiles0, int64_t lda, int64_t ldw, int N,
+    GemmSeg<TIn, Epi> s0, GemmSeg<TIn, Epi> s1, int tiles0, int64_t lda, int64_t ldw, int N,
     int K, int kw, int kdup, int n_half, int tiles_n, int full_tiles, int splits,
     float* __restrict__ partial) {
-  gemm_lds_body<bf16, BM, BN, BK, ST, STW, MI, NWM, NWN, Epi>(s0, s1, tiles0, lda, ldw, N, K, kw,
+  gemm_lds_body<TIn, BM, BN, BK, ST, STW, MI, NWM, NWN, Epi>(s0, s1, tiles0, lda, ldw, N, K, kw,
                                                               kdup, n_half, tiles_n, full_tiles,
                                                               splits, partial, nullptr, nullptr);
 }
@@ -1016,11 +1047,12 @@ static hipError_t ensure_lds_limit(LdsLimit& st, const void* fn, size_t bytes) {
 
 // Launch one large-tile configuration (sets the dynamic LDS limit once per instance) over
 // the products seg[0 .. nseg) (nseg 1 or 2; segment 1 may have no rows).
-template <int BM, int BN, int BK, int ST, int STW, int MI, int OCC, int NWM, int NWN, class Epi>
-static hipError_t launch_lds(const GemmSeg<bf16, Epi>* seg, int nseg, int64_t lda, int64_t ldw,
+template <int BM, int BN, int BK, int ST, int STW, int MI, int OCC, int NWM, int NWN, class Epi,
+          class TIn>
+static hipError_t launch_lds(const GemmSeg<TIn, Epi>* seg, int nseg, int64_t lda, int64_t ldw,
                              int N, int K, int kw, int kdup, int n_half, int splits,
                              float* partial, hipStream_t s) {
-  GemmSeg<bf16, Epi> g0 = seg[0], g1 = nseg > 1 ? seg[1] : seg[0];
+  GemmSeg<TIn, Epi> g0 = seg[0], g1 = nseg > 1 ? seg[1] : seg[0];
   const int tiles_n = (N + BN - 1) / BN;
   g0.tiles_m = (g0.M + BM - 1) / BM;
   g1.tiles_m = (g1.M + BM - 1) / BM;
@@ -1031,21 +1063,22 @@ static hipError_t launch_lds(const GemmSeg<bf16, Epi>* seg, int nseg, int64_t ld
   const int full = tiles - tail;
   if (tail == 0) splits = 1;
   if ((size_t)tail * splits * BM * BN * sizeof(float) > kSplitkBytes) return hipErrorInvalidValue;
-  const size_t lds = (size_t)(ST * BM + STW * BN) * BK * sizeof(bf16);
+  const size_t lds = (size_t)(ST * BM + STW * BN) * BK * sizeof(TIn);
   static LdsLimit limit;
   hipError_t le = ensure_lds_limit(
       limit,
-      reinterpret_cast<const void*>(&gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, MI, OCC, NWM, NWN, Epi>),
+      reinterpret_cast<const void*>(
+          &gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, MI, OCC, NWM, NWN, Epi, TIn>),
       lds);
   if (le != hipSuccess) return le;
-  hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, MI, OCC, NWM, NWN, Epi>),
+  hipLaunchKernelGGL((gemm_bf16_lds_kernel<BM, BN, BK, ST, STW, MI, OCC, NWM, NWN, Epi, TIn>),
                      dim3(full + tail * splits), dim3(64 * NWM * NWN), lds, s, g0, g1, tiles0, lda,
                      ldw, N, K, kw, kdup, n_half, tiles_n, full, splits, partial);
   if (tail > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int chunks = Epi::kPaired ? BM * BN / 8 / 256 : BM * BN / 4 / 256;
-    hipLaunchKernelGGL((splitk_reduce_kernel<BM, BN, Epi, bf16>), dim3(tail, chunks), dim3(256),
+    hipLaunchKernelGGL((splitk_reduce_kernel<BM, BN, Epi, TIn>), dim3(tail, chunks), dim3(256),
                        0, s, partial, splits, full, g0, g1, tiles0, tiles_n, N, n_half);
   }
   return hipGetLastError();
@@ -1216,9 +1249,9 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
     if (K % kBK == 0 && off32) {
       int best, best_split;
       pick_tile(M, N, K, kBK, 1.0, split_ws != nullptr, best, best_split, M1 > 0 ? M1 : 0);
-      const GemmSeg<bf16, Epi> seg[2] = {
-          {static_cast<const bf16*>(A), static_cast<const bf16*>(W), M, 0, epi},
-          {static_cast<const bf16*>(M1 > 0 ? A1 : A), static_cast<const bf16*>(M1 > 0 ? W1 : W),
+      const GemmSeg<T, Epi> seg[2] = {
+          {static_cast<const T*>(A), static_cast<const T*>(W), M, 0, epi},
+          {static_cast<const T*>(M1 > 0 ? A1 : A), static_cast<const T*>(M1 > 0 ? W1 : W),
            M1 > 0 ? M1 : M, 0, M1 > 0 ? *epi1 : epi}};
       const int nseg = M1 > 0 ? 2 : 1;
       if (best == 0)
@@ -1239,9 +1272,9 @@ static hipError_t launch(const void* A, int64_t lda, const void* W, int64_t ldw,
   if constexpr (sizeof(T) == 2) {
     constexpr int BM = 128, BN = 128;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const size_t lds = 2 * (BM + BN) * kBK * sizeof(bf16);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi>), dim3(tiles_m * tiles_n), dim3(kThreads),
-                       lds, s, static_cast<const bf16*>(A), lda, static_cast<const bf16*>(W), ldw,
+    const size_t lds = 2 * (BM + BN) * kBK * sizeof(T);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi, T>), dim3(tiles_m * tiles_n), dim3(kThreads),
+                       lds, s, static_cast<const T*>(A), lda, static_cast<const T*>(W), ldw,
                        M, N, K, kw, kdup, n_half, tiles_n, epi);
   } else {
     if (kdup) return hipErrorInvalidValue;  // hi / lo operands are a bf16-path feature
@@ -1305,9 +1338,11 @@ static hipError_t linear_t(const LinearArgs& a, const LinearArgs* b, hipStream_t
     case EPI_GATED_RESIDUAL:
       return gated<T>(a, b, s);
     case EPI_QKV:
+      // q | k and V^T feed the attention: fp32 for fp32 operands, else bf16
       return launch_args<T>(a, b, 0, [](const LinearArgs& q) {
-        EpiQKV<T> epi{static_cast<T*>(q.y), q.ldy, static_cast<T*>(q.vt), q.ldvt,
-                      2 * q.dim, q.dim, q.rows_per_batch, q.vt_off};
+        using TQ = typename std::conditional<sizeof(T) == 4, float, bf16>::type;
+        EpiQKV<TQ> epi{static_cast<TQ*>(q.y), q.ldy, static_cast<TQ*>(q.vt), q.ldvt,
+                       2 * q.dim, q.dim, q.rows_per_batch, q.vt_off};
         epi.set_vec();
         return epi;
       }, s);
@@ -1403,6 +1438,7 @@ hipError_t linear_static_scratch(float** ptr, size_t* bytes) {
 }
 
 hipError_t linear(int dtype, const LinearArgs& a, hipStream_t s) {
+  if (dtype == DT_F16) return linear_t<f16>(a, nullptr, s);
   return dtype == DT_BF16 ? linear_t<bf16>(a, nullptr, s) : linear_t<float>(a, nullptr, s);
 }
 
@@ -1416,6 +1452,7 @@ hipError_t linear_pair(int dtype, const LinearArgs& a, const LinearArgs& b, hipS
     if (e != hipSuccess) return e;
     return linear(dtype, b, s);
   }
+  if (dtype == DT_F16) return linear_t<f16>(a, &b, s);
   return dtype == DT_BF16 ? linear_t<bf16>(a, &b, s) : linear_t<float>(a, &b, s);
 }
 

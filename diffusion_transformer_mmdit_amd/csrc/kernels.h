@@ -50,7 +50,8 @@ size_t linear_splitk_bytes();
 // array, the one flux_linear_noalloc uses; resolved once per device.
 hipError_t linear_static_scratch(float** ptr, size_t* bytes);
 
-// y = x W^T with epilogue; dtype = type of x and W (DT_BF16 -> MFMA path).
+// y = x W^T with epilogue; dtype = type of x and W (DT_BF16 / DT_F16 -> MFMA path; with
+// DT_F16 the SwiGLU output is binary16 and the QKV outputs stay bf16).
 hipError_t linear(int dtype, const LinearArgs& a, hipStream_t s);
 // Two independent products with the same epilogue kind, n, k, operand strides and dtypes
 // (the double block's image and text streams) in one launch: b's tiles follow a's, so a
@@ -122,9 +123,10 @@ struct KvExtra {
   int64_t ld_vt;
   int n, nb;
 };
+// o_dtype: storage type of O (-1: dtype; bf16 operands may write DT_F16 instead)
 hipError_t attention(int dtype, SeqView q, SeqView k, const void* vt, int64_t ld_vt, SeqView o,
                      int batch, int seq, int heads, float* split_ws, hipStream_t s,
-                     const KvExtra* extra = nullptr);
+                     const KvExtra* extra = nullptr, int o_dtype = -1);
 size_t attention_split_bytes();
 
 // vt[(b * dim + f) * ld_vt + j] = v(b, j)[f] for j < seq

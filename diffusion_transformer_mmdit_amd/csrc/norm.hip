@@ -38,6 +38,10 @@ FLUX_DEV void store8<bf16>(bf16* p, const float* f) {
   st16(p, pack8(f));
 }
 template <>
+FLUX_DEV void store8<f16>(f16* p, const float* f) {
+  st16(p, pack8_as<f16>(f));
+}
+template <>
 FLUX_DEV void store8<float>(float* p, const float* f) {
   *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
@@ -91,7 +95,7 @@ FLUX_DEV void store_cw(T* p, const float* f) {
   if constexpr (CW == 8) {
     store8(p, f);
   } else if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(pack2(f[0], f[1]), pack2(f[2], f[3]));
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack2_as<T>(f[0], f[1]), pack2_as<T>(f[2], f[3]));
   } else {
     *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
   }
@@ -353,6 +357,10 @@ hipError_t layernorm_modulate(int x_dtype, int y_dtype, const void* x, int64_t l
                               int64_t ldy, int rows, int dim, int rpb, const float* shift,
                               const float* scale, int64_t mod_bs, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (y_dtype == DT_F16)  // binary16 outputs (the inputs of binary16 products)
+    return x_dtype == DT_BF16
+               ? ln_dispatch<bf16, f16>(x, ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps, s)
+               : ln_dispatch<float, f16>(x, ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps, s);
   if (x_dtype == DT_BF16)
     return y_dtype == DT_BF16
                ? ln_dispatch<bf16, bf16>(x, ldx, y, ldy, rows, dim, rpb, shift, scale, mod_bs, eps, s)

@@ -17,8 +17,17 @@ LIB_PATH = os.path.join(_HERE, "libflux.so")
 
 FLUX_OK, FLUX_EINVAL, FLUX_ESHAPE, FLUX_EDTYPE, FLUX_EALIGN, FLUX_EWORKSPACE, FLUX_EHIP = (
     0, -1, -2, -3, -4, -5, -6)
-FLUX_BF16, FLUX_F32 = 0, 1
-FLUX_PRECISION_BF16, FLUX_PRECISION_SPLIT = 0, 1
+FLUX_BF16, FLUX_F32, FLUX_F16 = 0, 1, 2
+FLUX_PRECISION_BF16, FLUX_PRECISION_SPLIT, FLUX_PRECISION_F16 = 0, 1, 2
+
+# Weights that FLUX_PRECISION_F16 takes in binary16: the block linears (a double block's
+# qkv, out, mlp_in, mlp_out per stream; a single block's linear1, linear2), named by the
+# last component of a weight's dotted name.
+BLOCK_LINEARS = ("qkv", "out", "mlp_in", "mlp_out", "linear1", "linear2")
+
+
+def is_block_linear(name: str) -> bool:
+    return name.rsplit(".", 1)[-1] in BLOCK_LINEARS
 FLUX_EPI_STORE, FLUX_EPI_SWIGLU, FLUX_EPI_GATED_RESIDUAL = 0, 1, 2
 
 STATUS_NAMES = {0: "FLUX_OK", -1: "FLUX_EINVAL", -2: "FLUX_ESHAPE", -3: "FLUX_EDTYPE",

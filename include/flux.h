@@ -52,7 +52,9 @@ typedef enum {
   FLUX_EHIP = -6        /* HIP runtime error while enqueuing                         */
 } flux_status;
 
-typedef enum { FLUX_BF16 = 0, FLUX_F32 = 1 } flux_dtype;
+/* FLUX_F16 (IEEE binary16) is never a cfg->dtype: it is the storage of the block linears'
+ * operands under FLUX_PRECISION_F16 (below). */
+typedef enum { FLUX_BF16 = 0, FLUX_F32 = 1, FLUX_F16 = 2 } flux_dtype;
 
 /* Operand precision of the bf16 path (flux_cfg.precision).
  *   FLUX_PRECISION_BF16  every MFMA operand is stored in bf16 (fp32 accumulation).
@@ -65,15 +67,34 @@ typedef enum { FLUX_BF16 = 0, FLUX_F32 = 1 } flux_dtype;
  *                        Klein-9B step (D 4096) the bf16 rounding of these two operands is
  *                        amplified more than any other; carrying them removes most of the
  *                        step's error against the exact forward.
- * Both modes project the step's final LayerNorm output as a hi + lo pair.  FLUX_F32
- * workloads take FLUX_PRECISION_BF16 only (their operands are fp32 already). */
-typedef enum { FLUX_PRECISION_BF16 = 0, FLUX_PRECISION_SPLIT = 1 } flux_precision;
+ *   FLUX_PRECISION_F16   the operands of the block linears are IEEE binary16 (fp16 MFMA,
+ *                        fp32 accumulation): the LayerNorm + modulate outputs, the
+ *                        attention output and the SwiGLU outputs are stored in binary16,
+ *                        and the block linears' weights (double blocks: qkv, out, mlp_in,
+ *                        mlp_out; single blocks: linear1, linear2) must be given in
+ *                        binary16 (the caller converts the bf16 weights once: exact for
+ *                        |w| in [2^-14, 65504], an absolute error of at most 2^-25 below).
+ *                        Binary16 keeps 3 more mantissa bits than bf16, so these roundings
+ *                        shrink 8x at the same MFMA rate; values must stay below 65504 in
+ *                        magnitude.  q / k / v, the attention probabilities, the
+ *                        embedders, the modulation and the output head stay bf16.
+ * Every mode projects the step's final LayerNorm output as a hi + lo pair.  FLUX_F32
+ * workloads take FLUX_PRECISION_BF16 only (their operands are fp32 already).
+ * The operation-level entry points follow the block: under FLUX_PRECISION_F16,
+ * flux_layernorm_modulate writes binary16, flux_attention writes a binary16 O, and
+ * flux_linear takes binary16 x and w (a SwiGLU y in binary16). */
+typedef enum {
+  FLUX_PRECISION_BF16 = 0,
+  FLUX_PRECISION_SPLIT = 1,
+  FLUX_PRECISION_F16 = 2
+} flux_precision;
 
 /* Model hyper-parameters ([DIFF] 模型配置参数全解; [KLEIN] config table).
  * head_dim must be 128; dim = heads * head_dim; axes_dim are the per-axis RoPE widths
  * (even, summing to head_dim; the pages use 32,32,32,32); rope_theta 2000; eps 1e-6.
  * in_channels / context_dim / n_double / n_single are used by the step only.
- * FLUX_PRECISION_SPLIT needs dtype FLUX_BF16 and mlp_hidden a multiple of 64. */
+ * FLUX_PRECISION_SPLIT needs dtype FLUX_BF16 and mlp_hidden a multiple of 64;
+ * FLUX_PRECISION_F16 needs dtype FLUX_BF16. */
 typedef struct {
   int32_t dim;
   int32_t heads;

@@ -23,7 +23,7 @@ def torch():
 
 def dt(dtype: str):
     t = torch()
-    return t.bfloat16 if dtype == "bf16" else t.float32
+    return {"bf16": t.bfloat16, "f16": t.float16}.get(dtype, t.float32)
 
 
 def dev(a, dtype: str | None = None):
@@ -41,6 +41,17 @@ def upload_weights(w: dict, dtype: str) -> dict:
     for k, v in w.items():
         out[k] = dev(v, "f32" if k.endswith("_norm") else dtype)
     return out
+
+
+def for_precision(w_dev: dict, precision: int) -> dict:
+    """The device weights a precision mode takes: under FLUX_PRECISION_F16 the block
+    linears converted to binary16 (exact for the bf16 values in binary16's normal range),
+    the rest unchanged."""
+    from diffusion_transformer_mmdit_amd import flux as F
+    if precision != F.FLUX_PRECISION_F16:
+        return w_dev
+    t = torch()
+    return {k: (v.to(t.float16) if F.is_block_linear(k) else v) for k, v in w_dev.items()}
 
 
 def host(x) -> np.ndarray:
@@ -117,7 +128,7 @@ def run_double_block(wl: fs.Workload, inp: dict, w_dev: dict | None = None, prec
     from diffusion_transformer_mmdit_amd import flux as F
     t = torch()
     cfg = cfg_for(wl, precision)
-    w_dev = w_dev or upload_weights(inp["weights"], wl.dtype)
+    w_dev = for_precision(w_dev or upload_weights(inp["weights"], wl.dtype), precision)
     img, txt = dev(inp["img"], wl.dtype), dev(inp["txt"], wl.dtype)
     img_out, txt_out = t.empty_like(img), t.empty_like(txt)
     nbytes = F.flux_double_block_workspace_size(cfg, wl.batch, wl.n_img, wl.n_txt)
@@ -133,7 +144,7 @@ def run_single_block(wl: fs.Workload, inp: dict, w_dev: dict | None = None, prec
     from diffusion_transformer_mmdit_amd import flux as F
     t = torch()
     cfg = cfg_for(wl, precision)
-    w_dev = w_dev or upload_weights(inp["weights"], wl.dtype)
+    w_dev = for_precision(w_dev or upload_weights(inp["weights"], wl.dtype), precision)
     img, txt = dev(inp["img"], wl.dtype), dev(inp["txt"], wl.dtype)
     img_out, txt_out = t.empty_like(img), t.empty_like(txt)
     nbytes = F.flux_single_block_workspace_size(cfg, wl.batch, wl.n_img, wl.n_txt)
@@ -149,7 +160,7 @@ def run_step(wl: fs.Workload, inp: dict, w_dev: dict | None = None, precision: i
     from diffusion_transformer_mmdit_amd import flux as F
     t = torch()
     cfg = cfg_for(wl, precision)
-    w_dev = w_dev or upload_weights(inp["weights"], wl.dtype)
+    w_dev = for_precision(w_dev or upload_weights(inp["weights"], wl.dtype), precision)
     mw = F.ModelWeights(w_dev, wl.n_double, wl.n_single)
     out = t.empty((wl.batch, wl.n_img, wl.in_channels), dtype=t.float32, device="cuda")
     nbytes = F.flux_denoiser_step_workspace_size(cfg, wl.batch, wl.n_img, wl.n_txt)

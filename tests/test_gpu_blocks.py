@@ -59,7 +59,7 @@ def test_tiny_fp32_block(kind):
     check_block(kind, wl, inp, f"tiny fp32 {kind}")
 
 
-@pytest.mark.parametrize("precision", [0, 1])
+@pytest.mark.parametrize("precision", [0, 1, 2])
 @pytest.mark.parametrize("kind", ["single", "double"])
 # (1, 64): a one-token text stream; (300, 289): both streams' products in one launch with
 # several tiles each and ragged last tiles in both
@@ -94,15 +94,17 @@ def test_klein9b_double_block_1024():
     check_block("double", wl, inp, "Klein-9B double 1024^2")
 
 
+@pytest.mark.parametrize("precision", [1, 2])
 @pytest.mark.parametrize("kind,name", [("single", "klein4b_single_512"),
                                        ("double", "klein9b_double_1024")])
-def test_split_precision_block_full_shape(kind, name):
-    """FLUX_PRECISION_SPLIT (LayerNorm and SwiGLU outputs as bf16 hi + lo pairs) at the
-    Klein-4B single / Klein-9B double block shapes: the hi / lo products take other K extents
-    (2D, 2H, D + 2H) and the SwiGLU epilogue writes two planes."""
+def test_precise_modes_block_full_shape(kind, name, precision):
+    """FLUX_PRECISION_SPLIT (LayerNorm and SwiGLU outputs as bf16 hi + lo pairs: the hi / lo
+    products take other K extents, 2D, 2H, D + 2H, and the SwiGLU epilogue writes two planes)
+    and FLUX_PRECISION_F16 (binary16 operands of every block linear) at the Klein-4B single /
+    Klein-9B double block shapes."""
     wl = fs.workload(name)
     inp = fs.block_inputs(wl, kind=kind)
-    check_block(kind, wl, inp, f"{name} {kind} (split precision)", precision=1)
+    check_block(kind, wl, inp, f"{name} {kind} (precision {precision})", precision=precision)
 
 
 def test_klein9b_single_block_1024():

@@ -25,9 +25,15 @@ def F():
     return flux
 
 
-def cfg(D, dtype="bf16", H=None):
+def cfg(D, dtype="bf16", H=None, precision=0):
     f = F()
-    return f.make_cfg(D, D // 128, H or 3 * D, dtype=f.FLUX_BF16 if dtype == "bf16" else f.FLUX_F32)
+    return f.make_cfg(D, D // 128, H or 3 * D, dtype=f.FLUX_BF16 if dtype == "bf16" else f.FLUX_F32,
+                      precision=precision)
+
+
+# binary16 storage (FLUX_PRECISION_F16) moves a value by at most half an ulp: 2^-11 of its
+# magnitude in the normal range
+F16_HALF_ULP = 2.0 ** -11
 
 
 # ------------------------------------------------------------------------------------
@@ -123,6 +129,33 @@ def test_layernorm_modulate(D, rows, rpb, x_dtype, y_dtype):
         G.assert_op_close(G.host(y), ref, f"LN+mod D={D} rows={rows}")
     else:
         G.assert_close(G.host(y), ref, "f32", f"LN+mod D={D} rows={rows}")
+
+
+@pytest.mark.parametrize("D,rows,rpb,x_dtype", [
+    (256, 77, 7, "bf16"), (6144, 333, 111, "bf16"), (4096, 4608, 4608, "f32"),
+    (3072, 150, 75, "f32"), (6144, 222, 37, "f32"), (8192, 37, 37, "f32"), (4096, 9, 1, "f32")])
+def test_layernorm_modulate_f16_output(D, rows, rpb, x_dtype):
+    """FLUX_PRECISION_F16: the same LayerNorm + modulate stored in binary16 (every kernel
+    variant: fp32 rows per item, the split fp32 kernel at 6144 / 8192, bf16 rows)."""
+    t = G.torch()
+    seed = 11 + rows
+    B = -(-rows // rpb)
+    x = fs.normal(seed, "x", (rows, D), std=2.0, mean=0.5, dtype=x_dtype)
+    shift = fs.normal(seed, "shift", (B, D), std=0.3, dtype="f32")
+    scale = fs.normal(seed, "scale", (B, D), std=0.3, dtype="f32")
+    y = t.empty((rows, D), dtype=t.float16, device="cuda")
+    f = F()
+    f.flux_layernorm_modulate(cfg(D, precision=f.FLUX_PRECISION_F16), rows, rpb, G.dev(x, x_dtype),
+                              f.FLUX_BF16 if x_dtype == "bf16" else f.FLUX_F32, G.dev(shift),
+                              G.dev(scale), y, G.stream())
+    t.cuda.synchronize()
+    xp = np.zeros((B * rpb, D), np.float64)
+    xp[:rows] = x.astype(np.float64)
+    xp[rows:] = 1.0 + np.arange(D) / D
+    ref = O.layernorm_modulate(xp.reshape(B, rpb, D), shift.astype(np.float64),
+                               scale.astype(np.float64)).reshape(B * rpb, D)[:rows]
+    G.assert_op_close(G.host(y), ref, f"LN+mod D={D} rows={rows} -> binary16",
+                      rtol=F16_HALF_ULP, atol_rms=1e-4, nl2=1e-3)
 
 
 # ------------------------------------------------------------------------------------
@@ -274,6 +307,54 @@ def test_linear_gated_residual(m, n, k, dtype, use_ws):
         G.assert_close(G.host(rd)[rows], ref, dtype, f"linear+gated residual {m}x{n}x{k} (in place)")
 
 
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("m,n,k", [(77, 200, 136), (300, 390, 520), (1030, 2050, 320),
+                                   (513, 700, 192), (8192, 8192, 128), (4608, 12288, 4096)])
+def test_linear_f16_operands(m, n, k, use_ws):
+    """FLUX_PRECISION_F16 linears: binary16 x and W (fp16 MFMA, fp32 accumulation) with each
+    epilogue, against the exact product of the same binary16 operands: a store to fp32 (only
+    accumulation error remains) and to bf16, SwiGLU to binary16, a gated residual into bf16.
+    The small shapes take the generic kernel, the others the large-tile one (whole rounds and
+    a split-K tail)."""
+    t = G.torch()
+    f = F()
+    seed = 7 * m + n + k
+    x = fs.normal(seed, "x", (m, k), dtype="f32").astype(np.float16)
+    w = fs.normal(seed, "w", (n, k), std=0.02, dtype="f32").astype(np.float16)
+    xd, wd = G.dev(x), G.dev(w)
+    c = cfg(256, precision=f.FLUX_PRECISION_F16)
+    ws, nb = _lin_ws(use_ws)
+    rows = _sample_rows(m) if m * n * k > 2e9 else np.arange(m)
+    acc = O.linear(x[rows].astype(np.float64), w.astype(np.float64))
+    for ydt, yt in ((f.FLUX_F32, t.float32), (f.FLUX_BF16, t.bfloat16)):
+        y = t.empty((m, n), dtype=yt, device="cuda")
+        f.flux_linear(c, f.FLUX_EPI_STORE, m, n, k, xd, k, wd, k, y, n, ydt, workspace=ws,
+                      workspace_bytes=nb, stream=G.stream())
+        t.cuda.synchronize()
+        if ydt == f.FLUX_F32:
+            # fp32 accumulation only (the MFMA sums of exact products: within 2^-16 of
+            # sum |x w| per element, ~0.6e-3 of the RMS here; measured nL2 ~1e-5)
+            G.assert_op_close(G.host(y)[rows], acc, f"f16 linear {m}x{n}x{k} -> f32",
+                              rtol=2.0 ** -16, atol_rms=1e-3, nl2=1e-4)
+        else:
+            G.assert_op_close(G.host(y)[rows], acc, f"f16 linear {m}x{n}x{k} -> bf16")
+    ys = t.empty((m, n // 2), dtype=t.float16, device="cuda")
+    f.flux_linear(c, f.FLUX_EPI_SWIGLU, m, n, k, xd, k, wd, k, ys, n // 2, 0, workspace=ws,
+                  workspace_bytes=nb, stream=G.stream())
+    rpb = m // 2 if m % 2 == 0 else m
+    r = fs.normal(seed, "r", (m, n), dtype="bf16")
+    gate = fs.normal(seed, "gate", (m // rpb, n), std=0.5, dtype="f32")
+    rd = G.dev(r, "bf16")
+    f.flux_linear(c, f.FLUX_EPI_GATED_RESIDUAL, m, n, k, xd, k, wd, k, rd, n, f.FLUX_BF16,
+                  resid=rd, ldr=n, gate=G.dev(gate), rows_per_batch=rpb, workspace=ws,
+                  workspace_bytes=nb, stream=G.stream())
+    t.cuda.synchronize()
+    G.assert_op_close(G.host(ys)[rows], O.swiglu(acc), f"f16 linear+SwiGLU {m}x{n}x{k} -> binary16",
+                      rtol=F16_HALF_ULP, atol_rms=1e-4, nl2=1e-3)
+    ref = r[rows].astype(np.float64) + gate[rows // rpb].astype(np.float64) * acc
+    G.assert_op_close(G.host(rd)[rows], ref, f"f16 linear+gated residual {m}x{n}x{k}")
+
+
 # ------------------------------------------------------------------------------------
 # a6: joint attention
 # ------------------------------------------------------------------------------------
@@ -316,6 +397,46 @@ def test_attention(seq, heads, batch, dtype, n_q):
             p = O.attention_weights(q[b, rows, h], k[b, :, h])
             ref[b, :, h] = p @ v[b, :, h]
     G.assert_close(got[:, rows], ref.reshape(batch, len(rows), D), dtype, f"attention L={seq} h={heads}")
+
+
+@pytest.mark.parametrize("seq,heads,batch,n_q", [
+    (80, 2, 1, None), (200, 3, 2, None), (1100, 64, 1, 64), (1300, 24, 1, 64),
+    (4608, 32, 1, 48)])
+def test_attention_f16_output(seq, heads, batch, n_q):
+    """FLUX_PRECISION_F16: O stored in binary16 (whole units, and units split along the keys
+    whose merge writes O).  Against the oracle at the block bars, and against the bf16 O of
+    the same kernel: both round the same fp32 value, so they differ by at most the sum of the
+    two unit roundoffs (2^-8 + 2^-11 of |O|, plus half binary16's subnormal spacing)."""
+    t = G.torch()
+    f = F()
+    seed = seq + heads
+    D = heads * 128
+    ld = 3 * D
+    qkv = fs.normal(seed, "qkv", (batch, seq, ld), dtype="bf16")
+    xb = G.dev(qkv, "bf16")
+    outs = {}
+    for prec, odt in ((f.FLUX_PRECISION_BF16, t.bfloat16), (f.FLUX_PRECISION_F16, t.float16)):
+        c = cfg(D, precision=prec)
+        o = t.empty((batch, seq, D), dtype=odt, device="cuda")
+        nb = f.flux_attention_workspace_size(c, batch, seq)
+        ws = G.workspace(nb)
+        f.flux_attention(c, batch, seq, xb, xb[..., D:], xb[..., 2 * D:], ld, o, D, ws, nb,
+                         G.stream())
+        t.cuda.synchronize()
+        outs[prec] = G.host(o)
+    got, got_bf = outs[f.FLUX_PRECISION_F16], outs[f.FLUX_PRECISION_BF16]
+    bound = (2.0 ** -8 + 2.0 ** -11) * (1 + 2.0 ** -11) * np.abs(got) + 2.0 ** -25
+    assert (np.abs(got - got_bf) <= bound).all(), float((np.abs(got - got_bf) - bound).max())
+    q = qkv[..., :D].astype(np.float64).reshape(batch, seq, heads, 128)
+    k = qkv[..., D:2 * D].astype(np.float64).reshape(batch, seq, heads, 128)
+    v = qkv[..., 2 * D:].astype(np.float64).reshape(batch, seq, heads, 128)
+    rows = np.arange(seq) if n_q is None else _sample_rows(seq, n_q, seed)
+    ref = np.empty((batch, len(rows), heads, 128))
+    for b in range(batch):
+        for h in range(heads):
+            ref[b, :, h] = O.attention_weights(q[b, rows, h], k[b, :, h]) @ v[b, :, h]
+    G.assert_close(got[:, rows], ref.reshape(batch, len(rows), D), "bf16",
+                   f"attention L={seq} h={heads} -> binary16")
 
 
 def test_attention_equal_scores_give_mean():

@@ -47,7 +47,7 @@ def cache_views(wl, cache, B, Nr):
 def run_fill_and_cached(wl, inp, ref, rid, w_dev=None, precision=0):
     F, t = F_(), G.torch()
     cfg = G.cfg_for(wl, precision)
-    w_dev = w_dev or G.upload_weights(inp["weights"], wl.dtype)
+    w_dev = G.for_precision(w_dev or G.upload_weights(inp["weights"], wl.dtype), precision)
     mw = F.ModelWeights(w_dev, wl.n_double, wl.n_single)
     B, Nr = wl.batch, ref.shape[1]
     cb = F.flux_ref_cache_size(cfg, B, Nr)
@@ -122,15 +122,17 @@ def test_small_bf16_cache_and_cached_step(batch):
     check_against_oracle(small_bf16(batch), 2, 5, 7, "small bf16")
 
 
-def test_klein9b_width_cache_and_cached_step_split_precision():
+@pytest.mark.parametrize("precision", [1, 2])
+def test_klein9b_width_cache_and_cached_step_precise_modes(precision):
     """The reference cache and the cached step at the Klein-9B width (D 4096, 32 heads,
     MLP 12288; 2 + 2 blocks): one 6 x 8 reference (48 tokens, a partial extra key tile).  In
     FLUX_PRECISION_SPLIT: with bf16 LayerNorm outputs the reference rows' own pipeline error
     grows with the width (the linears' gain 0.02 sqrt(D) > 1), and at D 4096 the cached K of
     the third block exceeded the element-wise bound above by 2e-3 while the cached step met
-    3e-2 / 1e-2 (2.1e-2 / 4.1e-3)."""
+    3e-2 / 1e-2 (2.1e-2 / 4.1e-3).  Also in FLUX_PRECISION_F16 (binary16 LayerNorm outputs)."""
     from tests.test_gpu_sampler import klein9b_width
-    check_against_oracle(klein9b_width(seed=1014), 1, 6, 8, "Klein-9B width (split)", precision=1)
+    check_against_oracle(klein9b_width(seed=1014), 1, 6, 8, f"Klein-9B width (p{precision})",
+                         precision=precision)
 
 
 def run_denoise_refs(wl, inp, refs, n_steps, use_cache, sigmas=None, w_dev=None, lat=None):

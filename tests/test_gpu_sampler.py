@@ -60,7 +60,7 @@ def run_denoise(wl, inp, n_steps, sigmas=None, guidance=1.0, guided=False, w_dev
                 precision=0):
     F, t = F_(), G.torch()
     cfg = G.cfg_for(wl, precision)
-    w_dev = w_dev or G.upload_weights(inp["weights"], wl.dtype)
+    w_dev = G.for_precision(w_dev or G.upload_weights(inp["weights"], wl.dtype), precision)
     mw = F.ModelWeights(w_dev, wl.n_double, wl.n_single)
     B, C, H, W = inp["noise"].shape if lat is None else lat
     noise = inp["noise_dev"] if "noise_dev" in inp else G.dev(inp["noise"], "f32")
@@ -120,21 +120,25 @@ def klein9b_width(batch=1, seed=1013):
                        n_single=2, n_img=64, n_txt=32, t_fixed=None, batch=batch, seed=seed)
 
 
-def test_denoise_klein9b_width_guided_split_precision():
+@pytest.mark.parametrize("precision", [1, 2])
+def test_denoise_klein9b_width_guided_precise_modes(precision):
     """Three guided Euler steps at the Klein-9B width against the fp64 oracle's loop (the
     model input rounded to bf16 as the sampler stores it): the sampler kernels, the batch-2
     guided forward and the step's GEMM tiles at D 4096 together.  In FLUX_PRECISION_SPLIT,
     the mode that meets the bars against the exact forward at this width (the bf16 operand
     path measured max-abs 6.4e-2 / nL2 1.18e-2 here: guidance 3.5 scales the difference of
-    the two forwards' errors)."""
+    the two forwards' errors), and in FLUX_PRECISION_F16 (binary16 operands of the block
+    linears)."""
     wl = klein9b_width()
     inp = fs.sample_inputs(wl, 16, 16, with_uncond=True)
     sig = [1.0, 0.6, 0.25, 0.0]
-    print("[sampler] Klein-9B width (D 4096), 2 + 2 blocks, 3 guided steps, split", flush=True)
-    got = G.host(run_denoise(wl, inp, 3, sigmas=sig, guidance=3.5, guided=True, precision=1))
+    print(f"[sampler] Klein-9B width (D 4096), 2 + 2 blocks, 3 guided steps, precision "
+          f"{precision}", flush=True)
+    got = G.host(run_denoise(wl, inp, 3, sigmas=sig, guidance=3.5, guided=True,
+                             precision=precision))
     ref = O.denoise(inp["noise"], inp["ctx"], inp["weights"], sig, 2, 2,
                     ctx_uncond=inp["ctx_uncond"], guidance=3.5, model_input=O.bf16_storage)
-    G.assert_close(got, ref, "bf16", "Klein-9B width denoise (3 guided steps)")
+    G.assert_close(got, ref, "bf16", f"Klein-9B width denoise (3 guided steps, p{precision})")
 
 
 def test_denoise_guidance_with_equal_conditions_is_unguided():

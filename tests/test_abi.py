@@ -280,3 +280,42 @@ def test_status_codes_match_the_header():
                  "FLUX_EWORKSPACE", "FLUX_EHIP"):
         assert getattr(F, name) == vals[name], name
         assert name == "FLUX_OK" or vals[name] < 0
+
+
+def test_precision_constants_match_the_header():
+    src = open(HEADER).read()
+    for name in ("FLUX_BF16", "FLUX_F32", "FLUX_F16", "FLUX_PRECISION_BF16",
+                 "FLUX_PRECISION_SPLIT", "FLUX_PRECISION_F16"):
+        m = re.search(name + r"\s*=\s*(\d+)", src)
+        assert m and getattr(F, name) == int(m.group(1)), name
+
+
+def test_binary16_precision_workspace_and_rejections():
+    """FLUX_PRECISION_F16 stores 2-byte operands like bf16 (same workspaces); it needs the bf16
+    workload, and an unknown precision is refused."""
+    c = cfg9b()
+    c16 = cfg9b()
+    c16.precision = F.FLUX_PRECISION_F16
+    for fn in (F.flux_double_block_workspace_size, F.flux_single_block_workspace_size,
+               F.flux_denoiser_step_workspace_size):
+        assert fn(c16, 1, 4096, 512) == fn(c, 1, 4096, 512) > 0
+    bad = F.make_cfg(256, 2, 768, dtype=F.FLUX_F32, precision=F.FLUX_PRECISION_F16)
+    assert F.flux_single_block_workspace_size(bad, 1, 64, 16) == 0
+    assert "FLUX_PRECISION_F16" in F.flux_last_error()
+    bad = F.make_cfg(256, 2, 768, precision=3)
+    assert F.flux_double_block_workspace_size(bad, 1, 64, 16) == 0
+    assert "precision" in F.flux_last_error()
+
+
+def test_block_linear_names_are_the_block_weights():
+    """The weights FLUX_PRECISION_F16 takes in binary16 are exactly the block linears of the
+    step's weight set: every double / single block matrix except the modulation and the norm
+    scales, and none of the embedders, modulation or head."""
+    import flux_synth as fs
+    wl = fs.workload("klein9b_step_1024", n_double=2, n_single=2)
+    names = set(fs.step_weight_specs(wl))
+    got = {n for n in names if F.is_block_linear(n)}
+    want = {f"double.{i}.{s}.{m}" for i in range(2) for s in ("img", "txt")
+            for m in ("qkv", "out", "mlp_in", "mlp_out")}
+    want |= {f"single.{i}.{m}" for i in range(2) for m in ("linear1", "linear2")}
+    assert got == want

@@ -365,10 +365,12 @@ def generate_line(F, fs, wl) -> dict:
     (one batch-2 forward each), against the plain step; all on device-resident inputs."""
     import torch
     dtype = torch.bfloat16
-    w = device_weights(fs.step_weight_specs(wl), wl.seed, dtype)
+    # the benchmark's precision (binary16 block linears: the mode that meets the fp64 bars)
+    w = to_headline_precision(F, device_weights(fs.step_weight_specs(wl), wl.seed, dtype))
     mw = F.ModelWeights(w, wl.n_double, wl.n_single)
     cfg = F.make_cfg(wl.dim, wl.heads, wl.mlp_hidden, in_channels=wl.in_channels,
-                     context_dim=wl.context_dim, n_double=wl.n_double, n_single=wl.n_single)
+                     context_dim=wl.context_dim, n_double=wl.n_double, n_single=wl.n_single,
+                     precision=F.FLUX_PRECISION_F16)
     g = torch.Generator(device="cuda")
     g.manual_seed(wl.seed)
     lat = 2 * wl.grid
@@ -378,7 +380,8 @@ def generate_line(F, fs, wl) -> dict:
     unc = torch.randn((1, wl.n_txt, wl.context_dim), generator=g, device="cuda").to(dtype)
     out = torch.empty_like(noise)
     s = torch.cuda.current_stream()
-    res = {"workload": wl.name, "dtype": wl.dtype, "latent": [1, C, lat, lat], "n_txt": wl.n_txt}
+    res = {"workload": wl.name, "dtype": wl.dtype, "precision": "FLUX_PRECISION_F16",
+           "latent": [1, C, lat, lat], "n_txt": wl.n_txt}
     # the plain step on the same shapes
     x = torch.randn((1, wl.n_img, wl.in_channels), generator=g, device="cuda").to(dtype)
     t = torch.rand((1,), generator=g, device="cuda")
@@ -416,17 +419,18 @@ def edit_line(F, fs, wl) -> dict:
     sequence + reference keys) timed with the library's event hook."""
     import torch
     dtype = torch.bfloat16
-    w = device_weights(fs.step_weight_specs(wl), wl.seed, dtype)
+    w = to_headline_precision(F, device_weights(fs.step_weight_specs(wl), wl.seed, dtype))
     mw = F.ModelWeights(w, wl.n_double, wl.n_single)
     cfg = F.make_cfg(wl.dim, wl.heads, wl.mlp_hidden, in_channels=wl.in_channels,
-                     context_dim=wl.context_dim, n_double=wl.n_double, n_single=wl.n_single)
+                     context_dim=wl.context_dim, n_double=wl.n_double, n_single=wl.n_single,
+                     precision=F.FLUX_PRECISION_F16)
     g = torch.Generator(device="cuda")
     g.manual_seed(wl.seed)
     C = wl.in_channels // 4
     ctx = torch.randn((1, wl.n_txt, wl.context_dim), generator=g, device="cuda").to(dtype)
     s = torch.cuda.current_stream()
-    res = {"workload": wl.name, "dtype": wl.dtype, "n_steps": 4, "reference_side": 1024,
-           "cells": []}
+    res = {"workload": wl.name, "dtype": wl.dtype, "precision": "FLUX_PRECISION_F16", "n_steps": 4,
+           "reference_side": 1024, "cells": []}
     for n_refs, side in EDIT_CELLS:
         lat = side // 8                      # 8x VAE downsampling: latent side
         ref_lat = 1024 // 8
@@ -527,7 +531,10 @@ def per_config_line(F, fs, name: str) -> dict:
     fdt = F.FLUX_BF16 if wl.dtype == "bf16" else F.FLUX_F32
     D, H, B = wl.dim, wl.mlp_hidden, wl.batch
     Nt, Ni, L = wl.n_txt, wl.n_img, wl.seq
-    cfg = F.make_cfg(D, wl.heads, H, dtype=fdt)
+    # bf16 workloads in the benchmark's precision (binary16 block linears)
+    prec = F.FLUX_PRECISION_F16 if wl.dtype == "bf16" else F.FLUX_PRECISION_BF16
+    cfg = F.make_cfg(D, wl.heads, H, dtype=fdt, precision=prec)
+    conv = (lambda w: to_headline_precision(F, w)) if prec == F.FLUX_PRECISION_F16 else (lambda w: w)
     s = torch.cuda.current_stream()
     g = torch.Generator(device="cuda")
     g.manual_seed(wl.seed)
@@ -539,18 +546,19 @@ def per_config_line(F, fs, name: str) -> dict:
     img_o, txt_o = torch.empty_like(img), torch.empty_like(txt)
     kinds = {"single": ("single",), "double": ("double",), "step": ("double", "single"),
              "pair": ("double", "single")}[wl.kind]
-    res = {"workload": name, "dtype": wl.dtype, "dim": D, "heads": wl.heads, "mlp_hidden": H,
-           "n_txt": Nt, "n_img": Ni, "batch": B}
+    res = {"workload": name, "dtype": wl.dtype,
+           "precision": "FLUX_PRECISION_F16" if prec == F.FLUX_PRECISION_F16 else "FLUX_PRECISION_BF16",
+           "dim": D, "heads": wl.heads, "mlp_hidden": H, "n_txt": Nt, "n_img": Ni, "batch": B}
     for kind in kinds:
         if kind == "double":
-            w = device_weights(fs.double_block_weight_specs(D, H), wl.seed, dtype)
+            w = conv(device_weights(fs.double_block_weight_specs(D, H), wl.seed, dtype))
             nb = F.flux_double_block_workspace_size(cfg, B, Ni, Nt)
             ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
             bw = F.double_weights(w)
             fn = lambda: F.flux_double_block_fwd(cfg, bw, t, B, Ni, Nt, img, txt, img_ids, txt_ids,
                                                  img_o, txt_o, ws, nb, s)
         else:
-            w = device_weights(fs.single_block_weight_specs(D, H), wl.seed, dtype)
+            w = conv(device_weights(fs.single_block_weight_specs(D, H), wl.seed, dtype))
             nb = F.flux_single_block_workspace_size(cfg, B, Ni, Nt)
             ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
             bw = F.single_weights(w)
@@ -585,7 +593,9 @@ def bandwidth_kernels(F, fs, wl, cfg, t, txt_ids, img_ids, g, dtype, s):
     fns = []
     for _ in range(_sets_for(nbytes)):
         x32 = torch.randn((B * L, D), generator=g, device="cuda")
-        y = torch.empty((B * L, D), device="cuda", dtype=dtype)
+        # binary16 outputs under FLUX_PRECISION_F16 (the same bytes as bf16)
+        y = torch.empty((B * L, D), device="cuda",
+                        dtype=torch.float16 if cfg.precision == F.FLUX_PRECISION_F16 else dtype)
         fns.append(lambda x32=x32, y=y: F.flux_layernorm_modulate(cfg, B * L, L, x32, F.FLUX_F32,
                                                                   sh, sc, y, s))
     yield "ln_modulate", nbytes, fns

@@ -91,6 +91,16 @@ def bf16_storage(x) -> np.ndarray:
     return r.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+def f16_storage(x) -> np.ndarray:
+    """Value of x after it is computed in fp32 and stored as IEEE binary16 (round to nearest,
+    ties to even, at each step: fp64 -> fp32 -> binary16; beyond 65504 it overflows to inf),
+    returned as float64.  Used only through the `storage` argument, like bf16_storage.
+    """
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    with np.errstate(over="ignore"):
+        return x32.astype(np.float16).astype(np.float64)
+
+
 def _keep(x):
     return x
 

@@ -1,4 +1,5 @@
-"""Which bf16 rounding points decide the error of a bf16 denoiser step?  (CPU study)
+"""Which bf16 rounding points decide the error of a bf16 denoiser step, and what binary16
+storage at some of them does instead?  (CPU study)
 
 TEST INFRASTRUCTURE ONLY, like the rest of oracle/: it composes the oracle's own blocks.
 
@@ -15,6 +16,10 @@ A variant rounds values to bf16 at a subset of oracle.STORAGE_POINTS:
     all-X      every point except X (X carried exactly)
     all-X+Y    every point except X and Y
     only-X     X alone
+    f16-X+Y    X and Y rounded to IEEE binary16 instead, every other point to bf16 except the
+               final LayerNorm output, kept exact (the library's binary16 operand mode, whose
+               head carries that output as a bf16 hi + lo pair)
+    f16all-X+Y the same with the final LayerNorm output rounded like the other points
     none       no point (the exact step: error 0, a self-check)
 
 The weights are generated one block at a time and every variant advances through that
@@ -51,6 +56,11 @@ def variant_storage(name: str):
     pts = pts.split("+")
     if any(p not in O.STORAGE_POINTS for p in pts):
         raise ValueError(f"unknown point in variant {name!r}")
+    if kind in ("f16", "f16all"):
+        st = {p: (O.f16_storage if p in pts else O.bf16_storage) for p in O.STORAGE_POINTS}
+        if kind == "f16" and "final" not in pts:
+            del st["final"]
+        return st
     if kind == "all":
         return {p: O.bf16_storage for p in O.STORAGE_POINTS if p not in pts}
     if kind == "only":
@@ -117,7 +127,8 @@ def main(argv=None) -> int:
     print(f"|---|---|---|---|")
     for n in names[1:]:
         ma, nl = errors(out[n], ref)
-        pts = ", ".join(p for p in O.STORAGE_POINTS if p in stores[n]) or "-"
+        pts = ", ".join(p + (" (f16)" if stores[n][p] is O.f16_storage else "")
+                        for p in O.STORAGE_POINTS if p in stores[n]) or "-"
         print(f"| {n} | {pts} | {ma:.3e} | {nl:.3e} |", flush=True)
     return 0
 

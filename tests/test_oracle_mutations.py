@@ -305,3 +305,61 @@ def test_refkv_mutation_is_caught(name, monkeypatch):
             failed = True
             break
     assert failed, f"no pin caught mutation {name}"
+
+
+# ----------------------------------------------------------------------------------
+# Storage rounding: each planted mistake must fail a pin of tests/test_oracle_storage.py
+# ----------------------------------------------------------------------------------
+import tests.test_oracle_storage as stpins  # noqa: E402
+
+_orig_bf16 = O.bf16_storage
+
+
+def _mut_f16_truncates(x):
+    x16 = np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float16)
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    up = np.abs(x16.astype(np.float32)) > np.abs(x32)
+    x16 = np.where(up, np.nextafter(x16, np.float16(0)), x16)
+    return x16.astype(np.float64)
+
+
+def _mut_f16_is_bf16(x):
+    return _orig_bf16(x)
+
+
+def _mut_bf16_truncates(x):
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32)).view(np.uint32)
+    return (u & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+
+
+def _storage_pins():
+    pins = [stpins.test_f16_storage_matches_torch_conversion,
+            stpins.test_bf16_storage_matches_torch_conversion,
+            stpins.test_f16_storage_is_eight_times_finer_than_bf16]
+    for x, want in ((1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9), (65520.0, np.inf)):
+        pins.append(lambda x=x, want=want: stpins.test_f16_storage_worked_values(x, want))
+    for x, want in ((1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6), (1.0 / 3.0, 0.333984375)):
+        pins.append(lambda x=x, want=want: stpins.test_bf16_storage_worked_values(x, want))
+    return pins
+
+
+STORAGE_MUTATIONS = {
+    "f16_storage_truncates": ("f16_storage", _mut_f16_truncates),
+    "f16_storage_is_bf16": ("f16_storage", _mut_f16_is_bf16),
+    "bf16_storage_truncates": ("bf16_storage", _mut_bf16_truncates),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STORAGE_MUTATIONS))
+def test_storage_mutation_is_caught(name, monkeypatch):
+    attr, fn = STORAGE_MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for f in _storage_pins():
+        try:
+            with np.errstate(all="ignore"):
+                f()
+        except (AssertionError, ValueError):
+            failed.append(getattr(f, "__name__", "pin"))
+            break
+    assert failed, f"no pin caught mutation {name}"

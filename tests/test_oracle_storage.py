@@ -65,3 +65,39 @@ def test_storage_rounding_effect_is_bf16_sized(kind):
     rel = np.linalg.norm(rounded - exact) / np.linalg.norm(upd)
     # a few bf16 roundings (relative 2^-9 each) in the update's inputs
     assert 1e-4 < rel < 2e-2, rel
+
+
+def test_f16_storage_matches_torch_conversion():
+    import torch
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal(200_000) * np.exp(rng.uniform(-20, 10, 200_000))).astype(np.float64)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.f16_storage(x), ref)
+
+
+@pytest.mark.parametrize("x,want", [
+    (1.0, 1.0),
+    (1.0 + 2.0 ** -11, 1.0),                     # halfway, ties to the even neighbour 1.0
+    (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),     # halfway, ties to the even 1 + 2^-9
+    (1.0 / 3.0, 0.333251953125),
+    (65504.0, 65504.0),                          # the largest finite value
+    (65519.0, 65504.0),                          # below the halfway point to 2^16
+    (65520.0, np.inf),                           # halfway: overflows
+    (2.0 ** -25, 0.0),                           # half the subnormal spacing: ties to 0
+    (3 * 2.0 ** -25, 2.0 ** -23),                # ties to the even subnormal 2 * 2^-24
+])
+def test_f16_storage_worked_values(x, want):
+    assert O.f16_storage(np.array([x]))[0] == want
+
+
+def test_f16_storage_is_eight_times_finer_than_bf16():
+    """Relative rounding error of N(0, 1) values: unit roundoff 2^-11 for binary16 against
+    2^-8 for bf16, so the rms error ratio is close to 8."""
+    x = np.random.default_rng(7).standard_normal(400_000)
+    e16 = np.sqrt(np.mean(((O.f16_storage(x) - x) / x) ** 2))
+    eb = np.sqrt(np.mean(((O.bf16_storage(x) - x) / x) ** 2))
+    assert 7.0 < eb / e16 < 9.0, eb / e16
+    # in binary16's normal range the relative error is at most the unit roundoff (plus the
+    # fp32 step's 2^-24)
+    nrm = np.abs(x) >= 2.0 ** -14
+    assert np.abs((O.f16_storage(x[nrm]) - x[nrm]) / x[nrm]).max() <= 2.0 ** -11 + 2.0 ** -24

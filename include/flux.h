@@ -363,7 +363,7 @@ int flux_modulation(const flux_cfg* cfg, const flux_temb_weights* temb, const vo
 /* LayerNorm (no affine, eps = cfg->eps) + modulate (1 + scale) x_hat + shift, per row
  * ([DIFF] 双流块 AdaLN pre-norm).  x: device [rows, dim] of x_dtype (FLUX_BF16/FLUX_F32);
  * shift, scale: device float [batch, dim] where row r uses batch r / rows_per_batch;
- * y: device [rows, dim] of cfg->dtype. */
+ * y: device [rows, dim] of cfg->dtype (binary16 under FLUX_PRECISION_F16). */
 int flux_layernorm_modulate(const flux_cfg* cfg, int rows, int rows_per_batch, const void* x,
                             int x_dtype, const float* shift, const float* scale, void* y,
                             void* stream);
@@ -384,7 +384,8 @@ int flux_qk_norm_rope(const flux_cfg* cfg, int batch, int n_txt, int n_img, void
 /* Joint attention O = softmax(Q K^T / sqrt(head_dim)) V per head over the whole
  * sequence, no mask ([SDPA]; [TRACE] Joint multi-head attention).
  * q, k, v: device [batch, seq, ld_in] (cfg->dtype), head h at columns
- * [h*head_dim, (h+1)*head_dim); o: device [batch, seq, ld_out].  The workspace (size from
+ * [h*head_dim, (h+1)*head_dim); o: device [batch, seq, ld_out] (cfg->dtype; binary16 under
+ * FLUX_PRECISION_F16).  The workspace (size from
  * flux_attention_workspace_size) receives V transposed, the layout the kernel reads, and
  * the fp32 partial outputs of query blocks whose keys are split over several workgroups
  * (merged in a fixed order, so results are deterministic). */
@@ -397,11 +398,12 @@ int flux_attention(const flux_cfg* cfg, int batch, int seq, const void* q, const
  * 与 FFN):
  *   FLUX_EPI_STORE   y[m, n] = acc                                  (y: dtype y_dtype)
  *   FLUX_EPI_SWIGLU  W has 2*n_half rows [gate | up]; y[m, j] = silu(acc_gate) * acc_up
- *                    for j < n_half (pass n = 2*n_half)             (y: cfg->dtype)
+ *                    for j < n_half (pass n = 2*n_half)             (y: operand dtype)
  *   FLUX_EPI_GATED_RESIDUAL
  *                    y[m, n] = resid[m, n] + gate[m / rows_per_batch, n] * acc
  *                    (resid, y: dtype y_dtype; gate device float [batch, n])
- * x: device [m, ldx] (cfg->dtype); w: device [n, ldw] (cfg->dtype); k = reduction size. */
+ * x: device [m, ldx], w: device [n, ldw] of the operand dtype: cfg->dtype, or binary16 under
+ * FLUX_PRECISION_F16 (fp16 MFMA); k = reduction size. */
 typedef enum {
   FLUX_EPI_STORE = 0,
   FLUX_EPI_SWIGLU = 1,

@@ -117,7 +117,7 @@ def test_klein9b_step_1024_f16_precision_vs_fp64(klein9b_step):
     """The same whole-output parity with the block linears' operands in binary16
     (FLUX_PRECISION_F16: LayerNorm, attention and SwiGLU outputs and the block weights),
     which keeps bf16's MFMA rate; the oracle's storage study with these rounding points
-    (128 + 1024 tokens at D 4096) predicts max-abs 1.1e-2 / nL2 1.7e-3."""
+    (128 + 1024 tokens at D 4096) predicts max-abs 1.16e-2 / nL2 1.76e-3."""
     from diffusion_transformer_mmdit_amd import flux as F
     got = klein9b_step(F.FLUX_PRECISION_F16)
     G.assert_close(got, golden_9b(), "bf16", "Klein-9B 1024^2 step (binary16 precision) vs fp64")

@@ -126,26 +126,29 @@ def _sample(n, k, seed):
     return np.unique(np.concatenate([[0, n - 1], mid])).astype(np.int64)
 
 
+@pytest.mark.parametrize("precision", [0, 2])
 @pytest.mark.parametrize("kind", ["double", "single"])
-def test_dev_pair_block_2048_sampled_rows(kind):
+def test_dev_pair_block_2048_sampled_rows(kind, precision):
     """FLUX.2-dev shapes at 2048² (D 6144, 48 heads, 512 + 16384 tokens): the whole block
-    on the GPU, the oracle at sampled output rows (keys and values from every token)."""
+    on the GPU, the oracle at sampled output rows (keys and values from every token); bf16
+    operands and binary16 block-linear operands."""
     wl = fs.workload("dev_pair_2048")
     inp = fs.block_inputs(wl, kind=kind)
-    img, txt = run(kind, wl, inp)
+    img, txt = run(kind, wl, inp, precision)
     ri, rt = _sample(wl.n_img, 40, 11), _sample(wl.n_txt, 10, 12)
     fn = O.double_block_rows if kind == "double" else O.single_block_rows
     ref_img, ref_txt = fn(inp["img"], inp["txt"], inp["t"], inp["weights"], inp["img_ids"],
                           inp["txt_ids"], ri, rt)
     got_img, got_txt = G.host(img)[:, ri], G.host(txt)[:, rt]
-    G.assert_close(got_img, ref_img, wl.dtype, f"dev {kind} 2048^2 img rows")
-    G.assert_close(got_txt, ref_txt, wl.dtype, f"dev {kind} 2048^2 txt rows")
+    G.assert_close(got_img, ref_img, wl.dtype, f"dev {kind} 2048^2 img rows p{precision}")
+    G.assert_close(got_txt, ref_txt, wl.dtype, f"dev {kind} 2048^2 txt rows p{precision}")
     # the block's own update at those rows, against the rounding floor of the output
     d_got = got_img - inp["img"][:, ri].astype(np.float64)
     d_ref = ref_img - inp["img"][:, ri].astype(np.float64)
     _, nl = G.errors(d_got, d_ref)
     floor = np.linalg.norm(inp["img"][:, ri].astype(np.float64)) * 2.0 ** -9 / np.linalg.norm(d_ref)
-    print(f"[parity] dev {kind} img update at sampled rows: nL2={nl:.3e} (floor {floor:.1e})",
+    print(f"[parity] dev {kind} img update at sampled rows p{precision}: nL2={nl:.3e} "
+          f"(floor {floor:.1e})",
           flush=True)
     assert nl <= 2e-2 + 2 * floor, (nl, floor)
 
@@ -172,15 +175,16 @@ def test_zero_gate_block_is_bitwise_identity(kind, dtype):
     assert np.array_equal(G.host(txt), inp["txt"].astype(np.float64))
 
 
+@pytest.mark.parametrize("precision", [0, 2])
 @pytest.mark.parametrize("kind", ["single", "double"])
-def test_block_is_deterministic(kind):
+def test_block_is_deterministic(kind, precision):
     wl = fs.workload("tiny_single_f32", dtype="bf16", n_txt=64, n_img=256, t_fixed=None,
                      dim=512, heads=4, mlp_hidden=1536)
     inp = fs.block_inputs(wl, kind=kind)
     wd = G.upload_weights(inp["weights"], "bf16")
     fn = G.run_double_block if kind == "double" else G.run_single_block
-    a = fn(wl, inp, wd)
-    b = fn(wl, inp, wd)
+    a = fn(wl, inp, wd, precision=precision)
+    b = fn(wl, inp, wd, precision=precision)
     assert G.torch().equal(a[0], b[0]) and G.torch().equal(a[1], b[1])
 
 

@@ -759,9 +759,9 @@ def main(argv=None) -> int:
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     s = torch.cuda.current_stream()
 
-    def step():
+    def step(stream=s):
         F.flux_denoiser_step(cfg, mw, t, None, wl.batch, wl.n_img, wl.n_txt, x, ctx, img_ids,
-                             txt_ids, out, ws, nbytes, s)
+                             txt_ids, out, ws, nbytes, stream)
 
     for _ in range(args.warmup):
         step()
@@ -793,6 +793,27 @@ def main(argv=None) -> int:
     for r in sites:
         print(f"[bench]   {r['site']}: {r['avg_launch_us']} us, {r['achieved_tflops']} TFLOP/s "
               f"({100 * r['frac']:.1f}%)", file=sys.stderr, flush=True)
+    # the same step captured once into a HIP graph and replayed (no host launch work between
+    # kernels); the library enqueues only kernels, so the capture holds the whole step
+    step()
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(torch.cuda.current_stream())
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_equal = bool(torch.equal(out, eager_out))
+    ev.start()
+    for _ in range(args.steps):
+        graph.replay()
+    ms_graph = ev.stop_ms() / args.steps
+    torch.cuda.synchronize()
+    del graph, eager_out
+    graph_leg = {"steps": args.steps, "ms_per_step": round(ms_graph, 3),
+                 "time_vs_eager": round(ms_graph / ms, 4), "bitwise_equal_to_eager": graph_equal}
+    print(f"[bench] graph replay: {ms_graph:.2f} ms/step ({ms_graph / ms:.4f}x), output "
+          f"{'bitwise equal' if graph_equal else 'DIFFERENT'}", file=sys.stderr, flush=True)
     del ws, w16
     torch.cuda.empty_cache()
     mw_bf16 = F.ModelWeights(w, wl.n_double, wl.n_single)
@@ -869,6 +890,7 @@ def main(argv=None) -> int:
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "kernels": sites,
+        "graph_replay": graph_leg,
         "precision_bf16": bf16,
         "precision_split": split,
         "cpu_baseline": cpu,

@@ -146,7 +146,9 @@ extern "C" int flux_timing_end(int* launches, double* mean_us) {
 // validation helpers
 // ------------------------------------------------------------------------------------
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-static int esize(int dtype) { return dtype == FLUX_BF16 ? 2 : 4; }
+// the kernels take the public dtype codes as they are (DT_BF16, DT_F32, DT_F16 in common.h)
+static_assert(FLUX_BF16 == 0 && FLUX_F32 == 1 && FLUX_F16 == 2, "dtype codes of the kernels");
+static int esize(int dtype) { return dtype == FLUX_F32 ? 4 : 2; }
 
 static int check_cfg(const flux_cfg* c) {
   if (!c) return fail(FLUX_EINVAL, "cfg is NULL");

@@ -74,3 +74,30 @@ def test_site_table_and_split_flops():
     extra = 8 * 2.0 * 4608 * (3 * 4096 ** 2 + 2 * 12288 * 4096 + 12288 * 4096) + \
         24 * 2.0 * 4608 * ((3 * 4096 + 2 * 12288) * 4096 + 12288 * 4096) + 2.0 * 4096 * 4096 * 128
     assert bench.split_mfma_flops(wl) == pytest.approx(bench.step_flops(wl) + extra)
+
+
+def test_headline_precision_converts_exactly_the_block_linears():
+    """The benchmark's FLUX_PRECISION_F16 weight set: the block linears in binary16 (the same
+    values as the bf16 weights), everything else untouched (the same tensors)."""
+    import torch
+    from diffusion_transformer_mmdit_amd import flux as F
+    wl = fs.workload("tiny_single_f32", kind="step", dtype="bf16", dim=256, heads=2,
+                     mlp_hidden=768, in_channels=64, context_dim=32, n_double=1, n_single=1)
+    g = torch.Generator().manual_seed(3)
+    w = {name: (0.02 * torch.randn(shape, generator=g)).to(torch.bfloat16) if kind == "w"
+         else torch.ones(shape) for name, (shape, kind) in fs.step_weight_specs(wl).items()}
+    w16 = bench.to_headline_precision(F, w)
+    assert set(w16) == set(w)
+    for name, v in w.items():
+        if F.is_block_linear(name):
+            assert w16[name].dtype == torch.float16, name
+            # bf16 values in binary16's normal range convert exactly; below 2^-14 (its
+            # subnormals) the error is at most half the subnormal spacing, 2^-25
+            a, b = w16[name].double(), v.double()
+            nrm = b.abs() >= 2.0 ** -14
+            assert torch.equal(a[nrm], b[nrm]), name
+            assert (a - b).abs().max().item() <= 2.0 ** -25, name
+        else:
+            assert w16[name] is v, name
+    # one double block (4 linears per stream, 2 streams) and one single block (2 linears)
+    assert sum(F.is_block_linear(n) for n in w) == 8 + 2

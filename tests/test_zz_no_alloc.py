@@ -20,12 +20,14 @@ def _gpu():
     F.lib()
 
 
-def _run(noalloc: bool, epi_name: str, m: int, n: int, k: int, seed: int):
+def _run(noalloc: bool, epi_name: str, m: int, n: int, k: int, seed: int, precision: int = 0):
     from diffusion_transformer_mmdit_amd import flux as F
     t = G.torch()
-    cfg = F.make_cfg(256, 2, 768)
-    x = G.dev(fs.normal(seed, "x", (m, k), dtype="bf16"), "bf16")
-    w = G.dev(fs.normal(seed, "w", (n, k), std=0.02, dtype="bf16"), "bf16")
+    cfg = F.make_cfg(256, 2, 768, precision=precision)
+    # operands: bf16, or binary16 under FLUX_PRECISION_F16 (the SwiGLU output too)
+    op = "f16" if precision == F.FLUX_PRECISION_F16 else "bf16"
+    x = G.dev(fs.normal(seed, "x", (m, k), dtype="bf16"), op)
+    w = G.dev(fs.normal(seed, "w", (n, k), std=0.02, dtype="bf16"), op)
     epi = getattr(F, f"FLUX_EPI_{epi_name}")
     kw = {}
     if epi_name == "GATED_RESIDUAL":
@@ -36,13 +38,14 @@ def _run(noalloc: bool, epi_name: str, m: int, n: int, k: int, seed: int):
         kw = dict(resid=r, ldr=n, gate=gate, rows_per_batch=rpb)
         ldy, y_dt = n, F.FLUX_BF16
     elif epi_name == "SWIGLU":
-        y = t.empty((m, n // 2), dtype=t.bfloat16, device="cuda")
+        y = t.empty((m, n // 2), dtype=G.dt(op), device="cuda")
         ldy, y_dt = n // 2, F.FLUX_BF16
     else:
         y = t.empty((m, n), dtype=t.float32, device="cuda")
         ldy, y_dt = n, F.FLUX_F32
     y.fill_(float("nan"))
-    print(f"[no-alloc] {'noalloc' if noalloc else 'workspace'} {epi_name} {m}x{n}x{k}", flush=True)
+    print(f"[no-alloc] {'noalloc' if noalloc else 'workspace'} {epi_name} {m}x{n}x{k} {op}",
+          flush=True)
     if noalloc:
         F.flux_linear_noalloc(cfg, epi, m, n, k, x, k, w, k, y, ldy, y_dt, stream=G.stream(), **kw)
     else:
@@ -62,11 +65,12 @@ CASES = [("GATED_RESIDUAL", 4608, 4096, 16384), ("STORE", 1536, 3072, 12288),
          ("SWIGLU", 1536, 2 * 9216, 3072)]
 
 
-def test_linear_noalloc_matches_linear_with_workspace_on_calls_in_a_row():
+@pytest.mark.parametrize("precision", [0, 2])
+def test_linear_noalloc_matches_linear_with_workspace_on_calls_in_a_row(precision):
     for epi_name, m, n, k in CASES:
         seed = m + n + k
-        got = _run(True, epi_name, m, n, k, seed)
-        ref = _run(False, epi_name, m, n, k, seed)
+        got = _run(True, epi_name, m, n, k, seed, precision)
+        ref = _run(False, epi_name, m, n, k, seed, precision)
         assert np.isfinite(got).all()
         ma, nl = G.errors(got, ref)
         print(f"[parity] flux_linear_noalloc {epi_name} {m}x{n}x{k} vs flux_linear: "

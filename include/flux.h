@@ -29,7 +29,8 @@
  *     activation / weight pointer and leading dimension must be 16-byte aligned.
  *   - Storage type: `dtype` FLUX_BF16 = bfloat16 (compute: bf16 MFMA, fp32 accumulate);
  *     FLUX_F32 = float32 everywhere (fp32 compute).  QK-norm scales, timesteps and
- *     modulation vectors are always float32.
+ *     modulation vectors are always float32.  With FLUX_BF16, `precision` (below) selects
+ *     how the block linears' operands are stored: bf16, bf16 hi + lo pairs, or binary16.
  */
 #ifndef FLUX_H
 #define FLUX_H
